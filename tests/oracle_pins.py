@@ -1,0 +1,603 @@
+"""Pins of the CPU oracle: checks against what the pages and mathematics fix.
+
+Each ``check_*`` function takes an ``oracle.Oracle`` and raises AssertionError
+when the oracle disagrees with a closed form, a library routine, a published
+value or brute force.  The regular tests run them on the committed oracle; the
+mutation test runs them on copies of the oracle with a planted mistake and
+requires that every planted mistake trips at least one of them.
+"""
+from __future__ import annotations
+
+import math
+import os
+
+import numpy as np
+import scipy.integrate as si
+import scipy.linalg as sl
+from scipy.stats import norm as _norm
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+D = 128
+
+
+def _read_rows(name):
+    rows = []
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                rows.append(line)
+    return rows
+
+
+# ---------------------------------------------------------------------------
+# binary16 conversions: numpy's float16 is IEEE binary16 with RNE
+# ---------------------------------------------------------------------------
+
+def check_half_to_double(o):
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ref = bits.view(np.float16).astype(np.float64)
+    got = o.half_to_double(bits)
+    fin = np.isfinite(ref)
+    assert np.array_equal(got[fin], ref[fin])
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    assert np.array_equal(got[np.isinf(ref)], ref[np.isinf(ref)])
+
+
+def check_double_to_half(o, n=20000, seed=3):
+    rng = np.random.default_rng(seed)
+    # values spread over the whole binary16 range, plus exact ties
+    mags = np.exp(rng.uniform(np.log(1e-9), np.log(7e4), n))
+    x = mags * rng.choice([-1.0, 1.0], n)
+    h = np.arange(0, 0x7bff, 7, dtype=np.uint16)
+    lo = h.view(np.float16).astype(np.float64)
+    hi = (h + 1).view(np.float16).astype(np.float64)
+    ties = (lo + hi) / 2.0           # exactly half-way: must round to even
+    edge = np.array([65504.0, 65519.99, 65520.0, 1e6, 2.0 ** -24, 2.0 ** -25,
+                     3 * 2.0 ** -26, 2.0 ** -14 - 2.0 ** -26, -0.0, 0.0])
+    xs = np.concatenate([x, ties, -ties, edge])
+    ref = xs.astype(np.float16).view(np.uint16)
+    got = o.double_to_half(xs)
+    assert np.array_equal(got, ref)
+
+
+# ---------------------------------------------------------------------------
+# SplitMix64 and the sign vector
+# ---------------------------------------------------------------------------
+
+def check_splitmix64(o):
+    for row in _read_rows("splitmix64_vectors.txt"):
+        seed, idx, hexv = row.split()
+        seq = o.splitmix64(int(seed), int(idx) + 1)
+        assert int(seq[int(idx)]) == int(hexv, 16), (seed, idx)
+
+
+def check_signs(o):
+    # sigma_i = -1 exactly when the top bit of the i-th output is set
+    for seed in (0, 1, 42, 2 ** 63 + 5):
+        seq = o.splitmix64(seed, D)
+        s = o.signs(seed, D)
+        assert np.array_equal(s, np.where(seq >> np.uint64(63), -1, 1).astype(np.int8))
+    # seed 0 from the published outputs: 0xe2.. and 0x6e.. and 0x06..
+    s0 = o.signs(0, D)
+    assert list(s0[:3]) == [-1, 1, 1]
+    assert "".join("-" if v < 0 else "+" for v in s0[:16]) == "-++-+++-+-+-----"
+    assert int((s0 < 0).sum()) == 63
+
+
+# ---------------------------------------------------------------------------
+# Hadamard matrix and rotation
+# ---------------------------------------------------------------------------
+
+def check_hadamard(o):
+    for d in (2, 4, 32, 128):
+        H = o.hadamard(d).astype(np.int64)
+        assert np.array_equal(H, sl.hadamard(d))            # Sylvester construction
+        assert np.array_equal(H @ H.T, d * np.eye(d, dtype=np.int64))
+
+
+def check_rotation_unit_vectors(o, bits=4, seed=7):
+    """x = sigma_k e_k has D x = e_k, so z = H e_k = column k of H: every z is
+    +-1 exactly and the codes are those of +-1."""
+    s = o.signs(seed, D)
+    H = sl.hadamard(D)
+    c, t = o.codebook(bits)
+    code_p = int(np.sum(t < 1.0))
+    code_m = int(np.sum(t < -1.0))
+    for k in (0, 1, 5, 64, 127):
+        x = np.zeros((1, D), dtype=np.float16)
+        x[0, k] = s[k]
+        packed, norms, z = o.encode(x, bits, seed, want_z=True)
+        assert norms[0] == 1.0
+        assert np.array_equal(z[0], H[:, k].astype(np.float64))
+        codes = o.unpack(packed[0], D, bits)
+        assert np.array_equal(codes, np.where(H[:, k] > 0, code_p, code_m))
+
+
+def check_rotation_norm(o, seed=11):
+    rng = np.random.default_rng(seed)
+    x = (rng.standard_normal((64, D)) * rng.uniform(0.01, 100, (64, 1))).astype(np.float16)
+    _, norms, z = o.encode(x, 4, 3, want_z=True)
+    ref = np.sqrt((x.astype(np.float64) ** 2).sum(1))
+    assert np.array_equal(norms, ref.astype(np.float32))    # double norm, nearest f32
+    # ||z||^2 = d: H D / sqrt(d) is orthogonal
+    assert np.allclose((z ** 2).sum(1), D, rtol=0, atol=1e-10)
+    # z = H D x / ||x|| (library Hadamard, signs from the generator)
+    s = o.signs(3, D).astype(np.float64)
+    zr = (sl.hadamard(D) @ (s[:, None] * (x.astype(np.float64) / ref[:, None]).T)).T
+    assert np.allclose(z, zr, rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# Lloyd-Max codebook
+# ---------------------------------------------------------------------------
+
+def _cell_integrals(lo, hi):
+    mass = si.quad(_norm.pdf, lo, hi, epsabs=1e-14, epsrel=1e-13, limit=200)[0]
+    first = si.quad(lambda v: v * _norm.pdf(v), lo, hi, epsabs=1e-14, epsrel=1e-13,
+                    limit=200)[0]
+    return mass, first
+
+
+def check_codebook_closed_form_b1(o):
+    c, t = o.codebook(1)
+    assert abs(c[1] - math.sqrt(2 / math.pi)) < 1e-14 and c[0] == -c[1] and t[0] == 0.0
+    assert abs(o.codebook_distortion(1) - (1 - 2 / math.pi)) < 1e-14
+
+
+def check_codebook_structure(o):
+    for b in (2, 3, 4):
+        c, t = o.codebook(b)
+        L = 1 << b
+        assert np.all(np.diff(c) > 0)
+        assert np.array_equal(c, -c[::-1])                  # exactly symmetric
+        assert t[L // 2 - 1] == 0.0                        # middle threshold exactly 0
+        assert np.allclose(t, (c[:-1] + c[1:]) / 2, rtol=0, atol=1e-15)
+
+
+def check_codebook_centroids(o):
+    """Every level is the N(0,1) mean of its cell, by numerical integration."""
+    for b in (2, 3, 4):
+        c, t = o.codebook(b)
+        edges = np.concatenate([[-np.inf], t, [np.inf]])
+        for k in range(len(c)):
+            mass, first = _cell_integrals(edges[k], edges[k + 1])
+            assert abs(first / mass - c[k]) < 1e-9, (b, k)
+
+
+def check_codebook_distortion(o):
+    """Distortion by numerical integration of (x - q(x))^2 against N(0,1)."""
+    for b in (2, 3, 4):
+        c, t = o.codebook(b)
+        edges = np.concatenate([[-np.inf], t, [np.inf]])
+        tot = 0.0
+        for k in range(len(c)):
+            tot += si.quad(lambda v, ck=c[k]: (v - ck) ** 2 * _norm.pdf(v), edges[k],
+                           edges[k + 1], epsabs=1e-15, epsrel=1e-13, limit=200)[0]
+        assert abs(tot - o.codebook_distortion(b)) < 1e-10, b
+
+
+def check_codebook_textbook(o):
+    """Max (1960), Table I."""
+    for row in _read_rows("lloyd_max_gaussian.txt"):
+        f = row.split()
+        L, kind, vals = int(f[0]), f[1], [float(v) for v in f[2:]]
+        b = L.bit_length() - 1
+        c, t = o.codebook(b)
+        if kind == "level":
+            assert np.allclose(c[L // 2:], vals, rtol=0, atol=6e-4), (L, c[L // 2:])
+        elif kind == "threshold":
+            assert np.allclose(t[L // 2:], vals, rtol=0, atol=6e-4), (L, t[L // 2:])
+        else:
+            assert abs(o.codebook_distortion(b) / vals[0] - 1) < 5e-4, (L, kind)
+
+
+def check_codebook_is_local_minimum(o):
+    """Moving any one level or threshold raises the (integrated) distortion."""
+    b = 3
+    c, t = o.codebook(b)
+
+    def dist(cc, tt):
+        edges = np.concatenate([[-np.inf], tt, [np.inf]])
+        return sum(si.quad(lambda v, ck=cc[k]: (v - ck) ** 2 * _norm.pdf(v), edges[k],
+                           edges[k + 1], epsabs=1e-15, epsrel=1e-13)[0]
+                   for k in range(len(cc)))
+
+    base = dist(c, t)
+    for k in range(len(c)):
+        for eps in (1e-3, -1e-3):
+            cc = c.copy()
+            cc[k] += eps
+            assert dist(cc, t) > base
+    for k in range(len(t)):
+        for eps in (1e-3, -1e-3):
+            tt = t.copy()
+            tt[k] += eps
+            assert dist(c, tt) > base
+
+
+# ---------------------------------------------------------------------------
+# scalar quantizer
+# ---------------------------------------------------------------------------
+
+def check_quantizer_bruteforce(o, seed=5):
+    rng = np.random.default_rng(seed)
+    for b in (2, 3, 4):
+        c, t = o.codebook(b)
+        z = np.concatenate([np.linspace(-4, 4, 4001), rng.standard_normal(3000) * 2])
+        got = o.quantize_many(z, b)
+        # nearest level, first one on a tie (brute force over all levels)
+        ref = np.argmin(np.abs(z[:, None] - c[None, :]), axis=1)
+        assert np.array_equal(got, ref), b
+
+
+def check_quantizer_special_points(o):
+    for b in (2, 3, 4):
+        c, t = o.codebook(b)
+        L = 1 << b
+        assert np.array_equal(o.quantize_many(c, b), np.arange(L))        # z = c_k -> k
+        assert np.array_equal(o.quantize_many(t, b), np.arange(L - 1))    # tie -> lower
+        assert np.array_equal(o.quantize_many(np.nextafter(t, np.inf), b), np.arange(1, L))
+        assert list(o.quantize_many([0.0, -0.0], b)) == [L // 2 - 1] * 2
+        assert list(o.quantize_many([-1e9, 1e9], b)) == [0, L - 1]
+
+
+# ---------------------------------------------------------------------------
+# packing
+# ---------------------------------------------------------------------------
+
+def check_pack_vectors(o):
+    for row in _read_rows("pack_vectors.txt"):
+        bits_s, codes_s, bytes_s = [p.strip() for p in row.split(";")]
+        bits = int(bits_s)
+        codes = np.array([int(v) for v in codes_s.split()], dtype=np.uint8)
+        want = np.array([int(v, 16) for v in bytes_s.split()], dtype=np.uint8)
+        assert np.array_equal(o.pack(codes, bits), want), row
+        assert np.array_equal(o.unpack(want, len(codes), bits), codes), row
+
+
+def check_pack_roundtrip(o, seed=9):
+    rng = np.random.default_rng(seed)
+    for b in (2, 3, 4):
+        P = D * b // 8
+        for _ in range(20):
+            codes = rng.integers(0, 1 << b, D).astype(np.uint8)
+            p = o.pack(codes, b)
+            assert p.shape == (P,)
+            assert np.array_equal(o.unpack(p, D, b), codes)
+            raw = rng.integers(0, 256, P).astype(np.uint8)     # every byte string is valid
+            assert np.array_equal(o.pack(o.unpack(raw, D, b), b), raw)
+
+
+def check_sizes(o):
+    for b, P in ((2, 32), (3, 48), (4, 64)):
+        assert o.packed_bytes(D, b) == P
+    # 256 B of fp16 against P + 4 B (codes + f32 norm): 3.76x at 4 bits, 7.11x at 2 bits
+    assert round(256 / (64 + 4), 2) == 3.76 and round(256 / (32 + 4), 1) == 7.1
+
+
+# ---------------------------------------------------------------------------
+# round-trip MSE against the exact value for d = 128
+# ---------------------------------------------------------------------------
+
+def exact_mse_d(b: int, c, t, d: int = D) -> float:
+    """E[(z - q(z))^2] where z = sqrt(d) * (coordinate of a uniform unit vector):
+    density proportional to (1 - z^2/d)^((d-3)/2) on [-sqrt(d), sqrt(d)]."""
+    r = math.sqrt(d)
+    logc = math.lgamma(d / 2) - math.lgamma((d - 1) / 2) - 0.5 * math.log(math.pi * d)
+    pdf = lambda z: math.exp(logc + (d - 3) / 2 * math.log1p(-(z * z) / d))
+    edges = np.concatenate([[-r], t, [r]])
+    return sum(si.quad(lambda z, ck=c[k]: (z - ck) ** 2 * pdf(z), edges[k], edges[k + 1],
+                       epsabs=1e-15, epsrel=1e-12, limit=200)[0] for k in range(len(c)))
+
+
+GAUSS_D = {2: 0.1175, 3: 0.03455, 4: 0.009497}   # Max (1960) distortions
+
+
+def check_mse(o, n=50000, seed=21):
+    """Round trip on N(0,1) vectors: the per-coordinate MSE ||x - xhat||^2/||x||^2
+    equals the exact d=128 value (within Monte-Carlo error), is within 2% of the
+    Gaussian Lloyd-Max distortion, and within 2.7x of the 4^-b lower bound."""
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((n, D)).astype(np.float16)
+    xd = x.astype(np.float64)
+    for b in (2, 3, 4):
+        c, t = o.codebook(b)
+        packed, norms = o.encode(x, b, 1)
+        _, xh = o.decode(packed, norms, D, b, 1, want_f64=True)
+        mse = float(np.mean(((xd - xh) ** 2).sum(1) / (xd ** 2).sum(1)))
+        ex = exact_mse_d(b, c, t)
+        assert abs(mse / ex - 1) < 3e-3, (b, mse, ex)
+        assert abs(mse / GAUSS_D[b] - 1) < 0.02, (b, mse)
+        assert mse < 2.7 * 4.0 ** -b
+
+
+def check_z_distribution(o, seed=23):
+    """After the rotation, coordinates look N(0,1) (the pages' 'each coordinate
+    ~N(0, 1/d)', in units of the unit vector times sqrt(d)), and outlier
+    channels are spread over all coordinates."""
+    rng = np.random.default_rng(seed)
+    # iid Laplace input (far from Gaussian per channel): rotated coordinates
+    # have exactly unit mean square and Gaussian-like quantiles
+    x = rng.laplace(size=(4000, D))
+    _, _, z = o.encode(x.astype(np.float16), 4, 0, want_z=True)
+    zz = z.ravel()
+    assert abs(zz.mean()) < 0.01 and abs(np.mean(zz ** 2) - 1) < 1e-12
+    q = np.quantile(zz, [0.025, 0.5, 0.975])
+    assert np.allclose(q, [-1.96, 0.0, 1.96], atol=0.05)
+    # two x20 outlier channels: before rotation they reach ~6-11 in these
+    # units; after it no coordinate carries much more than its share
+    x = rng.standard_normal((4000, D))
+    x[:, [7, 93]] *= 20
+    xf = x.astype(np.float16).astype(np.float64)
+    u = np.sqrt(D) * xf / np.linalg.norm(xf, axis=1, keepdims=True)
+    _, _, z = o.encode(x.astype(np.float16), 4, 0, want_z=True)
+    assert np.abs(u).max() > 9 and np.abs(z).max() < 4.5
+
+
+# ---------------------------------------------------------------------------
+# invariants of encode
+# ---------------------------------------------------------------------------
+
+def check_scale_invariance(o, seed=31):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((256, D))
+    x = np.where(np.abs(x) < 0.05, np.copysign(0.05, x), x)   # keep 2^-3 x normal in fp16
+    x = x.astype(np.float16)
+    for b in (2, 3, 4):
+        p0, n0 = o.encode(x, b, 5)
+        for k in (-3, -1, 2, 4):
+            xs = (x.astype(np.float64) * 2.0 ** k).astype(np.float16)
+            assert np.array_equal(xs.astype(np.float64), x.astype(np.float64) * 2.0 ** k)
+            p, n = o.encode(xs, b, 5)
+            assert np.array_equal(p, p0)
+            assert np.array_equal(n, (n0.astype(np.float64) * 2.0 ** k).astype(np.float32))
+
+
+def check_negation(o, seed=37):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((256, D)).astype(np.float16)
+    for b in (2, 3, 4):
+        L = 1 << b
+        _, t = o.codebook(b)
+        p0, _, z = o.encode(x, b, 5, want_z=True)
+        p1, _ = o.encode(-x, b, 5)
+        on_thr = np.isin(z, t) | np.isin(-z, t)
+        for v in range(x.shape[0]):
+            c0 = o.unpack(p0[v], D, b).astype(int)
+            c1 = o.unpack(p1[v], D, b).astype(int)
+            ok = (c1 == L - 1 - c0) | on_thr[v]
+            assert ok.all()
+
+
+def check_zero_vector(o):
+    x = np.zeros((3, D), dtype=np.float16)
+    x[1] = -0.0
+    for b in (2, 3, 4):
+        L = 1 << b
+        p, n = o.encode(x, b, 9)
+        assert np.all(n == 0)
+        for v in range(3):
+            assert np.all(o.unpack(p[v], D, b) == L // 2 - 1)
+        y = o.decode(p, n, D, b, 9)
+        assert np.all(y.astype(np.float64) == 0)
+
+
+def check_reencode_fixed_point(o, seed=41):
+    """Build x = fp16(D H c[code] / d) from codes drawn with the Gaussian cell
+    probabilities; re-encoding it returns the same codes."""
+    rng = np.random.default_rng(seed)
+    H = sl.hadamard(D).astype(np.float64)
+    for b in (2, 3, 4):
+        c, t = o.codebook(b)
+        s = o.signs(13, D).astype(np.float64)
+        edges = np.concatenate([[-np.inf], t, [np.inf]])
+        prob = np.diff(_norm.cdf(edges))
+        done = 0
+        while done < 20:
+            code = rng.choice(len(c), size=D, p=prob)
+            if not (0.85 <= np.mean(c[code] ** 2) <= 1.2):
+                continue
+            x = (s * (H @ c[code]) / D).astype(np.float16)[None, :]
+            p, _ = o.encode(x, b, 13)
+            assert np.array_equal(o.unpack(p[0], D, b), code.astype(np.uint8)), b
+            done += 1
+
+
+def check_decode_definition(o, seed=43):
+    """Decode of hand-made codes: xhat = n * D * H * c[code] / d, with the
+    library Hadamard; the fp16 output is that value rounded to nearest-even."""
+    rng = np.random.default_rng(seed)
+    H = sl.hadamard(D).astype(np.float64)
+    for b in (2, 3, 4):
+        c, _ = o.codebook(b)
+        s = o.signs(17, D).astype(np.float64)
+        codes = rng.integers(0, 1 << b, (8, D)).astype(np.uint8)
+        packed = np.stack([o.pack(cc, b) for cc in codes])
+        norms = rng.uniform(0.5, 50, 8).astype(np.float32)
+        y, yf = o.decode(packed, norms, D, b, 17, want_f64=True)
+        ref = norms[:, None].astype(np.float64) * s[None, :] * (c[codes] @ H.T) / D
+        assert np.allclose(yf, ref, rtol=1e-13, atol=1e-12)
+        assert np.array_equal(y, yf.astype(np.float16))
+
+
+# ---------------------------------------------------------------------------
+# paged decode attention
+# ---------------------------------------------------------------------------
+
+def small_attn_case(o, B=2, Hq=8, Hkv=2, T=37, bs=16, bits=4, seed=51, ragged=True):
+    from kv_cache_vector_amd import workloads as w
+    wl = w.attn_workload(batch=B, num_q_heads=Hq, num_kv_heads=Hkv, context=T,
+                         block_size=bs, seed=seed, perm_seed=seed + 1, ragged=ragged,
+                         extra_blocks=3)
+    kp, kn = o.encode(wl["k"], bits, 0)
+    vp, vn = o.encode(wl["v"], bits, 0)
+    wl.update(kp=kp, kn=kn, vp=vp, vn=vn, bits=bits)
+    return wl
+
+
+def _attn(o, wl, q=None, cl=None, bt=None, kp=None, kn=None, vp=None, vn=None, scale=None):
+    q = wl["q"] if q is None else q
+    return o.attn_decode(q, wl["kp"] if kp is None else kp, wl["kn"] if kn is None else kn,
+                         wl["vp"] if vp is None else vp, wl["vn"] if vn is None else vn,
+                         wl["block_tables"] if bt is None else bt,
+                         wl["context_lens"] if cl is None else cl, wl["num_kv_heads"],
+                         wl["bits"], 0, 1 / math.sqrt(D) if scale is None else scale,
+                         want_f64=True)
+
+
+def _dequant_rows(o, wl, which, b, g):
+    """Decoded (double) rows of sequence b, kv head g, in token order."""
+    bs = wl["block_size"]
+    T = int(wl["context_lens"][b])
+    P = D * wl["bits"] // 8
+    pk = wl["kp" if which == "k" else "vp"]
+    nm = wl["kn" if which == "k" else "vn"]
+    rows_p = np.zeros((T, P), np.uint8)
+    rows_n = np.zeros(T, np.float32)
+    for j in range(T):
+        blk = wl["block_tables"][b, j // bs]
+        rows_p[j] = pk[blk, j % bs, g]
+        rows_n[j] = nm[blk, j % bs, g]
+    _, xh = o.decode(rows_p, rows_n, D, wl["bits"], 0, want_f64=True)
+    return xh
+
+
+def check_attn_rotated_domain_identity(o):
+    """Score and accumulate in the rotated domain (q rotated once, K and V
+    used as codebook values, one inverse rotation at the end) -- the fused
+    path the pages describe -- equals the plain definition."""
+    H = sl.hadamard(D).astype(np.float64)
+    for bits in (4, 3, 2):
+        wl = small_attn_case(o, bits=bits)
+        _, of = _attn(o, wl)
+        c, _ = o.codebook(bits)
+        s = o.signs(0, D).astype(np.float64)
+        B, Hq, _ = wl["q"].shape
+        grp = Hq // wl["num_kv_heads"]
+        bs = wl["block_size"]
+        for b in range(B):
+            T = int(wl["context_lens"][b])
+            for h in range(Hq):
+                g = h // grp
+                qt = H @ (s * wl["q"][b, h].astype(np.float64))         # rotate q once
+                sc = np.zeros(T)
+                vacc = np.zeros((T, D))
+                for j in range(T):
+                    blk = wl["block_tables"][b, j // bs]
+                    kc = c[o.unpack(wl["kp"][blk, j % bs, g], D, bits)]
+                    vc = c[o.unpack(wl["vp"][blk, j % bs, g], D, bits)]
+                    sc[j] = (1 / math.sqrt(D)) * float(wl["kn"][blk, j % bs, g]) / D * (qt @ kc)
+                    vacc[j] = float(wl["vn"][blk, j % bs, g]) * vc
+                p = np.exp(sc - sc.max())
+                acc = (p[:, None] * vacc).sum(0) / p.sum()
+                ref = s * (H @ acc) / D                                   # rotate back once
+                assert np.allclose(of[b, h], ref, rtol=0, atol=1e-10), (bits, b, h)
+
+
+def check_attn_special_cases(o):
+    wl = small_attn_case(o, B=4, T=40)
+    B, Hq, _ = wl["q"].shape
+    grp = Hq // wl["num_kv_heads"]
+    # context_len = 1: the output is the decoded first value row
+    cl1 = np.ones(B, np.int32)
+    wl1 = dict(wl, context_lens=cl1)
+    y, yf = _attn(o, wl1, cl=cl1)
+    for b in range(B):
+        for h in range(Hq):
+            v0 = _dequant_rows(o, wl1, "v", b, h // grp)[0]
+            assert np.allclose(yf[b, h], v0, rtol=0, atol=1e-12)
+            assert np.array_equal(y[b, h], v0.astype(np.float16))
+    # q = 0: uniform softmax, the output is the mean of the decoded values
+    _, yf = _attn(o, wl, q=np.zeros_like(wl["q"]))
+    for b in range(B):
+        for h in range(Hq):
+            vm = _dequant_rows(o, wl, "v", b, h // grp).mean(0)
+            assert np.allclose(yf[b, h], vm, rtol=0, atol=1e-12)
+    # all keys equal (every K row encodes the same vector): mean of V again
+    kp = np.broadcast_to(wl["kp"][0, 0, 0], wl["kp"].shape).copy()
+    kn = np.full_like(wl["kn"], wl["kn"][0, 0, 0])
+    _, yf = _attn(o, wl, kp=kp, kn=kn)
+    for b in range(B):
+        for h in range(Hq):
+            vm = _dequant_rows(o, wl, "v", b, h // grp).mean(0)
+            assert np.allclose(yf[b, h], vm, rtol=0, atol=1e-12)
+    # context_len = 0: zeros
+    cl0 = np.zeros(B, np.int32)
+    y, yf = _attn(o, wl, cl=cl0)
+    assert np.all(yf == 0) and np.all(y.astype(np.float64) == 0)
+
+
+def check_attn_paging_invariance(o, seed=61):
+    """Moving physical blocks (and the block table with them) and changing
+    cache rows beyond context_len leave the output unchanged."""
+    rng = np.random.default_rng(seed)
+    wl = small_attn_case(o, B=3, T=45)
+    y0, _ = _attn(o, wl)
+    nblk = wl["kp"].shape[0]
+    perm = rng.permutation(nblk)            # new physical position of every block
+    inv = np.argsort(perm)
+    kp, kn, vp, vn = (a[inv] for a in (wl["kp"], wl["kn"], wl["vp"], wl["vn"]))
+    bt = perm[wl["block_tables"]].astype(np.int32)
+    y1, _ = _attn(o, wl, bt=bt, kp=kp, kn=kn, vp=vp, vn=vn)
+    assert np.array_equal(y0, y1)
+    # garbage after the last valid token of every sequence
+    kp2, vp2, kn2 = wl["kp"].copy(), wl["vp"].copy(), wl["kn"].copy()
+    bs = wl["block_size"]
+    for b in range(3):
+        T = int(wl["context_lens"][b])
+        for j in range(T, wl["block_tables"].shape[1] * bs):
+            blk = wl["block_tables"][b, j // bs]
+            kp2[blk, j % bs] = rng.integers(0, 256, kp2.shape[2:])
+            vp2[blk, j % bs] = rng.integers(0, 256, vp2.shape[2:])
+            kn2[blk, j % bs] = 1e3
+    y2, _ = _attn(o, wl, kp=kp2, kn=kn2, vp=vp2)
+    assert np.array_equal(y0, y2)
+
+
+def check_attn_bruteforce_tiny(o):
+    """B=1, T=3, one kv head: softmax written out by hand on decoded rows."""
+    wl = small_attn_case(o, B=1, Hq=2, Hkv=1, T=3, ragged=False)
+    _, yf = _attn(o, wl)
+    K = _dequant_rows(o, wl, "k", 0, 0)
+    V = _dequant_rows(o, wl, "v", 0, 0)
+    for h in range(2):
+        q = wl["q"][0, h].astype(np.float64)
+        s0, s1, s2 = (float(q @ K[j]) / math.sqrt(D) for j in range(3))
+        m = max(s0, s1, s2)
+        e0, e1, e2 = math.exp(s0 - m), math.exp(s1 - m), math.exp(s2 - m)
+        ref = (e0 * V[0] + e1 * V[1] + e2 * V[2]) / (e0 + e1 + e2)
+        assert np.allclose(yf[0, h], ref, rtol=0, atol=1e-12)
+
+
+def check_attn_gqa_grouping(o):
+    """Query heads h and h' of the same kv group with the same query give
+    the same output; the group of head h is h // (Hq/Hkv)."""
+    wl = small_attn_case(o, B=1, Hq=8, Hkv=2, T=30, ragged=False)
+    q = wl["q"].copy()
+    q[0, 1] = q[0, 0]
+    q[0, 4] = q[0, 0]
+    y, _ = _attn(o, wl, q=q)
+    assert np.array_equal(y[0, 0], y[0, 1])
+    assert not np.array_equal(y[0, 0], y[0, 4])     # head 4 belongs to kv head 1
+    # swapping the two kv heads' cache content swaps the groups' outputs
+    sw = lambda a: a[:, :, ::-1].copy()
+    q2 = q.copy()
+    q2[0, 4:] = q[0, :4]
+    q2[0, :4] = q[0, 4:]
+    y2, _ = _attn(o, wl, q=q2, kp=sw(wl["kp"]), kn=sw(wl["kn"]), vp=sw(wl["vp"]),
+                  vn=sw(wl["vn"]))
+    assert np.array_equal(y2[0, 4:], y[0, :4]) and np.array_equal(y2[0, :4], y[0, 4:])
+
+
+ALL_CHECKS = [
+    check_half_to_double, check_double_to_half, check_splitmix64, check_signs,
+    check_hadamard, check_rotation_unit_vectors, check_rotation_norm,
+    check_codebook_closed_form_b1, check_codebook_structure, check_codebook_centroids,
+    check_codebook_distortion, check_codebook_textbook, check_codebook_is_local_minimum,
+    check_quantizer_bruteforce, check_quantizer_special_points, check_pack_vectors,
+    check_pack_roundtrip, check_sizes, check_mse, check_z_distribution,
+    check_scale_invariance, check_negation, check_zero_vector, check_reencode_fixed_point,
+    check_decode_definition, check_attn_rotated_domain_identity, check_attn_special_cases,
+    check_attn_paging_invariance, check_attn_bruteforce_tiny, check_attn_gqa_grouping,
+]
