@@ -1,0 +1,279 @@
+// libtq: the C ABI declared in include/tq.h.
+//
+// Host side only: argument checks, the Lloyd-Max codebook and the sign mask
+// (both computed here, on the host, and handed to the kernels by value), and
+// the kernel launches.  The library allocates no device memory.
+#include "tq.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <mutex>
+
+#include "tq_internal.h"
+
+namespace {
+
+using tq::CodecConsts;
+
+constexpr int kD = tq::kHeadDim;
+
+// ---------------------------------------------------------------------------
+// Lloyd-Max quantizer of the standard normal (aither-kvcache PyPI page,
+// "Algorithm" step 3: a precomputed Lloyd-Max codebook; qbc.network blog,
+// "What TurboQuant is": the best fixed levels for a bell curve).
+//
+// The optimum is symmetric, so only the positive half is solved: interior
+// decision points 0 = b_0 < b_1 < ... < b_{h-1} < b_h = inf, levels
+// p_j = E[X | b_j < X <= b_{h}] cell means.  This solver iterates on the
+// decision points in extended precision: each sweep computes the cell means
+// of the current points, then moves every interior point to the midpoint of
+// its two neighbouring means, until the points stop moving.
+// ---------------------------------------------------------------------------
+struct Codebook {
+    float level[16];
+    float thr[15];
+};
+
+long double upper_tail(long double t) {   // P(X > t)
+    return 0.5L * std::erfc(t / std::sqrt(2.0L));
+}
+
+long double density(long double t) {
+    return std::exp(-0.5L * t * t) / std::sqrt(2.0L * 3.141592653589793238462643383279502884L);
+}
+
+Codebook solve_codebook(int bits) {
+    const int L = 1 << bits, h = L / 2;
+    long double b[9], p[8];
+    b[0] = 0.0L;
+    for (int j = 1; j < h; ++j) b[j] = 4.0L * j / h;   // spread over (0, 4)
+    for (int it = 0; it < 1000000; ++it) {
+        for (int j = 0; j < h; ++j) {
+            const long double lo = b[j];
+            const long double dens_hi = (j + 1 < h) ? density(b[j + 1]) : 0.0L;
+            const long double mass_hi = (j + 1 < h) ? upper_tail(b[j + 1]) : 0.0L;
+            p[j] = (density(lo) - dens_hi) / (upper_tail(lo) - mass_hi);
+        }
+        long double moved = 0.0L;
+        for (int j = 1; j < h; ++j) {
+            const long double nb = 0.5L * (p[j - 1] + p[j]);
+            const long double dl = std::fabs(nb - b[j]);
+            if (dl > moved) moved = dl;
+            b[j] = nb;
+        }
+        if (moved < 1e-17L) break;
+    }
+    Codebook cb{};
+    for (int j = 0; j < h; ++j) {
+        cb.level[h + j] = (float)(double)p[j];
+        cb.level[h - 1 - j] = -(float)(double)p[j];
+    }
+    cb.thr[h - 1] = 0.0f;
+    for (int j = 1; j < h; ++j) {
+        const long double mid = 0.5L * (p[j - 1] + p[j]);
+        cb.thr[h - 1 + j] = (float)(double)mid;
+        cb.thr[h - 1 - j] = -(float)(double)mid;
+    }
+    return cb;
+}
+
+const Codebook &codebook(int bits) {
+    static Codebook cbs[5];
+    static std::once_flag once;
+    std::call_once(once, [] {
+        for (int b = 2; b <= 4; ++b) cbs[b] = solve_codebook(b);
+    });
+    return cbs[bits];
+}
+
+// SplitMix64 (Steele, Lea, Flood, OOPSLA 2014): sigma_i = -1 iff the top bit of
+// the i-th output is set.
+void sign_mask(uint64_t seed, uint32_t mask[4]) {
+    uint64_t state = seed;
+    for (int w = 0; w < 4; ++w) mask[w] = 0;
+    for (int i = 0; i < kD; ++i) {
+        state += 0x9e3779b97f4a7c15ULL;
+        uint64_t z = state;
+        z = (z ^ (z >> 30)) * 0xbf58476d1ce4e5b9ULL;
+        z = (z ^ (z >> 27)) * 0x94d049bb133111ebULL;
+        z ^= z >> 31;
+        if (z >> 63) mask[i >> 5] |= 1u << (i & 31);
+    }
+}
+
+CodecConsts make_consts(int bits, uint64_t seed) {
+    CodecConsts k{};
+    sign_mask(seed, k.sign);
+    const Codebook &cb = codebook(bits);
+    const int L = 1 << bits;
+    for (int i = 0; i < L; ++i) k.level[i] = cb.level[i];
+    for (int i = 0; i < L - 1; ++i) k.thr8[i] = 8.0f * cb.thr[i];
+    return k;
+}
+
+bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+// [a, a + na) and [b, b + nb) overlap (sizes in bytes)
+bool overlap(const void *a, size_t na, const void *b, size_t nb) {
+    const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+    return na && nb && x < y + nb && y < x + na;
+}
+
+tq_status check_shape(int head_dim, int bits) {
+    if (head_dim <= 0 || bits <= 0) return TQ_ERR_INVALID_ARG;
+    if (head_dim != kD || bits < 2 || bits > 4) return TQ_ERR_UNSUPPORTED;
+    return TQ_OK;
+}
+
+tq_status from_hip(hipError_t e) { return e == hipSuccess ? TQ_OK : TQ_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char *tq_status_string(tq_status s) {
+    switch (s) {
+        case TQ_OK: return "TQ_OK";
+        case TQ_ERR_INVALID_ARG: return "TQ_ERR_INVALID_ARG";
+        case TQ_ERR_UNSUPPORTED: return "TQ_ERR_UNSUPPORTED";
+        case TQ_ERR_MISALIGNED: return "TQ_ERR_MISALIGNED";
+        case TQ_ERR_WORKSPACE: return "TQ_ERR_WORKSPACE";
+        case TQ_ERR_HIP: return "TQ_ERR_HIP";
+    }
+    return "TQ_ERR_UNKNOWN";
+}
+
+int tq_abi_version(void) { return TQ_ABI_VERSION; }
+
+size_t tq_packed_bytes(int head_dim, int bits) {
+    if (check_shape(head_dim, bits) != TQ_OK) return 0;
+    return (size_t)head_dim * bits / 8;
+}
+
+tq_status tq_codebook(int bits, float *levels, float *thresholds) {
+    if (bits < 2 || bits > 4) return TQ_ERR_UNSUPPORTED;
+    if (!levels || !thresholds) return TQ_ERR_INVALID_ARG;
+    const Codebook &cb = codebook(bits);
+    const int L = 1 << bits;
+    std::memcpy(levels, cb.level, sizeof(float) * L);
+    std::memcpy(thresholds, cb.thr, sizeof(float) * (L - 1));
+    return TQ_OK;
+}
+
+tq_status tq_signs(uint64_t seed, int head_dim, uint32_t *mask) {
+    if (!mask || head_dim <= 0) return TQ_ERR_INVALID_ARG;
+    if (head_dim != kD) return TQ_ERR_UNSUPPORTED;
+    sign_mask(seed, mask);
+    return TQ_OK;
+}
+
+tq_status tq_encode(const void *x_f16, int64_t n, int head_dim, int bits, uint64_t seed,
+                    uint8_t *packed, float *norms, void *stream) {
+    tq_status st = check_shape(head_dim, bits);
+    if (st != TQ_OK) return st;
+    if (n < 0) return TQ_ERR_INVALID_ARG;
+    if (n == 0) return TQ_OK;
+    if (!x_f16 || !packed || !norms) return TQ_ERR_INVALID_ARG;
+    if (!aligned(x_f16, 16) || !aligned(packed, 16) || !aligned(norms, 4))
+        return TQ_ERR_MISALIGNED;
+    const size_t P = tq_packed_bytes(head_dim, bits);
+    const size_t nx = (size_t)n * kD * 2, np = (size_t)n * P, nn = (size_t)n * 4;
+    if (overlap(x_f16, nx, packed, np) || overlap(x_f16, nx, norms, nn) ||
+        overlap(packed, np, norms, nn))
+        return TQ_ERR_INVALID_ARG;
+    const CodecConsts k = make_consts(bits, seed);
+    return from_hip(tq::launch_encode(bits, x_f16, n, nullptr, 0, k, packed, norms,
+                                      (hipStream_t)stream));
+}
+
+tq_status tq_encode_paged(const void *x_f16, const int64_t *slots, int64_t n, int head_dim,
+                          int bits, uint64_t seed, uint8_t *cache_packed, float *cache_norms,
+                          int64_t num_slots, void *stream) {
+    tq_status st = check_shape(head_dim, bits);
+    if (st != TQ_OK) return st;
+    if (n < 0 || num_slots < 0) return TQ_ERR_INVALID_ARG;
+    if (n == 0) return TQ_OK;
+    if (!x_f16 || !slots || !cache_packed || !cache_norms) return TQ_ERR_INVALID_ARG;
+    if (!aligned(x_f16, 16) || !aligned(cache_packed, 16) || !aligned(cache_norms, 4) ||
+        !aligned(slots, 8))
+        return TQ_ERR_MISALIGNED;
+    const size_t P = tq_packed_bytes(head_dim, bits);
+    const size_t nx = (size_t)n * kD * 2, ns = (size_t)n * 8;
+    const size_t np = (size_t)num_slots * P, nn = (size_t)num_slots * 4;
+    if (overlap(x_f16, nx, cache_packed, np) || overlap(x_f16, nx, cache_norms, nn) ||
+        overlap(slots, ns, cache_packed, np) || overlap(slots, ns, cache_norms, nn) ||
+        overlap(cache_packed, np, cache_norms, nn))
+        return TQ_ERR_INVALID_ARG;
+    const CodecConsts k = make_consts(bits, seed);
+    return from_hip(tq::launch_encode(bits, x_f16, n, slots, num_slots, k, cache_packed,
+                                      cache_norms, (hipStream_t)stream));
+}
+
+tq_status tq_decode(const uint8_t *packed, const float *norms, int64_t n, int head_dim,
+                    int bits, uint64_t seed, void *out_f16, void *stream) {
+    tq_status st = check_shape(head_dim, bits);
+    if (st != TQ_OK) return st;
+    if (n < 0) return TQ_ERR_INVALID_ARG;
+    if (n == 0) return TQ_OK;
+    if (!packed || !norms || !out_f16) return TQ_ERR_INVALID_ARG;
+    if (!aligned(out_f16, 16) || !aligned(packed, 16) || !aligned(norms, 4))
+        return TQ_ERR_MISALIGNED;
+    const size_t P = tq_packed_bytes(head_dim, bits);
+    const size_t no = (size_t)n * kD * 2, np = (size_t)n * P, nn = (size_t)n * 4;
+    if (overlap(out_f16, no, packed, np) || overlap(out_f16, no, norms, nn))
+        return TQ_ERR_INVALID_ARG;
+    const CodecConsts k = make_consts(bits, seed);
+    return from_hip(tq::launch_decode(bits, packed, norms, n, k, out_f16, (hipStream_t)stream));
+}
+
+size_t tq_attn_workspace_bytes(int batch, int num_q_heads, int num_kv_heads, int head_dim,
+                               int block_size, int max_blocks_per_seq) {
+    if (batch < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim != kD ||
+        block_size != tq::kAttnBlockSize || max_blocks_per_seq < 0 ||
+        num_q_heads % num_kv_heads)
+        return 0;
+    tq::AttnShape s{batch, num_q_heads, num_kv_heads, 4, max_blocks_per_seq, 0};
+    return tq::attn_workspace_bytes(s);
+}
+
+tq_status tq_attn_decode(const void *q_f16, const uint8_t *k_packed, const float *k_norms,
+                         const uint8_t *v_packed, const float *v_norms,
+                         const int32_t *block_tables, const int32_t *context_lens, int batch,
+                         int num_q_heads, int num_kv_heads, int head_dim, int bits,
+                         uint64_t seed, int block_size, int max_blocks_per_seq,
+                         int64_t num_blocks, float scale, void *out_f16, void *workspace,
+                         size_t workspace_bytes, void *stream) {
+    tq_status st = check_shape(head_dim, bits);
+    if (st != TQ_OK) return st;
+    if (batch < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_blocks_per_seq < 0 ||
+        num_blocks < 0 || !std::isfinite(scale))
+        return TQ_ERR_INVALID_ARG;
+    if (num_q_heads % num_kv_heads) return TQ_ERR_INVALID_ARG;
+    if (num_q_heads / num_kv_heads > tq::kAttnMaxGroup || block_size != tq::kAttnBlockSize)
+        return TQ_ERR_UNSUPPORTED;
+    if (batch == 0) return TQ_OK;
+    if (!q_f16 || !out_f16 || !context_lens || (max_blocks_per_seq > 0 && !block_tables))
+        return TQ_ERR_INVALID_ARG;
+    if (num_blocks > 0 && (!k_packed || !k_norms || !v_packed || !v_norms))
+        return TQ_ERR_INVALID_ARG;
+    if (!aligned(q_f16, 16) || !aligned(out_f16, 16) || !aligned(k_packed, 16) ||
+        !aligned(v_packed, 16) || !aligned(k_norms, 4) || !aligned(v_norms, 4) ||
+        !aligned(block_tables, 4) || !aligned(context_lens, 4) || !aligned(workspace, 16))
+        return TQ_ERR_MISALIGNED;
+    tq::AttnShape s{batch, num_q_heads, num_kv_heads, bits, max_blocks_per_seq, num_blocks};
+    if (!tq::attn_supported(s)) return TQ_ERR_UNSUPPORTED;
+    const size_t need = tq::attn_workspace_bytes(s);
+    if (need > 0 && (!workspace || workspace_bytes < need)) return TQ_ERR_WORKSPACE;
+    const size_t nout = (size_t)batch * num_q_heads * kD * 2;
+    if (overlap(out_f16, nout, q_f16, nout) || overlap(out_f16, nout, workspace, need))
+        return TQ_ERR_INVALID_ARG;
+    const CodecConsts k = make_consts(bits, seed);
+    return from_hip(tq::launch_attn(s, k, q_f16, k_packed, k_norms, v_packed, v_norms,
+                                    block_tables, context_lens, scale, out_f16, workspace,
+                                    (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,482 @@
+// Fused single-token decode attention over the packed, paged TurboQuant cache,
+// for gfx950.
+//
+// Method: aither-kvcache PyPI page, "Zero-buffer fused attention" (rotate the
+// query forward once, score against codebook values in the rotated domain,
+// accumulate the weighted values in the rotated domain, rotate back once) and
+// "Paged KV cache" (16-token blocks, [16, heads, 64] uint8 + [16, heads] f32
+// per block at 4 bits); qbc.network blog, "What we shipped" item 2.
+//
+// With R = H D / sqrt(d) and a cached row decoding to n * R^T c[code] / sqrt(d):
+//   <q, k_j>      = (n_j / d) * <H D q, c[k_j]>
+//   sum_j p_j v_j = D H (sum_j p_j n_j c[v_j]) / d
+// so the query is transformed once per (sequence, query head), every cached
+// row is used as plain codebook values, and one inverse transform finishes.
+//
+// Two kernels, flash-decoding style:
+//   split   grid (context split, sequence, kv-head chunk), 4 waves.  Eight
+//           lanes own one (token, kv head) pair, 16 coordinates each; a wave
+//           covers 8 such pairs per step -- one token of all 8 kv heads of a
+//           Llama-style GQA cache, whose 8 rows of codes are 512 contiguous
+//           bytes.  Each lane keeps the rotated query (16 coordinates per query
+//           head of its group) and the running softmax state in registers.
+//           The softmax is online in base 2 with a lazily raised reference:
+//           the accumulators are rescaled only when a score exceeds the
+//           reference by more than 2^8, which after the first token is rare.
+//           The four waves merge through LDS; one partial state per
+//           (sequence, query head, split) goes to the workspace.
+//   combine grid (sequence * query head), one wave: log-sum-exp merge of the
+//           splits, the inverse transform D H / d, binary16 rounding.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "tq_internal.h"
+
+namespace tq {
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kPartial = 2 + kHeadDim;      // m, l, acc[128] per workspace entry
+constexpr float kLazy = 8.0f;               // rescale when a score passes m + 8 (base 2)
+constexpr int kTargetGroups = 512;          // split-kernel workgroups aimed for
+
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kQuadXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kQuadXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kRowHalfMirror = 0x141;  // lane i <- lane 7-i within each 8
+constexpr int kRowMirror = 0x140;      // lane i <- lane 15-i within each 16
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+    return __builtin_bit_cast(
+        float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
+}
+
+// Sum over the LPU lanes of a unit (LPU = 8 or 16, aligned groups).
+template <int LPU>
+__device__ __forceinline__ float unit_sum(float v) {
+    v += dpp<kQuadXor1>(v);
+    v += dpp<kQuadXor2>(v);
+    v += dpp<kRowHalfMirror>(v);
+    if (LPU == 16) v += dpp<kRowMirror>(v);
+    return v;
+}
+
+struct AttnParams {
+    const uint16_t *q;
+    const uint8_t *kp;
+    const float *kn;
+    const uint8_t *vp;
+    const float *vn;
+    const int32_t *block_tables;
+    const int32_t *context_lens;
+    float *ws;
+    uint16_t *out;
+    int batch, hq, hkv, max_blocks, split_tokens, num_splits;
+    int64_t num_blocks;
+    float qscale;        // scale * log2(e) / 128, folded into the rotated query
+    CodecConsts k;
+};
+
+__device__ __forceinline__ float half_bits_to_float(uint32_t h) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+}
+
+__device__ __forceinline__ int sign_of(const CodecConsts &k, int i) {
+    return (k.sign[i >> 5] >> (i & 31)) & 1;
+}
+
+// Codes of this lane's E coordinates -> f32 codebook values.
+template <int BITS, int E>
+__device__ __forceinline__ void load_codes(const uint8_t *row, int sub, uint32_t (&c)[2]) {
+    constexpr int BYTES = E * BITS / 8;
+    const uint8_t *p = row + sub * BYTES;
+    if (BYTES == 8) {
+        const u32x2 u = *reinterpret_cast<const u32x2 *>(p);
+        c[0] = u.x;
+        c[1] = u.y;
+    } else if (BYTES == 4) {
+        c[0] = *reinterpret_cast<const uint32_t *>(p);
+        c[1] = 0;
+    } else if (BYTES == 6) {   // b = 3, E = 16: 2-byte aligned
+        const uint16_t *h = reinterpret_cast<const uint16_t *>(p);
+        c[0] = (uint32_t)h[0] | ((uint32_t)h[1] << 16);
+        c[1] = h[2];
+    } else if (BYTES == 2) {   // b = 2, E = 8
+        c[0] = *reinterpret_cast<const uint16_t *>(p);
+        c[1] = 0;
+    } else {                   // b = 3, E = 8: 3 bytes, byte aligned
+        c[0] = (uint32_t)p[0] | ((uint32_t)p[1] << 8) | ((uint32_t)p[2] << 16);
+        c[1] = 0;
+    }
+}
+
+// LDS lookup table: pairs of codes (b = 3, 4) or bytes of four codes (b = 2).
+template <int BITS>
+struct LevelTable {
+    static constexpr int G = (BITS == 2) ? 4 : 2;
+    static constexpr int NENT = 1 << (G * BITS);
+};
+
+template <int BITS, int E>
+__device__ __forceinline__ void expand(const float *tab, const uint32_t (&c)[2], float (&val)[E]) {
+    constexpr int G = LevelTable<BITS>::G;
+    constexpr int IB = G * BITS;   // index bits per lookup
+#pragma unroll
+    for (int gi = 0; gi < E / G; ++gi) {
+        const int bit = gi * IB;
+        uint32_t idx;
+        if ((bit & 31) + IB <= 32)
+            idx = (c[bit >> 5] >> (bit & 31)) & ((1u << IB) - 1);
+        else
+            idx = __builtin_amdgcn_alignbit(c[(bit >> 5) + 1], c[bit >> 5], bit & 31) &
+                  ((1u << IB) - 1);
+        if (G == 2) {
+            const float2 e = reinterpret_cast<const float2 *>(tab)[idx];
+            val[2 * gi] = e.x;
+            val[2 * gi + 1] = e.y;
+        } else {
+            const float4 e = reinterpret_cast<const float4 *>(tab)[idx];
+            val[4 * gi] = e.x;
+            val[4 * gi + 1] = e.y;
+            val[4 * gi + 2] = e.z;
+            val[4 * gi + 3] = e.w;
+        }
+    }
+}
+
+template <int BITS, int GRP, int E>
+__global__ __launch_bounds__(kThreads) void attn_split_kernel(AttnParams p) {
+    constexpr int LPU = kHeadDim / E;     // lanes per (token, kv head) unit
+    constexpr int UPW = 64 / LPU;         // units per wave step
+    constexpr int P = kHeadDim * BITS / 8;
+    constexpr int L = 1 << BITS;
+    constexpr int G = LevelTable<BITS>::G;
+    constexpr int NENT = LevelTable<BITS>::NENT;
+    __shared__ float tab[NENT * G];
+    __shared__ float xchg[2][64 * (GRP * E + 2 * GRP)];
+
+    const int b = blockIdx.y;
+    const int split = blockIdx.x;
+    int T = p.context_lens[b];
+    T = T < 0 ? 0 : T;
+    const int tmax = p.max_blocks * kAttnBlockSize;
+    T = T > tmax ? tmax : T;
+    if (p.num_blocks <= 0) T = 0;
+    const int t0 = split * p.split_tokens;
+    if (t0 >= T) return;                 // nothing here; combine skips this split
+    const int t1 = (t0 + p.split_tokens < T) ? t0 + p.split_tokens : T;
+
+    for (int t = threadIdx.x; t < NENT; t += kThreads) {
+#pragma unroll
+        for (int j = 0; j < G; ++j) tab[G * t + j] = p.k.level[(t >> (BITS * j)) & (L - 1)];
+    }
+
+    const int wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int gam = lane / LPU;          // unit slot in the wave
+    const int sub = lane % LPU;          // coordinate slice [sub*E, sub*E + E)
+    const bool wide = p.hkv >= UPW;
+    const int g = wide ? blockIdx.z * UPW + gam : gam % p.hkv;
+    const int tau = wide ? 0 : gam / p.hkv;
+    const int tpi = wide ? 1 : UPW / p.hkv;   // tokens per wave step
+    const bool live = wide || (gam < tpi * p.hkv);
+
+    // rotated, pre-scaled query of the GRP heads of kv head g: q~ = H D q
+    float qt[GRP][E];
+#pragma unroll
+    for (int hh = 0; hh < GRP; ++hh) {
+        const int h = g * GRP + hh;
+        const uint16_t *qp = p.q + ((size_t)b * p.hq + h) * kHeadDim + sub * E;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            const float v = half_bits_to_float(live ? qp[e] : 0);
+            qt[hh][e] = sign_of(p.k, sub * E + e) ? -v : v;
+        }
+#pragma unroll
+        for (int s = 1; s < E; s <<= 1)
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                if (e & s) continue;
+                const float a = qt[hh][e], c = qt[hh][e + s];
+                qt[hh][e] = a + c;
+                qt[hh][e + s] = a - c;
+            }
+#pragma unroll
+        for (int s = 1; s < LPU; s <<= 1)
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                const float o = __shfl_xor(qt[hh][e], s, LPU);
+                qt[hh][e] = (sub & s) ? (o - qt[hh][e]) : (qt[hh][e] + o);
+            }
+#pragma unroll
+        for (int e = 0; e < E; ++e) qt[hh][e] *= p.qscale;
+    }
+    __syncthreads();
+
+    float m[GRP], l[GRP], acc[GRP][E];
+#pragma unroll
+    for (int hh = 0; hh < GRP; ++hh) {
+        m[hh] = -__builtin_inff();
+        l[hh] = 0.0f;
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc[hh][e] = 0.0f;
+    }
+
+    const int32_t *bt = p.block_tables + (size_t)b * p.max_blocks;
+    const int step = kWaves * tpi;
+    for (int tb = t0 + wave * tpi; tb < t1; tb += step) {   // wave-uniform loop
+        const int t = tb + tau;
+        const bool act = live && (t < t1);
+        int32_t blk = act ? bt[t / kAttnBlockSize] : 0;
+        const bool ok = act && blk >= 0 && blk < p.num_blocks;
+        blk = ok ? blk : 0;
+        const int64_t row = ((int64_t)blk * kAttnBlockSize + (t % kAttnBlockSize)) * p.hkv + g;
+        uint32_t kc[2] = {0, 0}, vc[2] = {0, 0};
+        float knv = 0.0f, vnv = 0.0f;
+        if (ok) {
+            load_codes<BITS, E>(p.kp + row * P, sub, kc);
+            load_codes<BITS, E>(p.vp + row * P, sub, vc);
+            knv = p.kn[row];
+            vnv = p.vn[row];
+        }
+        float val[E];
+        expand<BITS, E>(tab, kc, val);
+        float s[GRP];
+#pragma unroll
+        for (int hh = 0; hh < GRP; ++hh) {
+            float d = 0.0f;
+#pragma unroll
+            for (int e = 0; e < E; ++e) d = __builtin_fmaf(qt[hh][e], val[e], d);
+            s[hh] = ok ? unit_sum<LPU>(d) * knv : -__builtin_inff();
+        }
+        // lazily raised reference: rescale only when some score passes m + 8
+        bool need = false;
+#pragma unroll
+        for (int hh = 0; hh < GRP; ++hh) need |= s[hh] > m[hh] + kLazy;
+        if (__builtin_amdgcn_ballot_w64(need)) {
+#pragma unroll
+            for (int hh = 0; hh < GRP; ++hh) {
+                const float mn = (s[hh] > m[hh] + kLazy) ? s[hh] : m[hh];
+                const float a = (mn == m[hh]) ? 1.0f : __builtin_amdgcn_exp2f(m[hh] - mn);
+                l[hh] *= a;
+#pragma unroll
+                for (int e = 0; e < E; ++e) acc[hh][e] *= a;
+                m[hh] = mn;
+            }
+        }
+        expand<BITS, E>(tab, vc, val);
+#pragma unroll
+        for (int hh = 0; hh < GRP; ++hh) {
+            const float pr = ok ? __builtin_amdgcn_exp2f(s[hh] - m[hh]) : 0.0f;
+            l[hh] += pr;
+            const float w = pr * vnv;
+#pragma unroll
+            for (int e = 0; e < E; ++e) acc[hh][e] = __builtin_fmaf(w, val[e], acc[hh][e]);
+        }
+    }
+
+    // merge the TPI units of the same kv head inside the wave (narrow caches)
+    for (int off = p.hkv * LPU; off < tpi * p.hkv * LPU; off <<= 1) {
+#pragma unroll
+        for (int hh = 0; hh < GRP; ++hh) {
+            const float mo = __shfl_xor(m[hh], off);
+            const float lo = __shfl_xor(l[hh], off);
+            const float mn = m[hh] > mo ? m[hh] : mo;
+            const float a = (m[hh] == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(m[hh] - mn);
+            const float ao = (mo == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(mo - mn);
+            l[hh] = l[hh] * a + lo * ao;
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                const float o = __shfl_xor(acc[hh][e], off);
+                acc[hh][e] = acc[hh][e] * a + o * ao;
+            }
+            m[hh] = mn;
+        }
+    }
+
+    // merge the four waves through LDS: 2,3 -> 0,1, then 1 -> 0
+    auto put = [&](float *buf) {
+#pragma unroll
+        for (int hh = 0; hh < GRP; ++hh) {
+#pragma unroll
+            for (int e = 0; e < E; ++e) buf[(hh * E + e) * 64 + lane] = acc[hh][e];
+            buf[(GRP * E + 2 * hh) * 64 + lane] = m[hh];
+            buf[(GRP * E + 2 * hh + 1) * 64 + lane] = l[hh];
+        }
+    };
+    auto take = [&](const float *buf) {
+#pragma unroll
+        for (int hh = 0; hh < GRP; ++hh) {
+            const float mo = buf[(GRP * E + 2 * hh) * 64 + lane];
+            const float lo = buf[(GRP * E + 2 * hh + 1) * 64 + lane];
+            const float mn = m[hh] > mo ? m[hh] : mo;
+            const float a = (m[hh] == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(m[hh] - mn);
+            const float ao = (mo == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(mo - mn);
+            l[hh] = l[hh] * a + lo * ao;
+#pragma unroll
+            for (int e = 0; e < E; ++e)
+                acc[hh][e] = acc[hh][e] * a + buf[(hh * E + e) * 64 + lane] * ao;
+            m[hh] = mn;
+        }
+    };
+    if (wave >= 2) put(xchg[wave - 2]);
+    __syncthreads();
+    if (wave < 2) take(xchg[wave]);
+    __syncthreads();
+    if (wave == 1) put(xchg[0]);
+    __syncthreads();
+    if (wave != 0 || !live || tau != 0) return;
+    take(xchg[0]);
+
+#pragma unroll
+    for (int hh = 0; hh < GRP; ++hh) {
+        const int h = g * GRP + hh;
+        float *dst = p.ws + (((size_t)b * p.hq + h) * p.num_splits + split) * kPartial;
+        if (sub == 0) {
+            dst[0] = m[hh];
+            dst[1] = l[hh];
+        }
+#pragma unroll
+        for (int e = 0; e < E; ++e) dst[2 + sub * E + e] = acc[hh][e];
+    }
+}
+
+// One wave per (sequence, query head): merge the splits, undo the rotation.
+__global__ __launch_bounds__(64) void attn_combine_kernel(AttnParams p) {
+    const int bh = blockIdx.x;
+    const int b = bh / p.hq;
+    const int lane = threadIdx.x;
+    int T = p.context_lens[b];
+    T = T < 0 ? 0 : T;
+    const int tmax = p.max_blocks * kAttnBlockSize;
+    T = T > tmax ? tmax : T;
+    if (p.num_blocks <= 0) T = 0;
+    const int ns = (T + p.split_tokens - 1) / p.split_tokens;
+    const float *src = p.ws + (size_t)bh * p.num_splits * kPartial;
+
+    float mx = -__builtin_inff();
+    for (int s = 0; s < ns; ++s) {
+        const float ms = src[s * kPartial];
+        mx = ms > mx ? ms : mx;
+    }
+    float l = 0.0f, a0 = 0.0f, a1 = 0.0f;   // this lane: coordinates 2*lane, 2*lane+1
+    for (int s = 0; s < ns; ++s) {
+        const float *e = src + s * kPartial;
+        if (e[1] == 0.0f) continue;
+        const float w = __builtin_amdgcn_exp2f(e[0] - mx);
+        l += w * e[1];
+        a0 += w * e[2 + 2 * lane];
+        a1 += w * e[3 + 2 * lane];
+    }
+    const float inv = (l > 0.0f) ? 1.0f / l : 0.0f;
+    // inverse transform: x = D H acc / 128 -- coordinate bit 0 in registers,
+    // bits 1..6 across lanes
+    float x0 = (a0 + a1) * inv, x1 = (a0 - a1) * inv;
+#pragma unroll
+    for (int s = 1; s < 64; s <<= 1) {
+        const float o0 = __shfl_xor(x0, s), o1 = __shfl_xor(x1, s);
+        x0 = (lane & s) ? (o0 - x0) : (x0 + o0);
+        x1 = (lane & s) ? (o1 - x1) : (x1 + o1);
+    }
+    const int i0 = 2 * lane, i1 = 2 * lane + 1;
+    x0 *= (1.0f / kHeadDim);
+    x1 *= (1.0f / kHeadDim);
+    if (sign_of(p.k, i0)) x0 = -x0;
+    if (sign_of(p.k, i1)) x1 = -x1;
+    const _Float16 h0 = (_Float16)x0, h1 = (_Float16)x1;
+    uint16_t *o = p.out + (size_t)bh * kHeadDim;
+    const uint32_t packed2 = (uint32_t)__builtin_bit_cast(uint16_t, h0) |
+                             ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
+    reinterpret_cast<uint32_t *>(o)[lane] = packed2;
+}
+
+int wave_units(int grp) { return grp <= 4 ? 8 : 4; }   // units per wave: E = 16 or 8
+
+}  // namespace
+
+bool attn_supported(const AttnShape &s) {
+    const int grp = s.num_q_heads / s.num_kv_heads;
+    if (grp != 1 && grp != 2 && grp != 4 && grp != 8) return false;
+    const int upw = wave_units(grp);
+    return s.num_kv_heads % upw == 0 || upw % s.num_kv_heads == 0;
+}
+
+int attn_split_tokens(const AttnShape &s) {
+    const int ctx = s.max_blocks * kAttnBlockSize;
+    const int grp = s.num_q_heads / s.num_kv_heads;
+    const int upw = wave_units(grp);
+    const int zch = s.num_kv_heads >= upw ? s.num_kv_heads / upw : 1;
+    const int per_seq = s.batch * zch > 0 ? (kTargetGroups + s.batch * zch - 1) / (s.batch * zch) : 1;
+    int st = (ctx + per_seq - 1) / per_seq;
+    st = (st + 63) / 64 * 64;
+    return st < 256 ? 256 : st;
+}
+
+int attn_num_splits(const AttnShape &s) {
+    const int ctx = s.max_blocks * kAttnBlockSize;
+    const int st = attn_split_tokens(s);
+    const int ns = (ctx + st - 1) / st;
+    return ns < 1 ? 1 : ns;
+}
+
+size_t attn_workspace_bytes(const AttnShape &s) {
+    return (size_t)s.batch * s.num_q_heads * attn_num_splits(s) * kPartial * sizeof(float);
+}
+
+hipError_t launch_attn(const AttnShape &s, const CodecConsts &k, const void *q,
+                       const uint8_t *k_packed, const float *k_norms, const uint8_t *v_packed,
+                       const float *v_norms, const int32_t *block_tables,
+                       const int32_t *context_lens, float scale, void *out, void *workspace,
+                       hipStream_t stream) {
+    const int grp = s.num_q_heads / s.num_kv_heads;
+    const int upw = wave_units(grp);
+    if (!(s.num_kv_heads % upw == 0 || upw % s.num_kv_heads == 0)) return hipErrorInvalidValue;
+    AttnParams p;
+    p.q = static_cast<const uint16_t *>(q);
+    p.kp = k_packed;
+    p.kn = k_norms;
+    p.vp = v_packed;
+    p.vn = v_norms;
+    p.block_tables = block_tables;
+    p.context_lens = context_lens;
+    p.ws = static_cast<float *>(workspace);
+    p.out = static_cast<uint16_t *>(out);
+    p.batch = s.batch;
+    p.hq = s.num_q_heads;
+    p.hkv = s.num_kv_heads;
+    p.max_blocks = s.max_blocks;
+    p.split_tokens = attn_split_tokens(s);
+    p.num_splits = attn_num_splits(s);
+    p.num_blocks = s.num_blocks;
+    p.qscale = scale * 1.4426950408889634f / kHeadDim;
+    p.k = k;
+    const int zch = s.num_kv_heads >= upw ? s.num_kv_heads / upw : 1;
+    const dim3 grid(p.num_splits, s.batch, zch), block(kThreads);
+#define TQ_SPLIT(B, GR, E) \
+    hipLaunchKernelGGL((attn_split_kernel<B, GR, E>), grid, block, 0, stream, p)
+#define TQ_BITS(GR, E)                           \
+    switch (s.bits) {                            \
+        case 2: TQ_SPLIT(2, GR, E); break;       \
+        case 3: TQ_SPLIT(3, GR, E); break;       \
+        case 4: TQ_SPLIT(4, GR, E); break;       \
+        default: return hipErrorInvalidValue;   \
+    }
+    switch (grp) {
+        case 1: TQ_BITS(1, 16) break;
+        case 2: TQ_BITS(2, 16) break;
+        case 4: TQ_BITS(4, 16) break;
+        case 8: TQ_BITS(8, 8) break;
+        default: return hipErrorInvalidValue;
+    }
+#undef TQ_BITS
+#undef TQ_SPLIT
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(attn_combine_kernel, dim3(s.batch * s.num_q_heads), dim3(64), 0, stream, p);
+    return hipGetLastError();
+}
+
+}  // namespace tq

@@ -1,0 +1,60 @@
+// Internal interface between the C-ABI host code (tq_abi.cpp) and the HIP
+// kernels (tq_codec.hip, tq_attn.hip).  Not installed; not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tq {
+
+constexpr int kHeadDim = 128;
+
+// Everything the kernels need that is fixed by (bits, seed).  Passed by value
+// as a kernel argument, so the library needs no device allocation.
+struct CodecConsts {
+    uint32_t sign[4];   // bit i of sign[i / 32] set  <=>  sigma_i = -1
+    float thr8[15];     // decision thresholds times 8, ascending (2^bits - 1 used)
+    float level[16];    // Lloyd-Max levels, ascending (2^bits used)
+};
+
+// Encode `n` vectors.  With `slots` non-null, vector v is written to row
+// slots[v] of (packed, norms) and skipped when that row is outside
+// [0, num_slots); otherwise to row v.
+hipError_t launch_encode(int bits, const void *x, int64_t n, const int64_t *slots,
+                         int64_t num_slots, const CodecConsts &k, uint8_t *packed, float *norms,
+                         hipStream_t stream);
+
+hipError_t launch_decode(int bits, const uint8_t *packed, const float *norms, int64_t n,
+                         const CodecConsts &k, void *out, hipStream_t stream);
+
+// ---------------------------------------------------------------------------
+// decode attention
+// ---------------------------------------------------------------------------
+
+constexpr int kAttnBlockSize = 16;   // tokens per cache page
+constexpr int kAttnMaxGroup = 8;     // query heads per kv head
+
+struct AttnShape {
+    int batch, num_q_heads, num_kv_heads, bits, max_blocks;
+    int64_t num_blocks;
+};
+
+// Whether the split kernel has a variant for this (query heads per kv head,
+// kv heads) combination.
+bool attn_supported(const AttnShape &s);
+
+// Tokens handled by one workgroup of the split kernel, and the number of
+// splits of the longest possible context.
+int attn_split_tokens(const AttnShape &s);
+int attn_num_splits(const AttnShape &s);
+size_t attn_workspace_bytes(const AttnShape &s);
+
+hipError_t launch_attn(const AttnShape &s, const CodecConsts &k, const void *q,
+                       const uint8_t *k_packed, const float *k_norms, const uint8_t *v_packed,
+                       const float *v_norms, const int32_t *block_tables,
+                       const int32_t *context_lens, float scale, void *out, void *workspace,
+                       hipStream_t stream);
+
+int device_cu_count();
+
+}  // namespace tq

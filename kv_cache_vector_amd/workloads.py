@@ -89,6 +89,54 @@ def llama70b_layer(layer: int, tokens: int = 131072, heads: int = 8) -> np.ndarr
 # 32768 cached tokens per sequence in 16-token pages
 # ---------------------------------------------------------------------------
 
+def attn_kv_rows(b: int, g: int, tokens: int, seed: int = 500, outlier_p: float = 0.01,
+                 outlier_factor: float = 15.0) -> np.ndarray:
+    """K and V of sequence b, kv head g in token order: [2, tokens, 128] fp16,
+    N(0,1) with Bernoulli(outlier_p) outlier channels (x outlier_factor) fixed
+    for the (sequence, kv head).  Seeded by (seed, b, g) alone, so any one
+    stream can be regenerated without the others."""
+    rng = np.random.default_rng([seed, b, g])
+    mask = rng.random((2, 1, HEAD_DIM)) < outlier_p
+    kv = rng.standard_normal((2, tokens, HEAD_DIM), dtype=np.float32)
+    kv = np.where(mask, kv * np.float32(outlier_factor), kv)
+    return _f16(kv)
+
+
+def attn_query(batch: int, num_q_heads: int, seed: int = 500) -> np.ndarray:
+    rng = np.random.default_rng([seed, 1 << 30])
+    return _f16(rng.standard_normal((batch, num_q_heads, HEAD_DIM), dtype=np.float32))
+
+
+def attn_block_tables(batch: int, max_blocks: int, num_blocks: int,
+                      perm_seed: int = 501) -> np.ndarray:
+    """A seeded random permutation of the physical blocks, max_blocks per
+    sequence: [batch, max_blocks] int32."""
+    perm = np.random.default_rng(perm_seed).permutation(num_blocks)[: batch * max_blocks]
+    return perm.astype(np.int32).reshape(batch, max_blocks)
+
+
+def attn_context_lens(batch: int, context: int, ragged: bool, block_size: int = 16,
+                      seed: int = 500) -> np.ndarray:
+    """All equal to ``context``, or (ragged) drawn in [1, context] with 1, the
+    full length, block_size + 1 and context - 3 among them."""
+    if not ragged:
+        return np.full(batch, context, dtype=np.int32)
+    rng = np.random.default_rng([seed, 1 << 31])
+    cl = rng.integers(1, context + 1, size=batch).astype(np.int32)
+    fixed = [1, context, min(context, block_size + 1), max(1, context - 3)]
+    cl[: min(batch, 4)] = fixed[: min(batch, 4)]
+    return cl
+
+
+def scatter_pages(pages: np.ndarray, rows: np.ndarray, block_table_row: np.ndarray, g: int,
+                  block_size: int = 16) -> None:
+    """Write rows [T, ...] of one (sequence, kv head) into pages
+    [num_blocks, block_size, Hkv, ...] following that sequence's block table."""
+    T = rows.shape[0]
+    t = np.arange(T)
+    pages[block_table_row[t // block_size], t % block_size, g] = rows
+
+
 def attn_workload(batch: int = 16, num_q_heads: int = 32, num_kv_heads: int = 8,
                   context: int = 32768, block_size: int = 16, seed: int = 500,
                   perm_seed: int = 501, ragged: bool = False, outlier_p: float = 0.01,
@@ -96,47 +144,27 @@ def attn_workload(batch: int = 16, num_q_heads: int = 32, num_kv_heads: int = 8,
     """Returns a dict with
       q            [B, Hq, 128] fp16, N(0,1)
       k, v         [num_blocks, block_size, Hkv, 128] fp16 -- the cache content
-                   in physical (paged) order, N(0,1) with Bernoulli(outlier_p)
-                   outlier channels (x outlier_factor) per (sequence, kv head)
+                   in physical (paged) order (attn_kv_rows per sequence and kv
+                   head; pages no sequence uses hold N(0,1) filler)
       block_tables [B, max_blocks] int32 -- a seeded random permutation of the
                    physical blocks
-      context_lens [B] int32 -- all equal to ``context`` unless ragged=True,
-                   in which case they are drawn in [1, context] and include 1
-                   and lengths that are not multiples of the block size.
+      context_lens [B] int32 -- see attn_context_lens.
     """
-    rng = np.random.default_rng(seed)
     max_blocks = (context + block_size - 1) // block_size
     nblk = batch * max_blocks + extra_blocks
-    q = rng.standard_normal((batch, num_q_heads, HEAD_DIM), dtype=np.float32)
-    # logical [B, Hkv, T, 128] -> physical pages
-    mask = rng.random((2, batch, num_kv_heads, 1, HEAD_DIM)) < outlier_p
-    kv = rng.standard_normal((2, batch, num_kv_heads, max_blocks * block_size, HEAD_DIM),
-                             dtype=np.float32)
-    kv = np.where(mask, kv * np.float32(outlier_factor), kv)
-    prng = np.random.default_rng(perm_seed)
-    perm = prng.permutation(nblk)[: batch * max_blocks].astype(np.int32)
-    block_tables = perm.reshape(batch, max_blocks)
-    pages = np.zeros((2, nblk, block_size, num_kv_heads, HEAD_DIM), dtype=np.float32)
-    if extra_blocks:
-        pages[:] = rng.standard_normal(pages.shape, dtype=np.float32)
-    # token t of sequence b lives in block block_tables[b, t // bs], row t % bs
-    logical = kv.reshape(2, batch, num_kv_heads, max_blocks, block_size, HEAD_DIM)
-    logical = logical.transpose(0, 1, 3, 4, 2, 5)  # [2, B, max_blocks, bs, Hkv, 128]
-    pages[:, block_tables.reshape(-1)] = logical.reshape(2, batch * max_blocks, block_size,
-                                                         num_kv_heads, HEAD_DIM)
-    if ragged:
-        cl = rng.integers(1, context + 1, size=batch).astype(np.int32)
-        cl[0] = 1
-        if batch > 1:
-            cl[1] = context
-        if batch > 2:
-            cl[2] = min(context, block_size + 1)
-        if batch > 3:
-            cl[3] = max(1, context - 3)
-    else:
-        cl = np.full(batch, context, dtype=np.int32)
-    return dict(q=_f16(q), k=_f16(pages[0]), v=_f16(pages[1]), block_tables=block_tables,
-                context_lens=cl, block_size=block_size, num_kv_heads=num_kv_heads)
+    q = attn_query(batch, num_q_heads, seed)
+    bt = attn_block_tables(batch, max_blocks, nblk, perm_seed)
+    filler = np.random.default_rng([seed, 1 << 29])
+    pages = filler.standard_normal((2, nblk, block_size, num_kv_heads, HEAD_DIM),
+                                   dtype=np.float32).astype(np.float16)
+    for b in range(batch):
+        for g in range(num_kv_heads):
+            kv = attn_kv_rows(b, g, max_blocks * block_size, seed, outlier_p, outlier_factor)
+            scatter_pages(pages[0], kv[0], bt[b], g, block_size)
+            scatter_pages(pages[1], kv[1], bt[b], g, block_size)
+    cl = attn_context_lens(batch, context, ragged, block_size, seed)
+    return dict(q=q, k=pages[0], v=pages[1], block_tables=bt, context_lens=cl,
+                block_size=block_size, num_kv_heads=num_kv_heads)
 
 
 def gaussian(n: int, seed: int) -> np.ndarray:

@@ -1,0 +1,159 @@
+"""libtq on the CPU: the library loads, exports every entry point include/tq.h
+declares, and its host-only parts behave (codebook and sign hooks against the
+oracle, argument checks that return before anything is launched)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+from kv_cache_vector_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tq.h")
+
+OK, INVAL, UNSUP, MISAL, WS = 0, 1, 2, 3, 4
+
+
+@pytest.fixture(scope="module")
+def L():
+    return _lib.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(tq_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(L):
+    names = declared_functions()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(L, n), n
+    assert sorted(_lib.SYMBOLS) == names
+
+
+def test_version_and_status_strings(L):
+    assert L.tq_abi_version() == 1
+    for s, name in _lib.STATUS_NAMES.items():
+        assert _lib.tq_status_string(s) == name
+
+
+def test_packed_bytes(L):
+    assert [_lib.tq_packed_bytes(128, b) for b in (2, 3, 4)] == [32, 48, 64]
+    assert _lib.tq_packed_bytes(128, 5) == 0
+    assert _lib.tq_packed_bytes(96, 4) == 0
+    assert _lib.tq_packed_bytes(128, 1) == 0
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_codebook_hook_matches_oracle(L, bits):
+    """libtq solves the Lloyd-Max conditions with its own solver (extended
+    precision, iterating on the decision points); the oracle iterates on the
+    levels in double.  Both must land on the same f32 values."""
+    lv, th = _lib.tq_codebook(bits)
+    c, t = oracle.codebook(bits)
+    assert np.array_equal(np.array(lv, np.float32), c.astype(np.float32))
+    assert np.array_equal(np.array(th, np.float32), t.astype(np.float32))
+    lvf = np.array(lv, np.float32)
+    assert np.all(np.abs(lvf.astype(np.float64) - c) <= 0.5 * np.spacing(np.abs(lvf)))
+    assert th[len(th) // 2] == 0.0
+
+
+@pytest.mark.parametrize("seed", [0, 1, 42, 2 ** 64 - 1])
+def test_sign_hook_matches_oracle(L, seed):
+    words = _lib.tq_signs(seed)
+    s = oracle.signs(seed, 128)
+    bits = np.array([(words[i // 32] >> (i % 32)) & 1 for i in range(128)])
+    assert np.array_equal(bits, (s < 0).astype(int))
+
+
+def test_hook_errors(L):
+    buf = (ctypes.c_float * 16)()
+    assert L.tq_codebook(5, buf, buf) == UNSUP
+    assert L.tq_codebook(4, None, buf) == INVAL
+    assert L.tq_signs(0, 96, buf) == UNSUP
+    assert L.tq_signs(0, 128, None) == INVAL
+
+
+# Fake device addresses: every call below must be rejected (or be a no-op)
+# before anything touches them or the GPU.
+A = 0x10000000
+B = 0x20000000
+C = 0x30000000
+
+
+def test_encode_argument_errors(L):
+    e = L.tq_encode
+    assert e(A, 10, 128, 5, 0, B, C, None) == UNSUP
+    assert e(A, 10, 96, 4, 0, B, C, None) == UNSUP
+    assert e(A, 10, 0, 4, 0, B, C, None) == INVAL
+    assert e(A, -1, 128, 4, 0, B, C, None) == INVAL
+    assert e(A, 0, 128, 4, 0, B, C, None) == OK          # n == 0: nothing to do
+    assert e(None, 0, 128, 4, 0, None, None, None) == OK
+    assert e(None, 10, 128, 4, 0, B, C, None) == INVAL
+    assert e(A, 10, 128, 4, 0, None, C, None) == INVAL
+    assert e(A, 10, 128, 4, 0, B, None, None) == INVAL
+    assert e(A + 8, 10, 128, 4, 0, B, C, None) == MISAL
+    assert e(A, 10, 128, 4, 0, B + 4, C, None) == MISAL
+    assert e(A, 10, 128, 4, 0, B, C + 2, None) == MISAL
+    # overlapping input and output ranges
+    assert e(A, 10, 128, 4, 0, A + 256, C, None) == INVAL
+    assert e(A, 10, 128, 4, 0, B, B + 9 * 64, None) == INVAL
+
+
+def test_decode_argument_errors(L):
+    d = L.tq_decode
+    assert d(B, C, 10, 128, 1, 0, A, None) == UNSUP
+    assert d(B, C, -5, 128, 4, 0, A, None) == INVAL
+    assert d(B, C, 0, 128, 4, 0, A, None) == OK
+    assert d(None, C, 10, 128, 4, 0, A, None) == INVAL
+    assert d(B, C, 10, 128, 4, 0, A + 2, None) == MISAL
+    assert d(B, C, 10, 128, 4, 0, B + 64, None) == INVAL   # output overlaps codes
+
+
+def test_paged_encode_argument_errors(L):
+    p = L.tq_encode_paged
+    assert p(A, B, 4, 128, 6, 0, C, C + 4096, 100, None) == UNSUP
+    assert p(A, B, 4, 128, 4, 0, C, C + 1 << 20, -1, None) == INVAL
+    assert p(A, B, 0, 128, 4, 0, C, C + 4096, 100, None) == OK
+    assert p(A, None, 4, 128, 4, 0, C, C + 8192, 100, None) == INVAL
+    assert p(A, B + 4, 4, 128, 4, 0, C, C + 8192, 100, None) == MISAL
+    assert p(A, B, 4, 128, 4, 0, C, C + 64, 100, None) == INVAL   # packed overlaps norms
+
+
+def test_attention_argument_errors(L):
+    ws = L.tq_attn_workspace_bytes(16, 32, 8, 128, 16, 2048)
+    assert ws > 0 and ws % 16 == 0
+    assert L.tq_attn_workspace_bytes(16, 32, 8, 96, 16, 2048) == 0
+    assert L.tq_attn_workspace_bytes(16, 30, 8, 128, 16, 2048) == 0
+    a = L.tq_attn_decode
+
+    def call(**kw):
+        args = dict(q=A, kp=B, kn=B + (1 << 24), vp=C, vn=C + (1 << 24), bt=A + (1 << 24),
+                    cl=A + (1 << 25), batch=16, hq=32, hkv=8, d=128, bits=4, seed=0, bs=16,
+                    maxb=2048, nblk=32768, scale=0.088, out=A + (1 << 26), ws=0x40000000,
+                    wsb=ws)
+        args.update(kw)
+        return a(args["q"], args["kp"], args["kn"], args["vp"], args["vn"], args["bt"],
+                 args["cl"], args["batch"], args["hq"], args["hkv"], args["d"], args["bits"],
+                 args["seed"], args["bs"], args["maxb"], args["nblk"], args["scale"],
+                 args["out"], args["ws"], args["wsb"], None)
+
+    assert call(bits=5) == UNSUP
+    assert call(d=64) == UNSUP
+    assert call(bs=32) == UNSUP
+    assert call(hq=30) == INVAL
+    assert call(hq=8 * 16) == UNSUP                 # 16 query heads per kv head
+    assert call(hq=24, hkv=8) == UNSUP              # 3 query heads per kv head
+    assert call(batch=-1) == INVAL
+    assert call(scale=float("nan")) == INVAL
+    assert call(batch=0) == OK
+    assert call(q=None) == INVAL
+    assert call(out=A + (1 << 26) + 2) == MISAL
+    assert call(ws=None) == WS
+    assert call(wsb=ws - 16) == WS
+    assert call(out=A) == INVAL                     # output overlaps the query

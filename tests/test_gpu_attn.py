@@ -1,0 +1,166 @@
+"""GPU parity of tq_attn_decode (fused decode attention over the packed, paged
+cache) against the oracle's plain softmax attention on decoded rows.
+
+The packed cache fed to both sides is produced by the oracle's encoder (or is
+random bytes, which are valid codes, where no comparison is made)."""
+import math
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import parity as P
+from kv_cache_vector_amd import _lib
+from kv_cache_vector_amd import workloads as W
+from kv_cache_vector_amd.turboquant import TQPagedAttention, TurboQuant
+
+pytestmark = pytest.mark.gpu
+D = 128
+
+
+@pytest.fixture(scope="module")
+def dev():
+    assert torch.cuda.is_available(), "GPU tests need an AMD Instinct GPU"
+    _lib.load()
+    return torch.device("cuda:0")
+
+
+def oracle_encode_parallel(x, bits, seed, workers=16):
+    """Oracle encode of many rows, split into contiguous chunks over threads
+    (the ctypes call releases the GIL)."""
+    x2 = x.reshape(-1, D)
+    n = x2.shape[0]
+    chunks = [(i, min(n, i + 65536)) for i in range(0, n, 65536)]
+    packed = np.empty((n, D * bits // 8), np.uint8)
+    norms = np.empty(n, np.float32)
+
+    def job(c):
+        a, b = c
+        packed[a:b], norms[a:b] = oracle.encode(x2[a:b], bits, seed)
+
+    with ThreadPoolExecutor(workers) as ex:
+        list(ex.map(job, chunks))
+    lead = x.shape[:-1]
+    return packed.reshape(lead + (D * bits // 8,)), norms.reshape(lead)
+
+
+def run_attn(dev, what, bits=4, B=3, Hq=8, Hkv=2, T=37, ragged=True, seed=0, scale=None,
+             extra_blocks=2, sel=None, pad=None):
+    P.log("[attn] %s: B=%d Hq=%d Hkv=%d T=%d bits=%d ragged=%s" % (what, B, Hq, Hkv, T, bits,
+                                                                   ragged))
+    wl = W.attn_workload(batch=B, num_q_heads=Hq, num_kv_heads=Hkv, context=T, seed=700 + T,
+                         perm_seed=701 + T, ragged=ragged, extra_blocks=extra_blocks)
+    kp, kn = oracle_encode_parallel(wl["k"], bits, seed)
+    vp, vn = oracle_encode_parallel(wl["v"], bits, seed)
+    bt = wl["block_tables"].copy()
+    cl = wl["context_lens"].copy()
+    if pad is not None:                      # entries past each context: invalid ids
+        for b in range(B):
+            used = (int(cl[b]) + 15) // 16
+            bt[b, used:] = pad
+    sc = 1.0 / math.sqrt(D) if scale is None else scale
+    tq = TurboQuant(D, bits, seed, dev)
+    attn = TQPagedAttention(tq, Hq, scale=sc)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    out = attn.forward(t(wl["q"]), t(kp), t(kn), t(vp), t(vn), t(bt), t(cl))
+    torch.cuda.synchronize()
+    g = out.cpu().numpy()
+    bt_o = bt.copy()
+    if pad is not None:
+        bt_o[bt_o < 0] = 0
+        bt_o[bt_o >= kp.shape[0]] = 0
+    _, ref = oracle.attn_decode(wl["q"], kp, kn, vp, vn, bt_o, cl, Hkv, bits, seed, sc,
+                                sel=sel, want_f64=True)
+    if sel is None:
+        P.compare_attn(g, ref, what)
+    else:
+        m = np.asarray(sel, bool)
+        P.compare_attn(g[m], ref[m], what)
+    return g
+
+
+@pytest.mark.parametrize("bits", [4, 3, 2])
+def test_small_ragged(dev, bits):
+    run_attn(dev, "small b%d" % bits, bits=bits)
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(4, 4), (8, 4), (32, 8), (16, 2), (64, 16), (8, 1), (16, 16)])
+def test_gqa_shapes(dev, Hq, Hkv):
+    run_attn(dev, "gqa %d/%d" % (Hq, Hkv), B=2, Hq=Hq, Hkv=Hkv, T=50)
+
+
+@pytest.mark.parametrize("T", [1, 2, 15, 16, 17, 255, 256, 257, 1000, 1500])
+def test_context_lengths(dev, T):
+    run_attn(dev, "T=%d" % T, B=4, Hq=32, Hkv=8, T=T, ragged=(T > 3))
+
+
+def test_zero_context_and_padding(dev):
+    """Context 0 gives zeros; block-table entries past the context (here -1)
+    are never read."""
+    g = run_attn(dev, "pad -1", B=5, Hq=8, Hkv=2, T=40, pad=-1)
+    assert np.all(np.isfinite(g.astype(np.float64)))
+    wl = W.attn_workload(batch=2, num_q_heads=8, num_kv_heads=2, context=16, seed=9)
+    tq = TurboQuant(D, 4, 0, dev)
+    attn = TQPagedAttention(tq, 8)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    kp, kn = oracle.encode(wl["k"], 4, 0)
+    vp, vn = oracle.encode(wl["v"], 4, 0)
+    out = attn.forward(t(wl["q"]), t(kp), t(kn), t(vp), t(vn), t(wl["block_tables"]),
+                       t(np.zeros(2, np.int32)))
+    torch.cuda.synchronize()
+    assert torch.all(out == 0)
+
+
+def test_scale_and_peaked_softmax(dev):
+    """A large scale makes the softmax nearly one-hot (exercises the lazy
+    rescaling of the running maximum)."""
+    run_attn(dev, "scale 1.0", B=2, Hq=8, Hkv=2, T=300, scale=1.0)
+    run_attn(dev, "scale 0.02", B=2, Hq=8, Hkv=2, T=300, scale=0.02)
+
+
+def _c5(dev, ragged, samples):
+    """Batch 16, 32/8 heads, 32768 tokens, 4 bits, in the launch configuration
+    the benchmark times.  The sampled (sequence, kv head) streams hold
+    oracle-encoded N(0,1)+outlier data; the rest of the cache is random codes."""
+    B, Hq, Hkv, T, bs = 16, 32, 8, 32768, 16
+    maxb = T // bs
+    nblk = B * maxb
+    rng = np.random.default_rng(502)
+    kp = rng.integers(0, 256, (nblk, bs, Hkv, 64), dtype=np.uint8)
+    vp = rng.integers(0, 256, (nblk, bs, Hkv, 64), dtype=np.uint8)
+    kn = rng.uniform(8, 14, (nblk, bs, Hkv)).astype(np.float32)
+    vn = rng.uniform(8, 14, (nblk, bs, Hkv)).astype(np.float32)
+    q = W.attn_query(B, Hq)
+    bt = W.attn_block_tables(B, maxb, nblk)
+    cl = W.attn_context_lens(B, T, ragged)
+    sel = np.zeros((B, Hq), bool)
+    for b, g in samples:
+        kv = W.attn_kv_rows(b, g, T)
+        p_k, n_k = oracle_encode_parallel(kv[0], 4, 0)
+        p_v, n_v = oracle_encode_parallel(kv[1], 4, 0)
+        W.scatter_pages(kp, p_k, bt[b], g)
+        W.scatter_pages(kn, n_k, bt[b], g)
+        W.scatter_pages(vp, p_v, bt[b], g)
+        W.scatter_pages(vn, n_v, bt[b], g)
+        sel[b, g * 4:(g + 1) * 4] = True
+    P.log("[attn] C5-shaped full size ragged=%s samples=%s" % (ragged, samples))
+    tq = TurboQuant(D, 4, 0, dev)
+    attn = TQPagedAttention(tq, Hq)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    out = attn.forward(t(q), t(kp), t(kn), t(vp), t(vn), t(bt), t(cl))
+    torch.cuda.synchronize()
+    g = out.cpu().numpy()
+    assert np.all(np.isfinite(g.astype(np.float64)))
+    _, ref = oracle.attn_decode(q, kp, kn, vp, vn, bt, cl, Hkv, 4, 0, 1 / math.sqrt(D),
+                                sel=sel, want_f64=True)
+    P.compare_attn(g[sel], ref[sel], "full size ragged=%s" % ragged)
+
+
+def test_full_size_batch16_32k(dev):
+    _c5(dev, False, [(0, 0), (11, 5)])
+
+
+def test_full_size_batch16_ragged(dev):
+    _c5(dev, True, [(0, 3), (2, 7), (9, 1)])

@@ -1,0 +1,249 @@
+"""GPU parity of tq_encode / tq_decode / tq_encode_paged against the oracle.
+
+Every input is seeded and synthetic (kv_cache_vector_amd.workloads) and the
+same bytes go to libtq and to the oracle.  Expected values come from the
+oracle only; the decode checks feed both sides the oracle's own packed codes.
+"""
+import ctypes
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import parity as P
+from kv_cache_vector_amd import _lib
+from kv_cache_vector_amd import workloads as W
+from kv_cache_vector_amd.turboquant import TurboQuant
+
+pytestmark = pytest.mark.gpu
+D = 128
+
+
+@pytest.fixture(scope="module")
+def dev():
+    assert torch.cuda.is_available(), "GPU tests need an AMD Instinct GPU"
+    _lib.load()            # raises when libtq.so was not built
+    return torch.device("cuda:0")
+
+
+def run_codec(x_np, bits, seed, dev, what):
+    P.log("[codec] %s: n=%d bits=%d seed=%d" % (what, x_np.shape[0], bits, seed))
+    tq = TurboQuant(D, bits, seed, dev)
+    x = torch.from_numpy(np.ascontiguousarray(x_np)).to(dev)
+    gp, gn = tq.encode(x)
+    torch.cuda.synchronize()
+    gp, gn = gp.cpu().numpy(), gn.cpu().numpy()
+    rp, rn, z = oracle.encode(x_np, bits, seed, want_z=True)
+    _, t = oracle.codebook(bits)
+    band = P.compare_codes(gp, rp, z, t, bits, what)
+    P.compare_norms(gn, rn, what)
+    gd = tq.decode(torch.from_numpy(rp).to(dev), torch.from_numpy(rn).to(dev))
+    torch.cuda.synchronize()
+    _, xh = oracle.decode(rp, rn, D, bits, seed, want_f64=True)
+    P.compare_decoded(gd.cpu().numpy(), xh, rn, what)
+    return band
+
+
+def test_outlier_channels_4bit(dev):
+    """1 layer x 8 KV heads x 512 tokens, channels 7 and 93 x20, codec seed 0."""
+    x = W.outlier_channels_fixed()
+    run_codec(x, 4, 0, dev, "outliers-x20 b4")
+
+
+@pytest.mark.parametrize("bits", [3, 2])
+def test_student_t(dev, bits):
+    x = W.llama8b_layer(0, dist="student_t", tokens=256)
+    run_codec(x, bits, 0, dev, "student-t b%d" % bits)
+
+
+def test_scaled_heads_2bit(dev):
+    x = W.llama70b_layer(5, tokens=1024)
+    run_codec(x, 2, 5, dev, "per-head scales b2")
+
+
+@pytest.mark.parametrize("bits", [4, 3, 2])
+def test_gaussian_outliers_all_bits(dev, bits):
+    x = W.llama8b_layer(3, tokens=128)
+    run_codec(x, bits, 3, dev, "gauss+1%% outliers b%d" % bits)
+
+
+def _special_vectors(seed=0):
+    rng = np.random.default_rng(seed)
+    s = oracle.signs(seed, D)
+    rows = []
+    rows.append(np.zeros(D))                                  # zero vector
+    for k in (0, 31, 32, 64, 127):                            # rotate to exact +-1
+        e = np.zeros(D)
+        e[k] = s[k]
+        rows.append(e)
+    rows.append(np.full(D, 65504.0))                           # largest fp16
+    rows.append(np.full(D, 2.0 ** -24))                        # smallest subnormal
+    t = np.zeros(D)
+    t[[3, 77]] = 1.0                                           # z has exact zeros
+    rows.append(t)
+    rows.append(-t)
+    rows.append(np.where(np.arange(D) % 2 == 0, 1.0, -1.0))
+    for _ in range(8):
+        rows.append(rng.standard_normal(D) * 10.0 ** rng.uniform(-4, 4))
+    return np.array(rows).astype(np.float16)
+
+
+@pytest.mark.parametrize("bits", [4, 3, 2])
+def test_special_vectors(dev, bits):
+    run_codec(_special_vectors(), bits, 0, dev, "special b%d" % bits)
+
+
+@pytest.mark.parametrize("bits", [4, 3, 2])
+def test_ragged_counts_and_guard_bytes(dev, bits):
+    """Counts that leave partial quads, waves and blocks; nothing outside the
+    n rows may be written."""
+    Pb = D * bits // 8
+    for n in (1, 2, 3, 5, 15, 16, 17, 63, 64, 65, 127, 1000, 4097):
+        x_np = W.gaussian(n, seed=n)
+        x = torch.from_numpy(x_np).to(dev)
+        guard = 256
+        packed = torch.full((n * Pb + guard,), 0xA5, dtype=torch.uint8, device=dev)
+        norms = torch.full((n + 64,), -7.0, dtype=torch.float32, device=dev)
+        st = _lib.tq_encode(x.data_ptr(), n, D, bits, 11, packed.data_ptr(), norms.data_ptr(),
+                            torch.cuda.current_stream().cuda_stream)
+        assert st == 0
+        out = torch.full((n * D + 512,), 1234.0, dtype=torch.float16, device=dev)
+        st = _lib.tq_decode(packed.data_ptr(), norms.data_ptr(), n, D, bits, 11, out.data_ptr(),
+                            torch.cuda.current_stream().cuda_stream)
+        assert st == 0
+        torch.cuda.synchronize()
+        pk = packed.cpu().numpy()
+        nm = norms.cpu().numpy()
+        assert np.all(pk[n * Pb:] == 0xA5), n
+        assert np.all(nm[n:] == -7.0), n
+        assert np.all(out.cpu().numpy()[n * D:] == 1234.0), n
+        rp, rn, z = oracle.encode(x_np, bits, 11, want_z=True)
+        _, t = oracle.codebook(bits)
+        P.compare_codes(pk[: n * Pb].reshape(n, Pb), rp, z, t, bits, "n=%d" % n)
+        P.compare_norms(nm[:n], rn, "n=%d" % n)
+
+
+def test_zero_count_is_noop(dev):
+    buf = torch.full((64,), 3, dtype=torch.uint8, device=dev)
+    s = torch.cuda.current_stream().cuda_stream
+    assert _lib.tq_encode(buf.data_ptr(), 0, D, 4, 0, buf.data_ptr(), buf.data_ptr(), s) == 0
+    assert _lib.tq_decode(buf.data_ptr(), buf.data_ptr(), 0, D, 4, 0, buf.data_ptr(), s) == 0
+    torch.cuda.synchronize()
+    assert torch.all(buf == 3)
+
+
+def test_deterministic_and_scale_invariant(dev):
+    """Two runs give the same bytes; scaling the input by 2^k leaves the codes
+    unchanged and scales the norms by exactly 2^k."""
+    x_np = W.gaussian(4096, seed=7)
+    x_np = np.where(np.abs(x_np) < 0.05, np.float16(0.05), x_np).astype(np.float16)
+    tq = TurboQuant(D, 4, 9, dev)
+    x = torch.from_numpy(x_np).to(dev)
+    p1, n1 = tq.encode(x)
+    p2, n2 = tq.encode(x)
+    assert torch.equal(p1, p2) and torch.equal(n1, n2)
+    for k in (-2, 3):
+        p3, n3 = tq.encode(x * (2.0 ** k))
+        assert torch.equal(p3, p1)
+        assert torch.equal(n3, n1 * (2.0 ** k))
+
+
+@pytest.mark.parametrize("bits", [4, 3, 2])
+def test_encode_paged(dev, bits):
+    """Encoding into scattered cache rows writes exactly the rows tq_encode
+    would, skips negative and out-of-range slots, and touches nothing else."""
+    rng = np.random.default_rng(bits)
+    nblk, bs, hkv = 40, 16, 8
+    num_slots = nblk * bs * hkv
+    n = 300
+    x_np = W.gaussian(n, seed=100 + bits)
+    slots_np = rng.permutation(num_slots)[:n].astype(np.int64)
+    slots_np[5] = -1
+    slots_np[17] = num_slots + 3
+    tq = TurboQuant(D, bits, 42, dev)
+    Pb = tq.packed_dim
+    cache_p = torch.full((nblk, bs, hkv, Pb), 0x5A, dtype=torch.uint8, device=dev)
+    cache_n = torch.full((nblk, bs, hkv), -1.0, dtype=torch.float32, device=dev)
+    x = torch.from_numpy(x_np).to(dev)
+    tq.encode_into(x, torch.from_numpy(slots_np).to(dev), cache_p, cache_n)
+    torch.cuda.synchronize()
+    cp = cache_p.cpu().numpy().reshape(num_slots, Pb)
+    cn = cache_n.cpu().numpy().reshape(num_slots)
+    rp, rn, z = oracle.encode(x_np, bits, 42, want_z=True)
+    _, t = oracle.codebook(bits)
+    keep = (slots_np >= 0) & (slots_np < num_slots)
+    P.compare_codes(cp[slots_np[keep]], rp[keep], z[keep], t, bits, "paged b%d" % bits)
+    P.compare_norms(cn[slots_np[keep]], rn[keep], "paged b%d" % bits)
+    untouched = np.ones(num_slots, bool)
+    untouched[slots_np[keep]] = False
+    assert np.all(cp[untouched] == 0x5A) and np.all(cn[untouched] == -1.0)
+
+
+# ---------------------------------------------------------------------------
+# full-size caches, in the launch configuration the benchmark times
+# ---------------------------------------------------------------------------
+
+def _upload_llama8b(dev, dist):
+    """All 32 layers of the 8B-shaped cache in one device tensor
+    [16,777,216, 128] fp16 (4 GiB), generated layer by layer."""
+    per = 2 * 4 * 8 * 8192
+    x = torch.empty((32 * per, D), dtype=torch.float16, device=dev)
+    for layer in range(32):
+        x[layer * per:(layer + 1) * per] = torch.from_numpy(W.llama8b_layer(layer, dist=dist)).to(dev)
+    return x, per
+
+
+def _full_size(dev, dist, bits, seed, what, nsample=4096):
+    x, per = _upload_llama8b(dev, dist)
+    n = x.shape[0]
+    P.log("[codec] %s: full size n=%d bits=%d (one launch)" % (what, n, bits))
+    tq = TurboQuant(D, bits, seed, dev)
+    packed, norms = tq.encode(x)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(12345)
+    rows = np.sort(rng.choice(n, nsample, replace=False))
+    # include the first, last and a 2^31-byte-crossing row
+    rows = np.unique(np.concatenate([rows, [0, n - 1, (1 << 31) // 256, (1 << 31) // 256 + 1]]))
+    ridx = torch.from_numpy(rows).to(dev)
+    xs = x[ridx].cpu().numpy()
+    rp, rn, z = oracle.encode(xs, bits, seed, want_z=True)
+    _, t = oracle.codebook(bits)
+    band, _ = P.compare_codes(packed[ridx].cpu().numpy(), rp, z, t, bits, what)
+    P.compare_norms(norms[ridx].cpu().numpy(), rn, what)
+    assert band <= 1e-5 * 3   # reported; the expected fraction is a few 1e-6
+    # decode: the sampled rows carry the oracle's own codes
+    packed[ridx] = torch.from_numpy(rp).to(dev)
+    norms[ridx] = torch.from_numpy(rn).to(dev)
+    del x
+    out = tq.decode(packed, norms)
+    torch.cuda.synchronize()
+    _, xh = oracle.decode(rp, rn, D, bits, seed, want_f64=True)
+    P.compare_decoded(out[ridx].cpu().numpy(), xh, rn, what)
+
+
+def test_full_size_llama8b_4bit(dev):
+    _full_size(dev, "gauss_outliers", 4, 0, "llama8b cache b4")
+
+
+@pytest.mark.parametrize("bits", [3, 2])
+def test_full_size_llama8b_student_t(dev, bits):
+    _full_size(dev, "student_t", bits, 0, "llama8b student-t b%d" % bits, nsample=2048)
+
+
+@pytest.mark.parametrize("layer", [0, 79])
+def test_llama70b_128k_layer_2bit(dev, layer):
+    """One layer of the 70B-class 128K cache (2,097,152 vectors), the unit of
+    the layer-by-layer streaming encode, codec seed = layer."""
+    x_np = W.llama70b_layer(layer)
+    x = torch.from_numpy(x_np).to(dev)
+    P.log("[codec] llama70b layer %d: n=%d b2" % (layer, x.shape[0]))
+    tq = TurboQuant(D, 2, layer, dev)
+    packed, norms = tq.encode(x)
+    torch.cuda.synchronize()
+    rows = np.sort(np.random.default_rng(layer).choice(x.shape[0], 4096, replace=False))
+    rp, rn, z = oracle.encode(x_np[rows], 2, layer, want_z=True)
+    _, t = oracle.codebook(2)
+    ridx = torch.from_numpy(rows).to(dev)
+    P.compare_codes(packed[ridx].cpu().numpy(), rp, z, t, 2, "llama70b L%d" % layer)
+    P.compare_norms(norms[ridx].cpu().numpy(), rn, "llama70b L%d" % layer)
