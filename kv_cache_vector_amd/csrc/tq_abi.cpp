@@ -111,7 +111,48 @@ CodecConsts make_consts(int bits, uint64_t seed) {
     const int L = 1 << bits;
     for (int i = 0; i < L; ++i) k.level[i] = cb.level[i];
     for (int i = 0; i < L - 1; ++i) k.thr8[i] = 8.0f * cb.thr[i];
+    k.one = 1.0f;
     return k;
+}
+
+// Cells of y = 8 z: cell i > 0 is [i, i+1), i < 0 is (i-1, i], i = 0 is
+// (-1, 1).  The narrowest gap between two thresholds at 4 bits is 0.258, i.e.
+// 2.07 in y units, so no cell holds more than one threshold.
+tq::EncTable make_enc_table(int bits) {
+    tq::EncTable t{};
+    const Codebook &cb = codebook(bits);
+    const int L = 1 << bits;
+    for (int c = 0; c < 2 * tq::kEncCells + 1; ++c) {
+        const int i = c - tq::kEncCells;
+        const float lo = (i > 0) ? float(i) : float(i - 1);
+        const float hi = (i < 0) ? float(i) : float(i + 1);
+        uint32_t base = 0;
+        float thr = INFINITY;
+        for (int j = 0; j < L - 1; ++j) {
+            const float T = 8.0f * cb.thr[j];
+            if (T < lo) ++base;
+            else if (T <= hi) thr = T;
+        }
+        // 4 bits: the four bytes hold base, base + 1, and both shifted into
+        // the high nibble, for the kernel's byte-select packing; otherwise
+        // the plain base code
+        uint32_t bb = (bits == 4) ? (base | (base + 1) << 8 | (base << 4) << 16 |
+                                     ((base + 1) << 4) << 24)
+                                  : base;
+        float bf;
+        std::memcpy(&bf, &bb, 4);
+        t.cell[c] = make_float2(thr, bf);
+    }
+    return t;
+}
+
+const tq::EncTable &enc_table(int bits) {
+    static tq::EncTable tabs[5];
+    static std::once_flag once;
+    std::call_once(once, [] {
+        for (int b = 2; b <= 4; ++b) tabs[b] = make_enc_table(b);
+    });
+    return tabs[bits];
 }
 
 bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
@@ -185,8 +226,8 @@ tq_status tq_encode(const void *x_f16, int64_t n, int head_dim, int bits, uint64
         overlap(packed, np, norms, nn))
         return TQ_ERR_INVALID_ARG;
     const CodecConsts k = make_consts(bits, seed);
-    return from_hip(tq::launch_encode(bits, x_f16, n, nullptr, 0, k, packed, norms,
-                                      (hipStream_t)stream));
+    return from_hip(tq::launch_encode(bits, x_f16, n, nullptr, 0, k, enc_table(bits), packed,
+                                      norms, (hipStream_t)stream));
 }
 
 tq_status tq_encode_paged(const void *x_f16, const int64_t *slots, int64_t n, int head_dim,
@@ -208,8 +249,8 @@ tq_status tq_encode_paged(const void *x_f16, const int64_t *slots, int64_t n, in
         overlap(cache_packed, np, cache_norms, nn))
         return TQ_ERR_INVALID_ARG;
     const CodecConsts k = make_consts(bits, seed);
-    return from_hip(tq::launch_encode(bits, x_f16, n, slots, num_slots, k, cache_packed,
-                                      cache_norms, (hipStream_t)stream));
+    return from_hip(tq::launch_encode(bits, x_f16, n, slots, num_slots, k, enc_table(bits),
+                                      cache_packed, cache_norms, (hipStream_t)stream));
 }
 
 tq_status tq_decode(const uint8_t *packed, const float *norms, int64_t n, int head_dim,
