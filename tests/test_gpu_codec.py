@@ -191,6 +191,8 @@ def _upload_llama8b(dev, dist):
     x = torch.empty((32 * per, D), dtype=torch.float16, device=dev)
     for layer in range(32):
         x[layer * per:(layer + 1) * per] = torch.from_numpy(W.llama8b_layer(layer, dist=dist)).to(dev)
+        if layer % 8 == 7:
+            P.log("  generated and uploaded layer %d/32 (%s)" % (layer + 1, dist))
     return x, per
 
 
