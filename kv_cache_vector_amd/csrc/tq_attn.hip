@@ -40,6 +40,8 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kPartial = 2 + kHeadDim;      // m, l, acc[128] per workspace entry
 constexpr float kLazy = 8.0f;               // rescale when a score passes m + 8 (base 2)
 constexpr int kTargetGroups = 512;          // split-kernel workgroups aimed for
+constexpr int kMaxSplitTokens = 4096;       // block-table entries of a split staged in LDS
+constexpr int kPrefetch = 4;                // wave steps of K/V loads kept in flight
 
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
@@ -52,6 +54,17 @@ template <int CTRL>
 __device__ __forceinline__ float dpp(float v) {
     return __builtin_bit_cast(
         float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
+}
+
+// Value of lane h of this lane's quad (quad_perm [h,h,h,h]).
+__device__ __forceinline__ float quad_bcast(float v, int h) {
+    const int x = __builtin_bit_cast(int, v);
+    switch (h & 3) {
+        case 0: return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(x, 0x00, 0xF, 0xF, true));
+        case 1: return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(x, 0x55, 0xF, 0xF, true));
+        case 2: return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(x, 0xAA, 0xF, 0xF, true));
+        default: return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(x, 0xFF, 0xF, 0xF, true));
+    }
 }
 
 // Sum over the LPU lanes of a unit (LPU = 8 or 16, aligned groups).
@@ -88,27 +101,40 @@ __device__ __forceinline__ int sign_of(const CodecConsts &k, int i) {
     return (k.sign[i >> 5] >> (i & 31)) & 1;
 }
 
-// Codes of this lane's E coordinates -> f32 codebook values.
+// Buffer resource over `bytes` bytes at `base` (wave-uniform).  Loads through
+// it take a scalar base and a 32-bit per-lane offset, and read 0 outside the
+// range instead of faulting.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t page_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, 0x00020000);
+}
+
+// This lane's E codes (E * BITS / 8 bytes at byte offset `off`).
 template <int BITS, int E>
-__device__ __forceinline__ void load_codes(const uint8_t *row, int sub, uint32_t (&c)[2]) {
+__device__ __forceinline__ void load_codes_buf(__amdgpu_buffer_rsrc_t r, uint32_t off,
+                                               uint32_t (&c)[2]) {
     constexpr int BYTES = E * BITS / 8;
-    const uint8_t *p = row + sub * BYTES;
-    if (BYTES == 8) {
-        const u32x2 u = *reinterpret_cast<const u32x2 *>(p);
+    if constexpr (BYTES == 8) {
+        typedef uint32_t u2 __attribute__((ext_vector_type(2)));
+        const u2 u = __builtin_bit_cast(u2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
         c[0] = u.x;
         c[1] = u.y;
-    } else if (BYTES == 4) {
-        c[0] = *reinterpret_cast<const uint32_t *>(p);
+    } else if constexpr (BYTES == 4) {
+        c[0] = __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
         c[1] = 0;
-    } else if (BYTES == 6) {   // b = 3, E = 16: 2-byte aligned
-        const uint16_t *h = reinterpret_cast<const uint16_t *>(p);
-        c[0] = (uint32_t)h[0] | ((uint32_t)h[1] << 16);
-        c[1] = h[2];
-    } else if (BYTES == 2) {   // b = 2, E = 8
-        c[0] = *reinterpret_cast<const uint16_t *>(p);
+    } else if constexpr (BYTES == 6) {   // b = 3, E = 16: 2-byte aligned
+        const uint32_t h0 = __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+        const uint32_t h1 = __builtin_amdgcn_raw_buffer_load_b16(r, off + 2, 0, 0);
+        const uint32_t h2 = __builtin_amdgcn_raw_buffer_load_b16(r, off + 4, 0, 0);
+        c[0] = h0 | (h1 << 16);
+        c[1] = h2;
+    } else if constexpr (BYTES == 2) {   // b = 2, E = 8
+        c[0] = __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
         c[1] = 0;
-    } else {                   // b = 3, E = 8: 3 bytes, byte aligned
-        c[0] = (uint32_t)p[0] | ((uint32_t)p[1] << 8) | ((uint32_t)p[2] << 16);
+    } else {                             // b = 3, E = 8: 3 bytes, byte aligned
+        const uint32_t b0 = __builtin_amdgcn_raw_buffer_load_b8(r, off, 0, 0);
+        const uint32_t b1 = __builtin_amdgcn_raw_buffer_load_b8(r, off + 1, 0, 0);
+        const uint32_t b2 = __builtin_amdgcn_raw_buffer_load_b8(r, off + 2, 0, 0);
+        c[0] = b0 | (b1 << 8) | (b2 << 16);
         c[1] = 0;
     }
 }
@@ -173,8 +199,16 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(AttnParams p) {
 #pragma unroll
         for (int j = 0; j < G; ++j) tab[G * t + j] = p.k.level[(t >> (BITS * j)) & (L - 1)];
     }
+    // block-table entries of this split's pages (read before the token loop so
+    // the code loads of a token do not wait on a dependent global load)
+    __shared__ int32_t bt_lds[kMaxSplitTokens / kAttnBlockSize];
+    {
+        const int32_t *bt = p.block_tables + (size_t)b * p.max_blocks + t0 / kAttnBlockSize;
+        const int npages = (t1 - t0 + kAttnBlockSize - 1) / kAttnBlockSize;
+        for (int i = threadIdx.x; i < npages; i += kThreads) bt_lds[i] = bt[i];
+    }
 
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
     const int lane = threadIdx.x & 63;
     const int gam = lane / LPU;          // unit slot in the wave
     const int sub = lane % LPU;          // coordinate slice [sub*E, sub*E + E)
@@ -216,84 +250,171 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(AttnParams p) {
     }
     __syncthreads();
 
-    float m[GRP], l[GRP], acc[GRP][E];
+    float acc[GRP][E];
 #pragma unroll
-    for (int hh = 0; hh < GRP; ++hh) {
-        m[hh] = -__builtin_inff();
-        l[hh] = 0.0f;
+    for (int hh = 0; hh < GRP; ++hh)
 #pragma unroll
         for (int e = 0; e < E; ++e) acc[hh][e] = 0.0f;
+    // Softmax state.  With at most 4 query heads per kv head, lane q of each
+    // quad of a unit owns head q % GRP: it alone runs the online softmax of
+    // that head, and the value weights reach the other lanes by DPP
+    // broadcast within the quad.  With 8 query heads every lane runs all of
+    // them.
+    constexpr bool SPLIT = GRP <= 4;
+    constexpr int NS = SPLIT ? 1 : GRP;          // softmax states per lane
+    const int hown = sub % GRP;
+    float m[NS], l[NS];
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+        m[i] = -__builtin_inff();
+        l[i] = 0.0f;
     }
 
-    const int32_t *bt = p.block_tables + (size_t)b * p.max_blocks;
     const int step = kWaves * tpi;
-    for (int tb = t0 + wave * tpi; tb < t1; tb += step) {   // wave-uniform loop
-        const int t = tb + tau;
-        const bool act = live && (t < t1);
-        int32_t blk = act ? bt[t / kAttnBlockSize] : 0;
-        const bool ok = act && blk >= 0 && blk < p.num_blocks;
-        blk = ok ? blk : 0;
-        const int64_t row = ((int64_t)blk * kAttnBlockSize + (t % kAttnBlockSize)) * p.hkv + g;
-        uint32_t kc[2] = {0, 0}, vc[2] = {0, 0};
-        float knv = 0.0f, vnv = 0.0f;
-        if (ok) {
-            load_codes<BITS, E>(p.kp + row * P, sub, kc);
-            load_codes<BITS, E>(p.vp + row * P, sub, vc);
-            knv = p.kn[row];
-            vnv = p.vn[row];
-        }
-        float val[E];
-        expand<BITS, E>(tab, kc, val);
-        float s[GRP];
+    const int tfirst = t0 + wave * tpi + tau;    // this lane group's first token
+    // tokens tb = t0 + wave*tpi + i*step (i < nsteps) are this wave's steps
+    const int nsteps = (t1 - (t0 + wave * tpi) + step - 1) / step;
+
+    // K/V codes and norms of step i, loaded kPrefetch steps ahead of use into
+    // a ring of kPrefetch + 1 slots (the slot refilled is the one used by the
+    // previous step, so nothing is copied).
+    //
+    // All lanes of a wave step read the same 16-token page (a step covers tpi
+    // tokens, tpi divides 16, and steps start on multiples of tpi), so the
+    // page's block number and the step's row inside the page are
+    // wave-uniform: they form a scalar base address, and every lane adds the
+    // same per-lane byte offset each step.
+    constexpr int R = kPrefetch + 1;
+    const uint32_t lane_row = (uint32_t)(tau * p.hkv + g);          // row within a token's rows
+    const uint32_t lane_code = lane_row * P + (uint32_t)(sub * (E * BITS / 8));
+    const uint32_t lane_norm = lane_row * 4u;
+    const uint64_t page_rows = (uint64_t)kAttnBlockSize * p.hkv;    // rows per block
+    const uint32_t step_rows = (uint32_t)(tpi * p.hkv);             // rows read per step
+    uint32_t rk[R][2], rv[R][2];
+    float rkn[R], rvn[R];
+    bool rok[R];
+    auto fetch = [&](int i, int slot) {
+        const int tb = t0 + wave * tpi + i * step;                    // wave-uniform
+        int32_t blk = (tb < t1) ? bt_lds[(tb - t0) / kAttnBlockSize] : 0;
+        blk = __builtin_amdgcn_readfirstlane(blk);
+        const bool bok = blk >= 0 && blk < p.num_blocks;
+        blk = bok ? blk : 0;
+        rok[slot] = bok && live && (tb + tau < t1);
+        // first row of this step: block * rows-per-block + token-in-page * hkv;
+        // the step's rows are [row0, row0 + step_rows)
+        const uint64_t row0 = (uint64_t)blk * page_rows + (uint64_t)((tb % kAttnBlockSize) * p.hkv);
+        // unconditional loads: a step past the end reads block 0, which exists
+        // whenever any token does; its score is masked below
+        load_codes_buf<BITS, E>(page_rsrc(p.kp + row0 * P, step_rows * P), lane_code, rk[slot]);
+        load_codes_buf<BITS, E>(page_rsrc(p.vp + row0 * P, step_rows * P), lane_code, rv[slot]);
+        rkn[slot] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                  page_rsrc(p.kn + row0, step_rows * 4), lane_norm, 0, 0));
+        rvn[slot] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                  page_rsrc(p.vn + row0, step_rows * 4), lane_norm, 0, 0));
+    };
 #pragma unroll
-        for (int hh = 0; hh < GRP; ++hh) {
-            float d = 0.0f;
+    for (int d = 0; d < kPrefetch; ++d) fetch(d, d);
+
+    for (int i0 = 0; i0 < nsteps; i0 += R) {     // wave-uniform
 #pragma unroll
-            for (int e = 0; e < E; ++e) d = __builtin_fmaf(qt[hh][e], val[e], d);
-            s[hh] = ok ? unit_sum<LPU>(d) * knv : -__builtin_inff();
-        }
-        // lazily raised reference: rescale only when some score passes m + 8
-        bool need = false;
-#pragma unroll
-        for (int hh = 0; hh < GRP; ++hh) need |= s[hh] > m[hh] + kLazy;
-        if (__builtin_amdgcn_ballot_w64(need)) {
+        for (int d = 0; d < R; ++d) {
+            if (i0 + d >= nsteps) break;
+            fetch(i0 + d + kPrefetch, (d + kPrefetch) % R);
+            const bool ok = rok[d];
+            float val[E];
+            expand<BITS, E>(tab, rk[d], val);
+            float s[GRP];
 #pragma unroll
             for (int hh = 0; hh < GRP; ++hh) {
-                const float mn = (s[hh] > m[hh] + kLazy) ? s[hh] : m[hh];
-                const float a = (mn == m[hh]) ? 1.0f : __builtin_amdgcn_exp2f(m[hh] - mn);
-                l[hh] *= a;
+                float dd = 0.0f;
 #pragma unroll
-                for (int e = 0; e < E; ++e) acc[hh][e] *= a;
-                m[hh] = mn;
+                for (int e = 0; e < E; ++e) dd = __builtin_fmaf(qt[hh][e], val[e], dd);
+                s[hh] = unit_sum<LPU>(dd) * rkn[d];
             }
-        }
-        expand<BITS, E>(tab, vc, val);
+            if constexpr (!SPLIT) {
 #pragma unroll
-        for (int hh = 0; hh < GRP; ++hh) {
-            const float pr = ok ? __builtin_amdgcn_exp2f(s[hh] - m[hh]) : 0.0f;
-            l[hh] += pr;
-            const float w = pr * vnv;
+                for (int hh = 0; hh < GRP; ++hh) s[hh] = ok ? s[hh] : -__builtin_inff();
+            }
+            float w[GRP];
+            if constexpr (SPLIT) {
+                float so = s[0];
 #pragma unroll
-            for (int e = 0; e < E; ++e) acc[hh][e] = __builtin_fmaf(w, val[e], acc[hh][e]);
+                for (int hh = 1; hh < GRP; ++hh) so = (hown == hh) ? s[hh] : so;
+                so = ok ? so : -__builtin_inff();
+                // lazily raised reference: rescale only when a score passes m + 8
+                if (__builtin_amdgcn_ballot_w64(so > m[0] + kLazy)) {
+                    const float mn = (so > m[0] + kLazy) ? so : m[0];
+                    const float a = (mn == m[0]) ? 1.0f : __builtin_amdgcn_exp2f(m[0] - mn);
+                    l[0] *= a;
+                    m[0] = mn;
+#pragma unroll
+                    for (int hh = 0; hh < GRP; ++hh) {
+                        const float ah = quad_bcast(a, hh);
+#pragma unroll
+                        for (int e = 0; e < E; ++e) acc[hh][e] *= ah;
+                    }
+                }
+                const float pr = ok ? __builtin_amdgcn_exp2f(so - m[0]) : 0.0f;
+                l[0] += pr;
+                const float wo = pr * rvn[d];
+#pragma unroll
+                for (int hh = 0; hh < GRP; ++hh) w[hh] = quad_bcast(wo, hh);
+            } else {
+                bool need = false;
+#pragma unroll
+                for (int hh = 0; hh < GRP; ++hh) need |= s[hh] > m[hh % NS] + kLazy;
+                if (__builtin_amdgcn_ballot_w64(need)) {
+#pragma unroll
+                    for (int hh = 0; hh < GRP; ++hh) {
+                        const int i = hh % NS;
+                        const float mn = (s[hh] > m[i] + kLazy) ? s[hh] : m[i];
+                        const float a = (mn == m[i]) ? 1.0f : __builtin_amdgcn_exp2f(m[i] - mn);
+                        l[i] *= a;
+#pragma unroll
+                        for (int e = 0; e < E; ++e) acc[hh][e] *= a;
+                        m[i] = mn;
+                    }
+                }
+#pragma unroll
+                for (int hh = 0; hh < GRP; ++hh) {
+                    const int i = hh % NS;
+                    const float pr = ok ? __builtin_amdgcn_exp2f(s[hh] - m[i]) : 0.0f;
+                    l[i] += pr;
+                    w[hh] = pr * rvn[d];
+                }
+            }
+            expand<BITS, E>(tab, rv[d], val);
+#pragma unroll
+            for (int hh = 0; hh < GRP; ++hh)
+#pragma unroll
+                for (int e = 0; e < E; ++e) acc[hh][e] = __builtin_fmaf(w[hh], val[e], acc[hh][e]);
         }
+    }
+
+    // every lane gets the softmax state of all its heads for the merges
+    float mh[GRP], lh[GRP];
+#pragma unroll
+    for (int hh = 0; hh < GRP; ++hh) {
+        mh[hh] = SPLIT ? quad_bcast(m[0], hh) : m[hh % NS];
+        lh[hh] = SPLIT ? quad_bcast(l[0], hh) : l[hh % NS];
     }
 
     // merge the TPI units of the same kv head inside the wave (narrow caches)
     for (int off = p.hkv * LPU; off < tpi * p.hkv * LPU; off <<= 1) {
 #pragma unroll
         for (int hh = 0; hh < GRP; ++hh) {
-            const float mo = __shfl_xor(m[hh], off);
-            const float lo = __shfl_xor(l[hh], off);
-            const float mn = m[hh] > mo ? m[hh] : mo;
-            const float a = (m[hh] == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(m[hh] - mn);
+            const float mo = __shfl_xor(mh[hh], off);
+            const float lo = __shfl_xor(lh[hh], off);
+            const float mn = mh[hh] > mo ? mh[hh] : mo;
+            const float a = (mh[hh] == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(mh[hh] - mn);
             const float ao = (mo == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(mo - mn);
-            l[hh] = l[hh] * a + lo * ao;
+            lh[hh] = lh[hh] * a + lo * ao;
 #pragma unroll
             for (int e = 0; e < E; ++e) {
                 const float o = __shfl_xor(acc[hh][e], off);
                 acc[hh][e] = acc[hh][e] * a + o * ao;
             }
-            m[hh] = mn;
+            mh[hh] = mn;
         }
     }
 
@@ -303,8 +424,8 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(AttnParams p) {
         for (int hh = 0; hh < GRP; ++hh) {
 #pragma unroll
             for (int e = 0; e < E; ++e) buf[(hh * E + e) * 64 + lane] = acc[hh][e];
-            buf[(GRP * E + 2 * hh) * 64 + lane] = m[hh];
-            buf[(GRP * E + 2 * hh + 1) * 64 + lane] = l[hh];
+            buf[(GRP * E + 2 * hh) * 64 + lane] = mh[hh];
+            buf[(GRP * E + 2 * hh + 1) * 64 + lane] = lh[hh];
         }
     };
     auto take = [&](const float *buf) {
@@ -312,14 +433,14 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(AttnParams p) {
         for (int hh = 0; hh < GRP; ++hh) {
             const float mo = buf[(GRP * E + 2 * hh) * 64 + lane];
             const float lo = buf[(GRP * E + 2 * hh + 1) * 64 + lane];
-            const float mn = m[hh] > mo ? m[hh] : mo;
-            const float a = (m[hh] == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(m[hh] - mn);
+            const float mn = mh[hh] > mo ? mh[hh] : mo;
+            const float a = (mh[hh] == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(mh[hh] - mn);
             const float ao = (mo == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(mo - mn);
-            l[hh] = l[hh] * a + lo * ao;
+            lh[hh] = lh[hh] * a + lo * ao;
 #pragma unroll
             for (int e = 0; e < E; ++e)
                 acc[hh][e] = acc[hh][e] * a + buf[(hh * E + e) * 64 + lane] * ao;
-            m[hh] = mn;
+            mh[hh] = mn;
         }
     };
     if (wave >= 2) put(xchg[wave - 2]);
@@ -336,8 +457,8 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(AttnParams p) {
         const int h = g * GRP + hh;
         float *dst = p.ws + (((size_t)b * p.hq + h) * p.num_splits + split) * kPartial;
         if (sub == 0) {
-            dst[0] = m[hh];
-            dst[1] = l[hh];
+            dst[0] = mh[hh];
+            dst[1] = lh[hh];
         }
 #pragma unroll
         for (int e = 0; e < E; ++e) dst[2 + sub * E + e] = acc[hh][e];
@@ -357,21 +478,44 @@ __global__ __launch_bounds__(64) void attn_combine_kernel(AttnParams p) {
     const int ns = (T + p.split_tokens - 1) / p.split_tokens;
     const float *src = p.ws + (size_t)bh * p.num_splits * kPartial;
 
+    // the largest running maximum over the splits (lane s reads split s)
     float mx = -__builtin_inff();
-    for (int s = 0; s < ns; ++s) {
-        const float ms = src[s * kPartial];
-        mx = ms > mx ? ms : mx;
+    for (int s0 = 0; s0 < ns; s0 += 64) {
+        const int s = s0 + lane;
+        if (s < ns) {
+            const float ms = src[(size_t)s * kPartial];
+            mx = ms > mx ? ms : mx;
+        }
     }
-    float l = 0.0f, a0 = 0.0f, a1 = 0.0f;   // this lane: coordinates 2*lane, 2*lane+1
-    for (int s = 0; s < ns; ++s) {
-        const float *e = src + s * kPartial;
-        if (e[1] == 0.0f) continue;
-        const float w = __builtin_amdgcn_exp2f(e[0] - mx);
-        l += w * e[1];
-        a0 += w * e[2 + 2 * lane];
-        a1 += w * e[3 + 2 * lane];
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        const float other = __shfl_xor(mx, o);
+        mx = other > mx ? other : mx;
     }
-    const float inv = (l > 0.0f) ? 1.0f / l : 0.0f;
+    // split weights, then this lane's coordinates 2*lane, 2*lane+1
+    float lsum = 0.0f, a0 = 0.0f, a1 = 0.0f;
+    for (int s0 = 0; s0 < ns; s0 += 64) {
+        const int s = s0 + lane;
+        float w = 0.0f;
+        if (s < ns) {
+            const float ls = src[(size_t)s * kPartial + 1];
+            w = (ls > 0.0f) ? __builtin_amdgcn_exp2f(src[(size_t)s * kPartial] - mx) : 0.0f;
+            lsum += w * ls;
+        }
+        const int cnt = (ns - s0 < 64) ? ns - s0 : 64;
+#pragma unroll 8
+        for (int j = 0; j < cnt; ++j) {
+            const float wj = __builtin_bit_cast(
+                float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), j));
+            const float2 e =
+                *reinterpret_cast<const float2 *>(src + (size_t)(s0 + j) * kPartial + 2 + 2 * lane);
+            a0 = __builtin_fmaf(wj, e.x, a0);
+            a1 = __builtin_fmaf(wj, e.y, a1);
+        }
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) lsum += __shfl_xor(lsum, o);
+    const float inv = (lsum > 0.0f) ? 1.0f / lsum : 0.0f;
     // inverse transform: x = D H acc / 128 -- coordinate bit 0 in registers,
     // bits 1..6 across lanes
     float x0 = (a0 + a1) * inv, x1 = (a0 - a1) * inv;
@@ -412,7 +556,8 @@ int attn_split_tokens(const AttnShape &s) {
     const int per_seq = s.batch * zch > 0 ? (kTargetGroups + s.batch * zch - 1) / (s.batch * zch) : 1;
     int st = (ctx + per_seq - 1) / per_seq;
     st = (st + 63) / 64 * 64;
-    return st < 256 ? 256 : st;
+    st = st < 256 ? 256 : st;
+    return st > kMaxSplitTokens ? kMaxSplitTokens : st;
 }
 
 int attn_num_splits(const AttnShape &s) {
