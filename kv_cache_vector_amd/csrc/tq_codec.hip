@@ -122,6 +122,13 @@ __device__ __forceinline__ void fwht_registers_scaled(float (&f)[32], float s) {
     }
 }
 
+// Buffer resource over `bytes` bytes at `base` (wave-uniform).  Accesses
+// through it take a scalar base and a 32-bit per-lane offset; reads outside
+// the range return 0 and writes outside it are dropped.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t span_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, 0x00020000);
+}
+
 // XOR masks flipping the binary16 sign bits of register pair (2i, 2i+1) of
 // lane q, i.e. of coordinates 32(i/4) + 8q + 2(i%4) + {0, 1}.  Thread t < 64
 // writes mask i = t % 16 of lane q = t / 16 to LDS once per block; every lane
@@ -147,6 +154,7 @@ __device__ __forceinline__ void load_sign_masks(const u32x4 *smask, int q, uint3
 // holds base / base + 1 in bytes S0 / S1 (pre-shifted by 0 or 4); a compare
 // against the cell's threshold picks one of them and an SDWA v_cndmask writes
 // it into the byte, leaving the other bytes untouched.
+// The first byte written into a dword (byte 0) zero-pads the rest.
 #define TQ_PUT_CODE(DB, S0, S1)                                                                \
     asm volatile("v_cmp_gt_f32 vcc, %1, %2\n\t"                                                 \
                  "v_cndmask_b32_sdwa %0, %3, %3, vcc dst_sel:BYTE_" #DB                         \
@@ -154,12 +162,19 @@ __device__ __forceinline__ void load_sign_masks(const u32x4 *smask, int q, uint3
                  : "+v"(acc)                                                                    \
                  : "v"(y), "v"(thr), "v"(W)                                                     \
                  : "vcc")
+#define TQ_PUT_FIRST(S0, S1)                                                                   \
+    asm volatile("v_cmp_gt_f32 vcc, %1, %2\n\t"                                                 \
+                 "v_cndmask_b32_sdwa %0, %3, %3, vcc dst_sel:BYTE_0"                            \
+                 " dst_unused:UNUSED_PAD src0_sel:BYTE_" #S0 " src1_sel:BYTE_" #S1               \
+                 : "=v"(acc)                                                                    \
+                 : "v"(y), "v"(thr), "v"(W)                                                     \
+                 : "vcc")
 
 template <int R>
 __device__ __forceinline__ void put_code4(uint32_t &acc, float y, float thr, uint32_t W) {
     constexpr int j = R & 7;
-    if (j == 0) TQ_PUT_CODE(0, 0, 1);
-    if (j == 1) TQ_PUT_CODE(0, 2, 3);
+    if (j == 0) TQ_PUT_FIRST(0, 1);
+    if (j == 1) TQ_PUT_FIRST(2, 3);
     if (j == 2) TQ_PUT_CODE(1, 0, 1);
     if (j == 3) TQ_PUT_CODE(1, 2, 3);
     if (j == 4) TQ_PUT_CODE(2, 0, 1);
@@ -168,6 +183,7 @@ __device__ __forceinline__ void put_code4(uint32_t &acc, float y, float thr, uin
     if (j == 7) TQ_PUT_CODE(3, 2, 3);
 }
 #undef TQ_PUT_CODE
+#undef TQ_PUT_FIRST
 
 template <int R>
 __device__ __forceinline__ void quantize4(const float (&f)[32], const float2 *qtab,
@@ -207,12 +223,19 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(const u32x4 *__restric
     const uint32_t sel2 = (q & 1) ? 0x03020706u : 0x05040100u;
 
     {
-        const int64_t v = (int64_t)blockIdx.x * kVecPerBlock + (threadIdx.x >> 2);
+        // this block's vectors [v0, v0 + nb): scalar base, per-lane offsets
+        const int64_t v0 = (int64_t)blockIdx.x * kVecPerBlock;
+        const uint32_t nb = (uint32_t)((n - v0 < kVecPerBlock) ? n - v0 : kVecPerBlock);
+        const uint32_t qi = threadIdx.x >> 2;
+        const int64_t v = v0 + qi;
         if (v >= n) return;   // uniform over the quad; no barrier follows
+        const __amdgpu_buffer_rsrc_t rx = span_rsrc(x + v0 * 16, nb * 256u);
+        const uint32_t xo = qi * 256u + 16u * q;
         uint32_t w[16];
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-            const u32x4 u = x[v * 16 + 4 * g + q];
+            const u32x4 u = __builtin_bit_cast(
+                u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, xo + 64u * g, 0, 0));
             w[4 * g + 0] = u.x;
             w[4 * g + 1] = u.y;
             w[4 * g + 2] = u.z;
@@ -239,7 +262,10 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(const u32x4 *__restric
         ss += quad_move<kQuadXor1>(ss);
         ss += quad_move<kQuadXor2>(ss);
         const float nrm = __builtin_sqrtf(ss);
-        const float kk = (nrm > 0.0f) ? eps8 / nrm : 0.0f;
+        // 8 eps / nrm: hardware reciprocal refined by one Newton step
+        float rc = __builtin_amdgcn_rcpf(nrm);
+        rc = __builtin_fmaf(rc, __builtin_fmaf(-nrm, rc, 1.0f), rc);
+        const float kk = (nrm > 0.0f) ? eps8 * rc : 0.0f;
 
         fwht_quad(f, ma, mb);
         fwht_registers_scaled<2>(f, kk);   // f[r] = 8 z of coordinate r
@@ -248,7 +274,7 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(const u32x4 *__restric
 #pragma unroll
         for (int i = 0; i < BITS; ++i) pk[i] = 0;
         if (BITS == 4) {
-            uint32_t lo[4] = {0, 0, 0, 0}, hi[4] = {0, 0, 0, 0};
+            uint32_t lo[4], hi[4];
             quantize4<0>(f, qtab, lo, hi);
 #pragma unroll
             for (int g = 0; g < 4; ++g) pk[g % BITS] = lo[g] | hi[g];
@@ -264,24 +290,29 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(const u32x4 *__restric
             }
         }
 
-        int64_t row = v;
-        if (PAGED) {
-            row = slots[v];
-            if (row < 0 || row >= num_slots) return;     // uniform over the quad
-        }
-        uint32_t *dst = packed + row * PW;
+        // the dwords this lane stores and their indices within the packed row
+        uint32_t sv[4];
+        int si[4];
+        int ns = 0;
         if (BITS == 4) {
             // group k of lane q is dword 4k + q
 #pragma unroll
-            for (int g = 0; g < 4; ++g) dst[4 * g + q] = pk[g % BITS];
+            for (int g = 0; g < 4; ++g) {
+                sv[g] = pk[g % BITS];
+                si[g] = 4 * g + q;
+            }
+            ns = 4;
         } else if (BITS == 2) {
             // group k of lane q is half (q & 1) of dword 2k + (q >> 1); lanes
             // q and q^1 splice their halves, each lane stores two dwords
             const uint32_t p0 = quad_move<kQuadXor1>(pk[0]);
             const uint32_t p1 = quad_move<kQuadXor1>(pk[1 % BITS]);
             const int base = 2 * (q & 1) + (q >> 1);
-            dst[base] = __builtin_amdgcn_perm(p0, pk[0], sel2);
-            dst[base + 4] = __builtin_amdgcn_perm(p1, pk[1 % BITS], sel2);
+            sv[0] = __builtin_amdgcn_perm(p0, pk[0], sel2);
+            si[0] = base;
+            sv[1] = __builtin_amdgcn_perm(p1, pk[1 % BITS], sel2);
+            si[1] = base + 4;
+            ns = 2;
         } else {
             // group k of lane q is the 24-bit field at bit 96k + 24q; lane q < 3
             // stores dword 3k + q, made of its field and lane q+1's
@@ -293,12 +324,30 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(const u32x4 *__restric
             const uint32_t sh = 8 * q + 8;
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-                const uint32_t nb = quad_move<kQuadNext>(G[g]);
-                const uint32_t e = __builtin_amdgcn_alignbit(nb, G[g] << 8, sh);
-                if (q < 3) dst[3 * g + q] = e;
+                const uint32_t nbv = quad_move<kQuadNext>(G[g]);
+                sv[g] = __builtin_amdgcn_alignbit(nbv, G[g] << 8, sh);
+                si[g] = 3 * g + q;   // stored only by lanes q < 3
             }
+            ns = 4;
         }
-        if (q == 0) norms[row] = nrm;
+        if (PAGED) {
+            const int64_t row = slots[v];
+            if (row < 0 || row >= num_slots) return;     // uniform over the quad
+            uint32_t *dst = packed + row * PW;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (i < ns && (BITS != 3 || q < 3)) dst[si[i]] = sv[i];
+            if (q == 0) norms[row] = nrm;
+        } else {
+            const __amdgpu_buffer_rsrc_t rp = span_rsrc(packed + v0 * PW, nb * (PW * 4u));
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (i < ns && (BITS != 3 || q < 3))
+                    __builtin_amdgcn_raw_buffer_store_b32(sv[i], rp, qi * (PW * 4u) + 4u * si[i], 0, 0);
+            if (q == 0)
+                __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, nrm),
+                                                      span_rsrc(norms + v0, nb * 4u), qi * 4u, 0, 0);
+        }
     }
 }
 
