@@ -35,6 +35,9 @@ def flags() -> list:
         "-mcode-object-version=5",
         # packed-FP32 VALU forms are kept out of the generated code
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        # matrix-core results in ordinary VGPRs: the attention accumulators are
+        # rescaled by VALU code, which otherwise copies them out of AGPRs per page
+        "-mllvm", "-amdgpu-mfma-vgpr-form",
         "-I" + INCLUDE, "-I" + CSRC,
     ]
 

@@ -86,7 +86,7 @@ def test_small_ragged(dev, bits):
     run_attn(dev, "small b%d" % bits, bits=bits)
 
 
-@pytest.mark.parametrize("Hq,Hkv", [(4, 4), (8, 4), (32, 8), (16, 2), (64, 16), (8, 1), (16, 16)])
+@pytest.mark.parametrize("Hq,Hkv", [(4, 4), (8, 4), (32, 8), (16, 2), (64, 16), (8, 1), (16, 16), (24, 8)])
 def test_gqa_shapes(dev, Hq, Hkv):
     run_attn(dev, "gqa %d/%d" % (Hq, Hkv), B=2, Hq=Hq, Hkv=Hkv, T=50)
 
