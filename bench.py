@@ -272,7 +272,9 @@ def side_measurements(torch, dev, stream, x, packed, norms):
     out = torch.empty_like(q)
     wsb = _lib.tq_attn_workspace_bytes(B, Hq, Hkv, 128, bs, maxb)
     ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
-    flush = torch.empty(512 * 1024 * 1024 // 4, dtype=torch.float32, device=dev)
+    # Cache eviction between repetitions reads a 512 MB buffer: a write flush
+    # would leave dirty lines whose write-back lands inside the timed kernel.
+    flush = torch.ones(512 * 1024 * 1024 // 4, dtype=torch.float32, device=dev)
 
     def attn():
         _lib.check(_lib.tq_attn_decode(q.data_ptr(), kp.data_ptr(), kn.data_ptr(),
@@ -284,7 +286,7 @@ def side_measurements(torch, dev, stream, x, packed, norms):
     attn()
     times = []
     for _ in range(10):
-        flush.zero_()      # evict the 256 MB last-level cache between repetitions
+        flush.sum()        # evict the 256 MB last-level cache between repetitions
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
         attn()
@@ -304,7 +306,7 @@ def side_measurements(torch, dev, stream, x, packed, norms):
     pk2 = packed[: n // 2].view(-1)[: n * 32].view(n, 32)
     times = []
     for layer in range(6):
-        flush.zero_()
+        flush.sum()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
         _lib.check(_lib.tq_encode(xl.data_ptr(), n, 128, 2, layer, pk2.data_ptr(),

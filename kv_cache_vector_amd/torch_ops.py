@@ -1,0 +1,193 @@
+"""libtq's entry points as torch custom operators (namespace kv_cache_vector).
+
+Registered with torch.library.custom_op, each with a fake (meta) kernel that
+gives output shapes and dtypes without running anything, so torch.compile
+traces calls to them without graph breaks (aither-kvcache PyPI page, "API
+Reference": the codec and the paged attention exposed as registered torch
+operators).
+
+    torch.ops.kv_cache_vector.tq_encode(x, bits, seed) -> (packed, norms)
+    torch.ops.kv_cache_vector.tq_decode(packed, norms, bits, seed) -> x_hat
+    torch.ops.kv_cache_vector.tq_encode_paged_(x, slots, cache_packed,
+                                               cache_norms, bits, seed) -> ()
+    torch.ops.kv_cache_vector.tq_attn_decode(q, k_packed, k_norms, v_packed,
+                                             v_norms, block_tables,
+                                             context_lens, bits, seed, scale)
+                                             -> out
+
+Seeds are unsigned 64-bit values; the schema's int is signed, so seeds at or
+above 2^63 travel as their two's-complement int64 and are converted back.
+The real kernels take GPU tensors only and call libtq on the current stream;
+there is no host implementation.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import _lib
+
+HEAD_DIM = 128
+_U64 = 1 << 64
+
+
+def seed_to_i64(seed: int) -> int:
+    s = int(seed) % _U64
+    return s - _U64 if s >= (1 << 63) else s
+
+
+def _seed_u64(seed: int) -> int:
+    return int(seed) % _U64
+
+
+def _stream(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _gpu(t: torch.Tensor, name: str) -> None:
+    if not t.is_cuda:
+        raise ValueError("%s must be a GPU tensor (libtq has no host implementation)" % name)
+
+
+def _packed_dim(head_dim: int, bits: int) -> int:
+    # codes of one vector: head_dim * bits / 8 bytes (same rule as tq_packed_bytes)
+    if head_dim != HEAD_DIM or bits not in (2, 3, 4):
+        raise ValueError("unsupported (head_dim=%d, bits=%d)" % (head_dim, bits))
+    return head_dim * bits // 8
+
+
+# ---------------------------------------------------------------------------
+# encode / decode
+
+@torch.library.custom_op("kv_cache_vector::tq_encode", mutates_args=())
+def tq_encode(x: torch.Tensor, bits: int, seed: int) -> tuple[torch.Tensor, torch.Tensor]:
+    _gpu(x, "x")
+    if x.dtype != torch.float16 or x.shape[-1] != HEAD_DIM:
+        raise ValueError("x must be float16 [..., %d]" % HEAD_DIM)
+    P = _packed_dim(HEAD_DIM, bits)
+    x = x.contiguous()
+    lead = tuple(x.shape[:-1])
+    n = x.numel() // HEAD_DIM
+    packed = torch.empty(lead + (P,), dtype=torch.uint8, device=x.device)
+    norms = torch.empty(lead, dtype=torch.float32, device=x.device)
+    _lib.check(_lib.tq_encode(x.data_ptr(), n, HEAD_DIM, bits, _seed_u64(seed),
+                              packed.data_ptr(), norms.data_ptr(), _stream(x.device)),
+               "tq_encode")
+    return packed, norms
+
+
+@tq_encode.register_fake
+def _(x, bits, seed):
+    P = _packed_dim(HEAD_DIM, bits)
+    lead = tuple(x.shape[:-1])
+    return x.new_empty(lead + (P,), dtype=torch.uint8), x.new_empty(lead, dtype=torch.float32)
+
+
+@torch.library.custom_op("kv_cache_vector::tq_decode", mutates_args=())
+def tq_decode(packed: torch.Tensor, norms: torch.Tensor, bits: int, seed: int) -> torch.Tensor:
+    _gpu(packed, "packed")
+    _gpu(norms, "norms")
+    P = _packed_dim(HEAD_DIM, bits)
+    if packed.dtype != torch.uint8 or packed.shape[-1] != P:
+        raise ValueError("packed must be uint8 [..., %d]" % P)
+    if norms.dtype != torch.float32 or tuple(norms.shape) != tuple(packed.shape[:-1]):
+        raise ValueError("norms must be float32 with packed's leading shape")
+    packed = packed.contiguous()
+    norms = norms.contiguous()
+    out = torch.empty(tuple(norms.shape) + (HEAD_DIM,), dtype=torch.float16,
+                      device=packed.device)
+    _lib.check(_lib.tq_decode(packed.data_ptr(), norms.data_ptr(), norms.numel(), HEAD_DIM,
+                              bits, _seed_u64(seed), out.data_ptr(), _stream(packed.device)),
+               "tq_decode")
+    return out
+
+
+@tq_decode.register_fake
+def _(packed, norms, bits, seed):
+    return norms.new_empty(tuple(norms.shape) + (HEAD_DIM,), dtype=torch.float16)
+
+
+# ---------------------------------------------------------------------------
+# paged write
+
+@torch.library.custom_op("kv_cache_vector::tq_encode_paged_",
+                         mutates_args=("cache_packed", "cache_norms"))
+def tq_encode_paged_(x: torch.Tensor, slots: torch.Tensor, cache_packed: torch.Tensor,
+                     cache_norms: torch.Tensor, bits: int, seed: int) -> None:
+    for t, name in ((x, "x"), (slots, "slots"), (cache_packed, "cache_packed"),
+                    (cache_norms, "cache_norms")):
+        _gpu(t, name)
+    P = _packed_dim(HEAD_DIM, bits)
+    if x.dtype != torch.float16 or x.shape[-1] != HEAD_DIM:
+        raise ValueError("x must be float16 [..., %d]" % HEAD_DIM)
+    if slots.dtype != torch.int64 or slots.numel() != x.numel() // HEAD_DIM:
+        raise ValueError("slots must be int64 with one entry per vector")
+    if not (cache_packed.is_contiguous() and cache_norms.is_contiguous()):
+        raise ValueError("the cache tensors must be contiguous")
+    if cache_packed.dtype != torch.uint8 or cache_packed.shape[-1] != P:
+        raise ValueError("cache_packed must be uint8 [..., %d]" % P)
+    if cache_norms.dtype != torch.float32:
+        raise ValueError("cache_norms must be float32")
+    num_slots = cache_norms.numel()
+    if cache_packed.numel() != num_slots * P:
+        raise ValueError("cache_packed and cache_norms disagree on the number of rows")
+    x = x.contiguous()
+    slots = slots.contiguous()
+    _lib.check(_lib.tq_encode_paged(x.data_ptr(), slots.data_ptr(), slots.numel(), HEAD_DIM,
+                                    bits, _seed_u64(seed), cache_packed.data_ptr(),
+                                    cache_norms.data_ptr(), num_slots, _stream(x.device)),
+               "tq_encode_paged")
+
+
+@tq_encode_paged_.register_fake
+def _(x, slots, cache_packed, cache_norms, bits, seed):
+    return None
+
+
+# ---------------------------------------------------------------------------
+# decode attention
+
+@torch.library.custom_op("kv_cache_vector::tq_attn_decode", mutates_args=())
+def tq_attn_decode(q: torch.Tensor, k_packed: torch.Tensor, k_norms: torch.Tensor,
+                   v_packed: torch.Tensor, v_norms: torch.Tensor, block_tables: torch.Tensor,
+                   context_lens: torch.Tensor, bits: int, seed: int,
+                   scale: float) -> torch.Tensor:
+    for t, name in ((q, "query"), (k_packed, "k_packed"), (k_norms, "k_norms"),
+                    (v_packed, "v_packed"), (v_norms, "v_norms"),
+                    (block_tables, "block_tables"), (context_lens, "context_lens")):
+        _gpu(t, name)
+    P = _packed_dim(HEAD_DIM, bits)
+    if q.dim() != 3 or q.shape[-1] != HEAD_DIM or q.dtype != torch.float16:
+        raise ValueError("query must be float16 [batch, num_q_heads, %d]" % HEAD_DIM)
+    B, Hq, _ = q.shape
+    if k_packed.dim() != 4:
+        raise ValueError("k_packed must be [num_blocks, block_size, num_kv_heads, P]")
+    nblk, bs, hkv, Pk = k_packed.shape
+    if Pk != P or tuple(v_packed.shape) != tuple(k_packed.shape):
+        raise ValueError("k_packed / v_packed shape mismatch")
+    if tuple(k_norms.shape) != (nblk, bs, hkv) or tuple(v_norms.shape) != (nblk, bs, hkv):
+        raise ValueError("norms must be [num_blocks, block_size, num_kv_heads]")
+    if k_packed.dtype != torch.uint8 or v_packed.dtype != torch.uint8 or \
+            k_norms.dtype != torch.float32 or v_norms.dtype != torch.float32:
+        raise ValueError("codes must be uint8 and norms float32")
+    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
+        raise ValueError("block_tables and context_lens must be int32")
+    if block_tables.dim() != 2 or block_tables.shape[0] != B or tuple(context_lens.shape) != (B,):
+        raise ValueError("block_tables [batch, max_blocks], context_lens [batch]")
+    q, k_packed, v_packed = q.contiguous(), k_packed.contiguous(), v_packed.contiguous()
+    k_norms, v_norms = k_norms.contiguous(), v_norms.contiguous()
+    block_tables, context_lens = block_tables.contiguous(), context_lens.contiguous()
+    maxb = block_tables.shape[1]
+    out = torch.empty_like(q)
+    nbytes = _lib.tq_attn_workspace_bytes(B, Hq, hkv, HEAD_DIM, bs, maxb)
+    ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+    _lib.check(_lib.tq_attn_decode(
+        q.data_ptr(), k_packed.data_ptr(), k_norms.data_ptr(), v_packed.data_ptr(),
+        v_norms.data_ptr(), block_tables.data_ptr(), context_lens.data_ptr(), B, Hq, hkv,
+        HEAD_DIM, bits, _seed_u64(seed), bs, maxb, nblk, float(scale), out.data_ptr(),
+        ws.data_ptr(), ws.numel(), _stream(q.device)), "tq_attn_decode")
+    return out
+
+
+@tq_attn_decode.register_fake
+def _(q, k_packed, k_norms, v_packed, v_norms, block_tables, context_lens, bits, seed, scale):
+    return torch.empty_like(q)

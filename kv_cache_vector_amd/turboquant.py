@@ -14,6 +14,7 @@ import math
 import torch
 
 from . import _lib
+from . import torch_ops  # registers torch.ops.kv_cache_vector.*
 
 HEAD_DIM = 128
 
@@ -50,35 +51,23 @@ class TurboQuant:
         return 2.0 * self.head_dim / (self.packed_dim + 4)
 
     def encode(self, x: torch.Tensor):
+        """x [..., head_dim] fp16 -> (packed [..., head_dim*bits/8] uint8, norms [...] f32),
+        through torch.ops.kv_cache_vector.tq_encode."""
         _require_gpu(x, "x")
         if x.dtype != torch.float16 or x.shape[-1] != self.head_dim:
             raise ValueError("x must be float16 [..., %d]" % self.head_dim)
-        x = x.contiguous()
-        lead = tuple(x.shape[:-1])
-        n = x.numel() // self.head_dim
-        packed = torch.empty(lead + (self.packed_dim,), dtype=torch.uint8, device=x.device)
-        norms = torch.empty(lead, dtype=torch.float32, device=x.device)
-        _lib.check(_lib.tq_encode(x.data_ptr(), n, self.head_dim, self.bits, self.seed,
-                                  packed.data_ptr(), norms.data_ptr(), _stream(x.device)),
-                   "tq_encode")
-        return packed, norms
+        return torch.ops.kv_cache_vector.tq_encode(x, self.bits, torch_ops.seed_to_i64(self.seed))
 
     def decode(self, packed: torch.Tensor, norms: torch.Tensor) -> torch.Tensor:
+        """Inverse of encode, through torch.ops.kv_cache_vector.tq_decode."""
         _require_gpu(packed, "packed")
         _require_gpu(norms, "norms")
         if packed.dtype != torch.uint8 or packed.shape[-1] != self.packed_dim:
             raise ValueError("packed must be uint8 [..., %d]" % self.packed_dim)
         if norms.dtype != torch.float32 or tuple(norms.shape) != tuple(packed.shape[:-1]):
             raise ValueError("norms must be float32 with packed's leading shape")
-        packed = packed.contiguous()
-        norms = norms.contiguous()
-        n = norms.numel()
-        out = torch.empty(tuple(norms.shape) + (self.head_dim,), dtype=torch.float16,
-                          device=packed.device)
-        _lib.check(_lib.tq_decode(packed.data_ptr(), norms.data_ptr(), n, self.head_dim,
-                                  self.bits, self.seed, out.data_ptr(), _stream(packed.device)),
-                   "tq_decode")
-        return out
+        return torch.ops.kv_cache_vector.tq_decode(packed, norms, self.bits,
+                                                   torch_ops.seed_to_i64(self.seed))
 
     def encode_into(self, x: torch.Tensor, slots: torch.Tensor, cache_packed: torch.Tensor,
                     cache_norms: torch.Tensor) -> None:

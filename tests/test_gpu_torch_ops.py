@@ -1,0 +1,91 @@
+"""The torch custom operators on the GPU: same bytes as the class API, the
+paged write mutates the cache in place, and torch.compile traces a decode
+step (paged write + attention) with fullgraph=True, i.e. without a graph
+break."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from kv_cache_vector_amd import _lib
+from kv_cache_vector_amd import torch_ops as T
+from kv_cache_vector_amd import workloads as W
+from kv_cache_vector_amd.turboquant import TQPagedAttention, TurboQuant
+
+pytestmark = pytest.mark.gpu
+OPS = torch.ops.kv_cache_vector
+
+
+@pytest.fixture(scope="module")
+def dev():
+    assert torch.cuda.is_available(), "GPU tests need an AMD Instinct GPU"
+    _lib.load()
+    return torch.device("cuda:0")
+
+
+def test_ops_match_direct_calls(dev):
+    print("[ops] encode/decode vs direct", flush=True)
+    x = torch.from_numpy(W.gaussian(4096, seed=3)).to(dev)
+    seed = 2 ** 64 - 5                                   # needs the int64 conversion
+    for bits in (2, 3, 4):
+        p1, n1 = OPS.tq_encode(x, bits, T.seed_to_i64(seed))
+        P = 16 * bits
+        p2 = torch.empty(4096, P, dtype=torch.uint8, device=dev)
+        n2 = torch.empty(4096, dtype=torch.float32, device=dev)
+        s = torch.cuda.current_stream().cuda_stream
+        _lib.check(_lib.tq_encode(x.data_ptr(), 4096, 128, bits, seed, p2.data_ptr(),
+                                  n2.data_ptr(), s), "tq_encode")
+        y1 = OPS.tq_decode(p1, n1, bits, T.seed_to_i64(seed))
+        y2 = torch.empty_like(x)
+        _lib.check(_lib.tq_decode(p2.data_ptr(), n2.data_ptr(), 4096, 128, bits, seed,
+                                  y2.data_ptr(), s), "tq_decode")
+        torch.cuda.synchronize()
+        assert torch.equal(p1, p2) and torch.equal(n1, n2) and torch.equal(y1, y2)
+
+
+def test_compiled_decode_step(dev):
+    """Encode the new token's K/V into its cache slots, then attend; the
+    compiled function must equal the eager one."""
+    print("[ops] torch.compile fullgraph decode step", flush=True)
+    B, Hq, Hkv, T_ctx, bits, seed = 2, 8, 2, 40, 4, 7
+    wl = W.attn_workload(batch=B, num_q_heads=Hq, num_kv_heads=Hkv, context=T_ctx, seed=11,
+                         perm_seed=12, ragged=False)
+    tq = TurboQuant(128, bits, seed, dev)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    kp, kn = tq.encode(t(wl["k"]).reshape(-1, 128))
+    vp, vn = tq.encode(t(wl["v"]).reshape(-1, 128))
+    nblk = wl["k"].shape[0]
+    kp, kn = kp.view(nblk, 16, Hkv, 64), kn.view(nblk, 16, Hkv)
+    vp, vn = vp.view(nblk, 16, Hkv, 64), vn.view(nblk, 16, Hkv)
+    bt, cl = t(wl["block_tables"]), t(wl["context_lens"])
+    q = t(wl["q"])
+    newk = torch.randn(B * Hkv, 128, device=dev).half()
+    newv = torch.randn(B * Hkv, 128, device=dev).half()
+    # the new token sits at position T_ctx - 1 of each sequence
+    pos = T_ctx - 1
+    blk = bt[:, pos // 16].long()
+    slots = ((blk * 16 + pos % 16)[:, None] * Hkv + torch.arange(Hkv, device=dev)).reshape(-1)
+    scale = 1 / math.sqrt(128)
+
+    def step(q, newk, newv, kp, kn, vp, vn):
+        OPS.tq_encode_paged_(newk, slots, kp, kn, bits, seed)
+        OPS.tq_encode_paged_(newv, slots, vp, vn, bits, seed)
+        return OPS.tq_attn_decode(q, kp, kn, vp, vn, bt, cl, bits, seed, scale)
+
+    caches = [c.clone() for c in (kp, kn, vp, vn)]
+    eager = step(q, newk, newv, *caches)
+    compiled = torch.compile(step, backend="aot_eager", fullgraph=True)
+    caches2 = [c.clone() for c in (kp, kn, vp, vn)]
+    got = compiled(q, newk, newv, *caches2)
+    torch.cuda.synchronize()
+    assert torch.equal(got, eager)
+    for a, b in zip(caches, caches2):
+        assert torch.equal(a, b)
+    # the written rows decode to the new vectors' codec round trip
+    rows = tq.decode(caches2[0].view(-1, 64)[slots], caches2[1].view(-1)[slots])
+    ref = tq.decode(*tq.encode(newk))
+    assert torch.equal(rows, ref)
+    # the class API gives the same attention
+    attn = TQPagedAttention(tq, Hq, scale=scale)
+    assert torch.equal(attn.forward(q, *caches2[:2], *caches2[2:], bt, cl), got)
