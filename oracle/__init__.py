@@ -66,6 +66,11 @@ def _bind(L: ctypes.CDLL) -> ctypes.CDLL:
                                   ctypes.c_int, ctypes.c_int, ctypes.c_uint64,
                                   ctypes.c_int, ctypes.c_int, ctypes.c_int64,
                                   ctypes.c_double, _P, _P, _P]
+    L.tqo_attn_decode_kv.argtypes = [_P, _P, _P, _P, _P, _P, _P,
+                                     ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                     ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_uint64,
+                                     ctypes.c_int, ctypes.c_int, ctypes.c_int64,
+                                     ctypes.c_double, _P, _P, _P]
     L.tqo_packed_bytes.argtypes = [ctypes.c_int, ctypes.c_int]
     return L
 
@@ -183,11 +188,12 @@ class Oracle:
 
     def attn_decode(self, q_f16, k_packed, k_norms, v_packed, v_norms, block_tables,
                     context_lens, num_kv_heads: int, bits: int, seed: int, scale: float,
-                    sel=None, want_f64: bool = False):
+                    sel=None, want_f64: bool = False, v_bits: int | None = None):
         """Plain paged decode attention.  q [B, Hq, d] float16; caches
         [num_blocks, block_size, Hkv, P] u8 and [num_blocks, block_size, Hkv] f32;
         block_tables [B, max_blocks] int32; context_lens [B] int32.
-        sel (optional bool [B, Hq]) restricts the (b, h) pairs computed."""
+        sel (optional bool [B, Hq]) restricts the (b, h) pairs computed.
+        v_bits (default: bits) is the width of the value codes."""
         q = np.asarray(q_f16)
         if q.dtype == np.float16:
             q = q.view(np.uint16)
@@ -205,12 +211,13 @@ class Oracle:
         s = None if sel is None else _c(sel, np.uint8)
         out = np.zeros((B, Hq, d), dtype=np.uint16)
         of = np.zeros((B, Hq, d), dtype=np.float64) if want_f64 else None
-        rc = self.L.tqo_attn_decode(_ptr(q), _ptr(k_packed), _ptr(k_norms), _ptr(v_packed),
-                                    _ptr(v_norms), _ptr(bt), _ptr(cl), B, Hq, num_kv_heads, d,
-                                    bits, ctypes.c_uint64(seed), bs, max_blocks, nblk,
-                                    float(scale), _ptr(s), _ptr(out), _ptr(of))
+        vb = bits if v_bits is None else v_bits
+        rc = self.L.tqo_attn_decode_kv(_ptr(q), _ptr(k_packed), _ptr(k_norms), _ptr(v_packed),
+                                       _ptr(v_norms), _ptr(bt), _ptr(cl), B, Hq, num_kv_heads,
+                                       d, bits, vb, ctypes.c_uint64(seed), bs, max_blocks, nblk,
+                                       float(scale), _ptr(s), _ptr(out), _ptr(of))
         if rc != 0:
-            raise ValueError("tqo_attn_decode rejected its arguments (rc=%d)" % rc)
+            raise ValueError("tqo_attn_decode_kv rejected its arguments (rc=%d)" % rc)
         out = out.view(np.float16)
         return (out, of) if want_f64 else out
 

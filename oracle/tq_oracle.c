@@ -424,22 +424,27 @@ int tqo_decode(const uint8_t *packed, const float *norms, int64_t n, int d, int 
  * out_f64 (optional, [B, Hq, d]) receives o unrounded.
  * Only the (b, h) pairs with sel[b * Hq + h] != 0 are computed when sel is
  * non-NULL (the others are left untouched); NULL computes all of them.
+ * Keys are decoded with the k_bits codebook and values with the v_bits one
+ * (keys and values at different widths, e.g. 4-bit keys with 2-bit values as
+ * on the KVarN repository page, "What it does"); both share the seed's
+ * rotation.
  */
-int tqo_attn_decode(const uint16_t *q, const uint8_t *k_packed, const float *k_norms,
-                    const uint8_t *v_packed, const float *v_norms,
-                    const int32_t *block_tables, const int32_t *context_lens,
-                    int B, int Hq, int Hkv, int d, int bits, uint64_t seed,
-                    int block_size, int max_blocks, int64_t num_blocks, double scale,
-                    const uint8_t *sel, uint16_t *out, double *out_f64)
+int tqo_attn_decode_kv(const uint16_t *q, const uint8_t *k_packed, const float *k_norms,
+                       const uint8_t *v_packed, const float *v_norms,
+                       const int32_t *block_tables, const int32_t *context_lens,
+                       int B, int Hq, int Hkv, int d, int k_bits, int v_bits, uint64_t seed,
+                       int block_size, int max_blocks, int64_t num_blocks, double scale,
+                       const uint8_t *sel, uint16_t *out, double *out_f64)
 {
-    if (!valid_shape(d, bits) || B < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv ||
+    if (!valid_shape(d, k_bits) || !valid_shape(d, v_bits) || B < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv ||
         block_size <= 0 || max_blocks < 0 || num_blocks < 0)
         return TQO_EINVAL;
     for (int b = 0; b < B; ++b)
         if (context_lens[b] < 0 || context_lens[b] > max_blocks * block_size) return TQO_EINVAL;
-    codec_t k;
-    if (codec_init(&k, d, bits, seed)) return TQO_EINVAL;
-    const int P = k.P;
+    codec_t k, v;
+    if (codec_init(&k, d, k_bits, seed)) return TQO_EINVAL;
+    if (codec_init(&v, d, v_bits, seed)) { codec_free(&k); return TQO_EINVAL; }
+    const int PK = k.P, PV = v.P;
     const int grp = Hq / Hkv;
     int rc = TQO_OK;
     double qd[1024];
@@ -459,8 +464,8 @@ int tqo_attn_decode(const uint16_t *q, const uint8_t *k_packed, const float *k_n
                 int32_t blk = block_tables[(size_t)b * max_blocks + j / block_size];
                 if (blk < 0 || blk >= num_blocks) { rc = TQO_EINVAL; break; }
                 int64_t row = ((int64_t)blk * block_size + j % block_size) * Hkv + g;
-                decode_one(&k, k_packed + row * P, k_norms[row], K + (size_t)j * d);
-                decode_one(&k, v_packed + row * P, v_norms[row], V + (size_t)j * d);
+                decode_one(&k, k_packed + row * PK, k_norms[row], K + (size_t)j * d);
+                decode_one(&v, v_packed + row * PV, v_norms[row], V + (size_t)j * d);
             }
             for (int hh = 0; hh < grp && rc == TQO_OK; ++hh) {
                 const int h = g * grp + hh;
@@ -488,7 +493,21 @@ int tqo_attn_decode(const uint16_t *q, const uint8_t *k_packed, const float *k_n
         }
     }
     codec_free(&k);
+    codec_free(&v);
     return rc;
+}
+
+/* The same with one bit width for K and V. */
+int tqo_attn_decode(const uint16_t *q, const uint8_t *k_packed, const float *k_norms,
+                    const uint8_t *v_packed, const float *v_norms,
+                    const int32_t *block_tables, const int32_t *context_lens,
+                    int B, int Hq, int Hkv, int d, int bits, uint64_t seed,
+                    int block_size, int max_blocks, int64_t num_blocks, double scale,
+                    const uint8_t *sel, uint16_t *out, double *out_f64)
+{
+    return tqo_attn_decode_kv(q, k_packed, k_norms, v_packed, v_norms, block_tables,
+                              context_lens, B, Hq, Hkv, d, bits, bits, seed, block_size,
+                              max_blocks, num_blocks, scale, sel, out, out_f64);
 }
 
 /* Bytes of packed codes per vector. */

@@ -590,6 +590,41 @@ def check_attn_gqa_grouping(o):
     assert np.array_equal(y2[0, 4:], y[0, :4]) and np.array_equal(y2[0, :4], y[0, 4:])
 
 
+def check_attn_mixed_widths(o):
+    """Keys at one width and values at another (4-bit keys with 2-bit values,
+    as on the KVarN repository page, "What it does", and the other pairs):
+    a softmax written out by hand over keys decoded at the key width and
+    values decoded at the value width; context_len = 1 gives the first value
+    row at the value width; equal widths reproduce the single-width call."""
+    from kv_cache_vector_amd import workloads as w
+    wl = w.attn_workload(batch=1, num_q_heads=2, num_kv_heads=1, context=3, block_size=16,
+                         seed=71, perm_seed=72, ragged=False, extra_blocks=1)
+    blk = int(wl["block_tables"][0, 0])
+    sc = 1 / math.sqrt(D)
+    for kb, vb in ((4, 2), (2, 4), (3, 4), (4, 3), (2, 3), (3, 2)):
+        kp, kn = o.encode(wl["k"], kb, 0)
+        vp, vn = o.encode(wl["v"], vb, 0)
+        args = (wl["q"], kp, kn, vp, vn, wl["block_tables"])
+        _, yf = o.attn_decode(*args, wl["context_lens"], 1, kb, 0, sc, want_f64=True, v_bits=vb)
+        _, K = o.decode(kp[blk, :3, 0], kn[blk, :3, 0], D, kb, 0, want_f64=True)
+        _, V = o.decode(vp[blk, :3, 0], vn[blk, :3, 0], D, vb, 0, want_f64=True)
+        for h in range(2):
+            q = wl["q"][0, h].astype(np.float64)
+            s = [float(q @ K[j]) * sc for j in range(3)]
+            m = max(s)
+            e = [math.exp(x - m) for x in s]
+            ref = (e[0] * V[0] + e[1] * V[1] + e[2] * V[2]) / sum(e)
+            assert np.allclose(yf[0, h], ref, rtol=0, atol=1e-12), (kb, vb, h)
+        y1, _ = o.attn_decode(*args, np.ones(1, np.int32), 1, kb, 0, sc, want_f64=True,
+                              v_bits=vb)
+        assert np.array_equal(y1[0, 0], V[0].astype(np.float16)), (kb, vb)
+    for b in (2, 3, 4):
+        kp, kn = o.encode(wl["k"], b, 0)
+        vp, vn = o.encode(wl["v"], b, 0)
+        args = (wl["q"], kp, kn, vp, vn, wl["block_tables"], wl["context_lens"], 1, b, 0, sc)
+        assert np.array_equal(o.attn_decode(*args), o.attn_decode(*args, v_bits=b))
+
+
 ALL_CHECKS = [
     check_half_to_double, check_double_to_half, check_splitmix64, check_signs,
     check_hadamard, check_rotation_unit_vectors, check_rotation_norm,
@@ -600,4 +635,5 @@ ALL_CHECKS = [
     check_scale_invariance, check_negation, check_zero_vector, check_reencode_fixed_point,
     check_decode_definition, check_attn_rotated_domain_identity, check_attn_special_cases,
     check_attn_paging_invariance, check_attn_bruteforce_tiny, check_attn_gqa_grouping,
+    check_attn_mixed_widths,
 ]

@@ -36,6 +36,9 @@ MUTATIONS = [
     ("norm_f32_truncated", "*nv_out = (float)nv;", "*nv_out = nextafterf((float)nv, 0.0f);"),
     ("half_round_away", "double r = rint(s);", "double r = floor(s + 0.5);"),
     ("attn_no_scale", "s[j] = scale * acc;", "s[j] = acc;"),
+    ("attn_values_with_key_codebook",
+     "decode_one(&v, v_packed + row * PV, v_norms[row], V + (size_t)j * d);",
+     "decode_one(&k, v_packed + row * PV, v_norms[row], V + (size_t)j * d);"),
     ("attn_no_max_sub", "s[j] = exp(s[j] - m);", "s[j] = exp(s[j] - m + 1e-3 * j);"),
     ("attn_gqa_mod", "int64_t row = ((int64_t)blk * block_size + j % block_size) * Hkv + g;",
      "int64_t row = ((int64_t)blk * block_size + j % block_size) * Hkv + (g + 1) % Hkv;"),
