@@ -153,9 +153,13 @@ size_t tq_attn_workspace_bytes(int batch, int num_q_heads, int num_kv_heads, int
  *                entry outside [0, num_blocks) is never dereferenced -- its
  *                tokens are left out of the softmax (the output for that
  *                sequence is then unspecified but memory stays in bounds)
- * num_q_heads must be a multiple of num_kv_heads with at most 8 query heads
+ * num_q_heads must be a multiple of num_kv_heads with at most 16 query heads
  * per kv head; block_size must be 16.  A context length outside
  * [0, max_blocks_per_seq * block_size] is clamped into that range.
+ * Errors: TQ_ERR_INVALID_ARG (null pointers, negative sizes, a non-finite
+ * scale, overlapping output), TQ_ERR_UNSUPPORTED (head_dim, bits, group size
+ * or block_size outside the supported set), TQ_ERR_MISALIGNED,
+ * TQ_ERR_WORKSPACE (missing or short workspace), TQ_ERR_HIP (launch failure).
  */
 tq_status tq_attn_decode(const void *q_f16, const uint8_t *k_packed, const float *k_norms,
                          const uint8_t *v_packed, const float *v_norms,
@@ -164,6 +168,22 @@ tq_status tq_attn_decode(const void *q_f16, const uint8_t *k_packed, const float
                          uint64_t seed, int block_size, int max_blocks_per_seq,
                          int64_t num_blocks, float scale, void *out_f16, void *workspace,
                          size_t workspace_bytes, void *stream);
+
+/*
+ * tq_attn_decode with keys and values stored at different widths: k_packed
+ * rows hold head_dim*k_bits/8 bytes and v_packed rows head_dim*v_bits/8
+ * (for instance 4-bit keys with 2-bit values, as on the KVarN repository
+ * page, "What it does").  Both use the seed's sign flip; every other argument,
+ * the workspace size and the error behaviour are those of tq_attn_decode,
+ * which equals this call with k_bits = v_bits = bits.
+ */
+tq_status tq_attn_decode_kv(const void *q_f16, const uint8_t *k_packed, const float *k_norms,
+                            const uint8_t *v_packed, const float *v_norms,
+                            const int32_t *block_tables, const int32_t *context_lens, int batch,
+                            int num_q_heads, int num_kv_heads, int head_dim, int k_bits,
+                            int v_bits, uint64_t seed, int block_size, int max_blocks_per_seq,
+                            int64_t num_blocks, float scale, void *out_f16, void *workspace,
+                            size_t workspace_bytes, void *stream);
 
 /*
  * Host-side test hooks (no device work).

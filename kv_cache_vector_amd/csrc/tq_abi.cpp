@@ -276,18 +276,20 @@ size_t tq_attn_workspace_bytes(int batch, int num_q_heads, int num_kv_heads, int
         block_size != tq::kAttnBlockSize || max_blocks_per_seq < 0 ||
         num_q_heads % num_kv_heads)
         return 0;
-    tq::AttnShape s{batch, num_q_heads, num_kv_heads, 4, max_blocks_per_seq, 0};
+    tq::AttnShape s{batch, num_q_heads, num_kv_heads, 4, 4, max_blocks_per_seq, 0};
     return tq::attn_workspace_bytes(s);
 }
 
-tq_status tq_attn_decode(const void *q_f16, const uint8_t *k_packed, const float *k_norms,
-                         const uint8_t *v_packed, const float *v_norms,
-                         const int32_t *block_tables, const int32_t *context_lens, int batch,
-                         int num_q_heads, int num_kv_heads, int head_dim, int bits,
-                         uint64_t seed, int block_size, int max_blocks_per_seq,
-                         int64_t num_blocks, float scale, void *out_f16, void *workspace,
-                         size_t workspace_bytes, void *stream) {
-    tq_status st = check_shape(head_dim, bits);
+tq_status tq_attn_decode_kv(const void *q_f16, const uint8_t *k_packed, const float *k_norms,
+                            const uint8_t *v_packed, const float *v_norms,
+                            const int32_t *block_tables, const int32_t *context_lens, int batch,
+                            int num_q_heads, int num_kv_heads, int head_dim, int k_bits,
+                            int v_bits, uint64_t seed, int block_size, int max_blocks_per_seq,
+                            int64_t num_blocks, float scale, void *out_f16, void *workspace,
+                            size_t workspace_bytes, void *stream) {
+    tq_status st = check_shape(head_dim, k_bits);
+    if (st != TQ_OK) return st;
+    st = check_shape(head_dim, v_bits);
     if (st != TQ_OK) return st;
     if (batch < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_blocks_per_seq < 0 ||
         num_blocks < 0 || !std::isfinite(scale))
@@ -304,17 +306,32 @@ tq_status tq_attn_decode(const void *q_f16, const uint8_t *k_packed, const float
         !aligned(v_packed, 16) || !aligned(k_norms, 4) || !aligned(v_norms, 4) ||
         !aligned(block_tables, 4) || !aligned(context_lens, 4) || !aligned(workspace, 16))
         return TQ_ERR_MISALIGNED;
-    tq::AttnShape s{batch, num_q_heads, num_kv_heads, bits, max_blocks_per_seq, num_blocks};
+    tq::AttnShape s{batch, num_q_heads, num_kv_heads, k_bits, v_bits, max_blocks_per_seq,
+                    num_blocks};
     if (!tq::attn_supported(s)) return TQ_ERR_UNSUPPORTED;
     const size_t need = tq::attn_workspace_bytes(s);
     if (need > 0 && (!workspace || workspace_bytes < need)) return TQ_ERR_WORKSPACE;
     const size_t nout = (size_t)batch * num_q_heads * kD * 2;
     if (overlap(out_f16, nout, q_f16, nout) || overlap(out_f16, nout, workspace, need))
         return TQ_ERR_INVALID_ARG;
-    const CodecConsts k = make_consts(bits, seed);
-    return from_hip(tq::launch_attn(s, k, q_f16, k_packed, k_norms, v_packed, v_norms,
+    const CodecConsts kc = make_consts(k_bits, seed);
+    const CodecConsts vc = make_consts(v_bits, seed);
+    return from_hip(tq::launch_attn(s, kc, vc, q_f16, k_packed, k_norms, v_packed, v_norms,
                                     block_tables, context_lens, scale, out_f16, workspace,
                                     (hipStream_t)stream));
+}
+
+tq_status tq_attn_decode(const void *q_f16, const uint8_t *k_packed, const float *k_norms,
+                         const uint8_t *v_packed, const float *v_norms,
+                         const int32_t *block_tables, const int32_t *context_lens, int batch,
+                         int num_q_heads, int num_kv_heads, int head_dim, int bits,
+                         uint64_t seed, int block_size, int max_blocks_per_seq,
+                         int64_t num_blocks, float scale, void *out_f16, void *workspace,
+                         size_t workspace_bytes, void *stream) {
+    return tq_attn_decode_kv(q_f16, k_packed, k_norms, v_packed, v_norms, block_tables,
+                             context_lens, batch, num_q_heads, num_kv_heads, head_dim, bits,
+                             bits, seed, block_size, max_blocks_per_seq, num_blocks, scale,
+                             out_f16, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

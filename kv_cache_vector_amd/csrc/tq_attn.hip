@@ -4,8 +4,10 @@
 // Method: aither-kvcache PyPI page, "Zero-buffer fused attention" (rotate the
 // query forward once, score against codebook values in the rotated domain,
 // accumulate the weighted values in the rotated domain, rotate back once) and
-// "Paged KV cache" (16-token blocks, [16, heads, 64] uint8 + [16, heads] f32
-// per block at 4 bits); qbc.network blog, "What we shipped" item 2.
+// "Paged KV cache" (16-token blocks, [16, heads, P] uint8 + [16, heads] f32
+// per block); qbc.network blog, "What we shipped" item 2.  Keys and values may
+// use different widths (4-bit keys with 2-bit values: KVarN repository page,
+// "What it does").
 //
 // With R = H D / sqrt(d) and a cached row decoding to n * R^T c[code] / sqrt(d):
 //   <q, k_j>      = (n_j / d) * <H D q, c[k_j]>
@@ -14,21 +16,39 @@
 // row is used as plain codebook values, and one inverse transform finishes.
 //
 // Two kernels, flash-decoding style:
-//   split   grid (context split, sequence, kv-head chunk), 4 waves.  Eight
-//           lanes own one (token, kv head) pair, 16 coordinates each; a wave
-//           covers 8 such pairs per step -- one token of all 8 kv heads of a
-//           Llama-style GQA cache, whose 8 rows of codes are 512 contiguous
-//           bytes.  Each lane keeps the rotated query (16 coordinates per query
-//           head of its group) and the running softmax state in registers.
-//           The softmax is online in base 2 with a lazily raised reference:
-//           the accumulators are rescaled only when a score exceeds the
-//           reference by more than 2^8, which after the first token is rare.
-//           The four waves merge through LDS; one partial state per
-//           (sequence, query head, split) goes to the workspace.
+//   split   grid (context split, sequence, kv-head chunk of 4), one wave per
+//           kv head.  Per 16-token page the scores and the value accumulation
+//           run as 16x16x32 f16 MFMA tiles:
+//             scores  S^T[16 tokens][16 heads] = C_k[16 tokens][K] Q[K][16 heads]
+//             values  O[16 heads][16 dims]    += W[16 heads][K] C_v[K][16 dims]
+//           with the group's query heads (up to 16) padded to 16.  One partial
+//           state per (sequence, query head, split) goes to the workspace.
 //   combine grid (sequence * query head), one wave: log-sum-exp merge of the
 //           splits, the inverse transform D H / d, binary16 rounding.
+//
+// binary16 carries 11 significant bits, too few for the 2e-3 output bound
+// under peaked softmaxes, so every operand is split as x = x_hi + x_lo (both
+// binary16) and the products x_hi y_hi + x_lo y_hi + x_hi y_lo are formed.
+// The split costs no repacking: a code is looked up as the binary16 pair
+// (c_hi, c_lo), which fills two adjacent K slots; the other operand holds
+// (q_hi, q_hi) in those slots for one product and (q_lo, 0) for a second.
+//
+// Scale factors keep every binary16 operand in range and its low part
+// normal: levels are stored times 16, the rotated query times a per-head
+// power of two, and the value weights times 2^6 / vlim (vlim a power of two
+// above the value norms); all are powers of two and removed exactly before
+// the partial state is written.
+//
+// Lane layouts (l = lane, m = l % 16, r = l / 16), verified on gfx950:
+//   A[m][8r .. 8r+7], B[8r .. 8r+7][m], C[4r .. 4r+3][m].
+// Scores: lane (token m, r) holds the codes of dims 32r .. 32r+31 of its token
+// (4 * bits bytes); chunk j covers dims 32r + 4j .. +3 of every r.  The query
+// operand of lane (head m, r) covers the same dims.  The score tile leaves
+// lane (head m, r) with tokens 4r .. 4r+3 -- exactly the K slots the value
+// product wants in its A operand, so the weights never move between lanes.
+// Values: lane (column m, r) reads dims 8m .. 8m+7 of tokens 4r .. 4r+3;
+// chunk jj accumulates dim 8m + jj.
 #include <hip/hip_runtime.h>
-#include <algorithm>
 #include <stdint.h>
 
 #include "tq_internal.h"
@@ -36,47 +56,23 @@
 namespace tq {
 namespace {
 
-constexpr int kWaves = 4;
-constexpr int kThreads = 64 * kWaves;
 constexpr int kPartial = 2 + kHeadDim;      // m, l, acc[128] per workspace entry
 constexpr float kLazy = 8.0f;               // rescale when a score passes m + 8 (base 2)
-constexpr int kTargetGroups = 512;          // split-kernel workgroups aimed for
 constexpr int kMaxSplitTokens = 4096;       // block-table entries of a split staged in LDS
-constexpr int kPrefetch = 4;                // wave steps of K/V loads kept in flight
+constexpr int kMWaves = 4;                  // kv heads (waves) per workgroup
+constexpr int kMThreads = 64 * kMWaves;
+constexpr int kMPrefetch = 1;               // extra ring slots: pages of loads in flight ahead of use
+constexpr int kMTargetWaves = 4096;         // split-kernel waves aimed for
+constexpr float kLevelScale = 16.0f;        // binary16 levels are 16 c
+constexpr float kWShift = 6.0f;             // value weights carry 2^6
+constexpr int kLutRow = 256;                // bytes per table row: keys' half, values' half
+constexpr int kQuadPrev = 0x90;             // quad_perm [0,0,1,2]: lane q <- lane q-1 (0 <- 0)
 
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-
-constexpr int kQuadXor1 = 0xB1;        // quad_perm [1,0,3,2]
-constexpr int kQuadXor2 = 0x4E;        // quad_perm [2,3,0,1]
-constexpr int kRowHalfMirror = 0x141;  // lane i <- lane 7-i within each 8
-constexpr int kRowMirror = 0x140;      // lane i <- lane 15-i within each 16
-
-template <int CTRL>
-__device__ __forceinline__ float dpp(float v) {
-    return __builtin_bit_cast(
-        float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
-}
-
-// Value of lane h of this lane's quad (quad_perm [h,h,h,h]).
-__device__ __forceinline__ float quad_bcast(float v, int h) {
-    const int x = __builtin_bit_cast(int, v);
-    switch (h & 3) {
-        case 0: return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(x, 0x00, 0xF, 0xF, true));
-        case 1: return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(x, 0x55, 0xF, 0xF, true));
-        case 2: return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(x, 0xAA, 0xF, 0xF, true));
-        default: return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(x, 0xFF, 0xF, 0xF, true));
-    }
-}
-
-// Sum over the LPU lanes of a unit (LPU = 8 or 16, aligned groups).
-template <int LPU>
-__device__ __forceinline__ float unit_sum(float v) {
-    v += dpp<kQuadXor1>(v);
-    v += dpp<kQuadXor2>(v);
-    v += dpp<kRowHalfMirror>(v);
-    if (LPU == 16) v += dpp<kRowMirror>(v);
-    return v;
-}
+typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef float f4 __attribute__((ext_vector_type(4)));
 
 struct AttnParams {
     const uint16_t *q;
@@ -90,8 +86,9 @@ struct AttnParams {
     uint16_t *out;
     int batch, hq, hkv, max_blocks, split_tokens, num_splits;
     int64_t num_blocks;
-    float qscale;        // scale * log2(e) / 128, folded into the rotated query
-    CodecConsts k;
+    float qscale;        // scale * log2(e) / 128
+    CodecConsts k;       // key codebook and the sign mask (shared by keys and values)
+    CodecConsts v;       // value codebook
 };
 
 __device__ __forceinline__ float half_bits_to_float(uint32_t h) {
@@ -109,406 +106,6 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t page_rsrc(const void *base, ui
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, 0x00020000);
 }
 
-// This lane's E codes (E * BITS / 8 bytes at byte offset `off`).
-template <int BITS, int E>
-__device__ __forceinline__ void load_codes_buf(__amdgpu_buffer_rsrc_t r, uint32_t off,
-                                               uint32_t (&c)[2]) {
-    constexpr int BYTES = E * BITS / 8;
-    if constexpr (BYTES == 8) {
-        typedef uint32_t u2 __attribute__((ext_vector_type(2)));
-        const u2 u = __builtin_bit_cast(u2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
-        c[0] = u.x;
-        c[1] = u.y;
-    } else if constexpr (BYTES == 4) {
-        c[0] = __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
-        c[1] = 0;
-    } else if constexpr (BYTES == 6) {   // b = 3, E = 16: 2-byte aligned
-        const uint32_t h0 = __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
-        const uint32_t h1 = __builtin_amdgcn_raw_buffer_load_b16(r, off + 2, 0, 0);
-        const uint32_t h2 = __builtin_amdgcn_raw_buffer_load_b16(r, off + 4, 0, 0);
-        c[0] = h0 | (h1 << 16);
-        c[1] = h2;
-    } else if constexpr (BYTES == 2) {   // b = 2, E = 8
-        c[0] = __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
-        c[1] = 0;
-    } else {                             // b = 3, E = 8: 3 bytes, byte aligned
-        const uint32_t b0 = __builtin_amdgcn_raw_buffer_load_b8(r, off, 0, 0);
-        const uint32_t b1 = __builtin_amdgcn_raw_buffer_load_b8(r, off + 1, 0, 0);
-        const uint32_t b2 = __builtin_amdgcn_raw_buffer_load_b8(r, off + 2, 0, 0);
-        c[0] = b0 | (b1 << 8) | (b2 << 16);
-        c[1] = 0;
-    }
-}
-
-// LDS lookup table: pairs of codes (b = 3, 4) or bytes of four codes (b = 2).
-template <int BITS>
-struct LevelTable {
-    static constexpr int G = (BITS == 2) ? 4 : 2;
-    static constexpr int NENT = 1 << (G * BITS);
-};
-
-template <int BITS, int E>
-__device__ __forceinline__ void expand(const float *tab, const uint32_t (&c)[2], float (&val)[E]) {
-    constexpr int G = LevelTable<BITS>::G;
-    constexpr int IB = G * BITS;   // index bits per lookup
-#pragma unroll
-    for (int gi = 0; gi < E / G; ++gi) {
-        const int bit = gi * IB;
-        uint32_t idx;
-        if ((bit & 31) + IB <= 32)
-            idx = (c[bit >> 5] >> (bit & 31)) & ((1u << IB) - 1);
-        else
-            idx = __builtin_amdgcn_alignbit(c[(bit >> 5) + 1], c[bit >> 5], bit & 31) &
-                  ((1u << IB) - 1);
-        if (G == 2) {
-            const float2 e = reinterpret_cast<const float2 *>(tab)[idx];
-            val[2 * gi] = e.x;
-            val[2 * gi + 1] = e.y;
-        } else {
-            const float4 e = reinterpret_cast<const float4 *>(tab)[idx];
-            val[4 * gi] = e.x;
-            val[4 * gi + 1] = e.y;
-            val[4 * gi + 2] = e.z;
-            val[4 * gi + 3] = e.w;
-        }
-    }
-}
-
-template <int BITS, int GRP, int E>
-__global__ __launch_bounds__(kThreads) void attn_split_kernel(AttnParams p) {
-    constexpr int LPU = kHeadDim / E;     // lanes per (token, kv head) unit
-    constexpr int UPW = 64 / LPU;         // units per wave step
-    constexpr int P = kHeadDim * BITS / 8;
-    constexpr int L = 1 << BITS;
-    constexpr int G = LevelTable<BITS>::G;
-    constexpr int NENT = LevelTable<BITS>::NENT;
-    __shared__ float tab[NENT * G];
-    __shared__ float xchg[2][64 * (GRP * E + 2 * GRP)];
-
-    const int b = blockIdx.y;
-    const int split = blockIdx.x;
-    int T = p.context_lens[b];
-    T = T < 0 ? 0 : T;
-    const int tmax = p.max_blocks * kAttnBlockSize;
-    T = T > tmax ? tmax : T;
-    if (p.num_blocks <= 0) T = 0;
-    const int t0 = split * p.split_tokens;
-    if (t0 >= T) return;                 // nothing here; combine skips this split
-    const int t1 = (t0 + p.split_tokens < T) ? t0 + p.split_tokens : T;
-
-    for (int t = threadIdx.x; t < NENT; t += kThreads) {
-#pragma unroll
-        for (int j = 0; j < G; ++j) tab[G * t + j] = p.k.level[(t >> (BITS * j)) & (L - 1)];
-    }
-    // block-table entries of this split's pages (read before the token loop so
-    // the code loads of a token do not wait on a dependent global load)
-    __shared__ int32_t bt_lds[kMaxSplitTokens / kAttnBlockSize];
-    {
-        const int32_t *bt = p.block_tables + (size_t)b * p.max_blocks + t0 / kAttnBlockSize;
-        const int npages = (t1 - t0 + kAttnBlockSize - 1) / kAttnBlockSize;
-        for (int i = threadIdx.x; i < npages; i += kThreads) bt_lds[i] = bt[i];
-    }
-
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
-    const int lane = threadIdx.x & 63;
-    const int gam = lane / LPU;          // unit slot in the wave
-    const int sub = lane % LPU;          // coordinate slice [sub*E, sub*E + E)
-    const bool wide = p.hkv >= UPW;
-    const int g = wide ? blockIdx.z * UPW + gam : gam % p.hkv;
-    const int tau = wide ? 0 : gam / p.hkv;
-    const int tpi = wide ? 1 : UPW / p.hkv;   // tokens per wave step
-    const bool live = wide || (gam < tpi * p.hkv);
-
-    // rotated, pre-scaled query of the GRP heads of kv head g: q~ = H D q
-    float qt[GRP][E];
-#pragma unroll
-    for (int hh = 0; hh < GRP; ++hh) {
-        const int h = g * GRP + hh;
-        const uint16_t *qp = p.q + ((size_t)b * p.hq + h) * kHeadDim + sub * E;
-#pragma unroll
-        for (int e = 0; e < E; ++e) {
-            const float v = half_bits_to_float(live ? qp[e] : 0);
-            qt[hh][e] = sign_of(p.k, sub * E + e) ? -v : v;
-        }
-#pragma unroll
-        for (int s = 1; s < E; s <<= 1)
-#pragma unroll
-            for (int e = 0; e < E; ++e) {
-                if (e & s) continue;
-                const float a = qt[hh][e], c = qt[hh][e + s];
-                qt[hh][e] = a + c;
-                qt[hh][e + s] = a - c;
-            }
-#pragma unroll
-        for (int s = 1; s < LPU; s <<= 1)
-#pragma unroll
-            for (int e = 0; e < E; ++e) {
-                const float o = __shfl_xor(qt[hh][e], s, LPU);
-                qt[hh][e] = (sub & s) ? (o - qt[hh][e]) : (qt[hh][e] + o);
-            }
-#pragma unroll
-        for (int e = 0; e < E; ++e) qt[hh][e] *= p.qscale;
-    }
-    __syncthreads();
-
-    float acc[GRP][E];
-#pragma unroll
-    for (int hh = 0; hh < GRP; ++hh)
-#pragma unroll
-        for (int e = 0; e < E; ++e) acc[hh][e] = 0.0f;
-    // Softmax state.  With at most 4 query heads per kv head, lane q of each
-    // quad of a unit owns head q % GRP: it alone runs the online softmax of
-    // that head, and the value weights reach the other lanes by DPP
-    // broadcast within the quad.  With 8 query heads every lane runs all of
-    // them.
-    constexpr bool SPLIT = GRP <= 4;
-    constexpr int NS = SPLIT ? 1 : GRP;          // softmax states per lane
-    const int hown = sub % GRP;
-    float m[NS], l[NS];
-#pragma unroll
-    for (int i = 0; i < NS; ++i) {
-        m[i] = -__builtin_inff();
-        l[i] = 0.0f;
-    }
-
-    const int step = kWaves * tpi;
-    const int tfirst = t0 + wave * tpi + tau;    // this lane group's first token
-    // tokens tb = t0 + wave*tpi + i*step (i < nsteps) are this wave's steps
-    const int nsteps = (t1 - (t0 + wave * tpi) + step - 1) / step;
-
-    // K/V codes and norms of step i, loaded kPrefetch steps ahead of use into
-    // a ring of kPrefetch + 1 slots (the slot refilled is the one used by the
-    // previous step, so nothing is copied).
-    //
-    // All lanes of a wave step read the same 16-token page (a step covers tpi
-    // tokens, tpi divides 16, and steps start on multiples of tpi), so the
-    // page's block number and the step's row inside the page are
-    // wave-uniform: they form a scalar base address, and every lane adds the
-    // same per-lane byte offset each step.
-    constexpr int R = kPrefetch + 1;
-    const uint32_t lane_row = (uint32_t)(tau * p.hkv + g);          // row within a token's rows
-    const uint32_t lane_code = lane_row * P + (uint32_t)(sub * (E * BITS / 8));
-    const uint32_t lane_norm = lane_row * 4u;
-    const uint64_t page_rows = (uint64_t)kAttnBlockSize * p.hkv;    // rows per block
-    const uint32_t step_rows = (uint32_t)(tpi * p.hkv);             // rows read per step
-    uint32_t rk[R][2], rv[R][2];
-    float rkn[R], rvn[R];
-    bool rok[R];
-    auto fetch = [&](int i, int slot) {
-        const int tb = t0 + wave * tpi + i * step;                    // wave-uniform
-        int32_t blk = (tb < t1) ? bt_lds[(tb - t0) / kAttnBlockSize] : 0;
-        blk = __builtin_amdgcn_readfirstlane(blk);
-        const bool bok = blk >= 0 && blk < p.num_blocks;
-        blk = bok ? blk : 0;
-        rok[slot] = bok && live && (tb + tau < t1);
-        // first row of this step: block * rows-per-block + token-in-page * hkv;
-        // the step's rows are [row0, row0 + step_rows)
-        const uint64_t row0 = (uint64_t)blk * page_rows + (uint64_t)((tb % kAttnBlockSize) * p.hkv);
-        // unconditional loads: a step past the end reads block 0, which exists
-        // whenever any token does; its score is masked below
-        load_codes_buf<BITS, E>(page_rsrc(p.kp + row0 * P, step_rows * P), lane_code, rk[slot]);
-        load_codes_buf<BITS, E>(page_rsrc(p.vp + row0 * P, step_rows * P), lane_code, rv[slot]);
-        rkn[slot] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-                                                  page_rsrc(p.kn + row0, step_rows * 4), lane_norm, 0, 0));
-        rvn[slot] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-                                                  page_rsrc(p.vn + row0, step_rows * 4), lane_norm, 0, 0));
-    };
-#pragma unroll
-    for (int d = 0; d < kPrefetch; ++d) fetch(d, d);
-
-    for (int i0 = 0; i0 < nsteps; i0 += R) {     // wave-uniform
-#pragma unroll
-        for (int d = 0; d < R; ++d) {
-            if (i0 + d >= nsteps) break;
-            fetch(i0 + d + kPrefetch, (d + kPrefetch) % R);
-            const bool ok = rok[d];
-            float val[E];
-            expand<BITS, E>(tab, rk[d], val);
-            float s[GRP];
-#pragma unroll
-            for (int hh = 0; hh < GRP; ++hh) {
-                float dd = 0.0f;
-#pragma unroll
-                for (int e = 0; e < E; ++e) dd = __builtin_fmaf(qt[hh][e], val[e], dd);
-                s[hh] = unit_sum<LPU>(dd) * rkn[d];
-            }
-            if constexpr (!SPLIT) {
-#pragma unroll
-                for (int hh = 0; hh < GRP; ++hh) s[hh] = ok ? s[hh] : -__builtin_inff();
-            }
-            float w[GRP];
-            if constexpr (SPLIT) {
-                float so = s[0];
-#pragma unroll
-                for (int hh = 1; hh < GRP; ++hh) so = (hown == hh) ? s[hh] : so;
-                so = ok ? so : -__builtin_inff();
-                // lazily raised reference: rescale only when a score passes m + 8
-                if (__builtin_amdgcn_ballot_w64(so > m[0] + kLazy)) {
-                    const float mn = (so > m[0] + kLazy) ? so : m[0];
-                    const float a = (mn == m[0]) ? 1.0f : __builtin_amdgcn_exp2f(m[0] - mn);
-                    l[0] *= a;
-                    m[0] = mn;
-#pragma unroll
-                    for (int hh = 0; hh < GRP; ++hh) {
-                        const float ah = quad_bcast(a, hh);
-#pragma unroll
-                        for (int e = 0; e < E; ++e) acc[hh][e] *= ah;
-                    }
-                }
-                const float pr = ok ? __builtin_amdgcn_exp2f(so - m[0]) : 0.0f;
-                l[0] += pr;
-                const float wo = pr * rvn[d];
-#pragma unroll
-                for (int hh = 0; hh < GRP; ++hh) w[hh] = quad_bcast(wo, hh);
-            } else {
-                bool need = false;
-#pragma unroll
-                for (int hh = 0; hh < GRP; ++hh) need |= s[hh] > m[hh % NS] + kLazy;
-                if (__builtin_amdgcn_ballot_w64(need)) {
-#pragma unroll
-                    for (int hh = 0; hh < GRP; ++hh) {
-                        const int i = hh % NS;
-                        const float mn = (s[hh] > m[i] + kLazy) ? s[hh] : m[i];
-                        const float a = (mn == m[i]) ? 1.0f : __builtin_amdgcn_exp2f(m[i] - mn);
-                        l[i] *= a;
-#pragma unroll
-                        for (int e = 0; e < E; ++e) acc[hh][e] *= a;
-                        m[i] = mn;
-                    }
-                }
-#pragma unroll
-                for (int hh = 0; hh < GRP; ++hh) {
-                    const int i = hh % NS;
-                    const float pr = ok ? __builtin_amdgcn_exp2f(s[hh] - m[i]) : 0.0f;
-                    l[i] += pr;
-                    w[hh] = pr * rvn[d];
-                }
-            }
-            expand<BITS, E>(tab, rv[d], val);
-#pragma unroll
-            for (int hh = 0; hh < GRP; ++hh)
-#pragma unroll
-                for (int e = 0; e < E; ++e) acc[hh][e] = __builtin_fmaf(w[hh], val[e], acc[hh][e]);
-        }
-    }
-
-    // every lane gets the softmax state of all its heads for the merges
-    float mh[GRP], lh[GRP];
-#pragma unroll
-    for (int hh = 0; hh < GRP; ++hh) {
-        mh[hh] = SPLIT ? quad_bcast(m[0], hh) : m[hh % NS];
-        lh[hh] = SPLIT ? quad_bcast(l[0], hh) : l[hh % NS];
-    }
-
-    // merge the TPI units of the same kv head inside the wave (narrow caches)
-    for (int off = p.hkv * LPU; off < tpi * p.hkv * LPU; off <<= 1) {
-#pragma unroll
-        for (int hh = 0; hh < GRP; ++hh) {
-            const float mo = __shfl_xor(mh[hh], off);
-            const float lo = __shfl_xor(lh[hh], off);
-            const float mn = mh[hh] > mo ? mh[hh] : mo;
-            const float a = (mh[hh] == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(mh[hh] - mn);
-            const float ao = (mo == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(mo - mn);
-            lh[hh] = lh[hh] * a + lo * ao;
-#pragma unroll
-            for (int e = 0; e < E; ++e) {
-                const float o = __shfl_xor(acc[hh][e], off);
-                acc[hh][e] = acc[hh][e] * a + o * ao;
-            }
-            mh[hh] = mn;
-        }
-    }
-
-    // merge the four waves through LDS: 2,3 -> 0,1, then 1 -> 0
-    auto put = [&](float *buf) {
-#pragma unroll
-        for (int hh = 0; hh < GRP; ++hh) {
-#pragma unroll
-            for (int e = 0; e < E; ++e) buf[(hh * E + e) * 64 + lane] = acc[hh][e];
-            buf[(GRP * E + 2 * hh) * 64 + lane] = mh[hh];
-            buf[(GRP * E + 2 * hh + 1) * 64 + lane] = lh[hh];
-        }
-    };
-    auto take = [&](const float *buf) {
-#pragma unroll
-        for (int hh = 0; hh < GRP; ++hh) {
-            const float mo = buf[(GRP * E + 2 * hh) * 64 + lane];
-            const float lo = buf[(GRP * E + 2 * hh + 1) * 64 + lane];
-            const float mn = mh[hh] > mo ? mh[hh] : mo;
-            const float a = (mh[hh] == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(mh[hh] - mn);
-            const float ao = (mo == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(mo - mn);
-            lh[hh] = lh[hh] * a + lo * ao;
-#pragma unroll
-            for (int e = 0; e < E; ++e)
-                acc[hh][e] = acc[hh][e] * a + buf[(hh * E + e) * 64 + lane] * ao;
-            mh[hh] = mn;
-        }
-    };
-    if (wave >= 2) put(xchg[wave - 2]);
-    __syncthreads();
-    if (wave < 2) take(xchg[wave]);
-    __syncthreads();
-    if (wave == 1) put(xchg[0]);
-    __syncthreads();
-    if (wave != 0 || !live || tau != 0) return;
-    take(xchg[0]);
-
-#pragma unroll
-    for (int hh = 0; hh < GRP; ++hh) {
-        const int h = g * GRP + hh;
-        float *dst = p.ws + (((size_t)b * p.hq + h) * p.num_splits + split) * kPartial;
-        if (sub == 0) {
-            dst[0] = mh[hh];
-            dst[1] = lh[hh];
-        }
-#pragma unroll
-        for (int e = 0; e < E; ++e) dst[2 + sub * E + e] = acc[hh][e];
-    }
-}
-
-// ---------------------------------------------------------------------------
-// Matrix-core split kernel (4-bit codes).
-//
-// Per (sequence, kv head, split) one wave walks the split's pages; per page it
-// runs the scores and the value accumulation as 16x16x32 f16 MFMA tiles:
-//   scores  S^T[16 tokens][16 heads] = C_k[16 tokens][K] * Q[K][16 heads]
-//   values  O[16 heads][16 dims]    += W[16 heads][K]   * C_v[K][16 dims]
-// with the group's query heads padded to 16 columns / rows.
-//
-// binary16 carries 11 significant bits, too few for the 2e-3 output bound
-// under peaked softmaxes, so every operand is split as x = x_hi + x_lo (both
-// binary16) and the products x_hi y_hi + x_lo y_hi + x_hi y_lo are formed.
-// The split costs no repacking: a code is looked up as the binary16 pair
-// (c_hi, c_lo), which fills two adjacent K slots; the other operand holds
-// (q_hi, q_hi) in those slots for one product and (q_lo, 0) for a second.
-//
-// Scale factors keep every binary16 operand in range and its low part
-// normal: levels are stored times 16, the rotated query times a per-head
-// power of two, and the value weights times 2^6 / vlim (vlim a power of two
-// above the value norms); all are powers of two and removed exactly before
-// the partial state is written.
-//
-// Lane layouts (l = lane, m = l % 16, r = l / 16), verified on gfx950:
-//   A[m][8r .. 8r+7], B[8r .. 8r+7][m], C[4r .. 4r+3][m].
-// Scores: lane (token m, r) holds codes of dims 32r .. 32r+31 of its token
-// (one 16-byte load); chunk j covers dims 32r + 4j .. +3 of every r.  The
-// query operand of lane (head m, r) covers the same dims.  The score tile
-// leaves lane (head m, r) with tokens 4r .. 4r+3 -- exactly the K slots the
-// value product wants in its A operand, so the weights never move between
-// lanes.  Values: lane (column m, r) reads dword m (dims 8m .. 8m+7) of
-// tokens 4r .. 4r+3; chunk jj accumulates dim 8m + jj.
-constexpr int kMWaves = 4;                 // kv heads (waves) per workgroup
-constexpr int kMThreads = 64 * kMWaves;
-constexpr int kMPrefetch = 1;              // extra ring slots: pages of loads in flight ahead of use
-constexpr float kLevelScale = 16.0f;       // binary16 levels are 16 c
-constexpr float kWShift = 6.0f;            // value weights carry 2^6
-constexpr int kLutStride = 256;            // bytes per table entry row (32 lane copies of 8 B)
-constexpr int kMTargetWaves = 4096;        // split-kernel waves aimed for
-
-typedef _Float16 h8 __attribute__((ext_vector_type(8)));
-typedef float f4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
 __device__ __forceinline__ uint32_t pack_half2(_Float16 a, _Float16 b) {
     return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
 }
@@ -521,34 +118,155 @@ __device__ __forceinline__ uint32_t level_pair(const CodecConsts &k, int code) {
     return pack_half2(hi, lo);
 }
 
-// Pairs of codes byte `k` of `word` decodes to.  The table holds, for each
-// byte value, (pair of the low nibble, pair of the high nibble) in 32 copies
-// 8 bytes apart -- one per lane of a 32-lane half wave -- filling a 256-byte
-// row per byte value: lane s of a half wave always hits banks 2s, 2s+1,
-// whatever the byte, so a table read never has a bank conflict.  One v_perm
-// forms the address (byte << 8 | 8 s).
-template <int K>
-__device__ __forceinline__ u32x2 lut_pair(const char *tab, uint32_t word, uint32_t laneoff) {
-    const uint32_t addr = __builtin_amdgcn_perm(word, laneoff, 0x0C0C0000u | ((4u + K) << 8));
-    return *reinterpret_cast<const u32x2 *>(tab + addr);
-}
-__device__ __forceinline__ u32x2 lut_pair_rt(const char *tab, uint32_t word, int k, uint32_t laneoff) {
-    switch (k & 3) {
-        case 0: return lut_pair<0>(tab, word, laneoff);
-        case 1: return lut_pair<1>(tab, word, laneoff);
-        case 2: return lut_pair<2>(tab, word, laneoff);
-        default: return lut_pair<3>(tab, word, laneoff);
-    }
-}
-
 __device__ __forceinline__ f4 mfma(const u32x4 &a, const u32x4 &b, f4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, a), __builtin_bit_cast(h8, b), c,
                                                   0, 0, 0);
 }
 
-__global__ __launch_bounds__(kMThreads) void attn_mfma_kernel(AttnParams p) {
-    constexpr int P = 64;                                    // packed bytes per row (4 bits)
-    __shared__ __attribute__((aligned(16))) char tab[256 * kLutStride];
+// Code lookup tables.  One table entry turns a group of codes into their
+// (c_hi, c_lo) pairs: a byte of two 4-bit codes (8 bytes), a byte of four
+// 2-bit codes (16 bytes) or a 6-bit field of two 3-bit codes (8 bytes).
+// Entry e of a side lives in row e of the LDS table (256 bytes: keys in the
+// first half, values in the second), repeated once per lane of a group of
+// 128 / entry-bytes lanes, so that lanes of a group never share a bank.  For
+// a byte index one v_perm forms the address (byte << 8 | lane offset).
+template <int B>
+struct Side {
+    static constexpr int P = 16 * B;                       // packed bytes per row
+    static constexpr int EB = (B == 2) ? 16 : 8;           // bytes per table entry
+    static constexpr int NE = (B == 3) ? 64 : 256;         // table entries
+    static constexpr int COPIES = 128 / EB;                // lane copies per half row
+};
+
+template <int B>
+__device__ __forceinline__ void fill_side(char *tab, const CodecConsts &k, int half) {
+    using S = Side<B>;
+    for (int t = threadIdx.x; t < S::NE * 32; t += kMThreads) {
+        const int e = t >> 5, w = t & 31;                  // entry, dword of the half row
+        const int dw = w % (S::EB / 4);                    // code group within the entry
+        int code;
+        if (B == 4) code = dw == 0 ? (e & 15) : (e >> 4);
+        else if (B == 3) code = dw == 0 ? (e & 7) : (e >> 3);
+        else code = (e >> (2 * dw)) & 3;
+        *reinterpret_cast<uint32_t *>(tab + e * kLutRow + half + 4 * w) = level_pair(k, code);
+    }
+}
+
+template <int K>
+__device__ __forceinline__ uint32_t byte_addr(uint32_t word, uint32_t laneoff) {
+    return __builtin_amdgcn_perm(word, laneoff, 0x0C0C0000u | ((4u + K) << 8));
+}
+
+// Pairs of the codes in byte K of `word` (4-bit codes: 2 pairs).
+template <int K>
+__device__ __forceinline__ u32x2 lut8(const char *tab, uint32_t word, uint32_t laneoff) {
+    return *reinterpret_cast<const u32x2 *>(tab + byte_addr<K>(word, laneoff));
+}
+// Pairs of the codes in byte K of `word` (2-bit codes: 4 pairs).
+template <int K>
+__device__ __forceinline__ u32x4 lut16(const char *tab, uint32_t word, uint32_t laneoff) {
+    return *reinterpret_cast<const u32x4 *>(tab + byte_addr<K>(word, laneoff));
+}
+// Pairs of the two 3-bit codes in a 6-bit field.
+__device__ __forceinline__ u32x2 lut8f(const char *tab, uint32_t field, uint32_t laneoff) {
+    return *reinterpret_cast<const u32x2 *>(tab + ((field << 8) | laneoff));
+}
+
+// Bits [b, b + 6) of the 96-bit little-endian string w.x, w.y, w.z.
+template <int b>
+__device__ __forceinline__ uint32_t field6(const u32x4 &w) {
+    constexpr int wi = b >> 5, sh = b & 31;
+    if constexpr (sh <= 26) return (w[wi] >> sh) & 63u;
+    else return __builtin_amdgcn_alignbit(w[wi + 1], w[wi], sh) & 63u;
+}
+
+template <int J, int KB>
+__device__ __forceinline__ u32x4 key_chunk(const char *tab, const u32x4 &kc, uint32_t laneoff) {
+    if constexpr (KB == 4) {             // bytes 2J, 2J+1: dims 4J .. 4J+3
+        const u32x2 a0 = lut8<(2 * J) & 3>(tab, kc[J >> 1], laneoff);
+        const u32x2 a1 = lut8<(2 * J + 1) & 3>(tab, kc[J >> 1], laneoff);
+        return u32x4{a0.x, a0.y, a1.x, a1.y};
+    } else if constexpr (KB == 2) {      // byte J
+        return lut16<J & 3>(tab, kc[J >> 2], laneoff);
+    } else {                             // bits 12J .. 12J+11
+        const u32x2 a0 = lut8f(tab, field6<12 * J>(kc), laneoff);
+        const u32x2 a1 = lut8f(tab, field6<12 * J + 6>(kc), laneoff);
+        return u32x4{a0.x, a0.y, a1.x, a1.y};
+    }
+}
+
+template <int J, int KB>
+__device__ __forceinline__ void score_chunks(const char *tab, const u32x4 &kc, uint32_t laneoff,
+                                             const u32x4 (&bq1)[8], const u32x4 (&bq2)[8],
+                                             f4 &S0, f4 &S1) {
+    const u32x4 A = key_chunk<J, KB>(tab, kc, laneoff);
+    S0 = mfma(A, bq1[J], S0);
+    S1 = mfma(A, bq2[J], S1);
+    if constexpr (J < 7) score_chunks<J + 1, KB>(tab, kc, laneoff, bq1, bq2, S0, S1);
+}
+
+template <int K>
+__device__ __forceinline__ void value_bytes4(const char *tab, const uint32_t (&vc)[4],
+                                             uint32_t laneoff, u32x4 (&Bv)[8]) {
+    u32x2 L[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) L[i] = lut8<K>(tab, vc[i], laneoff);
+    Bv[2 * K] = u32x4{L[0].x, L[1].x, L[2].x, L[3].x};
+    Bv[2 * K + 1] = u32x4{L[0].y, L[1].y, L[2].y, L[3].y};
+}
+
+template <int K>
+__device__ __forceinline__ void value_bytes2(const char *tab, const uint32_t (&vc)[4],
+                                             uint32_t laneoff, u32x4 (&Bv)[8]) {
+    u32x4 L[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) L[i] = lut16<K>(tab, vc[i], laneoff);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) Bv[4 * K + t] = u32x4{L[0][t], L[1][t], L[2][t], L[3][t]};
+}
+
+// The value operands of the page: Bv[jj] holds dim 8m + jj of tokens
+// 4r .. 4r+3 as (c_hi, c_lo) pairs.  vc[i] is this lane's raw load for token
+// 4r + i; q4 = m % 4.
+template <int VB>
+__device__ __forceinline__ void value_operands(const char *tab, const uint32_t (&vc)[4],
+                                               uint32_t laneoff, int q4, u32x4 (&Bv)[8]) {
+    if constexpr (VB == 4) {             // dword m: byte k holds dims 8m + 2k, +1
+        value_bytes4<0>(tab, vc, laneoff, Bv);
+        value_bytes4<1>(tab, vc, laneoff, Bv);
+        value_bytes4<2>(tab, vc, laneoff, Bv);
+        value_bytes4<3>(tab, vc, laneoff, Bv);
+    } else if constexpr (VB == 2) {      // 16 bits: byte k holds dims 8m + 4k .. +3
+        value_bytes2<0>(tab, vc, laneoff, Bv);
+        value_bytes2<1>(tab, vc, laneoff, Bv);
+    } else {
+        // 24 bits at bit 24m of the row.  Lanes m = 4a .. 4a+3 of a quad loaded
+        // dwords 3a, 3a+1, 3a+2, 3a+2; lane q's field starts in the dword of
+        // lane q-1 (lane 0: its own) at bit 24q mod 32.
+        const uint32_t sh = (24u * (uint32_t)q4) & 31u;
+        uint32_t v24[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t prev = (uint32_t)__builtin_amdgcn_mov_dpp((int)vc[i], kQuadPrev, 0xF, 0xF, true);
+            const uint32_t lo = q4 == 0 ? vc[i] : prev;
+            v24[i] = __builtin_amdgcn_alignbit(vc[i], lo, sh);
+        }
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {    // field s: dims 8m + 2s, +1
+            u32x2 L[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) L[i] = lut8f(tab, (v24[i] >> (6 * s)) & 63u, laneoff);
+            Bv[2 * s] = u32x4{L[0].x, L[1].x, L[2].x, L[3].x};
+            Bv[2 * s + 1] = u32x4{L[0].y, L[1].y, L[2].y, L[3].y};
+        }
+    }
+}
+
+template <int KB, int VB>
+__global__ __launch_bounds__(kMThreads) void attn_split_kernel(AttnParams p) {
+    using SK = Side<KB>;
+    using SV = Side<VB>;
+    __shared__ __attribute__((aligned(16))) char tab[256 * kLutRow];
     __shared__ int32_t bt_lds[kMaxSplitTokens / kAttnBlockSize];
 
     const int b = blockIdx.y;
@@ -563,13 +281,8 @@ __global__ __launch_bounds__(kMThreads) void attn_mfma_kernel(AttnParams p) {
     const int t1 = (t0 + p.split_tokens < T) ? t0 + p.split_tokens : T;
     const int npages = (t1 - t0 + kAttnBlockSize - 1) / kAttnBlockSize;
 
-    for (int i = threadIdx.x; i < 256 * 32; i += kMThreads) {
-        const int e = i >> 5, c = i & 31;
-        u32x2 v;
-        v.x = level_pair(p.k, e & 15);
-        v.y = level_pair(p.k, e >> 4);
-        *reinterpret_cast<u32x2 *>(tab + e * kLutStride + 8 * c) = v;
-    }
+    fill_side<KB>(tab, p.k, 0);
+    fill_side<VB>(tab, p.v, kLutRow / 2);
     {
         const int32_t *bt = p.block_tables + (size_t)b * p.max_blocks + t0 / kAttnBlockSize;
         for (int i = threadIdx.x; i < npages; i += kMThreads) bt_lds[i] = bt[i];
@@ -583,7 +296,8 @@ __global__ __launch_bounds__(kMThreads) void attn_mfma_kernel(AttnParams p) {
     const int m = lane & 15, r = lane >> 4;
     const int grp = p.hq / p.hkv;
     const bool hv = m < grp;                                  // a real query head column
-    const uint32_t laneoff = 8u * (uint32_t)(lane & 31);
+    const uint32_t lok = (uint32_t)(lane & (SK::COPIES - 1)) * SK::EB;
+    const uint32_t lov = kLutRow / 2 + (uint32_t)(lane & (SV::COPIES - 1)) * SV::EB;
 
     // ---- rotated query, one head per lane column, dims 32r .. 32r+31 ----
     u32x4 bq1[8], bq2[8];
@@ -648,16 +362,22 @@ __global__ __launch_bounds__(kMThreads) void attn_mfma_kernel(AttnParams p) {
     float vscale = 0.0f;                  // 2^6 / vlim
 
     // per-lane byte offsets inside one page of this kv head
-    const uint32_t row_bytes = (uint32_t)p.hkv * P;           // one token of all kv heads
-    const uint32_t offk = (uint32_t)m * row_bytes + (uint32_t)g * P + 16u * r;
+    const uint32_t rowk = (uint32_t)p.hkv * SK::P;            // one token of all kv heads
+    const uint32_t rowv = (uint32_t)p.hkv * SV::P;
+    const uint32_t offk = (uint32_t)m * rowk + (uint32_t)g * SK::P + 4u * KB * r;
+    const int q4 = m & 3;
     uint32_t offv[4], offn[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        offv[i] = (uint32_t)(4 * r + i) * row_bytes + (uint32_t)g * P + 4u * m;
+        const uint32_t row = (uint32_t)(4 * r + i) * rowv + (uint32_t)g * SV::P;
+        if (VB == 4) offv[i] = row + 4u * m;
+        else if (VB == 2) offv[i] = row + 2u * m;
+        else offv[i] = row + 4u * (3u * (uint32_t)(m >> 2) + (uint32_t)(q4 < 2 ? q4 : 2));
         offn[i] = ((uint32_t)(4 * r + i) * p.hkv + g) * 4u;
     }
-    const uint32_t page_bytes = kAttnBlockSize * row_bytes;
-    const uint32_t page_nbytes = kAttnBlockSize * p.hkv * 4u;
+    const uint32_t pagek = kAttnBlockSize * rowk;
+    const uint32_t pagev = kAttnBlockSize * rowv;
+    const uint32_t pagen = kAttnBlockSize * p.hkv * 4u;
 
     // Loads of page pg sit in ring slot pg % R.  The refill for page pg + R
     // is issued at the end of step pg, once the slot has been consumed; its
@@ -675,13 +395,24 @@ __global__ __launch_bounds__(kMThreads) void attn_mfma_kernel(AttnParams p) {
         const bool bok = pg < npages && blk >= 0 && blk < p.num_blocks;
         rok[slot] = bok;
         blk = (blk >= 0 && blk < p.num_blocks) ? blk : 0;
-        const __amdgpu_buffer_rsrc_t rsk = page_rsrc(p.kp + (size_t)blk * page_bytes, page_bytes);
-        const __amdgpu_buffer_rsrc_t rsv = page_rsrc(p.vp + (size_t)blk * page_bytes, page_bytes);
-        const __amdgpu_buffer_rsrc_t rkn_ = page_rsrc(p.kn + (size_t)blk * kAttnBlockSize * p.hkv, page_nbytes);
-        const __amdgpu_buffer_rsrc_t rvn_ = page_rsrc(p.vn + (size_t)blk * kAttnBlockSize * p.hkv, page_nbytes);
-        rk[slot] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsk, offk, 0, 0));
+        const __amdgpu_buffer_rsrc_t rsk = page_rsrc(p.kp + (size_t)blk * pagek, pagek);
+        const __amdgpu_buffer_rsrc_t rsv = page_rsrc(p.vp + (size_t)blk * pagev, pagev);
+        const __amdgpu_buffer_rsrc_t rkn_ = page_rsrc(p.kn + (size_t)blk * kAttnBlockSize * p.hkv, pagen);
+        const __amdgpu_buffer_rsrc_t rvn_ = page_rsrc(p.vn + (size_t)blk * kAttnBlockSize * p.hkv, pagen);
+        if constexpr (KB == 4) {
+            rk[slot] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsk, offk, 0, 0));
+        } else if constexpr (KB == 2) {
+            const u32x2 t = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rsk, offk, 0, 0));
+            rk[slot] = u32x4{t.x, t.y, 0u, 0u};
+        } else {
+            const u32x3 t = __builtin_bit_cast(u32x3, __builtin_amdgcn_raw_buffer_load_b96(rsk, offk, 0, 0));
+            rk[slot] = u32x4{t.x, t.y, t.z, 0u};
+        }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) rv[slot][i] = __builtin_amdgcn_raw_buffer_load_b32(rsv, offv[i], 0, 0);
+        for (int i = 0; i < 4; ++i) {
+            if constexpr (VB == 2) rv[slot][i] = __builtin_amdgcn_raw_buffer_load_b16(rsv, offv[i], 0, 0);
+            else rv[slot][i] = __builtin_amdgcn_raw_buffer_load_b32(rsv, offv[i], 0, 0);
+        }
 #pragma unroll
         for (int i = 0; i < 4; ++i)
             rkn[slot][i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rkn_, offn[i], 0, 0));
@@ -694,106 +425,91 @@ __global__ __launch_bounds__(kMThreads) void attn_mfma_kernel(AttnParams p) {
     for (int d = 0; d < R; ++d) fetch(d, bt_at(d), d);
     int32_t blk_next = bt_at(R);
 
-    // one page: table reads, score tiles, softmax, value tiles, refill
+    // one page: score tiles, value operands, softmax, value tiles, refill
     auto step = [&](const int pg, const int d) {
-            // scores of tokens 4r .. 4r+3 for head m, over two independent chains
-            u32x2 ka[16];
-#pragma unroll
-            for (int kb = 0; kb < 16; ++kb) ka[kb] = lut_pair_rt(tab, rk[d][kb >> 2], kb & 3, laneoff);
-            f4 S0 = f4{0.0f, 0.0f, 0.0f, 0.0f}, S1 = S0;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const u32x4 A = u32x4{ka[2 * j].x, ka[2 * j].y, ka[2 * j + 1].x, ka[2 * j + 1].y};
-                S0 = mfma(A, bq1[j], S0);
-                S1 = mfma(A, bq2[j], S1);
-            }
-            // value codes of the page, read while the score tiles finish
-            u32x2 va[4][4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int k2 = 0; k2 < 4; ++k2) va[i][k2] = lut_pair_rt(tab, rv[d][i], k2, laneoff);
-            const f4 S = S0 + S1;
+        // scores of tokens 4r .. 4r+3 for head m, over two independent chains
+        f4 S0 = f4{0.0f, 0.0f, 0.0f, 0.0f}, S1 = S0;
+        score_chunks<0, KB>(tab, rk[d], lok, bq1, bq2, S0, S1);
+        // value codes of the page, read while the score tiles finish
+        u32x4 Bv[8];
+        value_operands<VB>(tab, rv[d], lov, q4, Bv);
+        const f4 S = S0 + S1;
 
-            // online softmax in base 2.  Two lazily raised references: M per
-            // head (rescale when a score passes M + 8) and a power of two vlim
-            // per wave bounding the value norms (rescale when a norm passes
-            // it); the weights w = 2^(s - M) * n_v * 2^6 / vlim then stay
-            // below 2^14, inside binary16.
-            const int tbase = t0 + pg * kAttnBlockSize + 4 * r;
-            const bool full = rok[d] && (t0 + pg * kAttnBlockSize + kAttnBlockSize <= t1);
-            float s2[4], vn[4];
+        // online softmax in base 2.  Two lazily raised references: M per head
+        // (rescale when a score passes M + 8) and a power of two vlim per wave
+        // bounding the value norms (rescale when a norm passes it); the
+        // weights w = 2^(s - M) * n_v * 2^6 / vlim then stay below 2^14,
+        // inside binary16.
+        const int tbase = t0 + pg * kAttnBlockSize + 4 * r;
+        const bool full = rok[d] && (t0 + pg * kAttnBlockSize + kAttnBlockSize <= t1);
+        float s2[4], vn[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            s2[i] = S[i] * (rkn[d][i] * qsl);
+            vn[i] = rvn[d][i];
+        }
+        if (!full) {                                    // wave-uniform
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                s2[i] = S[i] * (rkn[d][i] * qsl);
-                vn[i] = rvn[d][i];
+                const bool ok = rok[d] && (tbase + i < t1);
+                s2[i] = ok ? s2[i] : -__builtin_inff();
+                vn[i] = ok ? vn[i] : 0.0f;
             }
-            if (!full) {                                    // wave-uniform
+        }
+        float smax = __builtin_fmaxf(__builtin_fmaxf(s2[0], s2[1]), __builtin_fmaxf(s2[2], s2[3]));
+        smax = hv ? smax : -__builtin_inff();
+        const float vmax = __builtin_fmaxf(__builtin_fmaxf(vn[0], vn[1]), __builtin_fmaxf(vn[2], vn[3]));
+        if (__builtin_amdgcn_ballot_w64(smax > M + kLazy || vmax > vlim)) {
+            // new score reference of every head whose scores passed it by 2^8
+            float mx = __builtin_fmaxf(smax, __shfl_xor(smax, 16));
+            mx = __builtin_fmaxf(mx, __shfl_xor(mx, 32));
+            const float Mn = (mx > M + kLazy) ? mx : M;
+            const float f = (Mn == M) ? 1.0f : __builtin_amdgcn_exp2f(M - Mn);
+            lsum *= f;
+            M = Mn;
+            // new norm bound: the power of two above the wave's largest norm
+            float vw = vmax;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const bool ok = rok[d] && (tbase + i < t1);
-                    s2[i] = ok ? s2[i] : -__builtin_inff();
-                    vn[i] = ok ? vn[i] : 0.0f;
-                }
+            for (int o = 1; o < 64; o <<= 1) vw = __builtin_fmaxf(vw, __shfl_xor(vw, o));
+            float fv = 1.0f;
+            if (vw > vlim) {                              // wave-uniform
+                const int e = __builtin_amdgcn_frexp_expf(vw);   // vw in [2^(e-1), 2^e)
+                const float vn_lim = __builtin_bit_cast(float, (uint32_t)(127 + (e > 127 ? 127 : e)) << 23);
+                fv = vlim / vn_lim;                         // exact: both powers of two (or 0)
+                vlim = vn_lim;
+                vscale = (float)(1 << (int)kWShift) / vlim;
             }
-            float smax = __builtin_fmaxf(__builtin_fmaxf(s2[0], s2[1]), __builtin_fmaxf(s2[2], s2[3]));
-            smax = hv ? smax : -__builtin_inff();
-            const float vmax = __builtin_fmaxf(__builtin_fmaxf(vn[0], vn[1]), __builtin_fmaxf(vn[2], vn[3]));
-            if (__builtin_amdgcn_ballot_w64(smax > M + kLazy || vmax > vlim)) {
-                // new score reference of every head whose scores passed it by 2^8
-                float mx = __builtin_fmaxf(smax, __shfl_xor(smax, 16));
-                mx = __builtin_fmaxf(mx, __shfl_xor(mx, 32));
-                const float Mn = (mx > M + kLazy) ? mx : M;
-                const float f = (Mn == M) ? 1.0f : __builtin_amdgcn_exp2f(M - Mn);
-                lsum *= f;
-                M = Mn;
-                // new norm bound: the power of two above the wave's largest norm
-                float vw = vmax;
-#pragma unroll
-                for (int o = 1; o < 64; o <<= 1) vw = __builtin_fmaxf(vw, __shfl_xor(vw, o));
-                float fv = 1.0f;
-                if (vw > vlim) {                              // wave-uniform
-                    const int e = __builtin_amdgcn_frexp_expf(vw);   // vw in [2^(e-1), 2^e)
-                    const float vn_lim = __builtin_bit_cast(float, (uint32_t)(127 + (e > 127 ? 127 : e)) << 23);
-                    fv = vlim / vn_lim;                         // exact: both powers of two (or 0)
-                    vlim = vn_lim;
-                    vscale = (float)(1 << (int)kWShift) / vlim;
-                }
-                // accumulator rows are heads 4r + i
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float fi = __shfl(f, 4 * r + i) * fv;
-#pragma unroll
-                    for (int jj = 0; jj < 8; ++jj) acc[jj][i] *= fi;
-                }
-            }
-            // before any valid token M is -inf; masked tokens must still give 0
-            const float Mc = (M == -__builtin_inff()) ? 0.0f : M;
-            uint32_t w1[4], w2[4];
+            // accumulator rows are heads 4r + i
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const float pr = __builtin_amdgcn_exp2f(s2[i] - Mc);
-                lsum += pr;
-                const float w = pr * (vn[i] * vscale);
-                // w = hi + lo; hi is w truncated to binary16, lo the remainder
-                const uint32_t hh = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(w, w));
-                const float hf = (float)__builtin_bit_cast(_Float16, (uint16_t)(hh & 0xFFFFu));
-                w1[i] = hh;
-                w2[i] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(w - hf));
-            }
-            const u32x4 A1 = u32x4{w1[0], w1[1], w1[2], w1[3]};
-            const u32x4 A2 = u32x4{w2[0], w2[1], w2[2], w2[3]};
-
-            // values: dims 8m + jj of tokens 4r .. 4r+3
+                const float fi = __shfl(f, 4 * r + i) * fv;
 #pragma unroll
-            for (int k2 = 0; k2 < 4; ++k2) {
-                const u32x4 B0 = u32x4{va[0][k2].x, va[1][k2].x, va[2][k2].x, va[3][k2].x};
-                const u32x4 B1 = u32x4{va[0][k2].y, va[1][k2].y, va[2][k2].y, va[3][k2].y};
-                acc[2 * k2] = mfma(A1, B0, acc[2 * k2]);
-                acc[2 * k2 + 1] = mfma(A1, B1, acc[2 * k2 + 1]);
-                acc[2 * k2] = mfma(A2, B0, acc[2 * k2]);
-                acc[2 * k2 + 1] = mfma(A2, B1, acc[2 * k2 + 1]);
+                for (int jj = 0; jj < 8; ++jj) acc[jj][i] *= fi;
             }
+        }
+        // before any valid token M is -inf; masked tokens must still give 0
+        const float Mc = (M == -__builtin_inff()) ? 0.0f : M;
+        uint32_t w1[4], w2[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float pr = __builtin_amdgcn_exp2f(s2[i] - Mc);
+            lsum += pr;
+            const float w = pr * (vn[i] * vscale);
+            // w = hi + lo; hi is w truncated to binary16, lo the remainder
+            const uint32_t hh = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(w, w));
+            const float hf = (float)__builtin_bit_cast(_Float16, (uint16_t)(hh & 0xFFFFu));
+            w1[i] = hh;
+            w2[i] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(w - hf));
+        }
+        const u32x4 A1 = u32x4{w1[0], w1[1], w1[2], w1[3]};
+        const u32x4 A2 = u32x4{w2[0], w2[1], w2[2], w2[3]};
+
+        // values: dims 8m + jj of tokens 4r .. 4r+3
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) {
+            acc[jj] = mfma(A1, Bv[jj], acc[jj]);
+            acc[jj] = mfma(A2, Bv[jj], acc[jj]);
+        }
 
         fetch(pg + R, blk_next, d);
         blk_next = bt_at(pg + R + 1);
@@ -903,42 +619,20 @@ __global__ __launch_bounds__(64) void attn_combine_kernel(AttnParams p) {
     reinterpret_cast<uint32_t *>(o)[lane] = packed2;
 }
 
-int wave_units(int grp) { return grp <= 4 ? 8 : 4; }   // units per wave: E = 16 or 8
-
-// The matrix-core kernel serves 4-bit caches with up to 16 query heads per
-// kv head; the vector kernel serves the rest.
-bool mfma_path(const AttnShape &s) {
-    const int grp = s.num_q_heads / s.num_kv_heads;
-    return s.bits == 4 && grp >= 1 && grp <= 16;
-}
+bool bits_ok(int b) { return b == 2 || b == 3 || b == 4; }
 
 }  // namespace
 
 bool attn_supported(const AttnShape &s) {
-    if (mfma_path(s)) return true;
+    if (s.num_kv_heads <= 0 || s.num_q_heads % s.num_kv_heads) return false;
     const int grp = s.num_q_heads / s.num_kv_heads;
-    if (grp != 1 && grp != 2 && grp != 4 && grp != 8) return false;
-    const int upw = wave_units(grp);
-    return s.num_kv_heads % upw == 0 || upw % s.num_kv_heads == 0;
+    return grp >= 1 && grp <= kAttnMaxGroup && bits_ok(s.k_bits) && bits_ok(s.v_bits);
 }
 
-namespace {
-
-int valu_split_tokens(const AttnShape &s) {
+int attn_split_tokens(const AttnShape &s) {
+    // one wave per (sequence, kv head) and split; about kMTargetWaves waves
     const int ctx = s.max_blocks * kAttnBlockSize;
-    const int grp = s.num_q_heads / s.num_kv_heads;
-    const int upw = wave_units(grp);
-    const int zch = s.num_kv_heads >= upw ? s.num_kv_heads / upw : 1;
-    const int per_seq = s.batch * zch > 0 ? (kTargetGroups + s.batch * zch - 1) / (s.batch * zch) : 1;
-    int st = (ctx + per_seq - 1) / per_seq;
-    st = (st + 63) / 64 * 64;
-    st = st < 256 ? 256 : st;
-    return st > kMaxSplitTokens ? kMaxSplitTokens : st;
-}
-
-int mfma_split_tokens(const AttnShape &s) {
-    const int ctx = s.max_blocks * kAttnBlockSize;
-    const int units = s.batch * s.num_kv_heads;           // one wave each per split
+    const int units = s.batch * s.num_kv_heads;
     const int per_seq = units > 0 ? (kMTargetWaves + units - 1) / units : 1;
     int st = (ctx + per_seq - 1) / per_seq;
     st = (st + kAttnBlockSize - 1) / kAttnBlockSize * kAttnBlockSize;
@@ -946,38 +640,23 @@ int mfma_split_tokens(const AttnShape &s) {
     return st > kMaxSplitTokens ? kMaxSplitTokens : st;
 }
 
-int splits_for(const AttnShape &s, int st) {
+int attn_num_splits(const AttnShape &s) {
     const int ctx = s.max_blocks * kAttnBlockSize;
+    const int st = attn_split_tokens(s);
     const int ns = (ctx + st - 1) / st;
     return ns < 1 ? 1 : ns;
 }
 
-}  // namespace
-
-int attn_split_tokens(const AttnShape &s) {
-    return mfma_path(s) ? mfma_split_tokens(s) : valu_split_tokens(s);
-}
-
-int attn_num_splits(const AttnShape &s) { return splits_for(s, attn_split_tokens(s)); }
-
 size_t attn_workspace_bytes(const AttnShape &s) {
-    // enough for either kernel, so that the size does not depend on the bit width
-    AttnShape s4 = s;
-    s4.bits = 4;
-    const int ns = std::max(splits_for(s, valu_split_tokens(s)),
-                            mfma_path(s4) ? splits_for(s, mfma_split_tokens(s4)) : 1);
-    return (size_t)s.batch * s.num_q_heads * ns * kPartial * sizeof(float);
+    return (size_t)s.batch * s.num_q_heads * attn_num_splits(s) * kPartial * sizeof(float);
 }
 
-hipError_t launch_attn(const AttnShape &s, const CodecConsts &k, const void *q,
-                       const uint8_t *k_packed, const float *k_norms, const uint8_t *v_packed,
-                       const float *v_norms, const int32_t *block_tables,
-                       const int32_t *context_lens, float scale, void *out, void *workspace,
-                       hipStream_t stream) {
-    const int grp = s.num_q_heads / s.num_kv_heads;
-    const int upw = wave_units(grp);
-    const bool mf = mfma_path(s);
-    if (!mf && !(s.num_kv_heads % upw == 0 || upw % s.num_kv_heads == 0)) return hipErrorInvalidValue;
+hipError_t launch_attn(const AttnShape &s, const CodecConsts &kc, const CodecConsts &vc,
+                       const void *q, const uint8_t *k_packed, const float *k_norms,
+                       const uint8_t *v_packed, const float *v_norms,
+                       const int32_t *block_tables, const int32_t *context_lens, float scale,
+                       void *out, void *workspace, hipStream_t stream) {
+    if (!attn_supported(s)) return hipErrorInvalidValue;
     AttnParams p;
     p.q = static_cast<const uint16_t *>(q);
     p.kp = k_packed;
@@ -996,34 +675,23 @@ hipError_t launch_attn(const AttnShape &s, const CodecConsts &k, const void *q,
     p.num_splits = attn_num_splits(s);
     p.num_blocks = s.num_blocks;
     p.qscale = scale * 1.4426950408889634f / kHeadDim;
-    p.k = k;
-    if (mf) {
-        const dim3 grid(p.num_splits, s.batch, (s.num_kv_heads + kMWaves - 1) / kMWaves);
-        hipLaunchKernelGGL(attn_mfma_kernel, grid, dim3(kMThreads), 0, stream, p);
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
-        hipLaunchKernelGGL(attn_combine_kernel, dim3(s.batch * s.num_q_heads), dim3(64), 0, stream, p);
-        return hipGetLastError();
-    }
-    const int zch = s.num_kv_heads >= upw ? s.num_kv_heads / upw : 1;
-    const dim3 grid(p.num_splits, s.batch, zch), block(kThreads);
-#define TQ_SPLIT(B, GR, E) \
-    hipLaunchKernelGGL((attn_split_kernel<B, GR, E>), grid, block, 0, stream, p)
-#define TQ_BITS(GR, E)                           \
-    switch (s.bits) {                            \
-        case 2: TQ_SPLIT(2, GR, E); break;       \
-        case 3: TQ_SPLIT(3, GR, E); break;       \
-        case 4: TQ_SPLIT(4, GR, E); break;       \
-        default: return hipErrorInvalidValue;   \
-    }
-    switch (grp) {
-        case 1: TQ_BITS(1, 16) break;
-        case 2: TQ_BITS(2, 16) break;
-        case 4: TQ_BITS(4, 16) break;
-        case 8: TQ_BITS(8, 8) break;
+    p.k = kc;
+    p.v = vc;
+    const dim3 grid(p.num_splits, s.batch, (s.num_kv_heads + kMWaves - 1) / kMWaves);
+    const dim3 block(kMThreads);
+#define TQ_SPLIT(KB, VB) hipLaunchKernelGGL((attn_split_kernel<KB, VB>), grid, block, 0, stream, p)
+    switch (s.k_bits * 10 + s.v_bits) {
+        case 44: TQ_SPLIT(4, 4); break;
+        case 43: TQ_SPLIT(4, 3); break;
+        case 42: TQ_SPLIT(4, 2); break;
+        case 34: TQ_SPLIT(3, 4); break;
+        case 33: TQ_SPLIT(3, 3); break;
+        case 32: TQ_SPLIT(3, 2); break;
+        case 24: TQ_SPLIT(2, 4); break;
+        case 23: TQ_SPLIT(2, 3); break;
+        case 22: TQ_SPLIT(2, 2); break;
         default: return hipErrorInvalidValue;
     }
-#undef TQ_BITS
 #undef TQ_SPLIT
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

@@ -44,28 +44,28 @@ hipError_t launch_decode(int bits, const uint8_t *packed, const float *norms, in
 // ---------------------------------------------------------------------------
 
 constexpr int kAttnBlockSize = 16;   // tokens per cache page
-constexpr int kAttnMaxGroup = 8;     // query heads per kv head
+constexpr int kAttnMaxGroup = 16;    // query heads per kv head
 
 struct AttnShape {
-    int batch, num_q_heads, num_kv_heads, bits, max_blocks;
+    int batch, num_q_heads, num_kv_heads, k_bits, v_bits, max_blocks;
     int64_t num_blocks;
 };
 
-// Whether the split kernel has a variant for this (query heads per kv head,
-// kv heads) combination.
+// Whether the split kernel serves this shape (1..16 query heads per kv head,
+// 2..4-bit keys and values).
 bool attn_supported(const AttnShape &s);
 
-// Tokens handled by one workgroup of the split kernel, and the number of
-// splits of the longest possible context.
+// Tokens handled by one wave of the split kernel, and the number of splits of
+// the longest possible context (neither depends on the bit widths).
 int attn_split_tokens(const AttnShape &s);
 int attn_num_splits(const AttnShape &s);
 size_t attn_workspace_bytes(const AttnShape &s);
 
-hipError_t launch_attn(const AttnShape &s, const CodecConsts &k, const void *q,
-                       const uint8_t *k_packed, const float *k_norms, const uint8_t *v_packed,
-                       const float *v_norms, const int32_t *block_tables,
-                       const int32_t *context_lens, float scale, void *out, void *workspace,
-                       hipStream_t stream);
+hipError_t launch_attn(const AttnShape &s, const CodecConsts &kc, const CodecConsts &vc,
+                       const void *q, const uint8_t *k_packed, const float *k_norms,
+                       const uint8_t *v_packed, const float *v_norms,
+                       const int32_t *block_tables, const int32_t *context_lens, float scale,
+                       void *out, void *workspace, hipStream_t stream);
 
 int device_cu_count();
 

@@ -12,8 +12,9 @@ operators).
                                                cache_norms, bits, seed) -> ()
     torch.ops.kv_cache_vector.tq_attn_decode(q, k_packed, k_norms, v_packed,
                                              v_norms, block_tables,
-                                             context_lens, bits, seed, scale)
-                                             -> out
+                                             context_lens, bits, seed, scale,
+                                             v_bits=-1) -> out
+      (v_bits: width of the value codes; -1 means the same as the keys')
 
 Seeds are unsigned 64-bit values; the schema's int is signed, so seeds at or
 above 2^63 travel as their two's-complement int64 and are converted back.
@@ -150,19 +151,21 @@ def _(x, slots, cache_packed, cache_norms, bits, seed):
 def tq_attn_decode(q: torch.Tensor, k_packed: torch.Tensor, k_norms: torch.Tensor,
                    v_packed: torch.Tensor, v_norms: torch.Tensor, block_tables: torch.Tensor,
                    context_lens: torch.Tensor, bits: int, seed: int,
-                   scale: float) -> torch.Tensor:
+                   scale: float, v_bits: int = -1) -> torch.Tensor:
     for t, name in ((q, "query"), (k_packed, "k_packed"), (k_norms, "k_norms"),
                     (v_packed, "v_packed"), (v_norms, "v_norms"),
                     (block_tables, "block_tables"), (context_lens, "context_lens")):
         _gpu(t, name)
+    vb = bits if v_bits < 0 else v_bits
     P = _packed_dim(HEAD_DIM, bits)
+    PV = _packed_dim(HEAD_DIM, vb)
     if q.dim() != 3 or q.shape[-1] != HEAD_DIM or q.dtype != torch.float16:
         raise ValueError("query must be float16 [batch, num_q_heads, %d]" % HEAD_DIM)
     B, Hq, _ = q.shape
     if k_packed.dim() != 4:
         raise ValueError("k_packed must be [num_blocks, block_size, num_kv_heads, P]")
     nblk, bs, hkv, Pk = k_packed.shape
-    if Pk != P or tuple(v_packed.shape) != tuple(k_packed.shape):
+    if Pk != P or tuple(v_packed.shape) != (nblk, bs, hkv, PV):
         raise ValueError("k_packed / v_packed shape mismatch")
     if tuple(k_norms.shape) != (nblk, bs, hkv) or tuple(v_norms.shape) != (nblk, bs, hkv):
         raise ValueError("norms must be [num_blocks, block_size, num_kv_heads]")
@@ -180,14 +183,17 @@ def tq_attn_decode(q: torch.Tensor, k_packed: torch.Tensor, k_norms: torch.Tenso
     out = torch.empty_like(q)
     nbytes = _lib.tq_attn_workspace_bytes(B, Hq, hkv, HEAD_DIM, bs, maxb)
     ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
-    _lib.check(_lib.tq_attn_decode(
+    _lib.check(_lib.tq_attn_decode_kv(
         q.data_ptr(), k_packed.data_ptr(), k_norms.data_ptr(), v_packed.data_ptr(),
         v_norms.data_ptr(), block_tables.data_ptr(), context_lens.data_ptr(), B, Hq, hkv,
-        HEAD_DIM, bits, _seed_u64(seed), bs, maxb, nblk, float(scale), out.data_ptr(),
-        ws.data_ptr(), ws.numel(), _stream(q.device)), "tq_attn_decode")
+        HEAD_DIM, bits, vb, _seed_u64(seed), bs, maxb, nblk, float(scale), out.data_ptr(),
+        ws.data_ptr(), ws.numel(), _stream(q.device)), "tq_attn_decode_kv")
     return out
 
 
 @tq_attn_decode.register_fake
-def _(q, k_packed, k_norms, v_packed, v_norms, block_tables, context_lens, bits, seed, scale):
+def _(q, k_packed, k_norms, v_packed, v_norms, block_tables, context_lens, bits, seed, scale,
+      v_bits=-1):
+    _packed_dim(HEAD_DIM, bits)
+    _packed_dim(HEAD_DIM, bits if v_bits < 0 else v_bits)
     return torch.empty_like(q)

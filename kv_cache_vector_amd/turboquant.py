@@ -130,10 +130,17 @@ class TurboQuant:
 
 
 class TQPagedAttention:
-    """Single-token decode attention straight from the packed, paged cache."""
+    """Single-token decode attention straight from the packed, paged cache.
+    Keys are in `tq`'s format; values in `v_tq`'s (default: the same codec).
+    A separate value codec may use another bit width (e.g. 4-bit keys, 2-bit
+    values) but must share the seed, i.e. the rotation."""
 
-    def __init__(self, tq: TurboQuant, num_query_heads: int, scale: float | None = None):
+    def __init__(self, tq: TurboQuant, num_query_heads: int, scale: float | None = None,
+                 v_tq: TurboQuant | None = None):
         self.tq = tq
+        self.v_tq = tq if v_tq is None else v_tq
+        if self.v_tq.seed != tq.seed or self.v_tq.head_dim != tq.head_dim:
+            raise ValueError("keys and values must share head_dim and seed")
         self.num_query_heads = num_query_heads
         self.scale = (1.0 / math.sqrt(tq.head_dim)) if scale is None else float(scale)
         self._ws = {}
@@ -163,7 +170,8 @@ class TQPagedAttention:
         if k_packed.dim() != 4 or k_packed.shape[1] != block_size:
             raise ValueError("k_packed must be [num_blocks, block_size, num_kv_heads, P]")
         nblk, _, hkv, P = k_packed.shape
-        if P != tq.packed_dim or tuple(v_packed.shape) != tuple(k_packed.shape):
+        if P != tq.packed_dim or \
+                tuple(v_packed.shape) != (nblk, block_size, hkv, self.v_tq.packed_dim):
             raise ValueError("k_packed / v_packed shape mismatch")
         if tuple(k_norms.shape) != (nblk, block_size, hkv) or \
                 tuple(v_norms.shape) != (nblk, block_size, hkv):
@@ -179,11 +187,12 @@ class TQPagedAttention:
         if out is None:
             out = torch.empty_like(query)
         ws = self.workspace(B, hkv, maxb, block_size, query.device)
-        _lib.check(_lib.tq_attn_decode(
+        _lib.check(_lib.tq_attn_decode_kv(
             query.data_ptr(), k_packed.data_ptr(), k_norms.data_ptr(), v_packed.data_ptr(),
             v_norms.data_ptr(), block_tables.data_ptr(), context_lens.data_ptr(), B, Hq, hkv,
-            tq.head_dim, tq.bits, tq.seed, block_size, maxb, nblk, self.scale, out.data_ptr(),
-            ws.data_ptr(), ws.numel(), _stream(query.device)), "tq_attn_decode")
+            tq.head_dim, tq.bits, self.v_tq.bits, tq.seed, block_size, maxb, nblk, self.scale,
+            out.data_ptr(), ws.data_ptr(), ws.numel(), _stream(query.device)),
+            "tq_attn_decode_kv")
         return out
 
     __call__ = forward

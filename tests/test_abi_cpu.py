@@ -147,11 +147,8 @@ def test_attention_argument_errors(L):
     assert call(d=64) == UNSUP
     assert call(bs=32) == UNSUP
     assert call(hq=30) == INVAL
-    assert call(hq=8 * 16) == UNSUP                 # 16 query heads per kv head
-    # 3 query heads per kv head: the 4-bit matrix-core kernel takes any group of
-    # up to 16 (the call then reaches the launch); the 2- and 3-bit kernel does not
-    assert call(hq=24, hkv=8, bits=2) == UNSUP
-    assert call(hq=24, hkv=8, bits=3) == UNSUP
+    assert call(hq=8 * 17) == UNSUP                 # 17 query heads per kv head
+    assert call(hq=8 * 17, bits=2) == UNSUP
     assert call(batch=-1) == INVAL
     assert call(scale=float("nan")) == INVAL
     assert call(batch=0) == OK
@@ -160,3 +157,24 @@ def test_attention_argument_errors(L):
     assert call(ws=None) == WS
     assert call(wsb=ws - 16) == WS
     assert call(out=A) == INVAL                     # output overlaps the query
+
+    # keys and values at different widths
+    kv = L.tq_attn_decode_kv
+
+    def call_kv(kb, vb, **kw):
+        args = dict(q=A, kp=B, kn=B + (1 << 24), vp=C, vn=C + (1 << 24), bt=A + (1 << 24),
+                    cl=A + (1 << 25), batch=16, hq=32, hkv=8, d=128, seed=0, bs=16,
+                    maxb=2048, nblk=32768, scale=0.088, out=A + (1 << 26), ws=0x40000000,
+                    wsb=ws)
+        args.update(kw)
+        return kv(args["q"], args["kp"], args["kn"], args["vp"], args["vn"], args["bt"],
+                  args["cl"], args["batch"], args["hq"], args["hkv"], args["d"], kb, vb,
+                  args["seed"], args["bs"], args["maxb"], args["nblk"], args["scale"],
+                  args["out"], args["ws"], args["wsb"], None)
+
+    assert call_kv(4, 5) == UNSUP
+    assert call_kv(1, 2) == UNSUP
+    assert call_kv(4, 2, d=64) == UNSUP
+    assert call_kv(4, 2, batch=0) == OK
+    assert call_kv(2, 4, q=None) == INVAL
+    assert call_kv(3, 4, wsb=ws - 16) == WS

@@ -47,13 +47,14 @@ def oracle_encode_parallel(x, bits, seed, workers=16):
 
 
 def run_attn(dev, what, bits=4, B=3, Hq=8, Hkv=2, T=37, ragged=True, seed=0, scale=None,
-             extra_blocks=2, sel=None, pad=None):
-    P.log("[attn] %s: B=%d Hq=%d Hkv=%d T=%d bits=%d ragged=%s" % (what, B, Hq, Hkv, T, bits,
-                                                                   ragged))
+             extra_blocks=2, sel=None, pad=None, v_bits=None):
+    vb = bits if v_bits is None else v_bits
+    P.log("[attn] %s: B=%d Hq=%d Hkv=%d T=%d bits=%d/%d ragged=%s" % (what, B, Hq, Hkv, T, bits,
+                                                                      vb, ragged))
     wl = W.attn_workload(batch=B, num_q_heads=Hq, num_kv_heads=Hkv, context=T, seed=700 + T,
                          perm_seed=701 + T, ragged=ragged, extra_blocks=extra_blocks)
     kp, kn = oracle_encode_parallel(wl["k"], bits, seed)
-    vp, vn = oracle_encode_parallel(wl["v"], bits, seed)
+    vp, vn = oracle_encode_parallel(wl["v"], vb, seed)
     bt = wl["block_tables"].copy()
     cl = wl["context_lens"].copy()
     if pad is not None:                      # entries past each context: invalid ids
@@ -62,7 +63,7 @@ def run_attn(dev, what, bits=4, B=3, Hq=8, Hkv=2, T=37, ragged=True, seed=0, sca
             bt[b, used:] = pad
     sc = 1.0 / math.sqrt(D) if scale is None else scale
     tq = TurboQuant(D, bits, seed, dev)
-    attn = TQPagedAttention(tq, Hq, scale=sc)
+    attn = TQPagedAttention(tq, Hq, scale=sc, v_tq=TurboQuant(D, vb, seed, dev))
     t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
     out = attn.forward(t(wl["q"]), t(kp), t(kn), t(vp), t(vn), t(bt), t(cl))
     torch.cuda.synchronize()
@@ -72,7 +73,7 @@ def run_attn(dev, what, bits=4, B=3, Hq=8, Hkv=2, T=37, ragged=True, seed=0, sca
         bt_o[bt_o < 0] = 0
         bt_o[bt_o >= kp.shape[0]] = 0
     _, ref = oracle.attn_decode(wl["q"], kp, kn, vp, vn, bt_o, cl, Hkv, bits, seed, sc,
-                                sel=sel, want_f64=True)
+                                sel=sel, want_f64=True, v_bits=vb)
     if sel is None:
         P.compare_attn(g, ref, what)
     else:
@@ -86,9 +87,21 @@ def test_small_ragged(dev, bits):
     run_attn(dev, "small b%d" % bits, bits=bits)
 
 
-@pytest.mark.parametrize("Hq,Hkv", [(4, 4), (8, 4), (32, 8), (16, 2), (64, 16), (8, 1), (16, 16), (24, 8)])
+@pytest.mark.parametrize("Hq,Hkv", [(4, 4), (8, 4), (32, 8), (16, 2), (64, 16), (8, 1), (16, 16),
+                                    (24, 8), (24, 2), (32, 2)])
 def test_gqa_shapes(dev, Hq, Hkv):
     run_attn(dev, "gqa %d/%d" % (Hq, Hkv), B=2, Hq=Hq, Hkv=Hkv, T=50)
+
+
+@pytest.mark.parametrize("kb,vb", [(4, 2), (2, 4), (4, 3), (3, 4), (3, 2), (2, 3)])
+def test_mixed_widths(dev, kb, vb):
+    run_attn(dev, "keys %d bits, values %d bits" % (kb, vb), bits=kb, v_bits=vb, B=3, Hq=16,
+             Hkv=4, T=300)
+
+
+@pytest.mark.parametrize("bits", [3, 2])
+def test_widths_gqa_16(dev, bits):
+    run_attn(dev, "b%d 16 heads per kv head" % bits, bits=bits, B=2, Hq=32, Hkv=2, T=77)
 
 
 @pytest.mark.parametrize("T", [1, 2, 15, 16, 17, 255, 256, 257, 1000, 1500])
@@ -120,16 +133,17 @@ def test_scale_and_peaked_softmax(dev):
     run_attn(dev, "scale 0.02", B=2, Hq=8, Hkv=2, T=300, scale=0.02)
 
 
-def _c5(dev, ragged, samples):
-    """Batch 16, 32/8 heads, 32768 tokens, 4 bits, in the launch configuration
-    the benchmark times.  The sampled (sequence, kv head) streams hold
-    oracle-encoded N(0,1)+outlier data; the rest of the cache is random codes."""
+def _c5(dev, ragged, samples, vb=4):
+    """Batch 16, 32/8 heads, 32768 tokens, 4-bit keys (values: vb bits), in the
+    launch configuration the benchmark times.  The sampled (sequence, kv head)
+    streams hold oracle-encoded N(0,1)+outlier data; the rest of the cache is
+    random codes."""
     B, Hq, Hkv, T, bs = 16, 32, 8, 32768, 16
     maxb = T // bs
     nblk = B * maxb
     rng = np.random.default_rng(502)
     kp = rng.integers(0, 256, (nblk, bs, Hkv, 64), dtype=np.uint8)
-    vp = rng.integers(0, 256, (nblk, bs, Hkv, 64), dtype=np.uint8)
+    vp = rng.integers(0, 256, (nblk, bs, Hkv, 16 * vb), dtype=np.uint8)
     kn = rng.uniform(8, 14, (nblk, bs, Hkv)).astype(np.float32)
     vn = rng.uniform(8, 14, (nblk, bs, Hkv)).astype(np.float32)
     q = W.attn_query(B, Hq)
@@ -139,23 +153,23 @@ def _c5(dev, ragged, samples):
     for b, g in samples:
         kv = W.attn_kv_rows(b, g, T)
         p_k, n_k = oracle_encode_parallel(kv[0], 4, 0)
-        p_v, n_v = oracle_encode_parallel(kv[1], 4, 0)
+        p_v, n_v = oracle_encode_parallel(kv[1], vb, 0)
         W.scatter_pages(kp, p_k, bt[b], g)
         W.scatter_pages(kn, n_k, bt[b], g)
         W.scatter_pages(vp, p_v, bt[b], g)
         W.scatter_pages(vn, n_v, bt[b], g)
         sel[b, g * 4:(g + 1) * 4] = True
-    P.log("[attn] C5-shaped full size ragged=%s samples=%s" % (ragged, samples))
+    P.log("[attn] C5-shaped full size ragged=%s values %d bits samples=%s" % (ragged, vb, samples))
     tq = TurboQuant(D, 4, 0, dev)
-    attn = TQPagedAttention(tq, Hq)
+    attn = TQPagedAttention(tq, Hq, v_tq=TurboQuant(D, vb, 0, dev))
     t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
     out = attn.forward(t(q), t(kp), t(kn), t(vp), t(vn), t(bt), t(cl))
     torch.cuda.synchronize()
     g = out.cpu().numpy()
     assert np.all(np.isfinite(g.astype(np.float64)))
     _, ref = oracle.attn_decode(q, kp, kn, vp, vn, bt, cl, Hkv, 4, 0, 1 / math.sqrt(D),
-                                sel=sel, want_f64=True)
-    P.compare_attn(g[sel], ref[sel], "full size ragged=%s" % ragged)
+                                sel=sel, want_f64=True, v_bits=vb)
+    P.compare_attn(g[sel], ref[sel], "full size ragged=%s values %d bits" % (ragged, vb))
 
 
 def test_full_size_batch16_32k(dev):
@@ -164,3 +178,7 @@ def test_full_size_batch16_32k(dev):
 
 def test_full_size_batch16_ragged(dev):
     _c5(dev, True, [(0, 3), (2, 7), (9, 1)])
+
+
+def test_full_size_batch16_k4_v2(dev):
+    _c5(dev, True, [(5, 2), (14, 6)], vb=2)
