@@ -8,6 +8,7 @@ of head_dim 128, fp16, 4 GiB; N(0,1) with 1% x15 outlier channels per
 tq_decode of it (one launch).  Inputs are resident in HBM before timing.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1]
+    python bench.py --attn-only [--steps K]     (attention side measurement only)
 
 Prints one JSON line.  `value` is fp16 key/value bytes passed through the
 codec per second (encode and decode both count their 256 B/vector of fp16).
@@ -126,11 +127,23 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the attention and streaming-encode side measurements")
+    ap.add_argument("--attn-only", action="store_true",
+                    help="only the batch-16 x 32K decode-attention measurement (for profiling)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: the codec is data-parallel over vectors and "
               "this build runs on a single MI355X (use --gpus 1)", file=sys.stderr)
         return 2
+    if args.attn_only:
+        import torch
+        from kv_cache_vector_amd import _lib
+        _lib.load()
+        dev = torch.device("cuda:0")
+        torch.cuda.set_device(dev)
+        res = attention_measurement(torch, dev, torch.cuda.current_stream(dev),
+                                    reps=max(1, args.steps))
+        print(json.dumps(res), flush=True)
+        return 0
 
     import numpy as np
     import torch
@@ -253,11 +266,19 @@ def side_measurements(torch, dev, stream, x, packed, norms):
     codes), and a 2-bit encode launch the size of one 70B-class 128K-context
     layer (2,097,152 vectors; timed on the first vectors of the resident
     cache, the launch shape of the layer-by-layer streaming encode)."""
+    res = attention_measurement(torch, dev, stream)
+    res.update(stream_encode_measurement(torch, dev, stream, x, packed, norms))
+    return res
+
+
+def attention_measurement(torch, dev, stream, reps: int = 10):
+    """Median time of tq_attn_decode (split + combine kernels) at batch 16,
+    32/8 heads, 32768 tokens, 4 bits, random codes and a random block
+    permutation, with the last-level cache evicted before each call."""
     from kv_cache_vector_amd import _lib
     import math
     s = stream.cuda_stream
     res = {}
-    # --- attention
     B, Hq, Hkv, T, bs = 16, 32, 8, 32768, 16
     maxb = T // bs
     nblk = B * maxb
@@ -285,7 +306,7 @@ def side_measurements(torch, dev, stream, x, packed, norms):
 
     attn()
     times = []
-    for _ in range(10):
+    for _ in range(reps):
         flush.sum()        # evict the 256 MB last-level cache between repetitions
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
@@ -299,8 +320,15 @@ def side_measurements(torch, dev, stream, x, packed, norms):
     res["attn_packed_GBps"] = round(packed_bytes / (t_us * 1e-6) / 1e9, 1)
     res["attn_fp16_equiv_GBps"] = round(B * Hkv * T * 2 * 256 / (t_us * 1e-6) / 1e9, 1)
     res["attn_hbm_frac"] = round(packed_bytes / (t_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)
-    del kp, vp, kn, vn
-    # --- streaming 2-bit encode of one 70B-class 128K layer
+    return res
+
+
+def stream_encode_measurement(torch, dev, stream, x, packed, norms):
+    """2-bit encode of one 70B-class 128K layer, cache evicted before each."""
+    from kv_cache_vector_amd import _lib
+    s = stream.cuda_stream
+    res = {}
+    flush = torch.ones(512 * 1024 * 1024 // 4, dtype=torch.float32, device=dev)
     n = 2 * 8 * 131072
     xl = x[:n]
     pk2 = packed[: n // 2].view(-1)[: n * 32].view(n, 32)
