@@ -16,8 +16,9 @@
 // row is used as plain codebook values, and one inverse transform finishes.
 //
 // Two kernels, flash-decoding style:
-//   split   grid (context split, sequence, kv-head chunk of 4), one wave per
-//           kv head.  Per 16-token page the scores and the value accumulation
+//   split   8 waves per workgroup, one per (kv head, context split) of a
+//           sequence: a workgroup takes 8 kv heads of one split, or, for
+//           caches with fewer kv heads, all of them for 8 / Hkv splits.  Per 16-token page the scores and the value accumulation
 //           run as 16x16x32 f16 MFMA tiles:
 //             scores  S^T[16 tokens][16 heads] = C_k[16 tokens][K] Q[K][16 heads]
 //             values  O[16 heads][16 dims]    += W[16 heads][K] C_v[K][16 dims]
@@ -59,7 +60,7 @@ namespace {
 constexpr int kPartial = 2 + kHeadDim;      // m, l, acc[128] per workspace entry
 constexpr float kLazy = 8.0f;               // rescale when a score passes m + 8 (base 2)
 constexpr int kMaxSplitTokens = 4096;       // block-table entries of a split staged in LDS
-constexpr int kMWaves = 4;                  // kv heads (waves) per workgroup
+constexpr int kMWaves = 8;                  // waves per workgroup
 constexpr int kMThreads = 64 * kMWaves;
 constexpr int kMPrefetch = 1;               // extra ring slots: pages of loads in flight ahead of use
 constexpr int kMTargetWaves = 4096;         // split-kernel waves aimed for
@@ -85,6 +86,7 @@ struct AttnParams {
     float *ws;
     uint16_t *out;
     int batch, hq, hkv, max_blocks, split_tokens, num_splits;
+    int spw;             // splits per workgroup of the split kernel
     int64_t num_blocks;
     float qscale;        // scale * log2(e) / 128
     CodecConsts k;       // key codebook and the sign mask (shared by keys and values)
@@ -267,31 +269,42 @@ __global__ __launch_bounds__(kMThreads) void attn_split_kernel(AttnParams p) {
     using SK = Side<KB>;
     using SV = Side<VB>;
     __shared__ __attribute__((aligned(16))) char tab[256 * kLutRow];
-    __shared__ int32_t bt_lds[kMaxSplitTokens / kAttnBlockSize];
+    __shared__ int32_t bt_all[kMWaves][kMaxSplitTokens / kAttnBlockSize];
 
+    // The workgroup's waves form p.spw slots of kMWaves / p.spw kv heads;
+    // slot s works on split blockIdx.x * p.spw + s (several splits per
+    // workgroup when the cache has fewer kv heads than waves).
     const int b = blockIdx.y;
-    const int split = blockIdx.x;
     int T = p.context_lens[b];
     T = T < 0 ? 0 : T;
     const int tmax = p.max_blocks * kAttnBlockSize;
     T = T > tmax ? tmax : T;
     if (p.num_blocks <= 0) T = 0;
-    const int t0 = split * p.split_tokens;
-    if (t0 >= T) return;                 // nothing here; combine skips this split
-    const int t1 = (t0 + p.split_tokens < T) ? t0 + p.split_tokens : T;
-    const int npages = (t1 - t0 + kAttnBlockSize - 1) / kAttnBlockSize;
+    const int hps = kMWaves / p.spw;                          // kv heads per slot
+    const int first = blockIdx.x * p.spw;
+    if (first * p.split_tokens >= T) return;                 // the whole workgroup is past the context
 
     fill_side<KB>(tab, p.k, 0);
     fill_side<VB>(tab, p.v, kLutRow / 2);
-    {
-        const int32_t *bt = p.block_tables + (size_t)b * p.max_blocks + t0 / kAttnBlockSize;
-        for (int i = threadIdx.x; i < npages; i += kMThreads) bt_lds[i] = bt[i];
+    for (int sl = 0; sl < p.spw; ++sl) {                      // block-table entries of every slot
+        const int u0 = (first + sl) * p.split_tokens;
+        if (u0 >= T) break;
+        const int u1 = (u0 + p.split_tokens < T) ? u0 + p.split_tokens : T;
+        const int np = (u1 - u0 + kAttnBlockSize - 1) / kAttnBlockSize;
+        const int32_t *bt = p.block_tables + (size_t)b * p.max_blocks + u0 / kAttnBlockSize;
+        for (int i = threadIdx.x; i < np; i += kMThreads) bt_all[sl][i] = bt[i];
     }
     __syncthreads();
 
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int g = blockIdx.z * kMWaves + wave;                // kv head
-    if (g >= p.hkv) return;                                   // no barrier follows
+    const int slot = wave / hps;
+    const int g = blockIdx.z * hps + wave % hps;              // kv head
+    const int split = first + slot;
+    const int t0 = split * p.split_tokens;
+    if (g >= p.hkv || t0 >= T) return;                        // no barrier follows
+    const int t1 = (t0 + p.split_tokens < T) ? t0 + p.split_tokens : T;
+    const int npages = (t1 - t0 + kAttnBlockSize - 1) / kAttnBlockSize;
+    const int32_t *bt_lds = bt_all[slot];
     const int lane = threadIdx.x & 63;
     const int m = lane & 15, r = lane >> 4;
     const int grp = p.hq / p.hkv;
@@ -677,7 +690,10 @@ hipError_t launch_attn(const AttnShape &s, const CodecConsts &kc, const CodecCon
     p.qscale = scale * 1.4426950408889634f / kHeadDim;
     p.k = kc;
     p.v = vc;
-    const dim3 grid(p.num_splits, s.batch, (s.num_kv_heads + kMWaves - 1) / kMWaves);
+    // fewer kv heads than waves: the spare waves take further splits
+    p.spw = (s.num_kv_heads < kMWaves && kMWaves % s.num_kv_heads == 0) ? kMWaves / s.num_kv_heads : 1;
+    const int hps = kMWaves / p.spw;
+    const dim3 grid((p.num_splits + p.spw - 1) / p.spw, s.batch, (s.num_kv_heads + hps - 1) / hps);
     const dim3 block(kMThreads);
 #define TQ_SPLIT(KB, VB) hipLaunchKernelGGL((attn_split_kernel<KB, VB>), grid, block, 0, stream, p)
     switch (s.k_bits * 10 + s.v_bits) {
