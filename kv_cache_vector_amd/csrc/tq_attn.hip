@@ -587,7 +587,8 @@ __global__ __launch_bounds__(64) void attn_combine_kernel(AttnParams p) {
         const float other = __shfl_xor(mx, o);
         mx = other > mx ? other : mx;
     }
-    // split weights, then this lane's coordinates 2*lane, 2*lane+1
+    // split weights, then this lane's coordinates 2*lane, 2*lane+1; the
+    // partials of 8 splits are loaded before any of them is accumulated
     float lsum = 0.0f, a0 = 0.0f, a1 = 0.0f;
     for (int s0 = 0; s0 < ns; s0 += 64) {
         const int s = s0 + lane;
@@ -598,14 +599,21 @@ __global__ __launch_bounds__(64) void attn_combine_kernel(AttnParams p) {
             lsum += w * ls;
         }
         const int cnt = (ns - s0 < 64) ? ns - s0 : 64;
-#pragma unroll 8
-        for (int j = 0; j < cnt; ++j) {
-            const float wj = __builtin_bit_cast(
-                float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), j));
-            const float2 e =
-                *reinterpret_cast<const float2 *>(src + (size_t)(s0 + j) * kPartial + 2 + 2 * lane);
-            a0 = __builtin_fmaf(wj, e.x, a0);
-            a1 = __builtin_fmaf(wj, e.y, a1);
+        for (int j0 = 0; j0 < cnt; j0 += 8) {
+            float2 e[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int j = (j0 + u < cnt) ? j0 + u : j0;          // in range; weight 0 below
+                e[u] = *reinterpret_cast<const float2 *>(src + (size_t)(s0 + j) * kPartial + 2 + 2 * lane);
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                float wj = __builtin_bit_cast(
+                    float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), (j0 + u) & 63));
+                wj = (j0 + u < cnt) ? wj : 0.0f;
+                a0 = __builtin_fmaf(wj, e[u].x, a0);
+                a1 = __builtin_fmaf(wj, e[u].y, a1);
+            }
         }
     }
 #pragma unroll
