@@ -18,7 +18,7 @@ namespace {
 
 using tq::CodecConsts;
 
-constexpr int kD = tq::kHeadDim;
+constexpr int kAttnD = tq::kHeadDim;
 
 // ---------------------------------------------------------------------------
 // Lloyd-Max quantizer of the standard normal (aither-kvcache PyPI page,
@@ -90,11 +90,11 @@ const Codebook &codebook(int bits) {
 }
 
 // SplitMix64 (Steele, Lea, Flood, OOPSLA 2014): sigma_i = -1 iff the top bit of
-// the i-th output is set.
-void sign_mask(uint64_t seed, uint32_t mask[4]) {
+// the i-th output is set (i < d; d / 32 mask words).
+void sign_mask(uint64_t seed, int d, uint32_t *mask) {
     uint64_t state = seed;
-    for (int w = 0; w < 4; ++w) mask[w] = 0;
-    for (int i = 0; i < kD; ++i) {
+    for (int w = 0; w < d / 32; ++w) mask[w] = 0;
+    for (int i = 0; i < d; ++i) {
         state += 0x9e3779b97f4a7c15ULL;
         uint64_t z = state;
         z = (z ^ (z >> 30)) * 0xbf58476d1ce4e5b9ULL;
@@ -104,9 +104,9 @@ void sign_mask(uint64_t seed, uint32_t mask[4]) {
     }
 }
 
-CodecConsts make_consts(int bits, uint64_t seed) {
+CodecConsts make_consts(int head_dim, int bits, uint64_t seed) {
     CodecConsts k{};
-    sign_mask(seed, k.sign);
+    sign_mask(seed, head_dim, k.sign);
     const Codebook &cb = codebook(bits);
     const int L = 1 << bits;
     for (int i = 0; i < L; ++i) k.level[i] = cb.level[i];
@@ -163,9 +163,12 @@ bool overlap(const void *a, size_t na, const void *b, size_t nb) {
     return na && nb && x < y + nb && y < x + na;
 }
 
+bool codec_head_dim(int d) { return d == 64 || d == 128 || d == 256; }
+
+// The codec takes head_dim 64, 128 or 256; the attention kernels 128.
 tq_status check_shape(int head_dim, int bits) {
     if (head_dim <= 0 || bits <= 0) return TQ_ERR_INVALID_ARG;
-    if (head_dim != kD || bits < 2 || bits > 4) return TQ_ERR_UNSUPPORTED;
+    if (!codec_head_dim(head_dim) || bits < 2 || bits > 4) return TQ_ERR_UNSUPPORTED;
     return TQ_OK;
 }
 
@@ -206,8 +209,8 @@ tq_status tq_codebook(int bits, float *levels, float *thresholds) {
 
 tq_status tq_signs(uint64_t seed, int head_dim, uint32_t *mask) {
     if (!mask || head_dim <= 0) return TQ_ERR_INVALID_ARG;
-    if (head_dim != kD) return TQ_ERR_UNSUPPORTED;
-    sign_mask(seed, mask);
+    if (!codec_head_dim(head_dim)) return TQ_ERR_UNSUPPORTED;
+    sign_mask(seed, head_dim, mask);
     return TQ_OK;
 }
 
@@ -221,13 +224,13 @@ tq_status tq_encode(const void *x_f16, int64_t n, int head_dim, int bits, uint64
     if (!aligned(x_f16, 16) || !aligned(packed, 16) || !aligned(norms, 4))
         return TQ_ERR_MISALIGNED;
     const size_t P = tq_packed_bytes(head_dim, bits);
-    const size_t nx = (size_t)n * kD * 2, np = (size_t)n * P, nn = (size_t)n * 4;
+    const size_t nx = (size_t)n * head_dim * 2, np = (size_t)n * P, nn = (size_t)n * 4;
     if (overlap(x_f16, nx, packed, np) || overlap(x_f16, nx, norms, nn) ||
         overlap(packed, np, norms, nn))
         return TQ_ERR_INVALID_ARG;
-    const CodecConsts k = make_consts(bits, seed);
-    return from_hip(tq::launch_encode(bits, x_f16, n, nullptr, 0, k, enc_table(bits), packed,
-                                      norms, (hipStream_t)stream));
+    const CodecConsts k = make_consts(head_dim, bits, seed);
+    return from_hip(tq::launch_encode(head_dim, bits, x_f16, n, nullptr, 0, k, enc_table(bits),
+                                      packed, norms, (hipStream_t)stream));
 }
 
 tq_status tq_encode_paged(const void *x_f16, const int64_t *slots, int64_t n, int head_dim,
@@ -242,15 +245,16 @@ tq_status tq_encode_paged(const void *x_f16, const int64_t *slots, int64_t n, in
         !aligned(slots, 8))
         return TQ_ERR_MISALIGNED;
     const size_t P = tq_packed_bytes(head_dim, bits);
-    const size_t nx = (size_t)n * kD * 2, ns = (size_t)n * 8;
+    const size_t nx = (size_t)n * head_dim * 2, ns = (size_t)n * 8;
     const size_t np = (size_t)num_slots * P, nn = (size_t)num_slots * 4;
     if (overlap(x_f16, nx, cache_packed, np) || overlap(x_f16, nx, cache_norms, nn) ||
         overlap(slots, ns, cache_packed, np) || overlap(slots, ns, cache_norms, nn) ||
         overlap(cache_packed, np, cache_norms, nn))
         return TQ_ERR_INVALID_ARG;
-    const CodecConsts k = make_consts(bits, seed);
-    return from_hip(tq::launch_encode(bits, x_f16, n, slots, num_slots, k, enc_table(bits),
-                                      cache_packed, cache_norms, (hipStream_t)stream));
+    const CodecConsts k = make_consts(head_dim, bits, seed);
+    return from_hip(tq::launch_encode(head_dim, bits, x_f16, n, slots, num_slots, k,
+                                      enc_table(bits), cache_packed, cache_norms,
+                                      (hipStream_t)stream));
 }
 
 tq_status tq_decode(const uint8_t *packed, const float *norms, int64_t n, int head_dim,
@@ -263,16 +267,17 @@ tq_status tq_decode(const uint8_t *packed, const float *norms, int64_t n, int he
     if (!aligned(out_f16, 16) || !aligned(packed, 16) || !aligned(norms, 4))
         return TQ_ERR_MISALIGNED;
     const size_t P = tq_packed_bytes(head_dim, bits);
-    const size_t no = (size_t)n * kD * 2, np = (size_t)n * P, nn = (size_t)n * 4;
+    const size_t no = (size_t)n * head_dim * 2, np = (size_t)n * P, nn = (size_t)n * 4;
     if (overlap(out_f16, no, packed, np) || overlap(out_f16, no, norms, nn))
         return TQ_ERR_INVALID_ARG;
-    const CodecConsts k = make_consts(bits, seed);
-    return from_hip(tq::launch_decode(bits, packed, norms, n, k, out_f16, (hipStream_t)stream));
+    const CodecConsts k = make_consts(head_dim, bits, seed);
+    return from_hip(tq::launch_decode(head_dim, bits, packed, norms, n, k, out_f16,
+                                      (hipStream_t)stream));
 }
 
 size_t tq_attn_workspace_bytes(int batch, int num_q_heads, int num_kv_heads, int head_dim,
                                int block_size, int max_blocks_per_seq) {
-    if (batch < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim != kD ||
+    if (batch < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim != kAttnD ||
         block_size != tq::kAttnBlockSize || max_blocks_per_seq < 0 ||
         num_q_heads % num_kv_heads)
         return 0;
@@ -291,6 +296,7 @@ tq_status tq_attn_decode_kv(const void *q_f16, const uint8_t *k_packed, const fl
     if (st != TQ_OK) return st;
     st = check_shape(head_dim, v_bits);
     if (st != TQ_OK) return st;
+    if (head_dim != kAttnD) return TQ_ERR_UNSUPPORTED;
     if (batch < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_blocks_per_seq < 0 ||
         num_blocks < 0 || !std::isfinite(scale))
         return TQ_ERR_INVALID_ARG;
@@ -311,11 +317,11 @@ tq_status tq_attn_decode_kv(const void *q_f16, const uint8_t *k_packed, const fl
     if (!tq::attn_supported(s)) return TQ_ERR_UNSUPPORTED;
     const size_t need = tq::attn_workspace_bytes(s);
     if (need > 0 && (!workspace || workspace_bytes < need)) return TQ_ERR_WORKSPACE;
-    const size_t nout = (size_t)batch * num_q_heads * kD * 2;
+    const size_t nout = (size_t)batch * num_q_heads * kAttnD * 2;
     if (overlap(out_f16, nout, q_f16, nout) || overlap(out_f16, nout, workspace, need))
         return TQ_ERR_INVALID_ARG;
-    const CodecConsts kc = make_consts(k_bits, seed);
-    const CodecConsts vc = make_consts(v_bits, seed);
+    const CodecConsts kc = make_consts(kAttnD, k_bits, seed);
+    const CodecConsts vc = make_consts(kAttnD, v_bits, seed);
     return from_hip(tq::launch_attn(s, kc, vc, q_f16, k_packed, k_norms, v_packed, v_norms,
                                     block_tables, context_lens, scale, out_f16, workspace,
                                     (hipStream_t)stream));

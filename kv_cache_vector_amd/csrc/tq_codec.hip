@@ -6,14 +6,15 @@
 // seeded sign flip followed by a Walsh-Hadamard transform (qbc.network blog,
 // "What TurboQuant is": a multiplier-free Walsh-Hadamard rotation).
 //
-// Work mapping.  Four lanes (a DPP quad) own one 128-dim vector.  Lane q of
-// the quad owns coordinates 32k + 8q + j (k = 0..3, j = 0..7), held in
-// register r = 8k + j.  Each fp16 access instruction therefore moves 64
-// contiguous bytes per quad (16 B per lane), and a wave of 16 quads touches
-// 16 whole 64-byte segments.  Coordinate bits 0-2 and 5-6 are register bits,
-// bits 3-4 are the lane's place in the quad: the 128-point fast
-// Walsh-Hadamard transform is 5 register butterfly stages plus 2 cross-lane
-// stages done with DPP quad permutations -- no LDS traffic for the transform.
+// Work mapping.  Four lanes (a DPP quad) own one vector of D = 64, 128 or
+// 256 coordinates; K = D / 32.  Lane q of the quad owns coordinates
+// 32k + 8q + j (k < K, j < 8), held in register r = 8k + j.  Each fp16 access
+// instruction therefore moves 64 contiguous bytes per quad (16 B per lane),
+// and a wave of 16 quads touches 16 whole 64-byte segments.  Coordinate bits
+// 0-2 and 5 up are register bits, bits 3-4 are the lane's place in the quad:
+// the D-point fast Walsh-Hadamard transform is log2(D) - 2 register butterfly
+// stages plus 2 cross-lane stages done with DPP quad permutations -- no LDS
+// traffic for the transform.
 //
 // The codes of one lane and group k are 8 consecutive codes, i.e. a
 // contiguous 8*bits-bit field of the packed row.  At 4 bits each field is a
@@ -27,7 +28,7 @@
 // the last register stage anyway.
 //
 // Quantizer.  y = 8 z is formed as w * (8 eps / ||x||).  The integer part of
-// y indexes a 193-entry LDS table whose cells are narrower than the smallest
+// y indexes a 257-entry LDS table whose cells are narrower than the smallest
 // gap between two thresholds, so each cell holds at most one threshold:
 // code = base[cell] + (y > thr[cell]).  A coordinate exactly on a threshold
 // takes the lower code, as in the definition.
@@ -39,7 +40,7 @@
 namespace tq {
 namespace {
 
-constexpr int kCells = kEncCells;     // quantizer cells cover y in (-97, 97)
+constexpr int kCells = kEncCells;     // quantizer cells cover y in (-129, 129)
 constexpr int kThreads = 256;         // 4 waves, 64 vectors per block iteration
 constexpr int kVecPerBlock = kThreads / 4;
 constexpr int kDecVpq = 4;            // decode: vectors per quad
@@ -64,50 +65,63 @@ __device__ __forceinline__ float quad_move(float v) {
 
 // The two cross-lane butterfly stages (coordinate bits 3 and 4):
 //   f[r] += f[r] of lane q^1 * ma,  then  f[r] += f[r] of lane q^2 * mb.
-// One v_fmac_f32 with a DPP source per value.  The leading s_nop 1 provides
-// the two wait states a DPP read of a VGPR needs after a VALU write; inside
-// the block no instruction reads a register written by the one before it.
-__device__ __forceinline__ void fwht_quad(float (&f)[32], float ma, float mb) {
-#define TQ_STAGE(CTRL, M)                                                                        \
-    asm volatile(                                                                                \
-        "s_nop 1\n\t"                                                                            \
-        "v_fmac_f32_dpp %0, %0, %32 " CTRL "\n\tv_fmac_f32_dpp %1, %1, %32 " CTRL "\n\t"         \
-        "v_fmac_f32_dpp %2, %2, %32 " CTRL "\n\tv_fmac_f32_dpp %3, %3, %32 " CTRL "\n\t"         \
-        "v_fmac_f32_dpp %4, %4, %32 " CTRL "\n\tv_fmac_f32_dpp %5, %5, %32 " CTRL "\n\t"         \
-        "v_fmac_f32_dpp %6, %6, %32 " CTRL "\n\tv_fmac_f32_dpp %7, %7, %32 " CTRL "\n\t"         \
-        "v_fmac_f32_dpp %8, %8, %32 " CTRL "\n\tv_fmac_f32_dpp %9, %9, %32 " CTRL "\n\t"         \
-        "v_fmac_f32_dpp %10, %10, %32 " CTRL "\n\tv_fmac_f32_dpp %11, %11, %32 " CTRL "\n\t"     \
-        "v_fmac_f32_dpp %12, %12, %32 " CTRL "\n\tv_fmac_f32_dpp %13, %13, %32 " CTRL "\n\t"     \
-        "v_fmac_f32_dpp %14, %14, %32 " CTRL "\n\tv_fmac_f32_dpp %15, %15, %32 " CTRL "\n\t"     \
-        "v_fmac_f32_dpp %16, %16, %32 " CTRL "\n\tv_fmac_f32_dpp %17, %17, %32 " CTRL "\n\t"     \
-        "v_fmac_f32_dpp %18, %18, %32 " CTRL "\n\tv_fmac_f32_dpp %19, %19, %32 " CTRL "\n\t"     \
-        "v_fmac_f32_dpp %20, %20, %32 " CTRL "\n\tv_fmac_f32_dpp %21, %21, %32 " CTRL "\n\t"     \
-        "v_fmac_f32_dpp %22, %22, %32 " CTRL "\n\tv_fmac_f32_dpp %23, %23, %32 " CTRL "\n\t"     \
-        "v_fmac_f32_dpp %24, %24, %32 " CTRL "\n\tv_fmac_f32_dpp %25, %25, %32 " CTRL "\n\t"     \
-        "v_fmac_f32_dpp %26, %26, %32 " CTRL "\n\tv_fmac_f32_dpp %27, %27, %32 " CTRL "\n\t"     \
-        "v_fmac_f32_dpp %28, %28, %32 " CTRL "\n\tv_fmac_f32_dpp %29, %29, %32 " CTRL "\n\t"     \
-        "v_fmac_f32_dpp %30, %30, %32 " CTRL "\n\tv_fmac_f32_dpp %31, %31, %32 " CTRL            \
-        : "+v"(f[0]), "+v"(f[1]), "+v"(f[2]), "+v"(f[3]), "+v"(f[4]), "+v"(f[5]), "+v"(f[6]),   \
-          "+v"(f[7]), "+v"(f[8]), "+v"(f[9]), "+v"(f[10]), "+v"(f[11]), "+v"(f[12]),            \
-          "+v"(f[13]), "+v"(f[14]), "+v"(f[15]), "+v"(f[16]), "+v"(f[17]), "+v"(f[18]),         \
-          "+v"(f[19]), "+v"(f[20]), "+v"(f[21]), "+v"(f[22]), "+v"(f[23]), "+v"(f[24]),         \
-          "+v"(f[25]), "+v"(f[26]), "+v"(f[27]), "+v"(f[28]), "+v"(f[29]), "+v"(f[30]),         \
-          "+v"(f[31])                                                                            \
-        : "v"(M))
-    TQ_STAGE("quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf", ma);
-    TQ_STAGE("quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf", mb);
-#undef TQ_STAGE
-}
+// One v_fmac_f32 with a DPP source per value, 16 or 32 values per asm block.
+// The leading s_nop 1 provides the two wait states a DPP read of a VGPR needs
+// after a VALU write; inside a block no instruction reads a register written
+// by the one before it.
+#define TQ_FMAC2(A, B, CTRL, M)                                                                  \
+    "v_fmac_f32_dpp %" #A ", %" #A ", %" #M " " CTRL "\n\t"                                     \
+    "v_fmac_f32_dpp %" #B ", %" #B ", %" #M " " CTRL "\n\t"
+#define TQ_FMAC16(CTRL, M)                                                                       \
+    TQ_FMAC2(0, 1, CTRL, M) TQ_FMAC2(2, 3, CTRL, M) TQ_FMAC2(4, 5, CTRL, M)                     \
+    TQ_FMAC2(6, 7, CTRL, M) TQ_FMAC2(8, 9, CTRL, M) TQ_FMAC2(10, 11, CTRL, M)                   \
+    TQ_FMAC2(12, 13, CTRL, M) TQ_FMAC2(14, 15, CTRL, M)
+#define TQ_FMAC32(CTRL, M)                                                                       \
+    TQ_FMAC16(CTRL, M) TQ_FMAC2(16, 17, CTRL, M) TQ_FMAC2(18, 19, CTRL, M)                      \
+    TQ_FMAC2(20, 21, CTRL, M) TQ_FMAC2(22, 23, CTRL, M) TQ_FMAC2(24, 25, CTRL, M)               \
+    TQ_FMAC2(26, 27, CTRL, M) TQ_FMAC2(28, 29, CTRL, M) TQ_FMAC2(30, 31, CTRL, M)
+#define TQ_OPS16(O)                                                                              \
+    "+v"(f[O + 0]), "+v"(f[O + 1]), "+v"(f[O + 2]), "+v"(f[O + 3]), "+v"(f[O + 4]),            \
+        "+v"(f[O + 5]), "+v"(f[O + 6]), "+v"(f[O + 7]), "+v"(f[O + 8]), "+v"(f[O + 9]),        \
+        "+v"(f[O + 10]), "+v"(f[O + 11]), "+v"(f[O + 12]), "+v"(f[O + 13]), "+v"(f[O + 14]),   \
+        "+v"(f[O + 15])
+#define TQ_XOR1 "quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf"
+#define TQ_XOR2 "quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf"
 
-// Register butterfly stages with strides FIRST..8 (register bits), then the
-// stride-16 stage fused with the per-vector scale s:
+template <int R>
+__device__ __forceinline__ void fwht_quad(float (&f)[R], float ma, float mb) {
+    static_assert(R == 16 || R % 32 == 0, "16, 32 or 64 registers");
+    if constexpr (R == 16) {
+        asm volatile("s_nop 1\n\t" TQ_FMAC16(TQ_XOR1, 16) : TQ_OPS16(0) : "v"(ma));
+        asm volatile("s_nop 1\n\t" TQ_FMAC16(TQ_XOR2, 16) : TQ_OPS16(0) : "v"(mb));
+    } else {
+#pragma unroll
+        for (int c = 0; c < R; c += 32)
+            asm volatile("s_nop 1\n\t" TQ_FMAC32(TQ_XOR1, 32)
+                         : TQ_OPS16(c), TQ_OPS16(c + 16) : "v"(ma));
+#pragma unroll
+        for (int c = 0; c < R; c += 32)
+            asm volatile("s_nop 1\n\t" TQ_FMAC32(TQ_XOR2, 32)
+                         : TQ_OPS16(c), TQ_OPS16(c + 16) : "v"(mb));
+    }
+}
+#undef TQ_XOR2
+#undef TQ_XOR1
+#undef TQ_OPS16
+#undef TQ_FMAC32
+#undef TQ_FMAC16
+#undef TQ_FMAC2
+
+// Register butterfly stages with strides FIRST..R/4 (register bits), then the
+// stride-R/2 stage fused with the per-vector scale s:
 //   (a, b) -> ((a + b) s, (a - b) s) = (fma(a, s, b s), fma(a, s, -b s)).
-template <int FIRST>
-__device__ __forceinline__ void fwht_registers_scaled(float (&f)[32], float s) {
+template <int FIRST, int R>
+__device__ __forceinline__ void fwht_registers_scaled(float (&f)[R], float s) {
+    constexpr int H = R / 2;
 #pragma unroll
-    for (int st = FIRST; st < 16; st <<= 1) {
+    for (int st = FIRST; st < H; st <<= 1) {
 #pragma unroll
-        for (int r = 0; r < 32; ++r) {
+        for (int r = 0; r < R; ++r) {
             if (r & st) continue;
             const float a = f[r], b = f[r + st];
             f[r] = a + b;
@@ -115,10 +129,10 @@ __device__ __forceinline__ void fwht_registers_scaled(float (&f)[32], float s) {
         }
     }
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-        const float a = f[r], bs = f[r + 16] * s;
+    for (int r = 0; r < H; ++r) {
+        const float a = f[r], bs = f[r + H] * s;
         f[r] = __builtin_fmaf(a, s, bs);
-        f[r + 16] = __builtin_fmaf(a, s, -bs);
+        f[r + H] = __builtin_fmaf(a, s, -bs);
     }
 }
 
@@ -130,19 +144,22 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t span_rsrc(const void *base, ui
 }
 
 // XOR masks flipping the binary16 sign bits of register pair (2i, 2i+1) of
-// lane q, i.e. of coordinates 32(i/4) + 8q + 2(i%4) + {0, 1}.  Thread t < 64
-// writes mask i = t % 16 of lane q = t / 16 to LDS once per block; every lane
-// then reads its 16 masks with four broadcast 16-byte LDS reads.
+// lane q, i.e. of coordinates 32(i/4) + 8q + 2(i%4) + {0, 1}.  Thread
+// t < 16K writes mask i = t % 4K of lane q = t / 4K to LDS once per block;
+// every lane then reads its 4K masks with K broadcast 16-byte LDS reads.
+template <int K>
 __device__ __forceinline__ void store_sign_mask(const CodecConsts &k, int t, uint32_t *smask) {
-    const int q = t >> 4, i = t & 15;
+    const int q = t / (4 * K), i = t % (4 * K);
     const uint32_t w = k.sign[i >> 2] >> (8 * q + 2 * (i & 3));
     smask[t] = ((w & 1u) << 15) | (((w >> 1) & 1u) << 31);
 }
 
-__device__ __forceinline__ void load_sign_masks(const u32x4 *smask, int q, uint32_t (&xm)[16]) {
+template <int K>
+__device__ __forceinline__ void load_sign_masks(const u32x4 *smask, int q,
+                                                uint32_t (&xm)[4 * K]) {
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-        const u32x4 u = smask[4 * q + m];
+    for (int m = 0; m < K; ++m) {
+        const u32x4 u = smask[K * q + m];
         xm[4 * m] = u.x;
         xm[4 * m + 1] = u.y;
         xm[4 * m + 2] = u.z;
@@ -185,36 +202,56 @@ __device__ __forceinline__ void put_code4(uint32_t &acc, float y, float thr, uin
 #undef TQ_PUT_CODE
 #undef TQ_PUT_FIRST
 
-template <int R>
-__device__ __forceinline__ void quantize4(const float (&f)[32], const float2 *qtab,
-                                          uint32_t (&lo)[4], uint32_t (&hi)[4]) {
-    if constexpr (R < 32) {
+template <int R, int N>
+__device__ __forceinline__ void quantize4(const float (&f)[N], const float2 *qtab,
+                                          uint32_t (&lo)[N / 8], uint32_t (&hi)[N / 8]) {
+    if constexpr (R < N) {
         const float y = f[R];
         const float2 e = qtab[(int)y + kCells];
         const uint32_t W = __builtin_bit_cast(uint32_t, e.y);
         if (R & 1) put_code4<R>(hi[R >> 3], y, e.x, W);
         else put_code4<R>(lo[R >> 3], y, e.x, W);
-        quantize4<R + 1>(f, qtab, lo, hi);
+        quantize4<R + 1, N>(f, qtab, lo, hi);
     }
 }
 
-template <int BITS, bool PAGED>
+// Bits [24 g, 24 g + 24) of the lane's 3-bit field stream.
+template <int G, int NPK>
+__device__ __forceinline__ uint32_t field24(const uint32_t (&pk)[NPK]) {
+    constexpr int w = (24 * G) >> 5, sh = (24 * G) & 31;
+    if constexpr (sh + 24 <= 32) return (pk[w] >> sh) & 0xFFFFFFu;
+    else return __builtin_amdgcn_alignbit(pk[w + 1], pk[w], sh) & 0xFFFFFFu;
+}
+
+template <int G, int K, int NPK>
+__device__ __forceinline__ void fields24(const uint32_t (&pk)[NPK], uint32_t (&F)[K]) {
+    if constexpr (G < K) {
+        F[G] = field24<G>(pk);
+        fields24<G + 1, K>(pk, F);
+    }
+}
+
+template <int D, int BITS, bool PAGED>
 __global__ __launch_bounds__(kThreads) void encode_kernel(const u32x4 *__restrict__ x, int64_t n,
                                                           const int64_t *__restrict__ slots,
                                                           int64_t num_slots,
                                                           uint32_t *__restrict__ packed,
                                                           float *__restrict__ norms,
                                                           CodecConsts k, EncTable tb) {
-    constexpr int PW = kHeadDim * BITS / 32;    // packed dwords per vector
+    constexpr int K = D / 32;                   // register groups per lane
+    constexpr int R = 8 * K;                    // coordinates per lane
+    constexpr int PW = D * BITS / 32;           // packed dwords per vector
+    constexpr uint32_t VB = 2 * D;              // fp16 bytes per vector
+    constexpr int NPK = (K * BITS + 3) / 4;     // dwords of the lane's field stream
     __shared__ float2 qtab[2 * kCells + 1];
-    __shared__ u32x4 smask[16];
+    __shared__ u32x4 smask[4 * K];
     for (int t = threadIdx.x; t < 2 * kCells + 1; t += blockDim.x) qtab[t] = tb.cell[t];
-    if (threadIdx.x < 64) store_sign_mask(k, threadIdx.x, reinterpret_cast<uint32_t *>(smask));
+    if (threadIdx.x < 16 * K) store_sign_mask<K>(k, threadIdx.x, reinterpret_cast<uint32_t *>(smask));
     __syncthreads();
 
     const int q = threadIdx.x & 3;
-    uint32_t xm[16];
-    load_sign_masks(smask, q, xm);
+    uint32_t xm[4 * K];
+    load_sign_masks<K>(smask, q, xm);
     const float ma = (q & 1) ? -1.0f : 1.0f;
     const float mb = (q & 2) ? -1.0f : 1.0f;
     const float eps8 = 8.0f * ma * mb;
@@ -229,11 +266,11 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(const u32x4 *__restric
         const uint32_t qi = threadIdx.x >> 2;
         const int64_t v = v0 + qi;
         if (v >= n) return;   // uniform over the quad; no barrier follows
-        const __amdgpu_buffer_rsrc_t rx = span_rsrc(x + v0 * 16, nb * 256u);
-        const uint32_t xo = qi * 256u + 16u * q;
-        uint32_t w[16];
+        const __amdgpu_buffer_rsrc_t rx = span_rsrc(x + v0 * (D / 8), nb * VB);
+        const uint32_t xo = qi * VB + 16u * q;
+        uint32_t w[4 * K];
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
+        for (int g = 0; g < K; ++g) {
             const u32x4 u = __builtin_bit_cast(
                 u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, xo + 64u * g, 0, 0));
             w[4 * g + 0] = u.x;
@@ -244,16 +281,16 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(const u32x4 *__restric
         // ||x||^2 from the fp16 pairs (products exact in f32, f32 accumulate)
         float ss = 0.0f;
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
+        for (int j = 0; j < 4 * K; ++j) {
             const half2_t h = __builtin_bit_cast(half2_t, w[j]);
             ss = __builtin_amdgcn_fdot2(h, h, ss, false);
         }
         // sign flip on the fp16 bits; widening to f32 fused with the first
         // butterfly stage (v_fma_mix: the multiplier `one` is a kernel
         // argument, so the compiler cannot fold these into plain adds)
-        float f[32];
+        float f[R];
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
+        for (int j = 0; j < 4 * K; ++j) {
             const half2_t h = __builtin_bit_cast(half2_t, w[j] ^ xm[j]);
             const float lo = (float)h.x, hi = (float)h.y;
             f[2 * j] = __builtin_fmaf(hi, one, lo);
@@ -267,20 +304,20 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(const u32x4 *__restric
         rc = __builtin_fmaf(rc, __builtin_fmaf(-nrm, rc, 1.0f), rc);
         const float kk = (nrm > 0.0f) ? eps8 * rc : 0.0f;
 
-        fwht_quad(f, ma, mb);
+        fwht_quad<R>(f, ma, mb);
         fwht_registers_scaled<2>(f, kk);   // f[r] = 8 z of coordinate r
 
-        uint32_t pk[BITS];
+        uint32_t pk[NPK];
 #pragma unroll
-        for (int i = 0; i < BITS; ++i) pk[i] = 0;
-        if (BITS == 4) {
-            uint32_t lo[4], hi[4];
+        for (int i = 0; i < NPK; ++i) pk[i] = 0;
+        if constexpr (BITS == 4) {
+            uint32_t lo[K], hi[K];
             quantize4<0>(f, qtab, lo, hi);
 #pragma unroll
-            for (int g = 0; g < 4; ++g) pk[g % BITS] = lo[g] | hi[g];
+            for (int g = 0; g < K; ++g) pk[g] = lo[g] | hi[g];
         } else {
 #pragma unroll
-            for (int r = 0; r < 32; ++r) {
+            for (int r = 0; r < R; ++r) {
                 const float y = f[r];
                 const float2 e = qtab[(int)y + kCells];
                 const uint32_t code = __builtin_bit_cast(uint32_t, e.y) + (y > e.x ? 1u : 0u);
@@ -291,58 +328,53 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(const u32x4 *__restric
         }
 
         // the dwords this lane stores and their indices within the packed row
-        uint32_t sv[4];
-        int si[4];
-        int ns = 0;
-        if (BITS == 4) {
+        constexpr int NS = (BITS == 2) ? K / 2 : K;
+        uint32_t sv[NS];
+        int si[NS];
+        if constexpr (BITS == 4) {
             // group k of lane q is dword 4k + q
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                sv[g] = pk[g % BITS];
+            for (int g = 0; g < K; ++g) {
+                sv[g] = pk[g];
                 si[g] = 4 * g + q;
             }
-            ns = 4;
-        } else if (BITS == 2) {
+        } else if constexpr (BITS == 2) {
             // group k of lane q is half (q & 1) of dword 2k + (q >> 1); lanes
-            // q and q^1 splice their halves, each lane stores two dwords
-            const uint32_t p0 = quad_move<kQuadXor1>(pk[0]);
-            const uint32_t p1 = quad_move<kQuadXor1>(pk[1 % BITS]);
+            // q and q^1 splice their halves (dword m of the stream holds
+            // groups 2m, 2m + 1), each lane stores K / 2 dwords
             const int base = 2 * (q & 1) + (q >> 1);
-            sv[0] = __builtin_amdgcn_perm(p0, pk[0], sel2);
-            si[0] = base;
-            sv[1] = __builtin_amdgcn_perm(p1, pk[1 % BITS], sel2);
-            si[1] = base + 4;
-            ns = 2;
+#pragma unroll
+            for (int m = 0; m < NS; ++m) {
+                const uint32_t p = quad_move<kQuadXor1>(pk[m]);
+                sv[m] = __builtin_amdgcn_perm(p, pk[m], sel2);
+                si[m] = base + 4 * m;
+            }
         } else {
             // group k of lane q is the 24-bit field at bit 96k + 24q; lane q < 3
             // stores dword 3k + q, made of its field and lane q+1's
-            uint32_t G[4];
-            G[0] = pk[0] & 0xFFFFFFu;
-            G[1] = __builtin_amdgcn_alignbit(pk[1 % BITS], pk[0], 24) & 0xFFFFFFu;
-            G[2] = __builtin_amdgcn_alignbit(pk[2 % BITS], pk[1 % BITS], 16) & 0xFFFFFFu;
-            G[3] = pk[2 % BITS] >> 8;
+            uint32_t G[K];
+            fields24<0, K>(pk, G);
             const uint32_t sh = 8 * q + 8;
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
+            for (int g = 0; g < K; ++g) {
                 const uint32_t nbv = quad_move<kQuadNext>(G[g]);
                 sv[g] = __builtin_amdgcn_alignbit(nbv, G[g] << 8, sh);
                 si[g] = 3 * g + q;   // stored only by lanes q < 3
             }
-            ns = 4;
         }
         if (PAGED) {
             const int64_t row = slots[v];
             if (row < 0 || row >= num_slots) return;     // uniform over the quad
             uint32_t *dst = packed + row * PW;
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                if (i < ns && (BITS != 3 || q < 3)) dst[si[i]] = sv[i];
+            for (int i = 0; i < NS; ++i)
+                if (BITS != 3 || q < 3) dst[si[i]] = sv[i];
             if (q == 0) norms[row] = nrm;
         } else {
             const __amdgpu_buffer_rsrc_t rp = span_rsrc(packed + v0 * PW, nb * (PW * 4u));
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                if (i < ns && (BITS != 3 || q < 3))
+            for (int i = 0; i < NS; ++i)
+                if (BITS != 3 || q < 3)
                     __builtin_amdgcn_raw_buffer_store_b32(sv[i], rp, qi * (PW * 4u) + 4u * si[i], 0, 0);
             if (q == 0)
                 __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, nrm),
@@ -351,13 +383,21 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(const u32x4 *__restric
     }
 }
 
-template <int BITS>
+// Decode: vectors per quad (all their loads are issued before the first one
+// is transformed); fewer at D = 256, where one vector already takes 64
+// registers of values.
+constexpr int dec_vpq(int d) { return d > 128 ? 2 : kDecVpq; }
+
+template <int D, int BITS>
 __global__ __launch_bounds__(kThreads) void decode_kernel(const uint32_t *__restrict__ packed,
                                                           const float *__restrict__ norms,
                                                           int64_t n, u32x4 *__restrict__ out,
                                                           CodecConsts k) {
     constexpr int L = 1 << BITS;
-    constexpr int PW = kHeadDim * BITS / 32;
+    constexpr int K = D / 32;
+    constexpr int R = 8 * K;
+    constexpr int PW = D * BITS / 32;
+    constexpr int VPQ = dec_vpq(D);
     // One lookup returns G already-transformed values: the first butterfly
     // stage (b = 3, 4: pairs of codes) or the first two (b = 2: a byte holds
     // four codes) is folded into the table.
@@ -379,65 +419,68 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const uint32_t *__rest
             tab[4 * t + 3] = a1 - a3;
         }
     }
-    __shared__ u32x4 smask[16];
-    if (threadIdx.x < 64) store_sign_mask(k, threadIdx.x, reinterpret_cast<uint32_t *>(smask));
+    __shared__ u32x4 smask[4 * K];
+    if (threadIdx.x < 16 * K) store_sign_mask<K>(k, threadIdx.x, reinterpret_cast<uint32_t *>(smask));
     __syncthreads();
 
     const int q = threadIdx.x & 3;
-    uint32_t xm[16];
-    load_sign_masks(smask, q, xm);
+    uint32_t xm[4 * K];
+    load_sign_masks<K>(smask, q, xm);
     const float ma = (q & 1) ? -1.0f : 1.0f;
     const float mb = (q & 2) ? -1.0f : 1.0f;
-    const float eps_d = (ma * mb) * (1.0f / kHeadDim);
+    const float eps_d = (ma * mb) * (1.0f / D);
     const uint32_t sel2 = (q & 1) ? 0x07060302u : 0x05040100u;   // halves (q & 1) of two dwords
     const int w3a = (3 * q) >> 2;                                 // 3-bit: first dword of the field
     const int w3b = (w3a + 1 < 3) ? w3a + 1 : 2;
     const uint32_t s3 = (24u * q) & 31u;
 
-    // kDecVpq vectors per quad, 64 apart, so that every access instruction of
+    // VPQ vectors per quad, 64 apart, so that every access instruction of
     // a wave covers 16 consecutive vectors; all their loads are issued before
     // the first vector is transformed.
-    constexpr int NW = (BITS == 3) ? 8 : 4;   // packed dwords this lane reads per vector
-    const int64_t vb = (int64_t)blockIdx.x * (kVecPerBlock * kDecVpq) + (threadIdx.x >> 2);
-    uint32_t raw[kDecVpq][NW];
-    float nrm[kDecVpq];
+    constexpr int NW = (BITS == 3) ? 2 * K : K;   // packed dwords this lane reads per vector
+    const int64_t vb = (int64_t)blockIdx.x * (kVecPerBlock * VPQ) + (threadIdx.x >> 2);
+    uint32_t raw[VPQ][NW];
+    float nrm[VPQ];
 #pragma unroll
-    for (int i = 0; i < kDecVpq; ++i) {
+    for (int i = 0; i < VPQ; ++i) {
         const int64_t v = vb + (int64_t)i * kVecPerBlock;
         if (v >= n) break;   // uniform over the quad
         const uint32_t *src = packed + v * PW;
         nrm[i] = norms[v];
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            if (BITS == 4) {
+        for (int g = 0; g < K; ++g) {
+            if constexpr (BITS == 4) {
                 raw[i][g] = src[4 * g + q];
-            } else if (BITS == 2) {
+            } else if constexpr (BITS == 2) {
                 raw[i][g] = src[2 * g + (q >> 1)];
             } else {
                 raw[i][2 * g] = src[3 * g + w3a];
-                raw[i][2 * g + 1 % NW] = src[3 * g + w3b];
+                raw[i][2 * g + 1] = src[3 * g + w3b];
             }
         }
     }
 #pragma unroll
-    for (int i = 0; i < kDecVpq; ++i) {
+    for (int i = 0; i < VPQ; ++i) {
         const int64_t v = vb + (int64_t)i * kVecPerBlock;
         if (v >= n) break;
-        float f[32];
-        if (BITS == 4) {
+        float f[R];
+        if constexpr (BITS == 4) {
 #pragma unroll
-            for (int j = 0; j < 16; ++j) {
+            for (int j = 0; j < 4 * K; ++j) {
                 const uint32_t idx = (raw[i][j >> 2] >> (8 * (j & 3))) & 0xFFu;
                 const float2 e = reinterpret_cast<const float2 *>(tab)[idx];
                 f[2 * j] = e.x;
                 f[2 * j + 1] = e.y;
             }
-        } else if (BITS == 2) {
-            const uint32_t c0 = __builtin_amdgcn_perm(raw[i][1], raw[i][0], sel2);   // groups 0, 1
-            const uint32_t c1 = __builtin_amdgcn_perm(raw[i][3], raw[i][2], sel2);   // groups 2, 3
+        } else if constexpr (BITS == 2) {
+            // c[m]: this lane's halves of groups 2m and 2m + 1
+            uint32_t c[K / 2];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const uint32_t idx = ((j < 4 ? c0 : c1) >> (8 * (j & 3))) & 0xFFu;
+            for (int m = 0; m < K / 2; ++m)
+                c[m] = __builtin_amdgcn_perm(raw[i][2 * m + 1], raw[i][2 * m], sel2);
+#pragma unroll
+            for (int j = 0; j < 2 * K; ++j) {
+                const uint32_t idx = (c[j >> 2] >> (8 * (j & 3))) & 0xFFu;
                 const float4 e = reinterpret_cast<const float4 *>(tab)[idx];
                 f[4 * j] = e.x;
                 f[4 * j + 1] = e.y;
@@ -446,9 +489,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const uint32_t *__rest
             }
         } else {
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const uint32_t fld =
-                    __builtin_amdgcn_alignbit(raw[i][(2 * g + 1) % NW], raw[i][2 * g], s3);
+            for (int g = 0; g < K; ++g) {
+                const uint32_t fld = __builtin_amdgcn_alignbit(raw[i][2 * g + 1], raw[i][2 * g], s3);
 #pragma unroll
                 for (int p = 0; p < 4; ++p) {
                     const uint32_t idx = (fld >> (6 * p)) & 63u;
@@ -458,27 +500,27 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const uint32_t *__rest
                 }
             }
         }
-        fwht_quad(f, ma, mb);
+        fwht_quad<R>(f, ma, mb);
         fwht_registers_scaled<(BITS == 2) ? 4 : 2>(f, nrm[i] * eps_d);
 
-        uint32_t o[16];
+        uint32_t o[4 * K];
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
+        for (int j = 0; j < 4 * K; ++j) {
             half2_t h;
             h.x = (_Float16)f[2 * j];
             h.y = (_Float16)f[2 * j + 1];
             o[j] = __builtin_bit_cast(uint32_t, h) ^ xm[j];
         }
-        u32x4 *dst = out + v * 16 + q;
+        u32x4 *dst = out + v * (D / 8) + q;
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
+        for (int g = 0; g < K; ++g) {
             const u32x4 val = {o[4 * g], o[4 * g + 1], o[4 * g + 2], o[4 * g + 3]};
             dst[4 * g] = val;
         }
     }
 }
 
-// One block per 64 (encode) or 64 * kDecVpq (decode) vectors: a full grid, so
+// One block per 64 (encode) or 64 * dec_vpq(D) (decode) vectors: a full grid, so
 // the hardware keeps every CU fed without a tail of long-running blocks.
 dim3 grid_for(int64_t n, int vectors_per_block) {
     const int64_t b = (n + vectors_per_block - 1) / vectors_per_block;
@@ -496,42 +538,57 @@ int device_cu_count() {
     return cus;
 }
 
-hipError_t launch_encode(int bits, const void *x, int64_t n, const int64_t *slots,
+hipError_t launch_encode(int head_dim, int bits, const void *x, int64_t n, const int64_t *slots,
                          int64_t num_slots, const CodecConsts &k, const EncTable &tb,
                          uint8_t *packed, float *norms, hipStream_t stream) {
     if (n > (int64_t)kVecPerBlock * 0x7fffffff) return hipErrorInvalidValue;
     const dim3 grid = grid_for(n, kVecPerBlock), block(kThreads);
     const u32x4 *xs = static_cast<const u32x4 *>(x);
     uint32_t *pk = reinterpret_cast<uint32_t *>(packed);
-#define TQ_ENC(B)                                                                               \
+#define TQ_ENC(D, B)                                                                            \
     if (slots)                                                                                  \
-        hipLaunchKernelGGL((encode_kernel<B, true>), grid, block, 0, stream, xs, n, slots,      \
+        hipLaunchKernelGGL((encode_kernel<D, B, true>), grid, block, 0, stream, xs, n, slots,   \
                            num_slots, pk, norms, k, tb);                                        \
     else                                                                                        \
-        hipLaunchKernelGGL((encode_kernel<B, false>), grid, block, 0, stream, xs, n, slots,     \
+        hipLaunchKernelGGL((encode_kernel<D, B, false>), grid, block, 0, stream, xs, n, slots,  \
                            num_slots, pk, norms, k, tb);
-    switch (bits) {
-        case 2: TQ_ENC(2) break;
-        case 3: TQ_ENC(3) break;
-        case 4: TQ_ENC(4) break;
+    switch (head_dim * 10 + bits) {
+        case 642: TQ_ENC(64, 2) break;
+        case 643: TQ_ENC(64, 3) break;
+        case 644: TQ_ENC(64, 4) break;
+        case 1282: TQ_ENC(128, 2) break;
+        case 1283: TQ_ENC(128, 3) break;
+        case 1284: TQ_ENC(128, 4) break;
+        case 2562: TQ_ENC(256, 2) break;
+        case 2563: TQ_ENC(256, 3) break;
+        case 2564: TQ_ENC(256, 4) break;
         default: return hipErrorInvalidValue;
     }
 #undef TQ_ENC
     return hipGetLastError();
 }
 
-hipError_t launch_decode(int bits, const uint8_t *packed, const float *norms, int64_t n,
-                         const CodecConsts &k, void *out, hipStream_t stream) {
-    if (n > (int64_t)kVecPerBlock * kDecVpq * 0x7fffffff) return hipErrorInvalidValue;
-    const dim3 grid = grid_for(n, kVecPerBlock * kDecVpq), block(kThreads);
+hipError_t launch_decode(int head_dim, int bits, const uint8_t *packed, const float *norms,
+                         int64_t n, const CodecConsts &k, void *out, hipStream_t stream) {
+    const int vpb = kVecPerBlock * dec_vpq(head_dim);
+    if (n > (int64_t)vpb * 0x7fffffff) return hipErrorInvalidValue;
+    const dim3 grid = grid_for(n, vpb), block(kThreads);
     u32x4 *o = static_cast<u32x4 *>(out);
     const uint32_t *pk = reinterpret_cast<const uint32_t *>(packed);
-    switch (bits) {
-        case 2: hipLaunchKernelGGL(decode_kernel<2>, grid, block, 0, stream, pk, norms, n, o, k); break;
-        case 3: hipLaunchKernelGGL(decode_kernel<3>, grid, block, 0, stream, pk, norms, n, o, k); break;
-        case 4: hipLaunchKernelGGL(decode_kernel<4>, grid, block, 0, stream, pk, norms, n, o, k); break;
+#define TQ_DEC(D, B) hipLaunchKernelGGL((decode_kernel<D, B>), grid, block, 0, stream, pk, norms, n, o, k)
+    switch (head_dim * 10 + bits) {
+        case 642: TQ_DEC(64, 2); break;
+        case 643: TQ_DEC(64, 3); break;
+        case 644: TQ_DEC(64, 4); break;
+        case 1282: TQ_DEC(128, 2); break;
+        case 1283: TQ_DEC(128, 3); break;
+        case 1284: TQ_DEC(128, 4); break;
+        case 2562: TQ_DEC(256, 2); break;
+        case 2563: TQ_DEC(256, 3); break;
+        case 2564: TQ_DEC(256, 4); break;
         default: return hipErrorInvalidValue;
     }
+#undef TQ_DEC
     return hipGetLastError();
 }
 

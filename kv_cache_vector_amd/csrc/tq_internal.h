@@ -7,12 +7,13 @@
 
 namespace tq {
 
-constexpr int kHeadDim = 128;
+constexpr int kHeadDim = 128;      // the attention kernels' head dimension
+constexpr int kMaxHeadDim = 256;   // the codec kernels take 64, 128 and 256
 
 // Everything the kernels need that is fixed by (bits, seed).  Passed by value
 // as a kernel argument, so the library needs no device allocation.
 struct CodecConsts {
-    uint32_t sign[4];   // bit i of sign[i / 32] set  <=>  sigma_i = -1
+    uint32_t sign[kMaxHeadDim / 32];   // bit i of sign[i / 32] set  <=>  sigma_i = -1
     float thr8[15];     // decision thresholds times 8, ascending (2^bits - 1 used)
     float level[16];    // Lloyd-Max levels, ascending (2^bits used)
     float one;          // 1.0f, kept opaque to the compiler (see the encode kernel)
@@ -21,23 +22,25 @@ struct CodecConsts {
 // Decision table of the encode kernel: cell i (index i + kEncCells) covers
 // the values y = 8 z whose conversion to int (toward zero) is i; it holds the
 // one threshold inside the cell (+inf if none) and the number of thresholds
-// below the cell.  Built on the host from the f32 thresholds.
-constexpr int kEncCells = 96;
+// below the cell.  Built on the host from the f32 thresholds.  |y| is at most
+// 8 sqrt(head_dim) (all of the unit vector's mass on one rotated coordinate),
+// 128 at head_dim 256.
+constexpr int kEncCells = 128;
 struct EncTable {
     // (threshold * 8, code word): the code word is the base code, or at 4
     // bits the bytes {base, base + 1, base << 4, (base + 1) << 4}
     float2 cell[2 * kEncCells + 1];
 };
 
-// Encode `n` vectors.  With `slots` non-null, vector v is written to row
-// slots[v] of (packed, norms) and skipped when that row is outside
-// [0, num_slots); otherwise to row v.
-hipError_t launch_encode(int bits, const void *x, int64_t n, const int64_t *slots,
+// Encode `n` vectors of head_dim (64, 128 or 256) binary16 values.  With
+// `slots` non-null, vector v is written to row slots[v] of (packed, norms)
+// and skipped when that row is outside [0, num_slots); otherwise to row v.
+hipError_t launch_encode(int head_dim, int bits, const void *x, int64_t n, const int64_t *slots,
                          int64_t num_slots, const CodecConsts &k, const EncTable &t,
                          uint8_t *packed, float *norms, hipStream_t stream);
 
-hipError_t launch_decode(int bits, const uint8_t *packed, const float *norms, int64_t n,
-                         const CodecConsts &k, void *out, hipStream_t stream);
+hipError_t launch_decode(int head_dim, int bits, const uint8_t *packed, const float *norms,
+                         int64_t n, const CodecConsts &k, void *out, hipStream_t stream);
 
 // ---------------------------------------------------------------------------
 // decode attention

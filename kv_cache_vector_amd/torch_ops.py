@@ -16,6 +16,8 @@ operators).
                                              v_bits=-1) -> out
       (v_bits: width of the value codes; -1 means the same as the keys')
 
+The codec operators take head_dim 64, 128 or 256 (read off the tensors'
+last dimension); the attention operator takes head_dim 128.
 Seeds are unsigned 64-bit values; the schema's int is signed, so seeds at or
 above 2^63 travel as their two's-complement int64 and are converted back.
 The real kernels take GPU tensors only and call libtq on the current stream;
@@ -27,7 +29,8 @@ import torch
 
 from . import _lib
 
-HEAD_DIM = 128
+HEAD_DIM = 128                 # the attention operator's head dimension
+CODEC_HEAD_DIMS = (64, 128, 256)
 _U64 = 1 << 64
 
 
@@ -51,9 +54,20 @@ def _gpu(t: torch.Tensor, name: str) -> None:
 
 def _packed_dim(head_dim: int, bits: int) -> int:
     # codes of one vector: head_dim * bits / 8 bytes (same rule as tq_packed_bytes)
-    if head_dim != HEAD_DIM or bits not in (2, 3, 4):
+    if head_dim not in CODEC_HEAD_DIMS or bits not in (2, 3, 4):
         raise ValueError("unsupported (head_dim=%d, bits=%d)" % (head_dim, bits))
     return head_dim * bits // 8
+
+
+def _decoded_dim(packed: torch.Tensor, bits: int) -> int:
+    # head_dim of packed rows of `bits`-bit codes
+    if packed.dtype != torch.uint8 or packed.dim() < 1 or bits not in (2, 3, 4):
+        raise ValueError("packed must be uint8 [..., head_dim*bits/8], bits 2, 3 or 4")
+    D = packed.shape[-1] * 8 // bits
+    if packed.shape[-1] * 8 % bits or D not in CODEC_HEAD_DIMS:
+        raise ValueError("packed rows of %d bytes match no head_dim in %s at %d bits"
+                         % (packed.shape[-1], CODEC_HEAD_DIMS, bits))
+    return D
 
 
 # ---------------------------------------------------------------------------
@@ -62,15 +76,16 @@ def _packed_dim(head_dim: int, bits: int) -> int:
 @torch.library.custom_op("kv_cache_vector::tq_encode", mutates_args=())
 def tq_encode(x: torch.Tensor, bits: int, seed: int) -> tuple[torch.Tensor, torch.Tensor]:
     _gpu(x, "x")
-    if x.dtype != torch.float16 or x.shape[-1] != HEAD_DIM:
-        raise ValueError("x must be float16 [..., %d]" % HEAD_DIM)
-    P = _packed_dim(HEAD_DIM, bits)
+    if x.dtype != torch.float16 or x.dim() < 1:
+        raise ValueError("x must be float16 [..., head_dim]")
+    D = x.shape[-1]
+    P = _packed_dim(D, bits)
     x = x.contiguous()
     lead = tuple(x.shape[:-1])
-    n = x.numel() // HEAD_DIM
+    n = x.numel() // D
     packed = torch.empty(lead + (P,), dtype=torch.uint8, device=x.device)
     norms = torch.empty(lead, dtype=torch.float32, device=x.device)
-    _lib.check(_lib.tq_encode(x.data_ptr(), n, HEAD_DIM, bits, _seed_u64(seed),
+    _lib.check(_lib.tq_encode(x.data_ptr(), n, D, bits, _seed_u64(seed),
                               packed.data_ptr(), norms.data_ptr(), _stream(x.device)),
                "tq_encode")
     return packed, norms
@@ -78,7 +93,7 @@ def tq_encode(x: torch.Tensor, bits: int, seed: int) -> tuple[torch.Tensor, torc
 
 @tq_encode.register_fake
 def _(x, bits, seed):
-    P = _packed_dim(HEAD_DIM, bits)
+    P = _packed_dim(x.shape[-1], bits)
     lead = tuple(x.shape[:-1])
     return x.new_empty(lead + (P,), dtype=torch.uint8), x.new_empty(lead, dtype=torch.float32)
 
@@ -87,16 +102,13 @@ def _(x, bits, seed):
 def tq_decode(packed: torch.Tensor, norms: torch.Tensor, bits: int, seed: int) -> torch.Tensor:
     _gpu(packed, "packed")
     _gpu(norms, "norms")
-    P = _packed_dim(HEAD_DIM, bits)
-    if packed.dtype != torch.uint8 or packed.shape[-1] != P:
-        raise ValueError("packed must be uint8 [..., %d]" % P)
+    D = _decoded_dim(packed, bits)
     if norms.dtype != torch.float32 or tuple(norms.shape) != tuple(packed.shape[:-1]):
         raise ValueError("norms must be float32 with packed's leading shape")
     packed = packed.contiguous()
     norms = norms.contiguous()
-    out = torch.empty(tuple(norms.shape) + (HEAD_DIM,), dtype=torch.float16,
-                      device=packed.device)
-    _lib.check(_lib.tq_decode(packed.data_ptr(), norms.data_ptr(), norms.numel(), HEAD_DIM,
+    out = torch.empty(tuple(norms.shape) + (D,), dtype=torch.float16, device=packed.device)
+    _lib.check(_lib.tq_decode(packed.data_ptr(), norms.data_ptr(), norms.numel(), D,
                               bits, _seed_u64(seed), out.data_ptr(), _stream(packed.device)),
                "tq_decode")
     return out
@@ -104,7 +116,8 @@ def tq_decode(packed: torch.Tensor, norms: torch.Tensor, bits: int, seed: int) -
 
 @tq_decode.register_fake
 def _(packed, norms, bits, seed):
-    return norms.new_empty(tuple(norms.shape) + (HEAD_DIM,), dtype=torch.float16)
+    return norms.new_empty(tuple(norms.shape) + (_decoded_dim(packed, bits),),
+                           dtype=torch.float16)
 
 
 # ---------------------------------------------------------------------------
@@ -117,10 +130,11 @@ def tq_encode_paged_(x: torch.Tensor, slots: torch.Tensor, cache_packed: torch.T
     for t, name in ((x, "x"), (slots, "slots"), (cache_packed, "cache_packed"),
                     (cache_norms, "cache_norms")):
         _gpu(t, name)
-    P = _packed_dim(HEAD_DIM, bits)
-    if x.dtype != torch.float16 or x.shape[-1] != HEAD_DIM:
-        raise ValueError("x must be float16 [..., %d]" % HEAD_DIM)
-    if slots.dtype != torch.int64 or slots.numel() != x.numel() // HEAD_DIM:
+    if x.dtype != torch.float16 or x.dim() < 1:
+        raise ValueError("x must be float16 [..., head_dim]")
+    D = x.shape[-1]
+    P = _packed_dim(D, bits)
+    if slots.dtype != torch.int64 or slots.numel() != x.numel() // D:
         raise ValueError("slots must be int64 with one entry per vector")
     if not (cache_packed.is_contiguous() and cache_norms.is_contiguous()):
         raise ValueError("the cache tensors must be contiguous")
@@ -133,7 +147,7 @@ def tq_encode_paged_(x: torch.Tensor, slots: torch.Tensor, cache_packed: torch.T
         raise ValueError("cache_packed and cache_norms disagree on the number of rows")
     x = x.contiguous()
     slots = slots.contiguous()
-    _lib.check(_lib.tq_encode_paged(x.data_ptr(), slots.data_ptr(), slots.numel(), HEAD_DIM,
+    _lib.check(_lib.tq_encode_paged(x.data_ptr(), slots.data_ptr(), slots.numel(), D,
                                     bits, _seed_u64(seed), cache_packed.data_ptr(),
                                     cache_norms.data_ptr(), num_slots, _stream(x.device)),
                "tq_encode_paged")

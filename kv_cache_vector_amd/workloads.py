@@ -167,7 +167,19 @@ def attn_workload(batch: int = 16, num_q_heads: int = 32, num_kv_heads: int = 8,
                 block_size=block_size, num_kv_heads=num_kv_heads)
 
 
-def gaussian(n: int, seed: int) -> np.ndarray:
-    """n plain N(0,1) vectors of dimension 128 (fp16)."""
+def gaussian(n: int, seed: int, head_dim: int = HEAD_DIM) -> np.ndarray:
+    """n plain N(0,1) vectors of dimension head_dim (fp16)."""
     rng = np.random.default_rng(seed)
-    return _f16(rng.standard_normal((n, HEAD_DIM), dtype=np.float32))
+    return _f16(rng.standard_normal((n, head_dim), dtype=np.float32))
+
+
+def kv_heads_outliers(head_dim: int, tokens: int, heads: int = 8, seed: int = 600,
+                      outlier_p: float = 0.01, outlier_factor: float = 15.0) -> np.ndarray:
+    """K and V of `heads` KV heads at another head dimension (64 or 256), the
+    8B-shaped layer's recipe: N(0,1), every channel of a (K/V, head) an outlier
+    (x outlier_factor) with probability outlier_p.  [2*heads*tokens, head_dim]."""
+    rng = np.random.default_rng([seed, head_dim])
+    mask = rng.random((2, heads, 1, head_dim)) < outlier_p
+    x = rng.standard_normal((2, heads, tokens, head_dim), dtype=np.float32)
+    x = np.where(mask, x * np.float32(outlier_factor), x)
+    return _f16(x.reshape(-1, head_dim))

@@ -90,41 +90,41 @@ def check_signs(o):
 # ---------------------------------------------------------------------------
 
 def check_hadamard(o):
-    for d in (2, 4, 32, 128):
+    for d in (2, 4, 32, 64, 128, 256):
         H = o.hadamard(d).astype(np.int64)
         assert np.array_equal(H, sl.hadamard(d))            # Sylvester construction
         assert np.array_equal(H @ H.T, d * np.eye(d, dtype=np.int64))
 
 
-def check_rotation_unit_vectors(o, bits=4, seed=7):
+def check_rotation_unit_vectors(o, bits=4, seed=7, d=D):
     """x = sigma_k e_k has D x = e_k, so z = H e_k = column k of H: every z is
     +-1 exactly and the codes are those of +-1."""
-    s = o.signs(seed, D)
-    H = sl.hadamard(D)
+    s = o.signs(seed, d)
+    H = sl.hadamard(d)
     c, t = o.codebook(bits)
     code_p = int(np.sum(t < 1.0))
     code_m = int(np.sum(t < -1.0))
-    for k in (0, 1, 5, 64, 127):
-        x = np.zeros((1, D), dtype=np.float16)
+    for k in (0, 1, 5, d // 2, d - 1):
+        x = np.zeros((1, d), dtype=np.float16)
         x[0, k] = s[k]
         packed, norms, z = o.encode(x, bits, seed, want_z=True)
         assert norms[0] == 1.0
         assert np.array_equal(z[0], H[:, k].astype(np.float64))
-        codes = o.unpack(packed[0], D, bits)
+        codes = o.unpack(packed[0], d, bits)
         assert np.array_equal(codes, np.where(H[:, k] > 0, code_p, code_m))
 
 
-def check_rotation_norm(o, seed=11):
+def check_rotation_norm(o, seed=11, d=D):
     rng = np.random.default_rng(seed)
-    x = (rng.standard_normal((64, D)) * rng.uniform(0.01, 100, (64, 1))).astype(np.float16)
+    x = (rng.standard_normal((64, d)) * rng.uniform(0.01, 100, (64, 1))).astype(np.float16)
     _, norms, z = o.encode(x, 4, 3, want_z=True)
     ref = np.sqrt((x.astype(np.float64) ** 2).sum(1))
     assert np.array_equal(norms, ref.astype(np.float32))    # double norm, nearest f32
     # ||z||^2 = d: H D / sqrt(d) is orthogonal
-    assert np.allclose((z ** 2).sum(1), D, rtol=0, atol=1e-10)
+    assert np.allclose((z ** 2).sum(1), d, rtol=0, atol=1e-10)
     # z = H D x / ||x|| (library Hadamard, signs from the generator)
-    s = o.signs(3, D).astype(np.float64)
-    zr = (sl.hadamard(D) @ (s[:, None] * (x.astype(np.float64) / ref[:, None]).T)).T
+    s = o.signs(3, d).astype(np.float64)
+    zr = (sl.hadamard(d) @ (s[:, None] * (x.astype(np.float64) / ref[:, None]).T)).T
     assert np.allclose(z, zr, rtol=0, atol=1e-12)
 
 
@@ -383,40 +383,40 @@ def check_zero_vector(o):
         assert np.all(y.astype(np.float64) == 0)
 
 
-def check_reencode_fixed_point(o, seed=41):
+def check_reencode_fixed_point(o, seed=41, d=D):
     """Build x = fp16(D H c[code] / d) from codes drawn with the Gaussian cell
     probabilities; re-encoding it returns the same codes."""
     rng = np.random.default_rng(seed)
-    H = sl.hadamard(D).astype(np.float64)
+    H = sl.hadamard(d).astype(np.float64)
     for b in (2, 3, 4):
         c, t = o.codebook(b)
-        s = o.signs(13, D).astype(np.float64)
+        s = o.signs(13, d).astype(np.float64)
         edges = np.concatenate([[-np.inf], t, [np.inf]])
         prob = np.diff(_norm.cdf(edges))
         done = 0
         while done < 20:
-            code = rng.choice(len(c), size=D, p=prob)
+            code = rng.choice(len(c), size=d, p=prob)
             if not (0.85 <= np.mean(c[code] ** 2) <= 1.2):
                 continue
-            x = (s * (H @ c[code]) / D).astype(np.float16)[None, :]
+            x = (s * (H @ c[code]) / d).astype(np.float16)[None, :]
             p, _ = o.encode(x, b, 13)
-            assert np.array_equal(o.unpack(p[0], D, b), code.astype(np.uint8)), b
+            assert np.array_equal(o.unpack(p[0], d, b), code.astype(np.uint8)), b
             done += 1
 
 
-def check_decode_definition(o, seed=43):
+def check_decode_definition(o, seed=43, d=D):
     """Decode of hand-made codes: xhat = n * D * H * c[code] / d, with the
     library Hadamard; the fp16 output is that value rounded to nearest-even."""
     rng = np.random.default_rng(seed)
-    H = sl.hadamard(D).astype(np.float64)
+    H = sl.hadamard(d).astype(np.float64)
     for b in (2, 3, 4):
         c, _ = o.codebook(b)
-        s = o.signs(17, D).astype(np.float64)
-        codes = rng.integers(0, 1 << b, (8, D)).astype(np.uint8)
+        s = o.signs(17, d).astype(np.float64)
+        codes = rng.integers(0, 1 << b, (8, d)).astype(np.uint8)
         packed = np.stack([o.pack(cc, b) for cc in codes])
         norms = rng.uniform(0.5, 50, 8).astype(np.float32)
-        y, yf = o.decode(packed, norms, D, b, 17, want_f64=True)
-        ref = norms[:, None].astype(np.float64) * s[None, :] * (c[codes] @ H.T) / D
+        y, yf = o.decode(packed, norms, d, b, 17, want_f64=True)
+        ref = norms[:, None].astype(np.float64) * s[None, :] * (c[codes] @ H.T) / d
         assert np.allclose(yf, ref, rtol=1e-13, atol=1e-12)
         assert np.array_equal(y, yf.astype(np.float16))
 
@@ -625,6 +625,43 @@ def check_attn_mixed_widths(o):
         assert np.array_equal(o.attn_decode(*args), o.attn_decode(*args, v_bits=b))
 
 
+def check_mse_head_dim(o, d, n, seed=25):
+    """Round-trip MSE on N(0,1) vectors of dimension d against the exact value
+    for that d (the rotated coordinate is sqrt(d) times a coordinate of a
+    uniform unit vector, whose law depends on d), within five standard errors
+    of the sample mean, and under the 2.7 x 4^-b bound."""
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((n, d)).astype(np.float16)
+    xd = x.astype(np.float64)
+    for b in (2, 3, 4):
+        c, t = o.codebook(b)
+        packed, norms = o.encode(x, b, 2)
+        _, xh = o.decode(packed, norms, d, b, 2, want_f64=True)
+        r = ((xd - xh) ** 2).sum(1) / (xd ** 2).sum(1)
+        mse = float(np.mean(r))
+        se = float(np.std(r) / np.sqrt(n))
+        ex = exact_mse_d(b, c, t, d)
+        assert se < 2e-3 * ex, (d, b, se)                 # the sample resolves 1%
+        assert abs(mse - ex) < 5 * se, (d, b, mse, ex, se)
+        assert mse < 2.7 * 4.0 ** -b
+
+
+def check_head_dims(o):
+    """The codec at head_dim 64 and 256 against the same closed forms and
+    definitions as at 128: unit vectors rotate onto Hadamard columns, the
+    rotation is H D / ||x|| with ||z||^2 = d, decode is n D H c / d, decoded
+    codes re-encode to themselves, and the round-trip MSE is the exact value
+    for d."""
+    for d in (64, 256):
+        check_rotation_unit_vectors(o, d=d)
+        check_rotation_norm(o, d=d)
+        check_decode_definition(o, d=d)
+        check_reencode_fixed_point(o, d=d)
+        assert [o.packed_bytes(d, b) for b in (2, 3, 4)] == [d // 4, 3 * d // 8, d // 2]
+    check_mse_head_dim(o, 64, 40000)
+    check_mse_head_dim(o, 256, 12000)
+
+
 ALL_CHECKS = [
     check_half_to_double, check_double_to_half, check_splitmix64, check_signs,
     check_hadamard, check_rotation_unit_vectors, check_rotation_norm,
@@ -635,5 +672,5 @@ ALL_CHECKS = [
     check_scale_invariance, check_negation, check_zero_vector, check_reencode_fixed_point,
     check_decode_definition, check_attn_rotated_domain_identity, check_attn_special_cases,
     check_attn_paging_invariance, check_attn_bruteforce_tiny, check_attn_gqa_grouping,
-    check_attn_mixed_widths,
+    check_attn_mixed_widths, check_head_dims,
 ]

@@ -6,7 +6,7 @@ Tolerances (fixed by the target this build is held to):
     differ by exactly 1.  The fraction of such coordinates is reported.
   - norms and decoded values within 1e-3 relative; decoded values are
     compared on identical packed input, against
-    1e-3 * max(|ref|, norm/sqrt(128)) so that a coordinate near zero is
+    1e-3 * max(|ref|, norm/sqrt(d)) so that a coordinate near zero is
     measured against the vector's scale, or one binary16 ulp of the exact
     value where that is coarser (subnormal outputs), and an infinity of the
     right sign where the exact value is past the binary16 range;
@@ -32,10 +32,11 @@ def log(*a):
 
 
 def unpack_codes(packed: np.ndarray, bits: int) -> np.ndarray:
-    """LSB-first bitstream -> codes [..., 128] (numpy, independent of the oracle)."""
+    """LSB-first bitstream -> codes [..., d] (numpy, independent of the oracle)."""
     p = np.ascontiguousarray(packed, dtype=np.uint8)
+    d = p.shape[-1] * 8 // bits
     b = np.unpackbits(p, axis=-1, bitorder="little")
-    b = b.reshape(p.shape[:-1] + (D, bits)).astype(np.int16)
+    b = b.reshape(p.shape[:-1] + (d, bits)).astype(np.int16)
     return (b << np.arange(bits, dtype=np.int16)).sum(-1)
 
 
@@ -82,7 +83,8 @@ def compare_decoded(gpu_f16, ref_f64, norms, what=""):
     tolerance when the exact value sits just above 65504."""
     g = np.asarray(gpu_f16).astype(np.float64)
     r = np.asarray(ref_f64, np.float64)
-    scale = np.maximum(np.abs(r), np.asarray(norms, np.float64)[..., None] / np.sqrt(D))
+    d = r.shape[-1]
+    scale = np.maximum(np.abs(r), np.asarray(norms, np.float64)[..., None] / np.sqrt(d))
     fin = np.isfinite(g)
     err = np.where(fin, np.abs(g - r), 0.0)
     # the output is binary16: one ulp of it is the finest agreement possible

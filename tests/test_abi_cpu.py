@@ -44,8 +44,12 @@ def test_version_and_status_strings(L):
 
 def test_packed_bytes(L):
     assert [_lib.tq_packed_bytes(128, b) for b in (2, 3, 4)] == [32, 48, 64]
+    assert [_lib.tq_packed_bytes(64, b) for b in (2, 3, 4)] == [16, 24, 32]
+    assert [_lib.tq_packed_bytes(256, b) for b in (2, 3, 4)] == [64, 96, 128]
     assert _lib.tq_packed_bytes(128, 5) == 0
     assert _lib.tq_packed_bytes(96, 4) == 0
+    assert _lib.tq_packed_bytes(32, 4) == 0
+    assert _lib.tq_packed_bytes(512, 4) == 0
     assert _lib.tq_packed_bytes(128, 1) == 0
 
 
@@ -63,11 +67,13 @@ def test_codebook_hook_matches_oracle(L, bits):
     assert th[len(th) // 2] == 0.0
 
 
+@pytest.mark.parametrize("d", [64, 128, 256])
 @pytest.mark.parametrize("seed", [0, 1, 42, 2 ** 64 - 1])
-def test_sign_hook_matches_oracle(L, seed):
-    words = _lib.tq_signs(seed)
-    s = oracle.signs(seed, 128)
-    bits = np.array([(words[i // 32] >> (i % 32)) & 1 for i in range(128)])
+def test_sign_hook_matches_oracle(L, seed, d):
+    words = _lib.tq_signs(seed, d)
+    assert len(words) == d // 32
+    s = oracle.signs(seed, d)
+    bits = np.array([(words[i // 32] >> (i % 32)) & 1 for i in range(d)])
     assert np.array_equal(bits, (s < 0).astype(int))
 
 
@@ -76,6 +82,7 @@ def test_hook_errors(L):
     assert L.tq_codebook(5, buf, buf) == UNSUP
     assert L.tq_codebook(4, None, buf) == INVAL
     assert L.tq_signs(0, 96, buf) == UNSUP
+    assert L.tq_signs(0, 512, buf) == UNSUP
     assert L.tq_signs(0, 128, None) == INVAL
 
 
@@ -103,6 +110,12 @@ def test_encode_argument_errors(L):
     # overlapping input and output ranges
     assert e(A, 10, 128, 4, 0, A + 256, C, None) == INVAL
     assert e(A, 10, 128, 4, 0, B, B + 9 * 64, None) == INVAL
+    # the ranges scale with head_dim: 10 vectors of 256 are 5120 bytes
+    assert e(A, 10, 256, 4, 0, A + 5120 - 16, C, None) == INVAL
+    assert e(A, 10, 256, 4, 0, B, B + 9 * 128, None) == INVAL
+    assert e(A, 10, 64, 4, 0, B, B + 9 * 32, None) == INVAL
+    assert e(A, 10, 512, 4, 0, B, C, None) == UNSUP
+    assert e(A, 10, 32, 4, 0, B, C, None) == UNSUP
 
 
 def test_decode_argument_errors(L):
@@ -113,6 +126,8 @@ def test_decode_argument_errors(L):
     assert d(None, C, 10, 128, 4, 0, A, None) == INVAL
     assert d(B, C, 10, 128, 4, 0, A + 2, None) == MISAL
     assert d(B, C, 10, 128, 4, 0, B + 64, None) == INVAL   # output overlaps codes
+    assert d(B, C, 10, 256, 4, 0, C - 5120 + 16, None) == INVAL   # output overlaps norms
+    assert d(B, C, 10, 96, 4, 0, A, None) == UNSUP
 
 
 def test_paged_encode_argument_errors(L):
@@ -123,6 +138,8 @@ def test_paged_encode_argument_errors(L):
     assert p(A, None, 4, 128, 4, 0, C, C + 8192, 100, None) == INVAL
     assert p(A, B + 4, 4, 128, 4, 0, C, C + 8192, 100, None) == MISAL
     assert p(A, B, 4, 128, 4, 0, C, C + 64, 100, None) == INVAL   # packed overlaps norms
+    assert p(A, B, 4, 256, 4, 0, C, C + 128 * 99, 100, None) == INVAL
+    assert p(A, B, 4, 96, 4, 0, C, C + 1 << 20, 100, None) == UNSUP
 
 
 def test_attention_argument_errors(L):

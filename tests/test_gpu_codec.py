@@ -28,8 +28,9 @@ def dev():
 
 
 def run_codec(x_np, bits, seed, dev, what):
-    P.log("[codec] %s: n=%d bits=%d seed=%d" % (what, x_np.shape[0], bits, seed))
-    tq = TurboQuant(D, bits, seed, dev)
+    d = x_np.shape[-1]
+    P.log("[codec] %s: n=%d d=%d bits=%d seed=%d" % (what, x_np.shape[0], d, bits, seed))
+    tq = TurboQuant(d, bits, seed, dev)
     x = torch.from_numpy(np.ascontiguousarray(x_np)).to(dev)
     gp, gn = tq.encode(x)
     torch.cuda.synchronize()
@@ -40,7 +41,7 @@ def run_codec(x_np, bits, seed, dev, what):
     P.compare_norms(gn, rn, what)
     gd = tq.decode(torch.from_numpy(rp).to(dev), torch.from_numpy(rn).to(dev))
     torch.cuda.synchronize()
-    _, xh = oracle.decode(rp, rn, D, bits, seed, want_f64=True)
+    _, xh = oracle.decode(rp, rn, d, bits, seed, want_f64=True)
     P.compare_decoded(gd.cpu().numpy(), xh, rn, what)
     return band
 
@@ -68,24 +69,26 @@ def test_gaussian_outliers_all_bits(dev, bits):
     run_codec(x, bits, 3, dev, "gauss+1%% outliers b%d" % bits)
 
 
-def _special_vectors(seed=0):
+def _special_vectors(seed=0, d=D):
     rng = np.random.default_rng(seed)
-    s = oracle.signs(seed, D)
+    s = oracle.signs(seed, d)
     rows = []
-    rows.append(np.zeros(D))                                  # zero vector
-    for k in (0, 31, 32, 64, 127):                            # rotate to exact +-1
-        e = np.zeros(D)
+    rows.append(np.zeros(d))                                  # zero vector
+    for k in (0, 31, 32, d // 2, d - 1):                      # rotate to exact +-1
+        e = np.zeros(d)
         e[k] = s[k]
         rows.append(e)
-    rows.append(np.full(D, 65504.0))                           # largest fp16
-    rows.append(np.full(D, 2.0 ** -24))                        # smallest subnormal
-    t = np.zeros(D)
-    t[[3, 77]] = 1.0                                           # z has exact zeros
+    rows.append(s.astype(np.float64))                          # all mass on z_0 = sqrt(d)
+    rows.append(-s.astype(np.float64))
+    rows.append(np.full(d, 65504.0))                           # largest fp16
+    rows.append(np.full(d, 2.0 ** -24))                        # smallest subnormal
+    t = np.zeros(d)
+    t[[3, d // 2 + 13]] = 1.0                                  # z has exact zeros
     rows.append(t)
     rows.append(-t)
-    rows.append(np.where(np.arange(D) % 2 == 0, 1.0, -1.0))
+    rows.append(np.where(np.arange(d) % 2 == 0, 1.0, -1.0))
     for _ in range(8):
-        rows.append(rng.standard_normal(D) * 10.0 ** rng.uniform(-4, 4))
+        rows.append(rng.standard_normal(d) * 10.0 ** rng.uniform(-4, 4))
     return np.array(rows).astype(np.float16)
 
 
@@ -94,34 +97,44 @@ def test_special_vectors(dev, bits):
     run_codec(_special_vectors(), bits, 0, dev, "special b%d" % bits)
 
 
-@pytest.mark.parametrize("bits", [4, 3, 2])
-def test_ragged_counts_and_guard_bytes(dev, bits):
+def _ragged_counts(dev, bits, d, counts):
     """Counts that leave partial quads, waves and blocks; nothing outside the
-    n rows may be written."""
-    Pb = D * bits // 8
-    for n in (1, 2, 3, 5, 15, 16, 17, 63, 64, 65, 127, 1000, 4097):
-        x_np = W.gaussian(n, seed=n)
+    n rows may be written.  The decode half runs on the oracle's codes."""
+    Pb = d * bits // 8
+    s = torch.cuda.current_stream().cuda_stream
+    for n in counts:
+        P.log("[codec] ragged n=%d d=%d bits=%d" % (n, d, bits))
+        x_np = W.gaussian(n, seed=n, head_dim=d)
         x = torch.from_numpy(x_np).to(dev)
         guard = 256
         packed = torch.full((n * Pb + guard,), 0xA5, dtype=torch.uint8, device=dev)
         norms = torch.full((n + 64,), -7.0, dtype=torch.float32, device=dev)
-        st = _lib.tq_encode(x.data_ptr(), n, D, bits, 11, packed.data_ptr(), norms.data_ptr(),
-                            torch.cuda.current_stream().cuda_stream)
-        assert st == 0
-        out = torch.full((n * D + 512,), 1234.0, dtype=torch.float16, device=dev)
-        st = _lib.tq_decode(packed.data_ptr(), norms.data_ptr(), n, D, bits, 11, out.data_ptr(),
-                            torch.cuda.current_stream().cuda_stream)
-        assert st == 0
+        assert _lib.tq_encode(x.data_ptr(), n, d, bits, 11, packed.data_ptr(),
+                              norms.data_ptr(), s) == 0
         torch.cuda.synchronize()
         pk = packed.cpu().numpy()
         nm = norms.cpu().numpy()
         assert np.all(pk[n * Pb:] == 0xA5), n
         assert np.all(nm[n:] == -7.0), n
-        assert np.all(out.cpu().numpy()[n * D:] == 1234.0), n
         rp, rn, z = oracle.encode(x_np, bits, 11, want_z=True)
         _, t = oracle.codebook(bits)
         P.compare_codes(pk[: n * Pb].reshape(n, Pb), rp, z, t, bits, "n=%d" % n)
         P.compare_norms(nm[:n], rn, "n=%d" % n)
+        packed[: n * Pb] = torch.from_numpy(rp.reshape(-1)).to(dev)
+        norms[:n] = torch.from_numpy(rn).to(dev)
+        out = torch.full((n * d + 512,), 1234.0, dtype=torch.float16, device=dev)
+        assert _lib.tq_decode(packed.data_ptr(), norms.data_ptr(), n, d, bits, 11,
+                              out.data_ptr(), s) == 0
+        torch.cuda.synchronize()
+        o = out.cpu().numpy()
+        assert np.all(o[n * d:] == 1234.0), n
+        _, xh = oracle.decode(rp, rn, d, bits, 11, want_f64=True)
+        P.compare_decoded(o[: n * d].reshape(n, d), xh, rn, "n=%d" % n)
+
+
+@pytest.mark.parametrize("bits", [4, 3, 2])
+def test_ragged_counts_and_guard_bytes(dev, bits):
+    _ragged_counts(dev, bits, D, (1, 2, 3, 5, 15, 16, 17, 63, 64, 65, 127, 1000, 4097))
 
 
 def test_zero_count_is_noop(dev):
@@ -149,19 +162,19 @@ def test_deterministic_and_scale_invariant(dev):
         assert torch.equal(n3, n1 * (2.0 ** k))
 
 
-@pytest.mark.parametrize("bits", [4, 3, 2])
-def test_encode_paged(dev, bits):
+def _encode_paged(dev, bits, d):
     """Encoding into scattered cache rows writes exactly the rows tq_encode
     would, skips negative and out-of-range slots, and touches nothing else."""
     rng = np.random.default_rng(bits)
     nblk, bs, hkv = 40, 16, 8
     num_slots = nblk * bs * hkv
     n = 300
-    x_np = W.gaussian(n, seed=100 + bits)
+    P.log("[codec] paged n=%d d=%d bits=%d" % (n, d, bits))
+    x_np = W.gaussian(n, seed=100 + bits, head_dim=d)
     slots_np = rng.permutation(num_slots)[:n].astype(np.int64)
     slots_np[5] = -1
     slots_np[17] = num_slots + 3
-    tq = TurboQuant(D, bits, 42, dev)
+    tq = TurboQuant(d, bits, 42, dev)
     Pb = tq.packed_dim
     cache_p = torch.full((nblk, bs, hkv, Pb), 0x5A, dtype=torch.uint8, device=dev)
     cache_n = torch.full((nblk, bs, hkv), -1.0, dtype=torch.float32, device=dev)
@@ -173,11 +186,71 @@ def test_encode_paged(dev, bits):
     rp, rn, z = oracle.encode(x_np, bits, 42, want_z=True)
     _, t = oracle.codebook(bits)
     keep = (slots_np >= 0) & (slots_np < num_slots)
-    P.compare_codes(cp[slots_np[keep]], rp[keep], z[keep], t, bits, "paged b%d" % bits)
-    P.compare_norms(cn[slots_np[keep]], rn[keep], "paged b%d" % bits)
+    P.compare_codes(cp[slots_np[keep]], rp[keep], z[keep], t, bits, "paged d=%d b%d" % (d, bits))
+    P.compare_norms(cn[slots_np[keep]], rn[keep], "paged d=%d b%d" % (d, bits))
     untouched = np.ones(num_slots, bool)
     untouched[slots_np[keep]] = False
     assert np.all(cp[untouched] == 0x5A) and np.all(cn[untouched] == -1.0)
+
+
+@pytest.mark.parametrize("bits", [4, 3, 2])
+def test_encode_paged(dev, bits):
+    _encode_paged(dev, bits, D)
+
+
+# ---------------------------------------------------------------------------
+# head_dim 64 and 256
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("d", [64, 256])
+@pytest.mark.parametrize("bits", [4, 3, 2])
+def test_head_dim_outlier_heads(dev, d, bits):
+    """8 KV heads x 256 tokens of K and V with 1% outlier channels (x15)."""
+    run_codec(W.kv_heads_outliers(d, tokens=256), bits, 7, dev, "d=%d outliers b%d" % (d, bits))
+
+
+@pytest.mark.parametrize("d", [64, 256])
+@pytest.mark.parametrize("bits", [4, 3, 2])
+def test_head_dim_special_vectors(dev, d, bits):
+    run_codec(_special_vectors(3, d), bits, 3, dev, "d=%d special b%d" % (d, bits))
+
+
+@pytest.mark.parametrize("d", [64, 256])
+@pytest.mark.parametrize("bits", [4, 3, 2])
+def test_head_dim_ragged_counts(dev, d, bits):
+    _ragged_counts(dev, bits, d, (1, 3, 17, 64, 65, 129, 511, 1000))
+
+
+@pytest.mark.parametrize("d", [64, 256])
+@pytest.mark.parametrize("bits", [4, 3, 2])
+def test_head_dim_encode_paged(dev, d, bits):
+    _encode_paged(dev, bits, d)
+
+
+@pytest.mark.parametrize("d", [64, 256])
+def test_head_dim_large_4bit(dev, d):
+    """8 KV heads x 32768 tokens of K and V (524,288 vectors) in one launch,
+    compared on 4096 sampled rows plus the first and last."""
+    x_np = W.kv_heads_outliers(d, tokens=32768)
+    n = x_np.shape[0]
+    P.log("[codec] d=%d large: n=%d b4" % (d, n))
+    tq = TurboQuant(d, 4, 1, dev)
+    x = torch.from_numpy(x_np).to(dev)
+    packed, norms = tq.encode(x)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([np.random.default_rng(d).choice(n, 4096, replace=False),
+                                     [0, n - 1]]))
+    ridx = torch.from_numpy(rows).to(dev)
+    rp, rn, z = oracle.encode(x_np[rows], 4, 1, want_z=True)
+    _, t = oracle.codebook(4)
+    P.compare_codes(packed[ridx].cpu().numpy(), rp, z, t, 4, "d=%d large" % d)
+    P.compare_norms(norms[ridx].cpu().numpy(), rn, "d=%d large" % d)
+    packed[ridx] = torch.from_numpy(rp).to(dev)
+    norms[ridx] = torch.from_numpy(rn).to(dev)
+    out = tq.decode(packed, norms)
+    torch.cuda.synchronize()
+    _, xh = oracle.decode(rp, rn, d, 4, 1, want_f64=True)
+    P.compare_decoded(out[ridx].cpu().numpy(), xh, rn, "d=%d large" % d)
 
 
 # ---------------------------------------------------------------------------

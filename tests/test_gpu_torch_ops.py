@@ -24,21 +24,23 @@ def dev():
     return torch.device("cuda:0")
 
 
-def test_ops_match_direct_calls(dev):
-    print("[ops] encode/decode vs direct", flush=True)
-    x = torch.from_numpy(W.gaussian(4096, seed=3)).to(dev)
+@pytest.mark.parametrize("d", [64, 128, 256])
+def test_ops_match_direct_calls(dev, d):
+    print("[ops] encode/decode vs direct, d=%d" % d, flush=True)
+    x = torch.from_numpy(W.gaussian(4096, seed=3, head_dim=d)).to(dev)
     seed = 2 ** 64 - 5                                   # needs the int64 conversion
     for bits in (2, 3, 4):
         p1, n1 = OPS.tq_encode(x, bits, T.seed_to_i64(seed))
-        P = 16 * bits
+        P = d * bits // 8
+        assert p1.shape == (4096, P)
         p2 = torch.empty(4096, P, dtype=torch.uint8, device=dev)
         n2 = torch.empty(4096, dtype=torch.float32, device=dev)
         s = torch.cuda.current_stream().cuda_stream
-        _lib.check(_lib.tq_encode(x.data_ptr(), 4096, 128, bits, seed, p2.data_ptr(),
+        _lib.check(_lib.tq_encode(x.data_ptr(), 4096, d, bits, seed, p2.data_ptr(),
                                   n2.data_ptr(), s), "tq_encode")
         y1 = OPS.tq_decode(p1, n1, bits, T.seed_to_i64(seed))
         y2 = torch.empty_like(x)
-        _lib.check(_lib.tq_decode(p2.data_ptr(), n2.data_ptr(), 4096, 128, bits, seed,
+        _lib.check(_lib.tq_decode(p2.data_ptr(), n2.data_ptr(), 4096, d, bits, seed,
                                   y2.data_ptr(), s), "tq_decode")
         torch.cuda.synchronize()
         assert torch.equal(p1, p2) and torch.equal(n1, n2) and torch.equal(y1, y2)

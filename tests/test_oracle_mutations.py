@@ -31,6 +31,7 @@ MUTATIONS = [
      "acc += (double)k->H[(size_t)i * d + j] * k->sg[i] * u[j];"),
     ("decode_missing_sign", "xhat[i] = nv * k->sg[i] * acc / d;", "xhat[i] = nv * acc / d;"),
     ("decode_sqrt_d", "xhat[i] = nv * k->sg[i] * acc / d;", "xhat[i] = nv * k->sg[i] * acc / sqrt(d);"),
+    ("decode_fixed_128", "xhat[i] = nv * k->sg[i] * acc / d;", "xhat[i] = nv * k->sg[i] * acc / 128;"),
     ("decode_transposed_H", "acc += (double)k->H[(size_t)i * d + j] * cv[j];",
      "acc += (double)k->H[(size_t)j * d + (i ^ 1)] * cv[j];"),
     ("norm_f32_truncated", "*nv_out = (float)nv;", "*nv_out = nextafterf((float)nv, 0.0f);"),
@@ -48,8 +49,9 @@ MUTATIONS = [
      "for (int j = 0; j < T; ++j) { s[j] = exp(s[j] - m); l += s[j]; }\n                if (T > 1) s[T - 1] = 0.0;"),
 ]
 
-# cheap checks first; the Monte-Carlo MSE last
-ORDER = sorted(pins.ALL_CHECKS, key=lambda f: f is pins.check_mse)
+# cheap checks first; the Monte-Carlo MSE and the other head dims last
+ORDER = sorted(pins.ALL_CHECKS,
+               key=lambda f: (f is pins.check_mse) + 2 * (f is pins.check_head_dims))
 
 
 @pytest.mark.parametrize("name,old,new", MUTATIONS, ids=[m[0] for m in MUTATIONS])

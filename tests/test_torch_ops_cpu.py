@@ -31,6 +31,26 @@ def test_fake_shapes(bits, P):
     assert o.shape == q.shape and o.dtype == torch.float16
 
 
+@pytest.mark.parametrize("d", [64, 256])
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_fake_shapes_other_head_dims(d, bits):
+    x = torch.empty(5, d, dtype=torch.float16, device="meta")
+    packed, norms = OPS.tq_encode(x, bits, 0)
+    assert packed.shape == (5, d * bits // 8) and norms.shape == (5,)
+    y = OPS.tq_decode(packed, norms, bits, 0)
+    assert y.shape == (5, d) and y.dtype == torch.float16
+
+
+def test_fake_rejects_unsupported_head_dims():
+    for d in (32, 96, 512):
+        x = torch.empty(4, d, dtype=torch.float16, device="meta")
+        with pytest.raises(ValueError):
+            OPS.tq_encode(x, 4, 0)
+    with pytest.raises(ValueError):                     # 20 bytes of 4-bit codes: d = 40
+        OPS.tq_decode(torch.empty(4, 20, dtype=torch.uint8, device="meta"),
+                      torch.empty(4, dtype=torch.float32, device="meta"), 4, 0)
+
+
 def test_fake_rejects_unsupported_bits():
     x = torch.empty(4, 128, dtype=torch.float16, device="meta")
     with pytest.raises(ValueError):
