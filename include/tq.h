@@ -16,7 +16,8 @@
  *              Gaussian-optimal levels); "What we shipped" item 2 (rotate the
  *              query once, fold the inverse rotation into the output).
  *
- * Encode, per vector x of head_dim = d = 128 binary16 values:
+ * Encode, per vector x of head_dim = d binary16 values (d = 64, 128 or 256;
+ * the crucible page's sample and the attention entry points use 128):
  *   n = ||x||_2 (stored as f32);  z = H * D * x / n  (D = diag(sigma), sigma
  *   the seeded +-1 sign flip, H the Sylvester Hadamard matrix, so
  *   z = sqrt(d) * R * (x/n) with R = H D / sqrt(d) orthogonal and z ~ N(0,1)
@@ -34,7 +35,10 @@
  *     surfaces at the caller's next synchronisation.
  *   - Argument errors are reported before anything is enqueued; no exception
  *     crosses the ABI.
- *   - head_dim must be 128 and bits 2, 3 or 4 (TQ_ERR_UNSUPPORTED otherwise).
+ *   - bits must be 2, 3 or 4; head_dim 64, 128 or 256 for the codec entry
+ *     points (tq_encode, tq_decode, tq_encode_paged, tq_packed_bytes,
+ *     tq_signs) and 128 for the attention ones (TQ_ERR_UNSUPPORTED
+ *     otherwise).
  *   - binary16 and packed arrays must be 16-byte aligned, f32/int32 arrays
  *     4-byte aligned (TQ_ERR_MISALIGNED otherwise).  Inputs and outputs must
  *     not overlap (TQ_ERR_INVALID_ARG).
@@ -191,7 +195,8 @@ tq_status tq_attn_decode_kv(const void *q_f16, const uint8_t *k_packed, const fl
  *   thresholds (2^bits - 1, the level midpoints) the kernels use
  *   ([PyPI] "Algorithm" step 3; [QBC] "What TurboQuant is").
  * tq_signs: the sign flip as a bit mask, bit i of mask[i/32] set iff
- *   sigma_i = -1 (head_dim/32 words).
+ *   sigma_i = -1 (head_dim/32 words; sigma of a shorter head_dim is a prefix
+ *   of sigma of a longer one).
  */
 tq_status tq_codebook(int bits, float *levels, float *thresholds);
 tq_status tq_signs(uint64_t seed, int head_dim, uint32_t *mask);
