@@ -68,6 +68,7 @@ constexpr float kLevelScale = 16.0f;        // binary16 levels are 16 c
 constexpr float kWShift = 6.0f;             // value weights carry 2^6
 constexpr int kLutRow = 256;                // bytes per table row: keys' half, values' half
 constexpr int kQuadPrev = 0x90;             // quad_perm [0,0,1,2]: lane q <- lane q-1 (0 <- 0)
+constexpr int kRowRor8 = 0x128;             // row_ror:8: lane m of a 16-lane row <- lane m ^ 8
 
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
@@ -118,6 +119,14 @@ __device__ __forceinline__ uint32_t level_pair(const CodecConsts &k, int code) {
     const _Float16 hi = (_Float16)c;
     const _Float16 lo = (_Float16)(c - (float)hi);
     return pack_half2(hi, lo);
+}
+
+// Lane m ^ 8 of this lane's 16-lane row.  The value is taken by value:
+// clang's __builtin_bit_cast applied directly to an element of an
+// ext_vector_type value reads element 0 whatever the element named.
+__device__ __forceinline__ float row_ror8(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), kRowRor8,
+                                                              0xF, 0xF, true));
 }
 
 __device__ __forceinline__ f4 mfma(const u32x4 &a, const u32x4 &b, f4 c) {
@@ -197,6 +206,16 @@ __device__ __forceinline__ u32x4 key_chunk(const char *tab, const u32x4 &kc, uin
     }
 }
 
+// One score chain: columns 0-7 carry (q_hi, q_hi) of heads 0-7 and columns
+// 8-15 carry (q_lo, 0) of the same heads (at most 8 query heads per kv head).
+template <int J, int KB>
+__device__ __forceinline__ void score_chunks_paired(const char *tab, const u32x4 &kc,
+                                                    uint32_t laneoff, const u32x4 (&bq)[8],
+                                                    f4 &S) {
+    S = mfma(key_chunk<J, KB>(tab, kc, laneoff), bq[J], S);
+    if constexpr (J < 7) score_chunks_paired<J + 1, KB>(tab, kc, laneoff, bq, S);
+}
+
 template <int J, int KB>
 __device__ __forceinline__ void score_chunks(const char *tab, const u32x4 &kc, uint32_t laneoff,
                                              const u32x4 (&bq1)[8], const u32x4 (&bq2)[8],
@@ -264,7 +283,12 @@ __device__ __forceinline__ void value_operands(const char *tab, const uint32_t (
     }
 }
 
-template <int KB, int VB>
+// PAIRED (at most 8 query heads per kv head): the low halves of the split
+// operands ride in the otherwise padded half of each tile -- score columns
+// and value rows 8-15 belong to heads 0-7 -- so each page takes 8 + 8 matrix
+// products instead of 16 + 16.  Otherwise (9-16 heads) the low halves take a
+// second product per tile.
+template <int KB, int VB, bool PAIRED>
 __global__ __launch_bounds__(kMThreads) void attn_split_kernel(AttnParams p) {
     using SK = Side<KB>;
     using SV = Side<VB>;
@@ -308,16 +332,18 @@ __global__ __launch_bounds__(kMThreads) void attn_split_kernel(AttnParams p) {
     const int lane = threadIdx.x & 63;
     const int m = lane & 15, r = lane >> 4;
     const int grp = p.hq / p.hkv;
-    const bool hv = m < grp;                                  // a real query head column
+    const int hcol = PAIRED ? (m & 7) : m;                    // head of this lane's column
+    const bool lo_col = PAIRED && m >= 8;                     // a column of low halves
+    const bool hv = hcol < grp;                               // a real query head column
     const uint32_t lok = (uint32_t)(lane & (SK::COPIES - 1)) * SK::EB;
     const uint32_t lov = kLutRow / 2 + (uint32_t)(lane & (SV::COPIES - 1)) * SV::EB;
 
     // ---- rotated query, one head per lane column, dims 32r .. 32r+31 ----
-    u32x4 bq1[8], bq2[8];
+    u32x4 bq1[8], bq2[PAIRED ? 1 : 8];
     float qsl;
     {
         float qv[32];
-        const int mq = hv ? m : 0;                            // padding columns read head 0, then drop it
+        const int mq = hv ? hcol : 0;                         // padding columns read head 0, then drop it
         const uint16_t *qp = p.q + ((size_t)b * p.hq + (size_t)g * grp + mq) * kHeadDim + 32 * r;
 #pragma unroll
         for (int e = 0; e < 32; ++e) {
@@ -361,8 +387,12 @@ __global__ __launch_bounds__(kMThreads) void attn_split_kernel(AttnParams p) {
                 w1[t] = pack_half2(hi, hi);
                 w2[t] = pack_half2(lo, (_Float16)0.0f);
             }
-            bq1[j] = u32x4{w1[0], w1[1], w1[2], w1[3]};
-            bq2[j] = u32x4{w2[0], w2[1], w2[2], w2[3]};
+            if constexpr (PAIRED) {
+                bq1[j] = lo_col ? u32x4{w2[0], w2[1], w2[2], w2[3]} : u32x4{w1[0], w1[1], w1[2], w1[3]};
+            } else {
+                bq1[j] = u32x4{w1[0], w1[1], w1[2], w1[3]};
+                bq2[j] = u32x4{w2[0], w2[1], w2[2], w2[3]};
+            }
         }
     }
 
@@ -440,13 +470,23 @@ __global__ __launch_bounds__(kMThreads) void attn_split_kernel(AttnParams p) {
 
     // one page: score tiles, value operands, softmax, value tiles, refill
     auto step = [&](const int pg, const int d) {
-        // scores of tokens 4r .. 4r+3 for head m, over two independent chains
-        f4 S0 = f4{0.0f, 0.0f, 0.0f, 0.0f}, S1 = S0;
-        score_chunks<0, KB>(tab, rk[d], lok, bq1, bq2, S0, S1);
-        // value codes of the page, read while the score tiles finish
+        // scores of tokens 4r .. 4r+3 for head hcol
+        f4 S;
+        if constexpr (PAIRED) {
+            f4 S0 = f4{0.0f, 0.0f, 0.0f, 0.0f};
+            score_chunks_paired<0, KB>(tab, rk[d], lok, bq1, S0);
+            // column m + (q_lo column m ^ 8): row_ror:8 pairs lanes m and m ^ 8
+            // of each 16-lane row, so both columns end with the full score
+#pragma unroll
+            for (int i = 0; i < 4; ++i) S[i] = S0[i] + row_ror8(S0[i]);
+        } else {
+            f4 S0 = f4{0.0f, 0.0f, 0.0f, 0.0f}, S1 = S0;   // two independent chains
+            score_chunks<0, KB>(tab, rk[d], lok, bq1, bq2, S0, S1);
+            S = S0 + S1;
+        }
+        // value codes of the page
         u32x4 Bv[8];
         value_operands<VB>(tab, rv[d], lov, q4, Bv);
-        const f4 S = S0 + S1;
 
         // online softmax in base 2.  Two lazily raised references: M per head
         // (rescale when a score passes M + 8) and a power of two vlim per wave
@@ -492,10 +532,10 @@ __global__ __launch_bounds__(kMThreads) void attn_split_kernel(AttnParams p) {
                 vlim = vn_lim;
                 vscale = (float)(1 << (int)kWShift) / vlim;
             }
-            // accumulator rows are heads 4r + i
+            // accumulator rows are heads 4r + i (PAIRED: row h holds head h % 8)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const float fi = __shfl(f, 4 * r + i) * fv;
+                const float fi = __shfl(f, PAIRED ? ((4 * r + i) & 7) : (4 * r + i)) * fv;
 #pragma unroll
                 for (int jj = 0; jj < 8; ++jj) acc[jj][i] *= fi;
             }
@@ -514,14 +554,20 @@ __global__ __launch_bounds__(kMThreads) void attn_split_kernel(AttnParams p) {
             w1[i] = hh;
             w2[i] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(w - hf));
         }
-        const u32x4 A1 = u32x4{w1[0], w1[1], w1[2], w1[3]};
-        const u32x4 A2 = u32x4{w2[0], w2[1], w2[2], w2[3]};
-
         // values: dims 8m + jj of tokens 4r .. 4r+3
+        if constexpr (PAIRED) {
+            // rows 0-7: (w_hi, w_hi) of heads 0-7; rows 8-15: (w_lo, 0)
+            const u32x4 A = lo_col ? u32x4{w2[0], w2[1], w2[2], w2[3]} : u32x4{w1[0], w1[1], w1[2], w1[3]};
 #pragma unroll
-        for (int jj = 0; jj < 8; ++jj) {
-            acc[jj] = mfma(A1, Bv[jj], acc[jj]);
-            acc[jj] = mfma(A2, Bv[jj], acc[jj]);
+            for (int jj = 0; jj < 8; ++jj) acc[jj] = mfma(A, Bv[jj], acc[jj]);
+        } else {
+            const u32x4 A1 = u32x4{w1[0], w1[1], w1[2], w1[3]};
+            const u32x4 A2 = u32x4{w2[0], w2[1], w2[2], w2[3]};
+#pragma unroll
+            for (int jj = 0; jj < 8; ++jj) {
+                acc[jj] = mfma(A1, Bv[jj], acc[jj]);
+                acc[jj] = mfma(A2, Bv[jj], acc[jj]);
+            }
         }
 
         fetch(pg + R, blk_next, d);
@@ -540,12 +586,20 @@ __global__ __launch_bounds__(kMThreads) void attn_split_kernel(AttnParams p) {
 
     lsum += __shfl_xor(lsum, 16);
     lsum += __shfl_xor(lsum, 32);
+    if constexpr (PAIRED) {
+        // rows 4r + i and 4r + i + 8 (lanes l and l ^ 32) are one head's
+        // high and low parts
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[jj][i] += __shfl_xor(acc[jj][i], 32);
+    }
     // partial state of head g*grp + h: m and l from lane h, accumulators from
     // lanes (column c, row h / 4) at register h % 4 -> dims 8c .. 8c+7
     const float unscale = vlim / (kLevelScale * 64.0f);     // undo 16 c and 2^6 / vlim
     float *base = p.ws + (((size_t)b * p.hq + (size_t)g * grp) * p.num_splits + split) * kPartial;
     const size_t hstride = (size_t)p.num_splits * kPartial;
-    if (r == 0 && hv) {
+    if (r == 0 && hv && !lo_col) {
         float *dst = base + (size_t)m * hstride;
         dst[0] = M;
         dst[1] = lsum;
@@ -553,7 +607,7 @@ __global__ __launch_bounds__(kMThreads) void attn_split_kernel(AttnParams p) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int h = 4 * r + i;
-        if (h >= grp) break;
+        if (h >= grp || (PAIRED && r >= 2)) break;
         float2 *dst = reinterpret_cast<float2 *>(base + (size_t)h * hstride + 2 + 8 * m);   // 8-byte aligned
 #pragma unroll
         for (int jj = 0; jj < 8; jj += 2) dst[jj >> 1] = float2(acc[jj][i] * unscale, acc[jj + 1][i] * unscale);
@@ -703,7 +757,10 @@ hipError_t launch_attn(const AttnShape &s, const CodecConsts &kc, const CodecCon
     const int hps = kMWaves / p.spw;
     const dim3 grid((p.num_splits + p.spw - 1) / p.spw, s.batch, (s.num_kv_heads + hps - 1) / hps);
     const dim3 block(kMThreads);
-#define TQ_SPLIT(KB, VB) hipLaunchKernelGGL((attn_split_kernel<KB, VB>), grid, block, 0, stream, p)
+    const bool paired = s.num_q_heads / s.num_kv_heads <= 8;
+#define TQ_SPLIT(KB, VB)                                                                            \
+    if (paired) hipLaunchKernelGGL((attn_split_kernel<KB, VB, true>), grid, block, 0, stream, p);   \
+    else hipLaunchKernelGGL((attn_split_kernel<KB, VB, false>), grid, block, 0, stream, p)
     switch (s.k_bits * 10 + s.v_bits) {
         case 44: TQ_SPLIT(4, 4); break;
         case 43: TQ_SPLIT(4, 3); break;
