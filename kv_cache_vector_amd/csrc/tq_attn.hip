@@ -22,8 +22,10 @@
 //           run as 16x16x32 f16 MFMA tiles:
 //             scores  S^T[16 tokens][16 heads] = C_k[16 tokens][K] Q[K][16 heads]
 //             values  O[16 heads][16 dims]    += W[16 heads][K] C_v[K][16 dims]
-//           with the group's query heads (up to 16) padded to 16.  One partial
-//           state per (sequence, query head, split) goes to the workspace.
+//           with the group's query heads (up to 16) padded to 16.  With at most
+//           8 heads per kv head the padding carries the operands' low halves
+//           (see below).  One partial state per (sequence, query head, split)
+//           goes to the workspace.
 //   combine grid (sequence * query head), one wave: log-sum-exp merge of the
 //           splits, the inverse transform D H / d, binary16 rounding.
 //
@@ -33,6 +35,8 @@
 // The split costs no repacking: a code is looked up as the binary16 pair
 // (c_hi, c_lo), which fills two adjacent K slots; the other operand holds
 // (q_hi, q_hi) in those slots for one product and (q_lo, 0) for a second.
+// With at most 8 query heads per kv head both products fit one tile: score
+// columns 8-15 and value rows 8-15 hold the low halves of heads 0-7.
 //
 // Scale factors keep every binary16 operand in range and its low part
 // normal: levels are stored times 16, the rotated query times a per-head
