@@ -18,7 +18,6 @@ namespace {
 
 using tq::CodecConsts;
 
-constexpr int kAttnD = tq::kHeadDim;
 
 // ---------------------------------------------------------------------------
 // Lloyd-Max quantizer of the standard normal (aither-kvcache PyPI page,
@@ -165,7 +164,7 @@ bool overlap(const void *a, size_t na, const void *b, size_t nb) {
 
 bool codec_head_dim(int d) { return d == 64 || d == 128 || d == 256; }
 
-// The codec takes head_dim 64, 128 or 256; the attention kernels 128.
+// Every entry point takes head_dim 64, 128 or 256 and bits 2, 3 or 4.
 tq_status check_shape(int head_dim, int bits) {
     if (head_dim <= 0 || bits <= 0) return TQ_ERR_INVALID_ARG;
     if (!codec_head_dim(head_dim) || bits < 2 || bits > 4) return TQ_ERR_UNSUPPORTED;
@@ -277,11 +276,11 @@ tq_status tq_decode(const uint8_t *packed, const float *norms, int64_t n, int he
 
 size_t tq_attn_workspace_bytes(int batch, int num_q_heads, int num_kv_heads, int head_dim,
                                int block_size, int max_blocks_per_seq) {
-    if (batch < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim != kAttnD ||
+    if (batch < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || !codec_head_dim(head_dim) ||
         block_size != tq::kAttnBlockSize || max_blocks_per_seq < 0 ||
         num_q_heads % num_kv_heads)
         return 0;
-    tq::AttnShape s{batch, num_q_heads, num_kv_heads, 4, 4, max_blocks_per_seq, 0};
+    tq::AttnShape s{batch, num_q_heads, num_kv_heads, head_dim, 4, 4, max_blocks_per_seq, 0};
     return tq::attn_workspace_bytes(s);
 }
 
@@ -296,7 +295,6 @@ tq_status tq_attn_decode_kv(const void *q_f16, const uint8_t *k_packed, const fl
     if (st != TQ_OK) return st;
     st = check_shape(head_dim, v_bits);
     if (st != TQ_OK) return st;
-    if (head_dim != kAttnD) return TQ_ERR_UNSUPPORTED;
     if (batch < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_blocks_per_seq < 0 ||
         num_blocks < 0 || !std::isfinite(scale))
         return TQ_ERR_INVALID_ARG;
@@ -312,16 +310,16 @@ tq_status tq_attn_decode_kv(const void *q_f16, const uint8_t *k_packed, const fl
         !aligned(v_packed, 16) || !aligned(k_norms, 4) || !aligned(v_norms, 4) ||
         !aligned(block_tables, 4) || !aligned(context_lens, 4) || !aligned(workspace, 16))
         return TQ_ERR_MISALIGNED;
-    tq::AttnShape s{batch, num_q_heads, num_kv_heads, k_bits, v_bits, max_blocks_per_seq,
-                    num_blocks};
+    tq::AttnShape s{batch, num_q_heads, num_kv_heads, head_dim, k_bits, v_bits,
+                    max_blocks_per_seq, num_blocks};
     if (!tq::attn_supported(s)) return TQ_ERR_UNSUPPORTED;
     const size_t need = tq::attn_workspace_bytes(s);
     if (need > 0 && (!workspace || workspace_bytes < need)) return TQ_ERR_WORKSPACE;
-    const size_t nout = (size_t)batch * num_q_heads * kAttnD * 2;
+    const size_t nout = (size_t)batch * num_q_heads * head_dim * 2;
     if (overlap(out_f16, nout, q_f16, nout) || overlap(out_f16, nout, workspace, need))
         return TQ_ERR_INVALID_ARG;
-    const CodecConsts kc = make_consts(kAttnD, k_bits, seed);
-    const CodecConsts vc = make_consts(kAttnD, v_bits, seed);
+    const CodecConsts kc = make_consts(head_dim, k_bits, seed);
+    const CodecConsts vc = make_consts(head_dim, v_bits, seed);
     return from_hip(tq::launch_attn(s, kc, vc, q_f16, k_packed, k_norms, v_packed, v_norms,
                                     block_tables, context_lens, scale, out_f16, workspace,
                                     (hipStream_t)stream));

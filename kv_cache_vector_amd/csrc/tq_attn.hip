@@ -61,7 +61,10 @@
 namespace tq {
 namespace {
 
-constexpr int kPartial = 2 + kHeadDim;      // m, l, acc[128] per workspace entry
+// workspace entry per (sequence, query head, split): m, l, acc[head_dim]
+constexpr int partial_floats(int head_dim) { return 2 + head_dim; }
+// waves per kv head of the split kernel (two at head_dim 256)
+constexpr int waves_per_head(int head_dim) { return head_dim > 128 ? 2 : 1; }
 constexpr float kLazy = 8.0f;               // rescale when a score passes m + 8 (base 2)
 constexpr int kMaxSplitTokens = 4096;       // block-table entries of a split staged in LDS
 constexpr int kMWaves = 8;                  // waves per workgroup
@@ -147,7 +150,6 @@ __device__ __forceinline__ f4 mfma(const u32x4 &a, const u32x4 &b, f4 c) {
 // a byte index one v_perm forms the address (byte << 8 | lane offset).
 template <int B>
 struct Side {
-    static constexpr int P = 16 * B;                       // packed bytes per row
     static constexpr int EB = (B == 2) ? 16 : 8;           // bytes per table entry
     static constexpr int NE = (B == 3) ? 64 : 256;         // table entries
     static constexpr int COPIES = 128 / EB;                // lane copies per half row
@@ -187,17 +189,19 @@ __device__ __forceinline__ u32x2 lut8f(const char *tab, uint32_t field, uint32_t
     return *reinterpret_cast<const u32x2 *>(tab + ((field << 8) | laneoff));
 }
 
-// Bits [b, b + 6) of the 96-bit little-endian string w.x, w.y, w.z.
-template <int b>
-__device__ __forceinline__ uint32_t field6(const u32x4 &w) {
+// Bits [b, b + 6) of the little-endian bit string w[0], w[1], ...
+template <int b, int N>
+__device__ __forceinline__ uint32_t field6(const uint32_t (&w)[N]) {
     constexpr int wi = b >> 5, sh = b & 31;
     if constexpr (sh <= 26) return (w[wi] >> sh) & 63u;
     else return __builtin_amdgcn_alignbit(w[wi + 1], w[wi], sh) & 63u;
 }
 
-template <int J, int KB>
-__device__ __forceinline__ u32x4 key_chunk(const char *tab, const u32x4 &kc, uint32_t laneoff) {
-    if constexpr (KB == 4) {             // bytes 2J, 2J+1: dims 4J .. 4J+3
+// A operand of score chunk J: dims 4J .. 4J+3 of the lane's slice of its
+// token, as (c_hi, c_lo) pairs, from the lane's packed key words kc.
+template <int J, int KB, int N>
+__device__ __forceinline__ u32x4 key_chunk(const char *tab, const uint32_t (&kc)[N], uint32_t laneoff) {
+    if constexpr (KB == 4) {             // bytes 2J, 2J+1
         const u32x2 a0 = lut8<(2 * J) & 3>(tab, kc[J >> 1], laneoff);
         const u32x2 a1 = lut8<(2 * J + 1) & 3>(tab, kc[J >> 1], laneoff);
         return u32x4{a0.x, a0.y, a1.x, a1.y};
@@ -210,29 +214,33 @@ __device__ __forceinline__ u32x4 key_chunk(const char *tab, const u32x4 &kc, uin
     }
 }
 
-// One score chain: columns 0-7 carry (q_hi, q_hi) of heads 0-7 and columns
-// 8-15 carry (q_lo, 0) of the same heads (at most 8 query heads per kv head).
-template <int J, int KB>
-__device__ __forceinline__ void score_chunks_paired(const char *tab, const u32x4 &kc,
-                                                    uint32_t laneoff, const u32x4 (&bq)[8],
+// One score chain over NJ chunks: columns 0-7 carry (q_hi, q_hi) of heads
+// 0-7 and columns 8-15 carry (q_lo, 0) of the same heads (at most 8 query
+// heads per kv head).
+template <int J, int NJ, int KB, int N>
+__device__ __forceinline__ void score_chunks_paired(const char *tab, const uint32_t (&kc)[N],
+                                                    uint32_t laneoff, const u32x4 (&bq)[NJ],
                                                     f4 &S) {
     S = mfma(key_chunk<J, KB>(tab, kc, laneoff), bq[J], S);
-    if constexpr (J < 7) score_chunks_paired<J + 1, KB>(tab, kc, laneoff, bq, S);
+    if constexpr (J + 1 < NJ) score_chunks_paired<J + 1, NJ, KB>(tab, kc, laneoff, bq, S);
 }
 
-template <int J, int KB>
-__device__ __forceinline__ void score_chunks(const char *tab, const u32x4 &kc, uint32_t laneoff,
-                                             const u32x4 (&bq1)[8], const u32x4 (&bq2)[8],
+template <int J, int NJ, int KB, int N>
+__device__ __forceinline__ void score_chunks(const char *tab, const uint32_t (&kc)[N], uint32_t laneoff,
+                                             const u32x4 (&bq1)[NJ], const u32x4 (&bq2)[NJ],
                                              f4 &S0, f4 &S1) {
     const u32x4 A = key_chunk<J, KB>(tab, kc, laneoff);
     S0 = mfma(A, bq1[J], S0);
     S1 = mfma(A, bq2[J], S1);
-    if constexpr (J < 7) score_chunks<J + 1, KB>(tab, kc, laneoff, bq1, bq2, S0, S1);
+    if constexpr (J + 1 < NJ) score_chunks<J + 1, NJ, KB>(tab, kc, laneoff, bq1, bq2, S0, S1);
 }
 
-template <int K>
+// Value operand builders: Bv[jj] holds value dim jj of the lane's slice for
+// tokens 4r .. 4r+3, as (c_hi, c_lo) pairs; vc[i] is the lane's packed value
+// bits for token 4r + i.
+template <int K, int NJJ>
 __device__ __forceinline__ void value_bytes4(const char *tab, const uint32_t (&vc)[4],
-                                             uint32_t laneoff, u32x4 (&Bv)[8]) {
+                                             uint32_t laneoff, u32x4 (&Bv)[NJJ]) {
     u32x2 L[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) L[i] = lut8<K>(tab, vc[i], laneoff);
@@ -240,9 +248,9 @@ __device__ __forceinline__ void value_bytes4(const char *tab, const uint32_t (&v
     Bv[2 * K + 1] = u32x4{L[0].y, L[1].y, L[2].y, L[3].y};
 }
 
-template <int K>
+template <int K, int NJJ>
 __device__ __forceinline__ void value_bytes2(const char *tab, const uint32_t (&vc)[4],
-                                             uint32_t laneoff, u32x4 (&Bv)[8]) {
+                                             uint32_t laneoff, u32x4 (&Bv)[NJJ]) {
     u32x4 L[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) L[i] = lut16<K>(tab, vc[i], laneoff);
@@ -250,40 +258,65 @@ __device__ __forceinline__ void value_bytes2(const char *tab, const uint32_t (&v
     for (int t = 0; t < 4; ++t) Bv[4 * K + t] = u32x4{L[0][t], L[1][t], L[2][t], L[3][t]};
 }
 
-// The value operands of the page: Bv[jj] holds dim 8m + jj of tokens
-// 4r .. 4r+3 as (c_hi, c_lo) pairs.  vc[i] is this lane's raw load for token
-// 4r + i; q4 = m % 4.
-template <int VB>
-__device__ __forceinline__ void value_operands(const char *tab, const uint32_t (&vc)[4],
-                                               uint32_t laneoff, int q4, u32x4 (&Bv)[8]) {
-    if constexpr (VB == 4) {             // dword m: byte k holds dims 8m + 2k, +1
-        value_bytes4<0>(tab, vc, laneoff, Bv);
-        value_bytes4<1>(tab, vc, laneoff, Bv);
-        value_bytes4<2>(tab, vc, laneoff, Bv);
-        value_bytes4<3>(tab, vc, laneoff, Bv);
-    } else if constexpr (VB == 2) {      // 16 bits: byte k holds dims 8m + 4k .. +3
-        value_bytes2<0>(tab, vc, laneoff, Bv);
-        value_bytes2<1>(tab, vc, laneoff, Bv);
-    } else {
-        // 24 bits at bit 24m of the row.  Lanes m = 4a .. 4a+3 of a quad loaded
-        // dwords 3a, 3a+1, 3a+2, 3a+2; lane q's field starts in the dword of
-        // lane q-1 (lane 0: its own) at bit 24q mod 32.
+// 3-bit values: v[i] holds the lane's fields (NJJ / 2 fields of two codes)
+// from bit 0 up.
+template <int NJJ>
+__device__ __forceinline__ void value_fields3(const char *tab, const uint32_t (&v)[4],
+                                              uint32_t laneoff, u32x4 (&Bv)[NJJ]) {
+#pragma unroll
+    for (int s = 0; s < NJJ / 2; ++s) {  // field s: dims 2s, 2s+1
+        u32x2 L[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) L[i] = lut8f(tab, (v[i] >> (6 * s)) & 63u, laneoff);
+        Bv[2 * s] = u32x4{L[0].x, L[1].x, L[2].x, L[3].x};
+        Bv[2 * s + 1] = u32x4{L[0].y, L[1].y, L[2].y, L[3].y};
+    }
+}
+
+// The value operands of the page for a slice of NJJ dims per lane column:
+// 4-bit NJJ / 2 bytes, 2-bit NJJ / 4 bytes, 3-bit 3 NJJ / 8 bytes.  vc holds
+// VW words per token as loaded (see the value loads in the split kernel);
+// vsh is the 3-bit field's bit offset within them.
+template <int NJJ, int VB, int VW>
+__device__ __forceinline__ void value_operands(const char *tab, const uint32_t (&vc)[4][VW],
+                                               uint32_t laneoff, int q4, uint32_t vsh,
+                                               u32x4 (&Bv)[NJJ]) {
+    if constexpr (VB == 4) {
+        uint32_t w[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) w[i] = vc[i][0];
+        value_bytes4<0>(tab, w, laneoff, Bv);
+        value_bytes4<1>(tab, w, laneoff, Bv);
+        if constexpr (NJJ == 8) {
+            value_bytes4<2>(tab, w, laneoff, Bv);
+            value_bytes4<3>(tab, w, laneoff, Bv);
+        }
+    } else if constexpr (VB == 2) {
+        uint32_t w[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) w[i] = vc[i][0];
+        value_bytes2<0>(tab, w, laneoff, Bv);
+        if constexpr (NJJ == 8) value_bytes2<1>(tab, w, laneoff, Bv);
+    } else if constexpr (NJJ == 8) {
+        // 24 bits at bit 24m of the slice.  Lanes m = 4a .. 4a+3 of a quad
+        // loaded dwords 3a, 3a+1, 3a+2, 3a+2; lane q's field starts in the
+        // dword of lane q-1 (lane 0: its own) at bit 24q mod 32.
         const uint32_t sh = (24u * (uint32_t)q4) & 31u;
         uint32_t v24[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const uint32_t prev = (uint32_t)__builtin_amdgcn_mov_dpp((int)vc[i], kQuadPrev, 0xF, 0xF, true);
-            const uint32_t lo = q4 == 0 ? vc[i] : prev;
-            v24[i] = __builtin_amdgcn_alignbit(vc[i], lo, sh);
+            const uint32_t prev = (uint32_t)__builtin_amdgcn_mov_dpp((int)vc[i][0], kQuadPrev, 0xF, 0xF, true);
+            const uint32_t lo = q4 == 0 ? vc[i][0] : prev;
+            v24[i] = __builtin_amdgcn_alignbit(vc[i][0], lo, sh);
         }
+        value_fields3<NJJ>(tab, v24, laneoff, Bv);
+    } else {
+        // 12 bits at bit 12m of the slice, inside the two dwords the lane
+        // loaded from the dword that holds its first bit
+        uint32_t v12[4];
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {    // field s: dims 8m + 2s, +1
-            u32x2 L[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) L[i] = lut8f(tab, (v24[i] >> (6 * s)) & 63u, laneoff);
-            Bv[2 * s] = u32x4{L[0].x, L[1].x, L[2].x, L[3].x};
-            Bv[2 * s + 1] = u32x4{L[0].y, L[1].y, L[2].y, L[3].y};
-        }
+        for (int i = 0; i < 4; ++i) v12[i] = __builtin_amdgcn_alignbit(vc[i][VW - 1], vc[i][0], vsh);
+        value_fields3<NJJ>(tab, v12, laneoff, Bv);
     }
 }
 
@@ -292,15 +325,80 @@ __device__ __forceinline__ void value_operands(const char *tab, const uint32_t (
 // and value rows 8-15 belong to heads 0-7 -- so each page takes 8 + 8 matrix
 // products instead of 16 + 16.  Otherwise (9-16 heads) the low halves take a
 // second product per tile.
-template <int KB, int VB, bool PAIRED>
+// Shape of the split kernel's per-lane slices for head dimension D.
+template <int D, int KB, int VB>
+struct Slices {
+    static constexpr int DG = D / 4;                  // score dims per lane row group r
+    static constexpr int NJ = DG / 4;                 // score chunks (4 dims each)
+    static constexpr int KBY = DG * KB / 8;           // key bytes per lane and token
+    // key words per lane: the slice, or at D = 64 and 3 bits (6 bytes at a
+    // 2-byte offset) the two dwords around it
+    static constexpr int KW = (KBY % 4) ? 2 : KBY / 4;
+    static constexpr int VH = D < 128 ? D : 128;      // value dims per wave
+    static constexpr int WPH = D / VH;                // waves per kv head
+    static constexpr int NJJ = VH / 16;               // value dims per lane column
+    // value words per lane and token: one, or at D = 64 and 3 bits (12 bits
+    // at bit 12m) the two dwords around the field
+    static constexpr int VW = (VB == 3 && NJJ == 4) ? 2 : 1;
+    static constexpr int PK = D * KB / 8;             // packed bytes per key row
+    static constexpr int PV = D * VB / 8;
+};
+
+// Loads of the lane's packed key words for one token (n bytes at `off`; at
+// D = 64 and 3 bits the 8 bytes from the dword holding the slice's start).
+template <int KBY, int KW>
+__device__ __forceinline__ void load_key(__amdgpu_buffer_rsrc_t rs, uint32_t off, uint32_t (&kc)[KW]) {
+    if constexpr (KBY == 4) {
+        kc[0] = __builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0);
+    } else if constexpr (KBY == 8 || KBY == 6) {
+        const u32x2 t = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, off, 0, 0));
+        kc[0] = t.x;
+        kc[1] = t.y;
+    } else if constexpr (KBY == 12) {
+        const u32x3 t = __builtin_bit_cast(u32x3, __builtin_amdgcn_raw_buffer_load_b96(rs, off, 0, 0));
+        kc[0] = t.x;
+        kc[1] = t.y;
+        kc[2] = t.z;
+    } else {
+        static_assert(KBY % 16 == 0 || KBY == 24, "key slice size");
+#pragma unroll
+        for (int c = 0; c < KBY / 16; ++c) {
+            const u32x4 t = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off + 16u * c, 0, 0));
+            kc[4 * c] = t.x;
+            kc[4 * c + 1] = t.y;
+            kc[4 * c + 2] = t.z;
+            kc[4 * c + 3] = t.w;
+        }
+        if constexpr (KBY % 16) {
+            const u32x2 t = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, off + 16u * (KBY / 16), 0, 0));
+            kc[KW - 2] = t.x;
+            kc[KW - 1] = t.y;
+        }
+    }
+}
+
+// PAIRED (at most 8 query heads per kv head): the low halves of the split
+// operands ride in the otherwise padded half of each tile -- score columns
+// and value rows 8-15 belong to heads 0-7 -- so each page takes NJ + NJJ
+// matrix products instead of twice that.  Otherwise (9-16 heads) the low
+// halves take a second product per tile.
+//
+// Head dimension D: lane row group r holds score dims D/4 r .. D/4 r + D/4 - 1.
+// Each wave accumulates VH = min(D, 128) value dims; at D = 256 a kv head
+// takes two waves, which both form the full scores and accumulate one half
+// of the value dims each.
+template <int D, int KB, int VB, bool PAIRED>
 __global__ __launch_bounds__(kMThreads) void attn_split_kernel(AttnParams p) {
     using SK = Side<KB>;
     using SV = Side<VB>;
+    using SL = Slices<D, KB, VB>;
+    constexpr int DG = SL::DG, NJ = SL::NJ, NJJ = SL::NJJ, WPH = SL::WPH;
+    constexpr int partial = 2 + D;
     __shared__ __attribute__((aligned(16))) char tab[256 * kLutRow];
     __shared__ int32_t bt_all[kMWaves][kMaxSplitTokens / kAttnBlockSize];
 
-    // The workgroup's waves form p.spw slots of kMWaves / p.spw kv heads;
-    // slot s works on split blockIdx.x * p.spw + s (several splits per
+    // The workgroup's waves form p.spw slots of kMWaves / (WPH p.spw) kv
+    // heads; slot s works on split blockIdx.x * p.spw + s (several splits per
     // workgroup when the cache has fewer kv heads than waves).
     const int b = blockIdx.y;
     int T = p.context_lens[b];
@@ -308,7 +406,7 @@ __global__ __launch_bounds__(kMThreads) void attn_split_kernel(AttnParams p) {
     const int tmax = p.max_blocks * kAttnBlockSize;
     T = T > tmax ? tmax : T;
     if (p.num_blocks <= 0) T = 0;
-    const int hps = kMWaves / p.spw;                          // kv heads per slot
+    const int hps = kMWaves / WPH / p.spw;                    // kv heads per slot
     const int first = blockIdx.x * p.spw;
     if (first * p.split_tokens >= T) return;                 // the whole workgroup is past the context
 
@@ -325,8 +423,9 @@ __global__ __launch_bounds__(kMThreads) void attn_split_kernel(AttnParams p) {
     __syncthreads();
 
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int slot = wave / hps;
-    const int g = blockIdx.z * hps + wave % hps;              // kv head
+    const int unit = wave / WPH, half = wave % WPH;           // kv-head unit, value half
+    const int slot = unit / hps;
+    const int g = blockIdx.z * hps + unit % hps;              // kv head
     const int split = first + slot;
     const int t0 = split * p.split_tokens;
     if (g >= p.hkv || t0 >= T) return;                        // no barrier follows
@@ -342,22 +441,22 @@ __global__ __launch_bounds__(kMThreads) void attn_split_kernel(AttnParams p) {
     const uint32_t lok = (uint32_t)(lane & (SK::COPIES - 1)) * SK::EB;
     const uint32_t lov = kLutRow / 2 + (uint32_t)(lane & (SV::COPIES - 1)) * SV::EB;
 
-    // ---- rotated query, one head per lane column, dims 32r .. 32r+31 ----
-    u32x4 bq1[8], bq2[PAIRED ? 1 : 8];
+    // ---- rotated query, one head per lane column, dims DG r .. DG r + DG - 1 ----
+    u32x4 bq1[NJ], bq2[PAIRED ? 1 : NJ];
     float qsl;
     {
-        float qv[32];
+        float qv[DG];
         const int mq = hv ? hcol : 0;                         // padding columns read head 0, then drop it
-        const uint16_t *qp = p.q + ((size_t)b * p.hq + (size_t)g * grp + mq) * kHeadDim + 32 * r;
+        const uint16_t *qp = p.q + ((size_t)b * p.hq + (size_t)g * grp + mq) * D + DG * r;
 #pragma unroll
-        for (int e = 0; e < 32; ++e) {
+        for (int e = 0; e < DG; ++e) {
             const float v = hv ? half_bits_to_float(qp[e]) : 0.0f;
-            qv[e] = sign_of(p.k, 32 * r + e) ? -v : v;
+            qv[e] = sign_of(p.k, DG * r + e) ? -v : v;
         }
 #pragma unroll
-        for (int s = 1; s < 32; s <<= 1)
+        for (int s = 1; s < DG; s <<= 1)
 #pragma unroll
-            for (int e = 0; e < 32; ++e) {
+            for (int e = 0; e < DG; ++e) {
                 if (e & s) continue;
                 const float a = qv[e], c = qv[e + s];
                 qv[e] = a + c;
@@ -366,14 +465,14 @@ __global__ __launch_bounds__(kMThreads) void attn_split_kernel(AttnParams p) {
 #pragma unroll
         for (int s = 16; s < 64; s <<= 1)
 #pragma unroll
-            for (int e = 0; e < 32; ++e) {
+            for (int e = 0; e < DG; ++e) {
                 const float o = __shfl_xor(qv[e], s);
                 qv[e] = (lane & s) ? (o - qv[e]) : (qv[e] + o);
             }
         // per-head power of two bringing max |q~| to [2^13, 2^14)
         float amax = 0.0f;
 #pragma unroll
-        for (int e = 0; e < 32; ++e) amax = __builtin_fmaxf(amax, __builtin_fabsf(qv[e]));
+        for (int e = 0; e < DG; ++e) amax = __builtin_fmaxf(amax, __builtin_fabsf(qv[e]));
         amax = __builtin_fmaxf(amax, __shfl_xor(amax, 16));
         amax = __builtin_fmaxf(amax, __shfl_xor(amax, 32));
         int ex = amax > 0.0f ? __builtin_amdgcn_frexp_expf(amax) : 14;   // amax in [2^(ex-1), 2^ex)
@@ -381,7 +480,7 @@ __global__ __launch_bounds__(kMThreads) void attn_split_kernel(AttnParams p) {
         const float sc = __builtin_bit_cast(float, (uint32_t)(127 + 14 - ex) << 23);   // 2^(14 - ex)
         qsl = p.qscale / (sc * kLevelScale);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
+        for (int j = 0; j < NJ; ++j) {
             uint32_t w1[4], w2[4];
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
@@ -400,26 +499,31 @@ __global__ __launch_bounds__(kMThreads) void attn_split_kernel(AttnParams p) {
         }
     }
 
-    f4 acc[8];
+    f4 acc[NJJ];
 #pragma unroll
-    for (int jj = 0; jj < 8; ++jj) acc[jj] = f4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int jj = 0; jj < NJJ; ++jj) acc[jj] = f4{0.0f, 0.0f, 0.0f, 0.0f};
     float M = -__builtin_inff();          // base-2 reference of head m (uniform over r)
     float lsum = 0.0f;                    // sum of exp2(s - M) over this lane's tokens
     float vlim = 0.0f;                    // power of two above every value norm seen (wave-uniform)
     float vscale = 0.0f;                  // 2^6 / vlim
 
     // per-lane byte offsets inside one page of this kv head
-    const uint32_t rowk = (uint32_t)p.hkv * SK::P;            // one token of all kv heads
-    const uint32_t rowv = (uint32_t)p.hkv * SV::P;
-    const uint32_t offk = (uint32_t)m * rowk + (uint32_t)g * SK::P + 4u * KB * r;
+    const uint32_t rowk = (uint32_t)p.hkv * SL::PK;           // one token of all kv heads
+    const uint32_t rowv = (uint32_t)p.hkv * SL::PV;
+    const uint32_t kslice = (uint32_t)SL::KBY * r;            // the slice's byte offset in the row
+    const uint32_t offk = (uint32_t)m * rowk + (uint32_t)g * SL::PK + (kslice & ~3u);
+    const uint32_t ksh = (kslice & 3u) * 8u;                  // 3 bits at D = 64: 0 or 16
     const int q4 = m & 3;
+    const uint32_t vhalf = (uint32_t)half * (SL::VH * VB / 8);
+    const uint32_t vsh = (12u * (uint32_t)m) & 31u;           // 3 bits at D = 64
     uint32_t offv[4], offn[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const uint32_t row = (uint32_t)(4 * r + i) * rowv + (uint32_t)g * SV::P;
-        if (VB == 4) offv[i] = row + 4u * m;
-        else if (VB == 2) offv[i] = row + 2u * m;
-        else offv[i] = row + 4u * (3u * (uint32_t)(m >> 2) + (uint32_t)(q4 < 2 ? q4 : 2));
+        const uint32_t row = (uint32_t)(4 * r + i) * rowv + (uint32_t)g * SL::PV + vhalf;
+        if (VB == 4) offv[i] = row + (uint32_t)(NJJ / 2) * m;
+        else if (VB == 2) offv[i] = row + (uint32_t)(NJJ / 4) * m;
+        else if (NJJ == 8) offv[i] = row + 4u * (3u * (uint32_t)(m >> 2) + (uint32_t)(q4 < 2 ? q4 : 2));
+        else offv[i] = row + 4u * ((12u * (uint32_t)m) >> 5);
         offn[i] = ((uint32_t)(4 * r + i) * p.hkv + g) * 4u;
     }
     const uint32_t pagek = kAttnBlockSize * rowk;
@@ -428,10 +532,12 @@ __global__ __launch_bounds__(kMThreads) void attn_split_kernel(AttnParams p) {
 
     // Loads of page pg sit in ring slot pg % R.  The refill for page pg + R
     // is issued at the end of step pg, once the slot has been consumed; its
-    // block number was read from LDS one step earlier.
-    constexpr int R = kMPrefetch + 1;
-    u32x4 rk[R];
-    uint32_t rv[R][4];
+    // block number was read from LDS one step earlier.  At D = 256 the ring
+    // has one slot: a second would not fit the register budget without spills.
+    constexpr int R = (D > 128) ? 1 : kMPrefetch + 1;
+    constexpr int KW = SL::KW, VW = SL::VW;
+    uint32_t rk[R][KW];
+    uint32_t rv[R][4][VW];
     float rkn[R][4], rvn[R][4];
     bool rok[R];
     // The loads are unconditional (a page past the split re-reads the split's
@@ -446,19 +552,20 @@ __global__ __launch_bounds__(kMThreads) void attn_split_kernel(AttnParams p) {
         const __amdgpu_buffer_rsrc_t rsv = page_rsrc(p.vp + (size_t)blk * pagev, pagev);
         const __amdgpu_buffer_rsrc_t rkn_ = page_rsrc(p.kn + (size_t)blk * kAttnBlockSize * p.hkv, pagen);
         const __amdgpu_buffer_rsrc_t rvn_ = page_rsrc(p.vn + (size_t)blk * kAttnBlockSize * p.hkv, pagen);
-        if constexpr (KB == 4) {
-            rk[slot] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsk, offk, 0, 0));
-        } else if constexpr (KB == 2) {
-            const u32x2 t = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rsk, offk, 0, 0));
-            rk[slot] = u32x4{t.x, t.y, 0u, 0u};
-        } else {
-            const u32x3 t = __builtin_bit_cast(u32x3, __builtin_amdgcn_raw_buffer_load_b96(rsk, offk, 0, 0));
-            rk[slot] = u32x4{t.x, t.y, t.z, 0u};
-        }
+        load_key<SL::KBY, KW>(rsk, offk, rk[slot]);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            if constexpr (VB == 2) rv[slot][i] = __builtin_amdgcn_raw_buffer_load_b16(rsv, offv[i], 0, 0);
-            else rv[slot][i] = __builtin_amdgcn_raw_buffer_load_b32(rsv, offv[i], 0, 0);
+            if constexpr (VW == 2) {
+                const u32x2 t = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rsv, offv[i], 0, 0));
+                rv[slot][i][0] = t.x;
+                rv[slot][i][VW - 1] = t.y;
+            } else if constexpr (VB == 2 && NJJ == 4) {
+                rv[slot][i][0] = __builtin_amdgcn_raw_buffer_load_b8(rsv, offv[i], 0, 0);
+            } else if constexpr ((VB == 2 && NJJ == 8) || (VB == 4 && NJJ == 4)) {
+                rv[slot][i][0] = __builtin_amdgcn_raw_buffer_load_b16(rsv, offv[i], 0, 0);
+            } else {
+                rv[slot][i][0] = __builtin_amdgcn_raw_buffer_load_b32(rsv, offv[i], 0, 0);
+            }
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i)
@@ -474,23 +581,32 @@ __global__ __launch_bounds__(kMThreads) void attn_split_kernel(AttnParams p) {
 
     // one page: score tiles, value operands, softmax, value tiles, refill
     auto step = [&](const int pg, const int d) {
+        // the lane's key slice, from bit 0 (3 bits at D = 64: shifted into place)
+        uint32_t kc[KW];
+        if constexpr (SL::KBY % 4) {
+            kc[0] = __builtin_amdgcn_alignbit(rk[d][1], rk[d][0], ksh);
+            kc[KW - 1] = rk[d][1] >> ksh;
+        } else {
+#pragma unroll
+            for (int w = 0; w < KW; ++w) kc[w] = rk[d][w];
+        }
         // scores of tokens 4r .. 4r+3 for head hcol
         f4 S;
         if constexpr (PAIRED) {
             f4 S0 = f4{0.0f, 0.0f, 0.0f, 0.0f};
-            score_chunks_paired<0, KB>(tab, rk[d], lok, bq1, S0);
+            score_chunks_paired<0, NJ, KB>(tab, kc, lok, bq1, S0);
             // column m + (q_lo column m ^ 8): row_ror:8 pairs lanes m and m ^ 8
             // of each 16-lane row, so both columns end with the full score
 #pragma unroll
             for (int i = 0; i < 4; ++i) S[i] = S0[i] + row_ror8(S0[i]);
         } else {
             f4 S0 = f4{0.0f, 0.0f, 0.0f, 0.0f}, S1 = S0;   // two independent chains
-            score_chunks<0, KB>(tab, rk[d], lok, bq1, bq2, S0, S1);
+            score_chunks<0, NJ, KB>(tab, kc, lok, bq1, bq2, S0, S1);
             S = S0 + S1;
         }
         // value codes of the page
-        u32x4 Bv[8];
-        value_operands<VB>(tab, rv[d], lov, q4, Bv);
+        u32x4 Bv[NJJ];
+        value_operands<NJJ, VB, VW>(tab, rv[d], lov, q4, vsh, Bv);
 
         // online softmax in base 2.  Two lazily raised references: M per head
         // (rescale when a score passes M + 8) and a power of two vlim per wave
@@ -541,7 +657,7 @@ __global__ __launch_bounds__(kMThreads) void attn_split_kernel(AttnParams p) {
             for (int i = 0; i < 4; ++i) {
                 const float fi = __shfl(f, PAIRED ? ((4 * r + i) & 7) : (4 * r + i)) * fv;
 #pragma unroll
-                for (int jj = 0; jj < 8; ++jj) acc[jj][i] *= fi;
+                for (int jj = 0; jj < NJJ; ++jj) acc[jj][i] *= fi;
             }
         }
         // before any valid token M is -inf; masked tokens must still give 0
@@ -558,17 +674,17 @@ __global__ __launch_bounds__(kMThreads) void attn_split_kernel(AttnParams p) {
             w1[i] = hh;
             w2[i] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(w - hf));
         }
-        // values: dims 8m + jj of tokens 4r .. 4r+3
+        // values: dims NJJ m + jj of the wave's half, tokens 4r .. 4r+3
         if constexpr (PAIRED) {
             // rows 0-7: (w_hi, w_hi) of heads 0-7; rows 8-15: (w_lo, 0)
             const u32x4 A = lo_col ? u32x4{w2[0], w2[1], w2[2], w2[3]} : u32x4{w1[0], w1[1], w1[2], w1[3]};
 #pragma unroll
-            for (int jj = 0; jj < 8; ++jj) acc[jj] = mfma(A, Bv[jj], acc[jj]);
+            for (int jj = 0; jj < NJJ; ++jj) acc[jj] = mfma(A, Bv[jj], acc[jj]);
         } else {
             const u32x4 A1 = u32x4{w1[0], w1[1], w1[2], w1[3]};
             const u32x4 A2 = u32x4{w2[0], w2[1], w2[2], w2[3]};
 #pragma unroll
-            for (int jj = 0; jj < 8; ++jj) {
+            for (int jj = 0; jj < NJJ; ++jj) {
                 acc[jj] = mfma(A1, Bv[jj], acc[jj]);
                 acc[jj] = mfma(A2, Bv[jj], acc[jj]);
             }
@@ -594,16 +710,17 @@ __global__ __launch_bounds__(kMThreads) void attn_split_kernel(AttnParams p) {
         // rows 4r + i and 4r + i + 8 (lanes l and l ^ 32) are one head's
         // high and low parts
 #pragma unroll
-        for (int jj = 0; jj < 8; ++jj)
+        for (int jj = 0; jj < NJJ; ++jj)
 #pragma unroll
             for (int i = 0; i < 4; ++i) acc[jj][i] += __shfl_xor(acc[jj][i], 32);
     }
     // partial state of head g*grp + h: m and l from lane h, accumulators from
-    // lanes (column c, row h / 4) at register h % 4 -> dims 8c .. 8c+7
+    // lanes (column c, row h / 4) at register h % 4 -> dims NJJ c .. NJJ c + NJJ - 1
+    // of the wave's value half
     const float unscale = vlim / (kLevelScale * 64.0f);     // undo 16 c and 2^6 / vlim
-    float *base = p.ws + (((size_t)b * p.hq + (size_t)g * grp) * p.num_splits + split) * kPartial;
-    const size_t hstride = (size_t)p.num_splits * kPartial;
-    if (r == 0 && hv && !lo_col) {
+    float *base = p.ws + (((size_t)b * p.hq + (size_t)g * grp) * p.num_splits + split) * partial;
+    const size_t hstride = (size_t)p.num_splits * partial;
+    if (r == 0 && hv && !lo_col && half == 0) {
         float *dst = base + (size_t)m * hstride;
         dst[0] = M;
         dst[1] = lsum;
@@ -612,14 +729,18 @@ __global__ __launch_bounds__(kMThreads) void attn_split_kernel(AttnParams p) {
     for (int i = 0; i < 4; ++i) {
         const int h = 4 * r + i;
         if (h >= grp || (PAIRED && r >= 2)) break;
-        float2 *dst = reinterpret_cast<float2 *>(base + (size_t)h * hstride + 2 + 8 * m);   // 8-byte aligned
+        float2 *dst = reinterpret_cast<float2 *>(base + (size_t)h * hstride + 2 + SL::VH * half + NJJ * m);   // 8-byte aligned
 #pragma unroll
-        for (int jj = 0; jj < 8; jj += 2) dst[jj >> 1] = float2(acc[jj][i] * unscale, acc[jj + 1][i] * unscale);
+        for (int jj = 0; jj < NJJ; jj += 2) dst[jj >> 1] = float2(acc[jj][i] * unscale, acc[jj + 1][i] * unscale);
     }
 }
 
 // One wave per (sequence, query head): merge the splits, undo the rotation.
+// Lane l holds coordinates E l .. E l + E - 1 (E = D / 64).
+template <int D>
 __global__ __launch_bounds__(64) void attn_combine_kernel(AttnParams p) {
+    constexpr int E = D / 64;
+    constexpr int partial = 2 + D;
     const int bh = blockIdx.x;
     const int b = bh / p.hq;
     const int lane = threadIdx.x;
@@ -629,14 +750,14 @@ __global__ __launch_bounds__(64) void attn_combine_kernel(AttnParams p) {
     T = T > tmax ? tmax : T;
     if (p.num_blocks <= 0) T = 0;
     const int ns = (T + p.split_tokens - 1) / p.split_tokens;
-    const float *src = p.ws + (size_t)bh * p.num_splits * kPartial;
+    const float *src = p.ws + (size_t)bh * p.num_splits * partial;
 
     // the largest running maximum over the splits (lane s reads split s)
     float mx = -__builtin_inff();
     for (int s0 = 0; s0 < ns; s0 += 64) {
         const int s = s0 + lane;
         if (s < ns) {
-            const float ms = src[(size_t)s * kPartial];
+            const float ms = src[(size_t)s * partial];
             mx = ms > mx ? ms : mx;
         }
     }
@@ -645,73 +766,120 @@ __global__ __launch_bounds__(64) void attn_combine_kernel(AttnParams p) {
         const float other = __shfl_xor(mx, o);
         mx = other > mx ? other : mx;
     }
-    // split weights, then this lane's coordinates 2*lane, 2*lane+1; the
-    // partials of 8 splits are loaded before any of them is accumulated
-    float lsum = 0.0f, a0 = 0.0f, a1 = 0.0f;
+    // split weights, then this lane's coordinates; the partials of 8 splits
+    // are loaded before any of them is accumulated
+    float lsum = 0.0f;
+    float a[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) a[e] = 0.0f;
     for (int s0 = 0; s0 < ns; s0 += 64) {
         const int s = s0 + lane;
         float w = 0.0f;
         if (s < ns) {
-            const float ls = src[(size_t)s * kPartial + 1];
-            w = (ls > 0.0f) ? __builtin_amdgcn_exp2f(src[(size_t)s * kPartial] - mx) : 0.0f;
+            const float ls = src[(size_t)s * partial + 1];
+            w = (ls > 0.0f) ? __builtin_amdgcn_exp2f(src[(size_t)s * partial] - mx) : 0.0f;
             lsum += w * ls;
         }
         const int cnt = (ns - s0 < 64) ? ns - s0 : 64;
         for (int j0 = 0; j0 < cnt; j0 += 8) {
-            float2 e[8];
+            float ev[8][E];
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
                 const int j = (j0 + u < cnt) ? j0 + u : j0;          // in range; weight 0 below
-                e[u] = *reinterpret_cast<const float2 *>(src + (size_t)(s0 + j) * kPartial + 2 + 2 * lane);
+                const float *q = src + (size_t)(s0 + j) * partial + 2 + E * lane;
+                if constexpr (E == 1) {
+                    ev[u][0] = *q;
+                } else {
+                    // entries are 4 (2 + D) bytes, so only 8-byte alignment holds
+#pragma unroll
+                    for (int e = 0; e < E; e += 2) {
+                        const float2 v = *reinterpret_cast<const float2 *>(q + e);
+                        ev[u][e] = v.x;
+                        ev[u][e + 1] = v.y;
+                    }
+                }
             }
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
                 float wj = __builtin_bit_cast(
                     float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), (j0 + u) & 63));
                 wj = (j0 + u < cnt) ? wj : 0.0f;
-                a0 = __builtin_fmaf(wj, e[u].x, a0);
-                a1 = __builtin_fmaf(wj, e[u].y, a1);
+#pragma unroll
+                for (int e = 0; e < E; ++e) a[e] = __builtin_fmaf(wj, ev[u][e], a[e]);
             }
         }
     }
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) lsum += __shfl_xor(lsum, o);
     const float inv = (lsum > 0.0f) ? 1.0f / lsum : 0.0f;
-    // inverse transform: x = D H acc / 128 -- coordinate bit 0 in registers,
-    // bits 1..6 across lanes
-    float x0 = (a0 + a1) * inv, x1 = (a0 - a1) * inv;
+    // inverse transform: x = D H acc / D -- the low log2(E) coordinate bits
+    // in registers, the next 6 across lanes
+    float x[E];
 #pragma unroll
-    for (int s = 1; s < 64; s <<= 1) {
-        const float o0 = __shfl_xor(x0, s), o1 = __shfl_xor(x1, s);
-        x0 = (lane & s) ? (o0 - x0) : (x0 + o0);
-        x1 = (lane & s) ? (o1 - x1) : (x1 + o1);
+    for (int e = 0; e < E; ++e) x[e] = a[e] * inv;
+#pragma unroll
+    for (int st = 1; st < E; st <<= 1)
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            if (e & st) continue;
+            const float u = x[e], v = x[e + st];
+            x[e] = u + v;
+            x[e + st] = u - v;
+        }
+#pragma unroll
+    for (int s = 1; s < 64; s <<= 1)
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            const float o = __shfl_xor(x[e], s);
+            x[e] = (lane & s) ? (o - x[e]) : (x[e] + o);
+        }
+    uint16_t hv[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        float v = x[e] * (1.0f / D);
+        if (sign_of(p.k, E * lane + e)) v = -v;
+        hv[e] = __builtin_bit_cast(uint16_t, (_Float16)v);
     }
-    const int i0 = 2 * lane, i1 = 2 * lane + 1;
-    x0 *= (1.0f / kHeadDim);
-    x1 *= (1.0f / kHeadDim);
-    if (sign_of(p.k, i0)) x0 = -x0;
-    if (sign_of(p.k, i1)) x1 = -x1;
-    const _Float16 h0 = (_Float16)x0, h1 = (_Float16)x1;
-    uint16_t *o = p.out + (size_t)bh * kHeadDim;
-    const uint32_t packed2 = (uint32_t)__builtin_bit_cast(uint16_t, h0) |
-                             ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
-    reinterpret_cast<uint32_t *>(o)[lane] = packed2;
+    uint16_t *o = p.out + (size_t)bh * D + E * lane;
+    if constexpr (E == 1) {
+        o[0] = hv[0];
+    } else {
+#pragma unroll
+        for (int e = 0; e < E; e += 2)
+            reinterpret_cast<uint32_t *>(o)[e >> 1] = (uint32_t)hv[e] | ((uint32_t)hv[e + 1] << 16);
+    }
 }
 
 bool bits_ok(int b) { return b == 2 || b == 3 || b == 4; }
+
+// The split kernel for (D, KB, VB); head_dim 256 has the paired form only
+// (attn_supported keeps its group size at 8 or below).
+template <int D, int KB, int VB>
+void launch_split(bool paired, dim3 grid, dim3 block, hipStream_t stream, const AttnParams &p) {
+    if constexpr (D <= 128) {
+        if (paired) hipLaunchKernelGGL((attn_split_kernel<D, KB, VB, true>), grid, block, 0, stream, p);
+        else hipLaunchKernelGGL((attn_split_kernel<D, KB, VB, false>), grid, block, 0, stream, p);
+    } else {
+        hipLaunchKernelGGL((attn_split_kernel<D, KB, VB, true>), grid, block, 0, stream, p);
+    }
+}
 
 }  // namespace
 
 bool attn_supported(const AttnShape &s) {
     if (s.num_kv_heads <= 0 || s.num_q_heads % s.num_kv_heads) return false;
+    if (s.head_dim != 64 && s.head_dim != 128 && s.head_dim != 256) return false;
     const int grp = s.num_q_heads / s.num_kv_heads;
-    return grp >= 1 && grp <= kAttnMaxGroup && bits_ok(s.k_bits) && bits_ok(s.v_bits);
+    // head_dim 256 runs the paired form only (its two-product form spills)
+    const int gmax = s.head_dim > 128 ? kAttnMaxGroupD256 : kAttnMaxGroup;
+    return grp >= 1 && grp <= gmax && bits_ok(s.k_bits) && bits_ok(s.v_bits);
 }
 
 int attn_split_tokens(const AttnShape &s) {
-    // one wave per (sequence, kv head) and split; about kMTargetWaves waves
+    // waves_per_head waves per (sequence, kv head) and split; about
+    // kMTargetWaves waves
     const int ctx = s.max_blocks * kAttnBlockSize;
-    const int units = s.batch * s.num_kv_heads;
+    const int units = s.batch * s.num_kv_heads * waves_per_head(s.head_dim);
     const int per_seq = units > 0 ? (kMTargetWaves + units - 1) / units : 1;
     int st = (ctx + per_seq - 1) / per_seq;
     st = (st + kAttnBlockSize - 1) / kAttnBlockSize * kAttnBlockSize;
@@ -727,7 +895,8 @@ int attn_num_splits(const AttnShape &s) {
 }
 
 size_t attn_workspace_bytes(const AttnShape &s) {
-    return (size_t)s.batch * s.num_q_heads * attn_num_splits(s) * kPartial * sizeof(float);
+    return (size_t)s.batch * s.num_q_heads * attn_num_splits(s) * partial_floats(s.head_dim) *
+           sizeof(float);
 }
 
 hipError_t launch_attn(const AttnShape &s, const CodecConsts &kc, const CodecConsts &vc,
@@ -753,34 +922,44 @@ hipError_t launch_attn(const AttnShape &s, const CodecConsts &kc, const CodecCon
     p.split_tokens = attn_split_tokens(s);
     p.num_splits = attn_num_splits(s);
     p.num_blocks = s.num_blocks;
-    p.qscale = scale * 1.4426950408889634f / kHeadDim;
+    p.qscale = scale * 1.4426950408889634f / s.head_dim;
     p.k = kc;
     p.v = vc;
-    // fewer kv heads than waves: the spare waves take further splits
-    p.spw = (s.num_kv_heads < kMWaves && kMWaves % s.num_kv_heads == 0) ? kMWaves / s.num_kv_heads : 1;
-    const int hps = kMWaves / p.spw;
+    // fewer kv heads than kv-head units: the spare waves take further splits
+    const int hpw = kMWaves / waves_per_head(s.head_dim);     // kv heads per workgroup
+    p.spw = (s.num_kv_heads < hpw && hpw % s.num_kv_heads == 0) ? hpw / s.num_kv_heads : 1;
+    const int hps = hpw / p.spw;
     const dim3 grid((p.num_splits + p.spw - 1) / p.spw, s.batch, (s.num_kv_heads + hps - 1) / hps);
     const dim3 block(kMThreads);
     const bool paired = s.num_q_heads / s.num_kv_heads <= 8;
-#define TQ_SPLIT(KB, VB)                                                                            \
-    if (paired) hipLaunchKernelGGL((attn_split_kernel<KB, VB, true>), grid, block, 0, stream, p);   \
-    else hipLaunchKernelGGL((attn_split_kernel<KB, VB, false>), grid, block, 0, stream, p)
-    switch (s.k_bits * 10 + s.v_bits) {
-        case 44: TQ_SPLIT(4, 4); break;
-        case 43: TQ_SPLIT(4, 3); break;
-        case 42: TQ_SPLIT(4, 2); break;
-        case 34: TQ_SPLIT(3, 4); break;
-        case 33: TQ_SPLIT(3, 3); break;
-        case 32: TQ_SPLIT(3, 2); break;
-        case 24: TQ_SPLIT(2, 4); break;
-        case 23: TQ_SPLIT(2, 3); break;
-        case 22: TQ_SPLIT(2, 2); break;
+#define TQ_WIDTHS(D)                                                                                 \
+    switch (s.k_bits * 10 + s.v_bits) {                                                              \
+        case 44: launch_split<D, 4, 4>(paired, grid, block, stream, p); break;                       \
+        case 43: launch_split<D, 4, 3>(paired, grid, block, stream, p); break;                       \
+        case 42: launch_split<D, 4, 2>(paired, grid, block, stream, p); break;                       \
+        case 34: launch_split<D, 3, 4>(paired, grid, block, stream, p); break;                       \
+        case 33: launch_split<D, 3, 3>(paired, grid, block, stream, p); break;                       \
+        case 32: launch_split<D, 3, 2>(paired, grid, block, stream, p); break;                       \
+        case 24: launch_split<D, 2, 4>(paired, grid, block, stream, p); break;                       \
+        case 23: launch_split<D, 2, 3>(paired, grid, block, stream, p); break;                       \
+        case 22: launch_split<D, 2, 2>(paired, grid, block, stream, p); break;                       \
+        default: return hipErrorInvalidValue;                                                        \
+    }
+    switch (s.head_dim) {
+        case 64: TQ_WIDTHS(64) break;
+        case 128: TQ_WIDTHS(128) break;
+        case 256: TQ_WIDTHS(256) break;
         default: return hipErrorInvalidValue;
     }
-#undef TQ_SPLIT
+#undef TQ_WIDTHS
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(attn_combine_kernel, dim3(s.batch * s.num_q_heads), dim3(64), 0, stream, p);
+    const dim3 cgrid(s.batch * s.num_q_heads);
+    switch (s.head_dim) {
+        case 64: hipLaunchKernelGGL(attn_combine_kernel<64>, cgrid, dim3(64), 0, stream, p); break;
+        case 128: hipLaunchKernelGGL(attn_combine_kernel<128>, cgrid, dim3(64), 0, stream, p); break;
+        default: hipLaunchKernelGGL(attn_combine_kernel<256>, cgrid, dim3(64), 0, stream, p); break;
+    }
     return hipGetLastError();
 }
 

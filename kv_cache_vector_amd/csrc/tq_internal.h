@@ -7,8 +7,7 @@
 
 namespace tq {
 
-constexpr int kHeadDim = 128;      // the attention kernels' head dimension
-constexpr int kMaxHeadDim = 256;   // the codec kernels take 64, 128 and 256
+constexpr int kMaxHeadDim = 256;   // the kernels take head_dim 64, 128 and 256
 
 // Everything the kernels need that is fixed by (bits, seed).  Passed by value
 // as a kernel argument, so the library needs no device allocation.
@@ -48,14 +47,15 @@ hipError_t launch_decode(int head_dim, int bits, const uint8_t *packed, const fl
 
 constexpr int kAttnBlockSize = 16;   // tokens per cache page
 constexpr int kAttnMaxGroup = 16;    // query heads per kv head
+constexpr int kAttnMaxGroupD256 = 8; // the same at head_dim 256
 
 struct AttnShape {
-    int batch, num_q_heads, num_kv_heads, k_bits, v_bits, max_blocks;
+    int batch, num_q_heads, num_kv_heads, head_dim, k_bits, v_bits, max_blocks;
     int64_t num_blocks;
 };
 
-// Whether the split kernel serves this shape (1..16 query heads per kv head,
-// 2..4-bit keys and values).
+// Whether the split kernel serves this shape (head_dim 64, 128 or 256, 1..16
+// query heads per kv head, 2..4-bit keys and values).
 bool attn_supported(const AttnShape &s);
 
 // Tokens handled by one wave of the split kernel, and the number of splits of

@@ -16,8 +16,8 @@ operators).
                                              v_bits=-1) -> out
       (v_bits: width of the value codes; -1 means the same as the keys')
 
-The codec operators take head_dim 64, 128 or 256 (read off the tensors'
-last dimension); the attention operator takes head_dim 128.
+Every operator takes head_dim 64, 128 or 256, read off the tensors' last
+dimension (the attention operator: at most 8 query heads per kv head at 256).
 Seeds are unsigned 64-bit values; the schema's int is signed, so seeds at or
 above 2^63 travel as their two's-complement int64 and are converted back.
 The real kernels take GPU tensors only and call libtq on the current stream;
@@ -29,7 +29,6 @@ import torch
 
 from . import _lib
 
-HEAD_DIM = 128                 # the attention operator's head dimension
 CODEC_HEAD_DIMS = (64, 128, 256)
 _U64 = 1 << 64
 
@@ -171,11 +170,11 @@ def tq_attn_decode(q: torch.Tensor, k_packed: torch.Tensor, k_norms: torch.Tenso
                     (block_tables, "block_tables"), (context_lens, "context_lens")):
         _gpu(t, name)
     vb = bits if v_bits < 0 else v_bits
-    P = _packed_dim(HEAD_DIM, bits)
-    PV = _packed_dim(HEAD_DIM, vb)
-    if q.dim() != 3 or q.shape[-1] != HEAD_DIM or q.dtype != torch.float16:
-        raise ValueError("query must be float16 [batch, num_q_heads, %d]" % HEAD_DIM)
-    B, Hq, _ = q.shape
+    if q.dim() != 3 or q.dtype != torch.float16:
+        raise ValueError("query must be float16 [batch, num_q_heads, head_dim]")
+    B, Hq, D = q.shape
+    P = _packed_dim(D, bits)
+    PV = _packed_dim(D, vb)
     if k_packed.dim() != 4:
         raise ValueError("k_packed must be [num_blocks, block_size, num_kv_heads, P]")
     nblk, bs, hkv, Pk = k_packed.shape
@@ -195,12 +194,12 @@ def tq_attn_decode(q: torch.Tensor, k_packed: torch.Tensor, k_norms: torch.Tenso
     block_tables, context_lens = block_tables.contiguous(), context_lens.contiguous()
     maxb = block_tables.shape[1]
     out = torch.empty_like(q)
-    nbytes = _lib.tq_attn_workspace_bytes(B, Hq, hkv, HEAD_DIM, bs, maxb)
+    nbytes = _lib.tq_attn_workspace_bytes(B, Hq, hkv, D, bs, maxb)
     ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
     _lib.check(_lib.tq_attn_decode_kv(
         q.data_ptr(), k_packed.data_ptr(), k_norms.data_ptr(), v_packed.data_ptr(),
         v_norms.data_ptr(), block_tables.data_ptr(), context_lens.data_ptr(), B, Hq, hkv,
-        HEAD_DIM, bits, vb, _seed_u64(seed), bs, maxb, nblk, float(scale), out.data_ptr(),
+        D, bits, vb, _seed_u64(seed), bs, maxb, nblk, float(scale), out.data_ptr(),
         ws.data_ptr(), ws.numel(), _stream(q.device)), "tq_attn_decode_kv")
     return out
 
@@ -208,6 +207,6 @@ def tq_attn_decode(q: torch.Tensor, k_packed: torch.Tensor, k_norms: torch.Tenso
 @tq_attn_decode.register_fake
 def _(q, k_packed, k_norms, v_packed, v_norms, block_tables, context_lens, bits, seed, scale,
       v_bits=-1):
-    _packed_dim(HEAD_DIM, bits)
-    _packed_dim(HEAD_DIM, bits if v_bits < 0 else v_bits)
+    _packed_dim(q.shape[-1], bits)
+    _packed_dim(q.shape[-1], bits if v_bits < 0 else v_bits)
     return torch.empty_like(q)

@@ -30,7 +30,7 @@ def _require_gpu(t: torch.Tensor, name: str) -> None:
 
 class TurboQuant:
     """TurboQuant codec: [..., head_dim] fp16 <-> ([..., head_dim*bits/8] uint8, [...] f32),
-    head_dim 64, 128 or 256 (the paged attention takes 128)."""
+    head_dim 64, 128 or 256."""
 
     def __init__(self, head_dim: int = HEAD_DIM, bits: int = 4, seed: int = 42,
                  device="cuda"):
@@ -142,9 +142,6 @@ class TQPagedAttention:
         self.v_tq = tq if v_tq is None else v_tq
         if self.v_tq.seed != tq.seed or self.v_tq.head_dim != tq.head_dim:
             raise ValueError("keys and values must share head_dim and seed")
-        if tq.head_dim != torch_ops.HEAD_DIM:
-            raise ValueError("the attention kernels take head_dim %d (got %d)"
-                             % (torch_ops.HEAD_DIM, tq.head_dim))
         self.num_query_heads = num_query_heads
         self.scale = (1.0 / math.sqrt(tq.head_dim)) if scale is None else float(scale)
         self._ws = {}

@@ -90,21 +90,22 @@ def llama70b_layer(layer: int, tokens: int = 131072, heads: int = 8) -> np.ndarr
 # ---------------------------------------------------------------------------
 
 def attn_kv_rows(b: int, g: int, tokens: int, seed: int = 500, outlier_p: float = 0.01,
-                 outlier_factor: float = 15.0) -> np.ndarray:
-    """K and V of sequence b, kv head g in token order: [2, tokens, 128] fp16,
-    N(0,1) with Bernoulli(outlier_p) outlier channels (x outlier_factor) fixed
-    for the (sequence, kv head).  Seeded by (seed, b, g) alone, so any one
-    stream can be regenerated without the others."""
+                 outlier_factor: float = 15.0, head_dim: int = HEAD_DIM) -> np.ndarray:
+    """K and V of sequence b, kv head g in token order: [2, tokens, head_dim]
+    fp16, N(0,1) with Bernoulli(outlier_p) outlier channels (x outlier_factor)
+    fixed for the (sequence, kv head).  Seeded by (seed, b, g) alone, so any
+    one stream can be regenerated without the others."""
     rng = np.random.default_rng([seed, b, g])
-    mask = rng.random((2, 1, HEAD_DIM)) < outlier_p
-    kv = rng.standard_normal((2, tokens, HEAD_DIM), dtype=np.float32)
+    mask = rng.random((2, 1, head_dim)) < outlier_p
+    kv = rng.standard_normal((2, tokens, head_dim), dtype=np.float32)
     kv = np.where(mask, kv * np.float32(outlier_factor), kv)
     return _f16(kv)
 
 
-def attn_query(batch: int, num_q_heads: int, seed: int = 500) -> np.ndarray:
+def attn_query(batch: int, num_q_heads: int, seed: int = 500,
+               head_dim: int = HEAD_DIM) -> np.ndarray:
     rng = np.random.default_rng([seed, 1 << 30])
-    return _f16(rng.standard_normal((batch, num_q_heads, HEAD_DIM), dtype=np.float32))
+    return _f16(rng.standard_normal((batch, num_q_heads, head_dim), dtype=np.float32))
 
 
 def attn_block_tables(batch: int, max_blocks: int, num_blocks: int,
@@ -140,10 +141,10 @@ def scatter_pages(pages: np.ndarray, rows: np.ndarray, block_table_row: np.ndarr
 def attn_workload(batch: int = 16, num_q_heads: int = 32, num_kv_heads: int = 8,
                   context: int = 32768, block_size: int = 16, seed: int = 500,
                   perm_seed: int = 501, ragged: bool = False, outlier_p: float = 0.01,
-                  outlier_factor: float = 15.0, extra_blocks: int = 0):
+                  outlier_factor: float = 15.0, extra_blocks: int = 0, head_dim: int = HEAD_DIM):
     """Returns a dict with
-      q            [B, Hq, 128] fp16, N(0,1)
-      k, v         [num_blocks, block_size, Hkv, 128] fp16 -- the cache content
+      q            [B, Hq, head_dim] fp16, N(0,1)
+      k, v         [num_blocks, block_size, Hkv, head_dim] fp16 -- the cache content
                    in physical (paged) order (attn_kv_rows per sequence and kv
                    head; pages no sequence uses hold N(0,1) filler)
       block_tables [B, max_blocks] int32 -- a seeded random permutation of the
@@ -152,14 +153,15 @@ def attn_workload(batch: int = 16, num_q_heads: int = 32, num_kv_heads: int = 8,
     """
     max_blocks = (context + block_size - 1) // block_size
     nblk = batch * max_blocks + extra_blocks
-    q = attn_query(batch, num_q_heads, seed)
+    q = attn_query(batch, num_q_heads, seed, head_dim)
     bt = attn_block_tables(batch, max_blocks, nblk, perm_seed)
     filler = np.random.default_rng([seed, 1 << 29])
-    pages = filler.standard_normal((2, nblk, block_size, num_kv_heads, HEAD_DIM),
+    pages = filler.standard_normal((2, nblk, block_size, num_kv_heads, head_dim),
                                    dtype=np.float32).astype(np.float16)
     for b in range(batch):
         for g in range(num_kv_heads):
-            kv = attn_kv_rows(b, g, max_blocks * block_size, seed, outlier_p, outlier_factor)
+            kv = attn_kv_rows(b, g, max_blocks * block_size, seed, outlier_p, outlier_factor,
+                              head_dim)
             scatter_pages(pages[0], kv[0], bt[b], g, block_size)
             scatter_pages(pages[1], kv[1], bt[b], g, block_size)
     cl = attn_context_lens(batch, context, ragged, block_size, seed)

@@ -425,11 +425,11 @@ def check_decode_definition(o, seed=43, d=D):
 # paged decode attention
 # ---------------------------------------------------------------------------
 
-def small_attn_case(o, B=2, Hq=8, Hkv=2, T=37, bs=16, bits=4, seed=51, ragged=True):
+def small_attn_case(o, B=2, Hq=8, Hkv=2, T=37, bs=16, bits=4, seed=51, ragged=True, d=D):
     from kv_cache_vector_amd import workloads as w
     wl = w.attn_workload(batch=B, num_q_heads=Hq, num_kv_heads=Hkv, context=T,
                          block_size=bs, seed=seed, perm_seed=seed + 1, ragged=ragged,
-                         extra_blocks=3)
+                         extra_blocks=3, head_dim=d)
     kp, kn = o.encode(wl["k"], bits, 0)
     vp, vn = o.encode(wl["v"], bits, 0)
     wl.update(kp=kp, kn=kn, vp=vp, vn=vn, bits=bits)
@@ -442,7 +442,7 @@ def _attn(o, wl, q=None, cl=None, bt=None, kp=None, kn=None, vp=None, vn=None, s
                          wl["vp"] if vp is None else vp, wl["vn"] if vn is None else vn,
                          wl["block_tables"] if bt is None else bt,
                          wl["context_lens"] if cl is None else cl, wl["num_kv_heads"],
-                         wl["bits"], 0, 1 / math.sqrt(D) if scale is None else scale,
+                         wl["bits"], 0, 1 / math.sqrt(q.shape[-1]) if scale is None else scale,
                          want_f64=True)
 
 
@@ -450,7 +450,8 @@ def _dequant_rows(o, wl, which, b, g):
     """Decoded (double) rows of sequence b, kv head g, in token order."""
     bs = wl["block_size"]
     T = int(wl["context_lens"][b])
-    P = D * wl["bits"] // 8
+    d = wl["q"].shape[-1]
+    P = d * wl["bits"] // 8
     pk = wl["kp" if which == "k" else "vp"]
     nm = wl["kn" if which == "k" else "vn"]
     rows_p = np.zeros((T, P), np.uint8)
@@ -459,17 +460,18 @@ def _dequant_rows(o, wl, which, b, g):
         blk = wl["block_tables"][b, j // bs]
         rows_p[j] = pk[blk, j % bs, g]
         rows_n[j] = nm[blk, j % bs, g]
-    _, xh = o.decode(rows_p, rows_n, D, wl["bits"], 0, want_f64=True)
+    _, xh = o.decode(rows_p, rows_n, d, wl["bits"], 0, want_f64=True)
     return xh
 
 
-def check_attn_rotated_domain_identity(o):
+def check_attn_rotated_domain_identity(o, d=D, bits_list=(4, 3, 2)):
     """Score and accumulate in the rotated domain (q rotated once, K and V
     used as codebook values, one inverse rotation at the end) -- the fused
     path the pages describe -- equals the plain definition."""
+    D = d
     H = sl.hadamard(D).astype(np.float64)
-    for bits in (4, 3, 2):
-        wl = small_attn_case(o, bits=bits)
+    for bits in bits_list:
+        wl = small_attn_case(o, bits=bits, d=D)
         _, of = _attn(o, wl)
         c, _ = o.codebook(bits)
         s = o.signs(0, D).astype(np.float64)
@@ -495,8 +497,8 @@ def check_attn_rotated_domain_identity(o):
                 assert np.allclose(of[b, h], ref, rtol=0, atol=1e-10), (bits, b, h)
 
 
-def check_attn_special_cases(o):
-    wl = small_attn_case(o, B=4, T=40)
+def check_attn_special_cases(o, d=D):
+    wl = small_attn_case(o, B=4, T=40, d=d)
     B, Hq, _ = wl["q"].shape
     grp = Hq // wl["num_kv_heads"]
     # context_len = 1: the output is the decoded first value row
@@ -662,6 +664,16 @@ def check_head_dims(o):
     check_mse_head_dim(o, 256, 12000)
 
 
+def check_attn_head_dims(o):
+    """Attention at head_dim 64 and 256: the rotated-domain computation
+    (with the d-point Hadamard matrix and the first d signs) equals the plain
+    definition, and the special cases (context 1, q = 0, equal keys, context
+    0) hold."""
+    for d in (64, 256):
+        check_attn_rotated_domain_identity(o, d=d, bits_list=(4, 3))
+        check_attn_special_cases(o, d=d)
+
+
 ALL_CHECKS = [
     check_half_to_double, check_double_to_half, check_splitmix64, check_signs,
     check_hadamard, check_rotation_unit_vectors, check_rotation_norm,
@@ -672,5 +684,5 @@ ALL_CHECKS = [
     check_scale_invariance, check_negation, check_zero_vector, check_reencode_fixed_point,
     check_decode_definition, check_attn_rotated_domain_identity, check_attn_special_cases,
     check_attn_paging_invariance, check_attn_bruteforce_tiny, check_attn_gqa_grouping,
-    check_attn_mixed_widths, check_head_dims,
+    check_attn_mixed_widths, check_head_dims, check_attn_head_dims,
 ]

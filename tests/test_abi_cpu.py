@@ -147,6 +147,11 @@ def test_attention_argument_errors(L):
     assert ws > 0 and ws % 16 == 0
     assert L.tq_attn_workspace_bytes(16, 32, 8, 96, 16, 2048) == 0
     assert L.tq_attn_workspace_bytes(16, 30, 8, 128, 16, 2048) == 0
+    # one f32 entry of 2 + head_dim floats per (sequence, query head, split)
+    for d in (64, 256):
+        wd = L.tq_attn_workspace_bytes(16, 32, 8, d, 16, 2048)
+        assert wd > 0 and wd % 16 == 0
+        assert wd % (16 * 32 * (2 + d) * 4) == 0
     a = L.tq_attn_decode
 
     def call(**kw):
@@ -161,7 +166,11 @@ def test_attention_argument_errors(L):
                  args["out"], args["ws"], args["wsb"], None)
 
     assert call(bits=5) == UNSUP
-    assert call(d=64) == UNSUP
+    assert call(d=96) == UNSUP
+    assert call(d=512) == UNSUP
+    assert call(d=64, batch=0) == OK
+    assert call(d=256, hq=8 * 9) == UNSUP          # head_dim 256: at most 8 query heads per kv head
+    assert call(d=256, hq=8 * 8, batch=0) == OK
     assert call(bs=32) == UNSUP
     assert call(hq=30) == INVAL
     assert call(hq=8 * 17) == UNSUP                 # 17 query heads per kv head
@@ -191,7 +200,8 @@ def test_attention_argument_errors(L):
 
     assert call_kv(4, 5) == UNSUP
     assert call_kv(1, 2) == UNSUP
-    assert call_kv(4, 2, d=64) == UNSUP
+    assert call_kv(4, 2, d=96) == UNSUP
+    assert call_kv(4, 2, d=64, batch=0) == OK
     assert call_kv(4, 2, batch=0) == OK
     assert call_kv(2, 4, q=None) == INVAL
     assert call_kv(3, 4, wsb=ws - 16) == WS

@@ -30,10 +30,11 @@ def dev():
 def oracle_encode_parallel(x, bits, seed, workers=16):
     """Oracle encode of many rows, split into contiguous chunks over threads
     (the ctypes call releases the GIL)."""
-    x2 = x.reshape(-1, D)
+    d = x.shape[-1]
+    x2 = x.reshape(-1, d)
     n = x2.shape[0]
     chunks = [(i, min(n, i + 65536)) for i in range(0, n, 65536)]
-    packed = np.empty((n, D * bits // 8), np.uint8)
+    packed = np.empty((n, d * bits // 8), np.uint8)
     norms = np.empty(n, np.float32)
 
     def job(c):
@@ -43,16 +44,17 @@ def oracle_encode_parallel(x, bits, seed, workers=16):
     with ThreadPoolExecutor(workers) as ex:
         list(ex.map(job, chunks))
     lead = x.shape[:-1]
-    return packed.reshape(lead + (D * bits // 8,)), norms.reshape(lead)
+    return packed.reshape(lead + (d * bits // 8,)), norms.reshape(lead)
 
 
 def run_attn(dev, what, bits=4, B=3, Hq=8, Hkv=2, T=37, ragged=True, seed=0, scale=None,
-             extra_blocks=2, sel=None, pad=None, v_bits=None):
+             extra_blocks=2, sel=None, pad=None, v_bits=None, d=D):
     vb = bits if v_bits is None else v_bits
-    P.log("[attn] %s: B=%d Hq=%d Hkv=%d T=%d bits=%d/%d ragged=%s" % (what, B, Hq, Hkv, T, bits,
-                                                                      vb, ragged))
+    P.log("[attn] %s: B=%d Hq=%d Hkv=%d T=%d d=%d bits=%d/%d ragged=%s"
+          % (what, B, Hq, Hkv, T, d, bits, vb, ragged))
     wl = W.attn_workload(batch=B, num_q_heads=Hq, num_kv_heads=Hkv, context=T, seed=700 + T,
-                         perm_seed=701 + T, ragged=ragged, extra_blocks=extra_blocks)
+                         perm_seed=701 + T, ragged=ragged, extra_blocks=extra_blocks,
+                         head_dim=d)
     kp, kn = oracle_encode_parallel(wl["k"], bits, seed)
     vp, vn = oracle_encode_parallel(wl["v"], vb, seed)
     bt = wl["block_tables"].copy()
@@ -61,9 +63,9 @@ def run_attn(dev, what, bits=4, B=3, Hq=8, Hkv=2, T=37, ragged=True, seed=0, sca
         for b in range(B):
             used = (int(cl[b]) + 15) // 16
             bt[b, used:] = pad
-    sc = 1.0 / math.sqrt(D) if scale is None else scale
-    tq = TurboQuant(D, bits, seed, dev)
-    attn = TQPagedAttention(tq, Hq, scale=sc, v_tq=TurboQuant(D, vb, seed, dev))
+    sc = 1.0 / math.sqrt(d) if scale is None else scale
+    tq = TurboQuant(d, bits, seed, dev)
+    attn = TQPagedAttention(tq, Hq, scale=sc, v_tq=TurboQuant(d, vb, seed, dev))
     t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
     out = attn.forward(t(wl["q"]), t(kp), t(kn), t(vp), t(vn), t(bt), t(cl))
     torch.cuda.synchronize()
@@ -107,6 +109,42 @@ def test_widths_gqa_16(dev, bits):
 @pytest.mark.parametrize("T", [1, 2, 15, 16, 17, 255, 256, 257, 1000, 1500])
 def test_context_lengths(dev, T):
     run_attn(dev, "T=%d" % T, B=4, Hq=32, Hkv=8, T=T, ragged=(T > 3))
+
+
+# ---------------------------------------------------------------------------
+# head_dim 64 and 256 (256: at most 8 query heads per kv head)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("d", [64, 256])
+@pytest.mark.parametrize("bits", [4, 3, 2])
+def test_head_dim_small(dev, d, bits):
+    run_attn(dev, "d=%d b%d" % (d, bits), bits=bits, d=d)
+
+
+@pytest.mark.parametrize("d", [64, 256])
+@pytest.mark.parametrize("kb,vb", [(4, 2), (3, 4), (2, 3)])
+def test_head_dim_mixed_widths(dev, d, kb, vb):
+    run_attn(dev, "d=%d keys %d bits, values %d bits" % (d, kb, vb), bits=kb, v_bits=vb, B=3,
+             Hq=16, Hkv=4, T=300, d=d)
+
+
+@pytest.mark.parametrize("d,Hq,Hkv", [(64, 32, 2), (64, 8, 8), (64, 24, 8), (256, 16, 2),
+                                      (256, 8, 8), (256, 4, 1), (256, 24, 8)])
+def test_head_dim_gqa(dev, d, Hq, Hkv):
+    run_attn(dev, "d=%d gqa %d/%d" % (d, Hq, Hkv), B=2, Hq=Hq, Hkv=Hkv, T=50, d=d)
+
+
+@pytest.mark.parametrize("d", [64, 256])
+@pytest.mark.parametrize("T", [1, 17, 1000, 1500])
+def test_head_dim_contexts(dev, d, T):
+    run_attn(dev, "d=%d T=%d" % (d, T), B=4, Hq=32, Hkv=8, T=T, ragged=(T > 3), d=d)
+
+
+@pytest.mark.parametrize("d", [64, 256])
+def test_head_dim_peaked_and_padding(dev, d):
+    run_attn(dev, "d=%d scale 1.0" % d, B=2, Hq=8, Hkv=2, T=300, scale=1.0, d=d)
+    g = run_attn(dev, "d=%d pad -1" % d, B=5, Hq=8, Hkv=2, T=40, pad=-1, d=d)
+    assert np.all(np.isfinite(g.astype(np.float64)))
 
 
 def test_zero_context_and_padding(dev):
