@@ -8,7 +8,9 @@ of head_dim 128, fp16, 4 GiB; N(0,1) with 1% x15 outlier channels per
 tq_decode of it (one launch).  Inputs are resident in HBM before timing.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1]
-    python bench.py --attn-only [--steps K]     (attention side measurement only)
+    python bench.py --attn-only [--steps K] [--head-dim D]
+                                                (attention side measurement only;
+                                                 D = 64, 128 (default) or 256)
 
 Prints one JSON line.  `value` is fp16 key/value bytes passed through the
 codec per second (encode and decode both count their 256 B/vector of fp16).
@@ -127,6 +129,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the attention and streaming-encode side measurements")
+    ap.add_argument("--head-dim", type=int, default=128, choices=(64, 128, 256),
+                    help="head_dim of the --attn-only measurement")
     ap.add_argument("--attn-only", action="store_true",
                     help="only the batch-16 x 32K decode-attention measurement (for profiling)")
     args = ap.parse_args()
@@ -141,7 +145,7 @@ def main() -> int:
         dev = torch.device("cuda:0")
         torch.cuda.set_device(dev)
         res = attention_measurement(torch, dev, torch.cuda.current_stream(dev),
-                                    reps=max(1, args.steps))
+                                    reps=max(1, args.steps), head_dim=args.head_dim)
         print(json.dumps(res), flush=True)
         return 0
 
@@ -271,10 +275,12 @@ def side_measurements(torch, dev, stream, x, packed, norms):
     return res
 
 
-def attention_measurement(torch, dev, stream, reps: int = 10):
+def attention_measurement(torch, dev, stream, reps: int = 10, head_dim: int = 128):
     """Median time of tq_attn_decode (split + combine kernels) at batch 16,
     32/8 heads, 32768 tokens, 4 bits, random codes and a random block
-    permutation, with the last-level cache evicted before each call."""
+    permutation, with the last-level cache evicted before each call.  The
+    keys are named attn_batch16_32k_* at head_dim 128 and carry a _d<D>
+    suffix otherwise."""
     from kv_cache_vector_amd import _lib
     import math
     s = stream.cuda_stream
@@ -283,15 +289,17 @@ def attention_measurement(torch, dev, stream, reps: int = 10):
     maxb = T // bs
     nblk = B * maxb
     g = torch.Generator(device=dev).manual_seed(5)
-    kp = torch.randint(0, 256, (nblk, bs, Hkv, 64), dtype=torch.uint8, device=dev, generator=g)
-    vp = torch.randint(0, 256, (nblk, bs, Hkv, 64), dtype=torch.uint8, device=dev, generator=g)
+    d = head_dim
+    P = d * 4 // 8                       # packed bytes per row at 4 bits
+    kp = torch.randint(0, 256, (nblk, bs, Hkv, P), dtype=torch.uint8, device=dev, generator=g)
+    vp = torch.randint(0, 256, (nblk, bs, Hkv, P), dtype=torch.uint8, device=dev, generator=g)
     kn = torch.rand((nblk, bs, Hkv), device=dev, generator=g) * 6 + 8
     vn = torch.rand((nblk, bs, Hkv), device=dev, generator=g) * 6 + 8
-    q = torch.randn((B, Hq, 128), device=dev, generator=g).half()
+    q = torch.randn((B, Hq, d), device=dev, generator=g).half()
     bt = torch.randperm(nblk, device=dev, generator=g).to(torch.int32).reshape(B, maxb)
     cl = torch.full((B,), T, dtype=torch.int32, device=dev)
     out = torch.empty_like(q)
-    wsb = _lib.tq_attn_workspace_bytes(B, Hq, Hkv, 128, bs, maxb)
+    wsb = _lib.tq_attn_workspace_bytes(B, Hq, Hkv, d, bs, maxb)
     ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
     # Cache eviction between repetitions reads a 512 MB buffer: a write flush
     # would leave dirty lines whose write-back lands inside the timed kernel.
@@ -300,8 +308,8 @@ def attention_measurement(torch, dev, stream, reps: int = 10):
     def attn():
         _lib.check(_lib.tq_attn_decode(q.data_ptr(), kp.data_ptr(), kn.data_ptr(),
                                        vp.data_ptr(), vn.data_ptr(), bt.data_ptr(),
-                                       cl.data_ptr(), B, Hq, Hkv, 128, 4, 0, bs, maxb, nblk,
-                                       1 / math.sqrt(128), out.data_ptr(), ws.data_ptr(), wsb,
+                                       cl.data_ptr(), B, Hq, Hkv, d, 4, 0, bs, maxb, nblk,
+                                       1 / math.sqrt(d), out.data_ptr(), ws.data_ptr(), wsb,
                                        s), "tq_attn_decode")
 
     attn()
@@ -315,11 +323,12 @@ def attention_measurement(torch, dev, stream, reps: int = 10):
         torch.cuda.synchronize()
         times.append(e0.elapsed_time(e1))
     t_us = statistics.median(times) * 1e3
-    packed_bytes = B * Hkv * T * 2 * (64 + 4)
-    res["attn_batch16_32k_us"] = round(t_us, 1)
-    res["attn_packed_GBps"] = round(packed_bytes / (t_us * 1e-6) / 1e9, 1)
-    res["attn_fp16_equiv_GBps"] = round(B * Hkv * T * 2 * 256 / (t_us * 1e-6) / 1e9, 1)
-    res["attn_hbm_frac"] = round(packed_bytes / (t_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)
+    packed_bytes = B * Hkv * T * 2 * (P + 4)
+    sfx = "" if d == 128 else "_d%d" % d
+    res["attn_batch16_32k_us" + sfx] = round(t_us, 1)
+    res["attn_packed_GBps" + sfx] = round(packed_bytes / (t_us * 1e-6) / 1e9, 1)
+    res["attn_fp16_equiv_GBps" + sfx] = round(B * Hkv * T * 2 * 2 * d / (t_us * 1e-6) / 1e9, 1)
+    res["attn_hbm_frac" + sfx] = round(packed_bytes / (t_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)
     return res
 
 

@@ -532,9 +532,10 @@ __global__ __launch_bounds__(kMThreads) void attn_split_kernel(AttnParams p) {
 
     // Loads of page pg sit in ring slot pg % R.  The refill for page pg + R
     // is issued at the end of step pg, once the slot has been consumed; its
-    // block number was read from LDS one step earlier.  At D = 256 the ring
-    // has one slot: a second would not fit the register budget without spills.
-    constexpr int R = (D > 128) ? 1 : kMPrefetch + 1;
+    // block number was read from LDS one step earlier.  (At D = 256 with
+    // 4-bit keys the two slots cost a few spilled registers; measured, that
+    // is still faster than a one-slot ring.)
+    constexpr int R = kMPrefetch + 1;
     constexpr int KW = SL::KW, VW = SL::VW;
     uint32_t rk[R][KW];
     uint32_t rv[R][4][VW];
