@@ -17,9 +17,11 @@
 //
 // Two kernels, flash-decoding style:
 //   split   8 waves per workgroup, one per (kv head, context split) of a
-//           sequence: a workgroup takes 8 kv heads of one split, or, for
-//           caches with fewer kv heads, all of them for 8 / Hkv splits.  Per 16-token page the scores and the value accumulation
-//           run as 16x16x32 f16 MFMA tiles:
+//           sequence (two per kv head at head_dim 256, each accumulating
+//           half of the value dims): a workgroup takes the kv heads of one
+//           split, or, for caches with fewer kv heads, all of them for
+//           several splits.  Per 16-token page the scores and the value
+//           accumulation run as 16x16x32 f16 MFMA tiles:
 //             scores  S^T[16 tokens][16 heads] = C_k[16 tokens][K] Q[K][16 heads]
 //             values  O[16 heads][16 dims]    += W[16 heads][K] C_v[K][16 dims]
 //           with the group's query heads (up to 16) padded to 16.  With at most
@@ -46,13 +48,14 @@
 //
 // Lane layouts (l = lane, m = l % 16, r = l / 16), verified on gfx950:
 //   A[m][8r .. 8r+7], B[8r .. 8r+7][m], C[4r .. 4r+3][m].
-// Scores: lane (token m, r) holds the codes of dims 32r .. 32r+31 of its token
-// (4 * bits bytes); chunk j covers dims 32r + 4j .. +3 of every r.  The query
-// operand of lane (head m, r) covers the same dims.  The score tile leaves
-// lane (head m, r) with tokens 4r .. 4r+3 -- exactly the K slots the value
-// product wants in its A operand, so the weights never move between lanes.
-// Values: lane (column m, r) reads dims 8m .. 8m+7 of tokens 4r .. 4r+3;
-// chunk jj accumulates dim 8m + jj.
+// Scores (head_dim d, G = d / 4): lane (token m, r) holds the codes of dims
+// G r .. G r + G - 1 of its token; chunk j covers dims G r + 4j .. +3 of every
+// r.  The query operand of lane (head m, r) covers the same dims.  The score
+// tile leaves lane (head m, r) with tokens 4r .. 4r+3 -- exactly the K slots
+// the value product wants in its A operand, so the weights never move
+// between lanes.  Values (N = min(d, 128) / 16 dims per lane column): lane
+// (column m, r) reads dims N m .. N m + N - 1 of tokens 4r .. 4r+3 (of the
+// wave's half at d = 256); chunk jj accumulates dim N m + jj.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -96,7 +99,7 @@ struct AttnParams {
     int batch, hq, hkv, max_blocks, split_tokens, num_splits;
     int spw;             // splits per workgroup of the split kernel
     int64_t num_blocks;
-    float qscale;        // scale * log2(e) / 128
+    float qscale;        // scale * log2(e) / head_dim
     CodecConsts k;       // key codebook and the sign mask (shared by keys and values)
     CodecConsts v;       // value codebook
 };
