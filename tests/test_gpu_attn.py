@@ -171,12 +171,15 @@ def test_scale_and_peaked_softmax(dev):
     run_attn(dev, "scale 0.02", B=2, Hq=8, Hkv=2, T=300, scale=0.02)
 
 
-def _c5(dev, ragged, samples, vb=4):
+def _c5(dev, ragged, samples, vb=4, B=16, Hq=32, Hkv=8, T=32768, heads_per_sample=None):
     """Batch 16, 32/8 heads, 32768 tokens, 4-bit keys (values: vb bits), in the
-    launch configuration the benchmark times.  The sampled (sequence, kv head)
-    streams hold oracle-encoded N(0,1)+outlier data; the rest of the cache is
-    random codes."""
-    B, Hq, Hkv, T, bs = 16, 32, 8, 32768, 16
+    launch configuration the benchmark times (or another shape).  The sampled
+    (sequence, kv head) streams hold oracle-encoded N(0,1)+outlier data; the
+    rest of the cache is random codes.  The first heads_per_sample query heads
+    of each sampled kv head are compared (default: all of the group)."""
+    bs = 16
+    grp = Hq // Hkv
+    hps = grp if heads_per_sample is None else heads_per_sample
     maxb = T // bs
     nblk = B * maxb
     rng = np.random.default_rng(502)
@@ -196,8 +199,9 @@ def _c5(dev, ragged, samples, vb=4):
         W.scatter_pages(kn, n_k, bt[b], g)
         W.scatter_pages(vp, p_v, bt[b], g)
         W.scatter_pages(vn, n_v, bt[b], g)
-        sel[b, g * 4:(g + 1) * 4] = True
-    P.log("[attn] C5-shaped full size ragged=%s values %d bits samples=%s" % (ragged, vb, samples))
+        sel[b, g * grp:g * grp + hps] = True
+    P.log("[attn] full size B=%d Hq=%d Hkv=%d T=%d ragged=%s values %d bits samples=%s"
+          % (B, Hq, Hkv, T, ragged, vb, samples))
     tq = TurboQuant(D, 4, 0, dev)
     attn = TQPagedAttention(tq, Hq, v_tq=TurboQuant(D, vb, 0, dev))
     t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
@@ -220,3 +224,9 @@ def test_full_size_batch16_ragged(dev):
 
 def test_full_size_batch16_k4_v2(dev):
     _c5(dev, True, [(5, 2), (14, 6)], vb=2)
+
+
+def test_long_context_batch1_128k(dev):
+    """One 131,072-token sequence, 64 query / 8 kv heads: 512 context splits
+    merged by the combine kernel."""
+    _c5(dev, False, [(0, 0), (0, 5)], B=1, Hq=64, Hkv=8, T=131072, heads_per_sample=2)
