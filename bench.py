@@ -272,6 +272,69 @@ def side_measurements(torch, dev, stream, x, packed, norms):
     cache, the launch shape of the layer-by-layer streaming encode)."""
     res = attention_measurement(torch, dev, stream)
     res.update(stream_encode_measurement(torch, dev, stream, x, packed, norms))
+    res.update(codec_side_measurement(torch, dev, stream, x, packed, norms))
+    return res
+
+
+def _median_min(times):
+    return statistics.median(times), min(times)
+
+
+def codec_side_measurement(torch, dev, stream, x, packed, norms):
+    """Other codec launch shapes on the resident cache (timing does not depend
+    on the values):
+      - 3- and 2-bit encode and decode of the whole 16,777,216-vector cache;
+      - 4-bit encode and decode of one layer (524,288 vectors), cache evicted
+        before each launch;
+      - 4-bit encode and decode latency of 4,096 vectors (cache-resident)."""
+    from kv_cache_vector_amd import _lib
+    s = stream.cuda_stream
+    res = {}
+    out = torch.empty_like(x)
+    flush = torch.ones(512 * 1024 * 1024 // 4, dtype=torch.float32, device=dev)
+
+    def timed(fn, reps, evict):
+        fn()
+        times = []
+        for _ in range(reps):
+            if evict:
+                flush.sum()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1))
+        return _median_min(times)
+
+    def enc(n, bits, pk):
+        return lambda: _lib.check(_lib.tq_encode(x.data_ptr(), n, D, bits, 0, pk.data_ptr(),
+                                                 norms.data_ptr(), s), "tq_encode")
+
+    def dec(n, bits, pk):
+        return lambda: _lib.check(_lib.tq_decode(pk.data_ptr(), norms.data_ptr(), n, D, bits, 0,
+                                                 out.data_ptr(), s), "tq_decode")
+
+    for bits in (3, 2):
+        P = D * bits // 8
+        pk = packed.view(-1)[: N * P].view(N, P)
+        for name, fn in (("encode", enc(N, bits, pk)), ("decode", dec(N, bits, pk))):
+            med, mn = timed(fn, 5, False)
+            res["%s_b%d_ms" % (name, bits)] = round(med, 4)
+            res["%s_b%d_min_ms" % (name, bits)] = round(mn, 4)
+            res["%s_b%d_hbm_frac" % (name, bits)] = round(
+                N * (2 * D + P + 4) / (med * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)
+    n = PER_LAYER
+    for name, fn in (("encode", enc(n, BITS, packed)), ("decode", dec(n, BITS, packed))):
+        med, mn = timed(fn, 10, True)
+        res["%s_layer_us" % name] = round(med * 1e3, 1)
+        res["%s_layer_hbm_frac" % name] = round(
+            n * ALGO_BYTES / (med * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)
+    n = 4096
+    for name, fn in (("encode", enc(n, BITS, packed)), ("decode", dec(n, BITS, packed))):
+        med, mn = timed(fn, 20, False)
+        res["%s_4096_vectors_us" % name] = round(med * 1e3, 1)
+        res["%s_4096_vectors_min_us" % name] = round(mn * 1e3, 1)
     return res
 
 

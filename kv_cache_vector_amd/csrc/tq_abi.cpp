@@ -133,11 +133,12 @@ tq::EncTable make_enc_table(int bits) {
             else if (T <= hi) thr = T;
         }
         // 4 bits: the four bytes hold base, base + 1, and both shifted into
-        // the high nibble, for the kernel's byte-select packing; otherwise
-        // the plain base code
-        uint32_t bb = (bits == 4) ? (base | (base + 1) << 8 | (base << 4) << 16 |
-                                     ((base + 1) << 4) << 24)
-                                  : base;
+        // the high nibble, for the kernel's byte-select packing; 2 bits:
+        // base and base + 1 in bytes 0 and 1; 3 bits: the plain base code
+        uint32_t bb = (bits == 4)   ? (base | (base + 1) << 8 | (base << 4) << 16 |
+                                       ((base + 1) << 4) << 24)
+                      : (bits == 2) ? (base | (base + 1) << 8)
+                                    : base;
         float bf;
         std::memcpy(&bf, &bb, 4);
         t.cell[c] = make_float2(thr, bf);

@@ -199,8 +199,36 @@ __device__ __forceinline__ void put_code4(uint32_t &acc, float y, float thr, uin
     if (j == 6) TQ_PUT_CODE(3, 0, 1);
     if (j == 7) TQ_PUT_CODE(3, 2, 3);
 }
+
+// 2-bit packing: the code word holds base / base + 1 in bytes 0 / 1, and the
+// selected code goes, unshifted, into byte DB of one of four accumulators (one
+// per code position within a byte); FIRST marks an accumulator's first write,
+// which is always byte 0.
+template <int DB, bool FIRST>
+__device__ __forceinline__ void put_code2(uint32_t &acc, float y, float thr, uint32_t W) {
+    if constexpr (FIRST) TQ_PUT_FIRST(0, 1);
+    else if constexpr (DB == 1) TQ_PUT_CODE(1, 0, 1);
+    else if constexpr (DB == 2) TQ_PUT_CODE(2, 0, 1);
+    else TQ_PUT_CODE(3, 0, 1);
+}
 #undef TQ_PUT_CODE
 #undef TQ_PUT_FIRST
+
+// 2-bit codes of f[R..]: code r = 8k + j of the lane's stream sits at bit
+// 16 (k & 1) + 2j of stream dword k / 2, i.e. in byte 2 (k & 1) + j / 4 at
+// position j % 4; a[p][m] collects position p of stream dword m.
+template <int R, int N>
+__device__ __forceinline__ void quantize2(const float (&f)[N], const float2 *qtab,
+                                          uint32_t (&a)[4][N / 16]) {
+    if constexpr (R < N) {
+        constexpr int k = R >> 3, j = R & 7;
+        constexpr int byte = 2 * (k & 1) + (j >> 2);
+        const float y = f[R];
+        const float2 e = qtab[(int)y + kCells];
+        put_code2<byte, byte == 0>(a[j & 3][k >> 1], y, e.x, __builtin_bit_cast(uint32_t, e.y));
+        quantize2<R + 1, N>(f, qtab, a);
+    }
+}
 
 template <int R, int N>
 __device__ __forceinline__ void quantize4(const float (&f)[N], const float2 *qtab,
@@ -315,6 +343,12 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(const u32x4 *__restric
             quantize4<0>(f, qtab, lo, hi);
 #pragma unroll
             for (int g = 0; g < K; ++g) pk[g] = lo[g] | hi[g];
+        } else if constexpr (BITS == 2) {
+            uint32_t a[4][NPK];
+            quantize2<0>(f, qtab, a);
+#pragma unroll
+            for (int m = 0; m < NPK; ++m)
+                pk[m] = (a[3][m] << 6) | (a[2][m] << 4) | (a[1][m] << 2) | a[0][m];
         } else {
 #pragma unroll
             for (int r = 0; r < R; ++r) {

@@ -26,8 +26,9 @@ struct CodecConsts {
 // 128 at head_dim 256.
 constexpr int kEncCells = 128;
 struct EncTable {
-    // (threshold * 8, code word): the code word is the base code, or at 4
-    // bits the bytes {base, base + 1, base << 4, (base + 1) << 4}
+    // (threshold * 8, code word): at 4 bits the bytes {base, base + 1,
+    // base << 4, (base + 1) << 4}, at 2 bits {base, base + 1, 0, 0}, at 3
+    // bits the base code
     float2 cell[2 * kEncCells + 1];
 };
 
