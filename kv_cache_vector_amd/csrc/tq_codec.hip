@@ -243,22 +243,6 @@ __device__ __forceinline__ void quantize4(const float (&f)[N], const float2 *qta
     }
 }
 
-// Bits [24 g, 24 g + 24) of the lane's 3-bit field stream.
-template <int G, int NPK>
-__device__ __forceinline__ uint32_t field24(const uint32_t (&pk)[NPK]) {
-    constexpr int w = (24 * G) >> 5, sh = (24 * G) & 31;
-    if constexpr (sh + 24 <= 32) return (pk[w] >> sh) & 0xFFFFFFu;
-    else return __builtin_amdgcn_alignbit(pk[w + 1], pk[w], sh) & 0xFFFFFFu;
-}
-
-template <int G, int K, int NPK>
-__device__ __forceinline__ void fields24(const uint32_t (&pk)[NPK], uint32_t (&F)[K]) {
-    if constexpr (G < K) {
-        F[G] = field24<G>(pk);
-        fields24<G + 1, K>(pk, F);
-    }
-}
-
 template <int D, int BITS, bool PAGED>
 __global__ __launch_bounds__(kThreads) void encode_kernel(const u32x4 *__restrict__ x, int64_t n,
                                                           const int64_t *__restrict__ slots,
@@ -270,7 +254,7 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(const u32x4 *__restric
     constexpr int R = 8 * K;                    // coordinates per lane
     constexpr int PW = D * BITS / 32;           // packed dwords per vector
     constexpr uint32_t VB = 2 * D;              // fp16 bytes per vector
-    constexpr int NPK = (K * BITS + 3) / 4;     // dwords of the lane's field stream
+    constexpr int NPK = (K * BITS + 3) / 4;     // dwords of the lane's field stream (4, 2 bits)
     __shared__ float2 qtab[2 * kCells + 1];
     __shared__ u32x4 smask[4 * K];
     for (int t = threadIdx.x; t < 2 * kCells + 1; t += blockDim.x) qtab[t] = tb.cell[t];
@@ -335,7 +319,8 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(const u32x4 *__restric
         fwht_quad<R>(f, ma, mb);
         fwht_registers_scaled<2>(f, kk);   // f[r] = 8 z of coordinate r
 
-        uint32_t pk[NPK];
+        uint32_t pk[NPK];   // the lane's field stream (4 and 2 bits)
+        uint32_t G3[K];     // 3 bits: group k's 24-bit field, code j at bit 3j
 #pragma unroll
         for (int i = 0; i < NPK; ++i) pk[i] = 0;
         if constexpr (BITS == 4) {
@@ -355,9 +340,8 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(const u32x4 *__restric
                 const float y = f[r];
                 const float2 e = qtab[(int)y + kCells];
                 const uint32_t code = __builtin_bit_cast(uint32_t, e.y) + (y > e.x ? 1u : 0u);
-                const int bit = r * BITS;   // lane-local field stream: group k at bits 8*BITS*k
-                pk[bit >> 5] |= code << (bit & 31);
-                if ((bit & 31) + BITS > 32) pk[(bit >> 5) + 1] |= code >> (32 - (bit & 31));
+                if ((r & 7) == 0) G3[r >> 3] = code;
+                else G3[r >> 3] |= code << (3 * (r & 7));
             }
         }
 
@@ -386,8 +370,7 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(const u32x4 *__restric
         } else {
             // group k of lane q is the 24-bit field at bit 96k + 24q; lane q < 3
             // stores dword 3k + q, made of its field and lane q+1's
-            uint32_t G[K];
-            fields24<0, K>(pk, G);
+            const uint32_t (&G)[K] = G3;
             const uint32_t sh = 8 * q + 8;
 #pragma unroll
             for (int g = 0; g < K; ++g) {
