@@ -158,7 +158,10 @@ size_t tq_attn_workspace_bytes(int batch, int num_q_heads, int num_kv_heads, int
  *                tokens are left out of the softmax (the output for that
  *                sequence is then unspecified but memory stays in bounds)
  * num_q_heads must be a multiple of num_kv_heads with at most 16 query heads
- * per kv head; block_size must be 16.  A context length outside
+ * per kv head (8 at head_dim 256); block_size must be 16; batch at most
+ * 65535, batch * num_q_heads at most 2^31 - 1 and max_blocks_per_seq at most
+ * (2^31 - 1) / 16 (TQ_ERR_UNSUPPORTED otherwise; tq_attn_workspace_bytes
+ * returns 0 for such shapes).  A context length outside
  * [0, max_blocks_per_seq * block_size] is clamped into that range.
  * Errors: TQ_ERR_INVALID_ARG (null pointers, negative sizes, a non-finite
  * scale, overlapping output), TQ_ERR_UNSUPPORTED (head_dim, bits, group size

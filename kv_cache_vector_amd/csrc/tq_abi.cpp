@@ -174,6 +174,14 @@ tq_status check_shape(int head_dim, int bits) {
 
 tq_status from_hip(hipError_t e) { return e == hipSuccess ? TQ_OK : TQ_ERR_HIP; }
 
+// Launch extents of the attention kernels: at most 65535 sequences (grid y),
+// batch * num_q_heads combine workgroups, and contexts whose token count
+// fits an int.
+bool attn_extents_ok(int batch, int num_q_heads, int max_blocks_per_seq) {
+    return batch <= tq::kAttnMaxBatch && max_blocks_per_seq <= tq::kAttnMaxBlocks &&
+           (int64_t)batch * num_q_heads <= 0x7fffffff;
+}
+
 }  // namespace
 
 extern "C" {
@@ -279,7 +287,7 @@ size_t tq_attn_workspace_bytes(int batch, int num_q_heads, int num_kv_heads, int
                                int block_size, int max_blocks_per_seq) {
     if (batch < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || !codec_head_dim(head_dim) ||
         block_size != tq::kAttnBlockSize || max_blocks_per_seq < 0 ||
-        num_q_heads % num_kv_heads)
+        num_q_heads % num_kv_heads || !attn_extents_ok(batch, num_q_heads, max_blocks_per_seq))
         return 0;
     tq::AttnShape s{batch, num_q_heads, num_kv_heads, head_dim, 4, 4, max_blocks_per_seq, 0};
     return tq::attn_workspace_bytes(s);
@@ -300,7 +308,8 @@ tq_status tq_attn_decode_kv(const void *q_f16, const uint8_t *k_packed, const fl
         num_blocks < 0 || !std::isfinite(scale))
         return TQ_ERR_INVALID_ARG;
     if (num_q_heads % num_kv_heads) return TQ_ERR_INVALID_ARG;
-    if (num_q_heads / num_kv_heads > tq::kAttnMaxGroup || block_size != tq::kAttnBlockSize)
+    if (num_q_heads / num_kv_heads > tq::kAttnMaxGroup || block_size != tq::kAttnBlockSize ||
+        !attn_extents_ok(batch, num_q_heads, max_blocks_per_seq))
         return TQ_ERR_UNSUPPORTED;
     if (batch == 0) return TQ_OK;
     if (!q_f16 || !out_f16 || !context_lens || (max_blocks_per_seq > 0 && !block_tables))

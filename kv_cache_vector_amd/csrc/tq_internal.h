@@ -49,6 +49,8 @@ hipError_t launch_decode(int head_dim, int bits, const uint8_t *packed, const fl
 constexpr int kAttnBlockSize = 16;   // tokens per cache page
 constexpr int kAttnMaxGroup = 16;    // query heads per kv head
 constexpr int kAttnMaxGroupD256 = 8; // the same at head_dim 256
+constexpr int kAttnMaxBatch = 65535;               // sequences: the split grid's y extent
+constexpr int kAttnMaxBlocks = 0x7fffffff / 16;    // pages per sequence: tokens fit an int
 
 struct AttnShape {
     int batch, num_q_heads, num_kv_heads, head_dim, k_bits, v_bits, max_blocks;

@@ -171,6 +171,12 @@ def test_attention_argument_errors(L):
     assert call(d=64, batch=0) == OK
     assert call(d=256, hq=8 * 9) == UNSUP          # head_dim 256: at most 8 query heads per kv head
     assert call(d=256, hq=8 * 8, batch=0) == OK
+    # launch extents: sequences on the grid's y axis, tokens per sequence in an int
+    assert call(batch=65536) == UNSUP
+    assert call(maxb=(2 ** 31 - 1) // 16 + 1) == UNSUP
+    assert call(batch=65535, hq=2049 * 16, hkv=2049) == UNSUP     # batch * hq > 2^31 - 1
+    assert L.tq_attn_workspace_bytes(65536, 32, 8, 128, 16, 2048) == 0
+    assert L.tq_attn_workspace_bytes(16, 32, 8, 128, 16, (2 ** 31 - 1) // 16 + 1) == 0
     assert call(bs=32) == UNSUP
     assert call(hq=30) == INVAL
     assert call(hq=8 * 17) == UNSUP                 # 17 query heads per kv head
