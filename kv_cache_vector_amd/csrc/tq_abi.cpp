@@ -12,7 +12,7 @@
 #include <cstring>
 #include <mutex>
 
-#include "tq_internal.h"
+#include "tq_attn_internal.h"
 
 namespace {
 

@@ -59,7 +59,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include "tq_internal.h"
+#include "tq_attn_internal.h"
 
 namespace tq {
 namespace {
