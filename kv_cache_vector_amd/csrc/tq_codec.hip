@@ -43,7 +43,6 @@ namespace {
 constexpr int kCells = kEncCells;     // quantizer cells cover y in (-129, 129)
 constexpr int kThreads = 256;         // 4 waves, 64 vectors per block iteration
 constexpr int kVecPerBlock = kThreads / 4;
-constexpr int kDecVpq = 4;            // decode: vectors per quad
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -52,6 +51,9 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kQuadXor1 = 0xB1;   // quad_perm [1,0,3,2]: partner q^1
 constexpr int kQuadXor2 = 0x4E;   // quad_perm [2,3,0,1]: partner q^2
 constexpr int kQuadNext = 0xF9;   // quad_perm [1,2,3,3]: lane q reads lane q+1
+// DPP row rotations
+constexpr int kRowRor4 = 0x124;   // row_ror:4: lane m of a 16-lane row <- lane (m - 4) mod 16
+constexpr int kRowRor12 = 0x12C;  // row_ror:12: lane m <- lane (m + 4) mod 16
 
 template <int CTRL>
 __device__ __forceinline__ uint32_t quad_move(uint32_t v) {
@@ -243,6 +245,12 @@ __device__ __forceinline__ void quantize4(const float (&f)[N], const float2 *qta
     }
 }
 
+// Encode: vectors per quad, chosen by timing 1, 2 and 4 on MI355X over a 4 GiB
+// cache.  At head_dim 64 a vector is only 128 bytes, and four per quad (all
+// loads issued first) run 9-12% faster than one; at 128 and 256 one is
+// fastest.
+constexpr int enc_vpq(int d) { return d == 64 ? 4 : 1; }
+
 template <int D, int BITS, bool PAGED>
 __global__ __launch_bounds__(kThreads) void encode_kernel(const u32x4 *__restrict__ x, int64_t n,
                                                           const int64_t *__restrict__ slots,
@@ -271,25 +279,37 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(const u32x4 *__restric
     // 2-bit: byte selectors splicing this lane's and the partner's 16-bit fields
     const uint32_t sel2 = (q & 1) ? 0x03020706u : 0x05040100u;
 
-    {
-        // this block's vectors [v0, v0 + nb): scalar base, per-lane offsets
-        const int64_t v0 = (int64_t)blockIdx.x * kVecPerBlock;
-        const uint32_t nb = (uint32_t)((n - v0 < kVecPerBlock) ? n - v0 : kVecPerBlock);
-        const uint32_t qi = threadIdx.x >> 2;
-        const int64_t v = v0 + qi;
-        if (v >= n) return;   // uniform over the quad; no barrier follows
-        const __amdgpu_buffer_rsrc_t rx = span_rsrc(x + v0 * (D / 8), nb * VB);
-        const uint32_t xo = qi * VB + 16u * q;
-        uint32_t w[4 * K];
+    // this block's vectors [v0, v0 + nb): scalar base, per-lane offsets.  Quad
+    // qi takes vectors v0 + 64 vi + qi (vi < VPQ), so that every access
+    // instruction of a wave covers 16 consecutive vectors; all their loads
+    // are issued before the first one is transformed.
+    constexpr int VPQ = enc_vpq(D);
+    constexpr int VPB = kVecPerBlock * VPQ;
+    const int64_t v0 = (int64_t)blockIdx.x * VPB;
+    const uint32_t nb = (uint32_t)((n - v0 < VPB) ? n - v0 : VPB);
+    const uint32_t qi = threadIdx.x >> 2;
+    if (v0 + qi >= n) return;   // uniform over the quad; no barrier follows
+    const __amdgpu_buffer_rsrc_t rx = span_rsrc(x + v0 * (D / 8), nb * VB);
+    uint32_t wv[VPQ][4 * K];   // lanes past the end read zeros (bounds check)
+#pragma unroll
+    for (int vi = 0; vi < VPQ; ++vi) {
+        const uint32_t xo = (vi * kVecPerBlock + qi) * VB + 16u * q;
 #pragma unroll
         for (int g = 0; g < K; ++g) {
             const u32x4 u = __builtin_bit_cast(
                 u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, xo + 64u * g, 0, 0));
-            w[4 * g + 0] = u.x;
-            w[4 * g + 1] = u.y;
-            w[4 * g + 2] = u.z;
-            w[4 * g + 3] = u.w;
+            wv[vi][4 * g + 0] = u.x;
+            wv[vi][4 * g + 1] = u.y;
+            wv[vi][4 * g + 2] = u.z;
+            wv[vi][4 * g + 3] = u.w;
         }
+    }
+#pragma unroll
+    for (int vi = 0; vi < VPQ; ++vi) {
+        const uint32_t qv = vi * kVecPerBlock + qi;   // vector within the block
+        const int64_t v = v0 + qv;
+        if (v >= n) break;   // uniform over the quad
+        const uint32_t (&w)[4 * K] = wv[vi];
         // ||x||^2 from the fp16 pairs (products exact in f32, f32 accumulate)
         float ss = 0.0f;
 #pragma unroll
@@ -381,7 +401,7 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(const u32x4 *__restric
         }
         if (PAGED) {
             const int64_t row = slots[v];
-            if (row < 0 || row >= num_slots) return;     // uniform over the quad
+            if (row < 0 || row >= num_slots) continue;   // uniform over the quad
             uint32_t *dst = packed + row * PW;
 #pragma unroll
             for (int i = 0; i < NS; ++i)
@@ -392,18 +412,24 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(const u32x4 *__restric
 #pragma unroll
             for (int i = 0; i < NS; ++i)
                 if (BITS != 3 || q < 3)
-                    __builtin_amdgcn_raw_buffer_store_b32(sv[i], rp, qi * (PW * 4u) + 4u * si[i], 0, 0);
+                    __builtin_amdgcn_raw_buffer_store_b32(sv[i], rp, qv * (PW * 4u) + 4u * si[i], 0, 0);
             if (q == 0)
                 __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, nrm),
-                                                      span_rsrc(norms + v0, nb * 4u), qi * 4u, 0, 0);
+                                                      span_rsrc(norms + v0, nb * 4u), qv * 4u, 0, 0);
         }
     }
 }
 
-// Decode: vectors per quad (all their loads are issued before the first one
-// is transformed); fewer at D = 256, where one vector already takes 64
-// registers of values.
-constexpr int dec_vpq(int d) { return d > 128 ? 2 : kDecVpq; }
+// Decode launch shape per (head_dim, bits), chosen by timing 1 or 2 vectors
+// per quad, each with and without paired stores, on MI355X over a 4 GiB cache:
+// - vectors per quad: all their loads are issued before the first one is
+//   transformed; one at 4 bits from head_dim 128 up, two otherwise;
+// - paired stores: neighbouring quads trade chunks so that every store
+//   instruction writes whole 128-byte lines; 3-10% faster than per-quad
+//   64-byte pieces in the write-heavy mix, except at head_dim 128 and 2 bits
+//   (3% slower there).
+constexpr int dec_vpq(int d, int bits) { return (bits == 4 && d >= 128) ? 1 : 2; }
+constexpr bool dec_pair(int d, int bits) { return !(d == 128 && bits == 2); }
 
 template <int D, int BITS>
 __global__ __launch_bounds__(kThreads) void decode_kernel(const uint32_t *__restrict__ packed,
@@ -414,7 +440,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const uint32_t *__rest
     constexpr int K = D / 32;
     constexpr int R = 8 * K;
     constexpr int PW = D * BITS / 32;
-    constexpr int VPQ = dec_vpq(D);
+    constexpr int VPQ = dec_vpq(D, BITS);
     // One lookup returns G already-transformed values: the first butterfly
     // stage (b = 3, 4: pairs of codes) or the first two (b = 2: a byte holds
     // four codes) is folded into the table.
@@ -528,16 +554,43 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const uint32_t *__rest
             h.y = (_Float16)f[2 * j + 1];
             o[j] = __builtin_bit_cast(uint32_t, h) ^ xm[j];
         }
-        u32x4 *dst = out + v * (D / 8) + q;
+        // Paired stores: quads 2p and 2p + 1 of a wave hold consecutive
+        // vectors a, a + 1.  When all 16 vectors of the wave exist, the two
+        // quads trade one 16-byte chunk per 128-byte line, so that each store
+        // instruction writes whole lines: line L of a vector is groups 2L
+        // (lanes of the even quad) and 2L + 1 (odd quad).  The ragged last
+        // wave keeps the per-quad pattern.
+        const int64_t wave_first = vb - (threadIdx.x & 63) / 4 + (int64_t)i * kVecPerBlock;
+        if (dec_pair(D, BITS) && __builtin_amdgcn_readfirstlane((int)(wave_first + 15 < n))) {
+            const int odd = (threadIdx.x >> 2) & 1;
+            u32x4 *dst = out + (v - odd) * (D / 8) + 4 * odd + q;
 #pragma unroll
-        for (int g = 0; g < K; ++g) {
-            const u32x4 val = {o[4 * g], o[4 * g + 1], o[4 * g + 2], o[4 * g + 3]};
-            dst[4 * g] = val;
+            for (int L = 0; L < K / 2; ++L) {
+                uint32_t xv[4], yv[4];
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    const uint32_t lo = o[8 * L + t], hi = o[8 * L + 4 + t];
+                    // odd lanes take the even quad's group 2L + 1 (four lanes
+                    // down: row_ror:4, banks 1 and 3); even lanes take the odd
+                    // quad's group 2L (four lanes up: row_ror:12, banks 0 and 2)
+                    xv[t] = (uint32_t)__builtin_amdgcn_update_dpp((int)lo, (int)hi, kRowRor4, 0xF, 0xA, false);
+                    yv[t] = (uint32_t)__builtin_amdgcn_update_dpp((int)hi, (int)lo, kRowRor12, 0xF, 0x5, false);
+                }
+                dst[8 * L] = u32x4{xv[0], xv[1], xv[2], xv[3]};
+                dst[8 * L + D / 8] = u32x4{yv[0], yv[1], yv[2], yv[3]};
+            }
+        } else {
+            u32x4 *dst = out + v * (D / 8) + q;
+#pragma unroll
+            for (int g = 0; g < K; ++g) {
+                const u32x4 val = {o[4 * g], o[4 * g + 1], o[4 * g + 2], o[4 * g + 3]};
+                dst[4 * g] = val;
+            }
         }
     }
 }
 
-// One block per 64 (encode) or 64 * dec_vpq(D) (decode) vectors: a full grid, so
+// One block per 64 (encode) or 64 * dec_vpq(d, bits) (decode) vectors: a full grid, so
 // the hardware keeps every CU fed without a tail of long-running blocks.
 dim3 grid_for(int64_t n, int vectors_per_block) {
     const int64_t b = (n + vectors_per_block - 1) / vectors_per_block;
@@ -558,8 +611,9 @@ int device_cu_count() {
 hipError_t launch_encode(int head_dim, int bits, const void *x, int64_t n, const int64_t *slots,
                          int64_t num_slots, const CodecConsts &k, const EncTable &tb,
                          uint8_t *packed, float *norms, hipStream_t stream) {
-    if (n > (int64_t)kVecPerBlock * 0x7fffffff) return hipErrorInvalidValue;
-    const dim3 grid = grid_for(n, kVecPerBlock), block(kThreads);
+    const int vpb = kVecPerBlock * enc_vpq(head_dim);
+    if (n > (int64_t)vpb * 0x7fffffff) return hipErrorInvalidValue;
+    const dim3 grid = grid_for(n, vpb), block(kThreads);
     const u32x4 *xs = static_cast<const u32x4 *>(x);
     uint32_t *pk = reinterpret_cast<uint32_t *>(packed);
 #define TQ_ENC(D, B)                                                                            \
@@ -587,7 +641,7 @@ hipError_t launch_encode(int head_dim, int bits, const void *x, int64_t n, const
 
 hipError_t launch_decode(int head_dim, int bits, const uint8_t *packed, const float *norms,
                          int64_t n, const CodecConsts &k, void *out, hipStream_t stream) {
-    const int vpb = kVecPerBlock * dec_vpq(head_dim);
+    const int vpb = kVecPerBlock * dec_vpq(head_dim, bits);
     if (n > (int64_t)vpb * 0x7fffffff) return hipErrorInvalidValue;
     const dim3 grid = grid_for(n, vpb), block(kThreads);
     u32x4 *o = static_cast<u32x4 *>(out);
