@@ -109,8 +109,6 @@ CodecConsts make_consts(int head_dim, int bits, uint64_t seed) {
     const Codebook &cb = codebook(bits);
     const int L = 1 << bits;
     for (int i = 0; i < L; ++i) k.level[i] = cb.level[i];
-    for (int i = 0; i < L - 1; ++i) k.thr8[i] = 8.0f * cb.thr[i];
-    k.one = 1.0f;
     return k;
 }
 

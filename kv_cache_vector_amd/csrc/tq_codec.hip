@@ -145,15 +145,32 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t span_rsrc(const void *base, ui
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, 0x00020000);
 }
 
-// XOR masks flipping the binary16 sign bits of register pair (2i, 2i+1) of
-// lane q, i.e. of coordinates 32(i/4) + 8q + 2(i%4) + {0, 1}.  Thread
-// t < 16K writes mask i = t % 4K of lane q = t / 4K to LDS once per block;
-// every lane then reads its 4K masks with K broadcast 16-byte LDS reads.
-template <int K>
+// Signs of register pair (2i, 2i+1) of lane q, i.e. of coordinates
+// 32(i/4) + 8q + 2(i%4) + {0, 1}: XOR masks of the binary16 sign bits, or
+// (ONES) the binary16 pair (sigma_a, sigma_b) itself.  Thread t < 16K writes
+// word i = t % 4K of lane q = t / 4K to LDS once per block; every lane then
+// reads its 4K words with K broadcast 16-byte LDS reads.
+template <int K, bool ONES>
 __device__ __forceinline__ void store_sign_mask(const CodecConsts &k, int t, uint32_t *smask) {
     const int q = t / (4 * K), i = t % (4 * K);
     const uint32_t w = k.sign[i >> 2] >> (8 * q + 2 * (i & 3));
-    smask[t] = ((w & 1u) << 15) | (((w >> 1) & 1u) << 31);
+    const uint32_t m = ((w & 1u) << 15) | (((w >> 1) & 1u) << 31);
+    smask[t] = ONES ? (m | 0x3C003C00u) : m;   // 0x3C00: binary16 1.0
+}
+
+// sigma_a a + sigma_b b and sigma_a a - sigma_b b for binary16 pairs
+// x = (a, b), s = (sigma_a, sigma_b): v_dot2_f32_f16 with a zero addend (the
+// three-operand form, which needs no zeroed destination), the second with
+// the high half of s negated.  The products are exact.
+__device__ __forceinline__ float dot2_sum(uint32_t x, uint32_t s) {
+    float r;
+    asm("v_dot2_f32_f16 %0, %1, %2, 0" : "=v"(r) : "v"(x), "v"(s));
+    return r;
+}
+__device__ __forceinline__ float dot2_diff(uint32_t x, uint32_t s) {
+    float r;
+    asm("v_dot2_f32_f16 %0, %1, %2, 0 neg_hi:[0,1,0]" : "=v"(r) : "v"(x), "v"(s));
+    return r;
 }
 
 template <int K>
@@ -266,16 +283,16 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(const u32x4 *__restric
     __shared__ float2 qtab[2 * kCells + 1];
     __shared__ u32x4 smask[4 * K];
     for (int t = threadIdx.x; t < 2 * kCells + 1; t += blockDim.x) qtab[t] = tb.cell[t];
-    if (threadIdx.x < 16 * K) store_sign_mask<K>(k, threadIdx.x, reinterpret_cast<uint32_t *>(smask));
+    if (threadIdx.x < 16 * K)
+        store_sign_mask<K, true>(k, threadIdx.x, reinterpret_cast<uint32_t *>(smask));
     __syncthreads();
 
     const int q = threadIdx.x & 3;
-    uint32_t xm[4 * K];
-    load_sign_masks<K>(smask, q, xm);
+    uint32_t sg[4 * K];   // binary16 sign pairs (sigma_a, sigma_b)
+    load_sign_masks<K>(smask, q, sg);
     const float ma = (q & 1) ? -1.0f : 1.0f;
     const float mb = (q & 2) ? -1.0f : 1.0f;
     const float eps8 = 8.0f * ma * mb;
-    const float one = k.one;
     // 2-bit: byte selectors splicing this lane's and the partner's 16-bit fields
     const uint32_t sel2 = (q & 1) ? 0x03020706u : 0x05040100u;
 
@@ -317,16 +334,13 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(const u32x4 *__restric
             const half2_t h = __builtin_bit_cast(half2_t, w[j]);
             ss = __builtin_amdgcn_fdot2(h, h, ss, false);
         }
-        // sign flip on the fp16 bits; widening to f32 fused with the first
-        // butterfly stage (v_fma_mix: the multiplier `one` is a kernel
-        // argument, so the compiler cannot fold these into plain adds)
+        // sign flip, widening to f32 and the first butterfly stage in one
+        // v_dot2_f32_f16 per output: sigma_a a + sigma_b b and sigma_a a - sigma_b b
         float f[R];
 #pragma unroll
         for (int j = 0; j < 4 * K; ++j) {
-            const half2_t h = __builtin_bit_cast(half2_t, w[j] ^ xm[j]);
-            const float lo = (float)h.x, hi = (float)h.y;
-            f[2 * j] = __builtin_fmaf(hi, one, lo);
-            f[2 * j + 1] = __builtin_fmaf(hi, -one, lo);
+            f[2 * j] = dot2_sum(w[j], sg[j]);
+            f[2 * j + 1] = dot2_diff(w[j], sg[j]);
         }
         ss += quad_move<kQuadXor1>(ss);
         ss += quad_move<kQuadXor2>(ss);
@@ -463,7 +477,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const uint32_t *__rest
         }
     }
     __shared__ u32x4 smask[4 * K];
-    if (threadIdx.x < 16 * K) store_sign_mask<K>(k, threadIdx.x, reinterpret_cast<uint32_t *>(smask));
+    if (threadIdx.x < 16 * K)
+        store_sign_mask<K, false>(k, threadIdx.x, reinterpret_cast<uint32_t *>(smask));
     __syncthreads();
 
     const int q = threadIdx.x & 3;

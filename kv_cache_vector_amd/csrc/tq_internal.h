@@ -14,9 +14,7 @@ constexpr int kMaxHeadDim = 256;   // the kernels take head_dim 64, 128 and 256
 // as a kernel argument, so the library needs no device allocation.
 struct CodecConsts {
     uint32_t sign[kMaxHeadDim / 32];   // bit i of sign[i / 32] set  <=>  sigma_i = -1
-    float thr8[15];     // decision thresholds times 8, ascending (2^bits - 1 used)
     float level[16];    // Lloyd-Max levels, ascending (2^bits used)
-    float one;          // 1.0f, kept opaque to the compiler (see the encode kernel)
 };
 
 // Decision table of the encode kernel: cell i (index i + kEncCells) covers
