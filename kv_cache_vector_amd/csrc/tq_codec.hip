@@ -41,7 +41,7 @@ namespace tq {
 namespace {
 
 constexpr int kCells = kEncCells;     // quantizer cells cover y in (-129, 129)
-constexpr int kThreads = 256;         // 4 waves, 64 vectors per block iteration
+constexpr int kThreads = 256;         // 4 waves: one vector per quad per pass, 64 per pass
 constexpr int kVecPerBlock = kThreads / 4;
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
@@ -605,8 +605,9 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const uint32_t *__rest
     }
 }
 
-// One block per 64 (encode) or 64 * dec_vpq(d, bits) (decode) vectors: a full grid, so
-// the hardware keeps every CU fed without a tail of long-running blocks.
+// One block per 64 enc_vpq(d) (encode) or 64 dec_vpq(d, bits) (decode)
+// vectors: a full grid, so the hardware keeps every CU fed without a tail of
+// long-running blocks (a grid-stride loop measured 10-30% slower).
 dim3 grid_for(int64_t n, int vectors_per_block) {
     const int64_t b = (n + vectors_per_block - 1) / vectors_per_block;
     return dim3((unsigned)b);
