@@ -286,7 +286,11 @@ def codec_side_measurement(torch, dev, stream, x, packed, norms):
       - 3- and 2-bit encode and decode of the whole 16,777,216-vector cache;
       - 4-bit encode and decode of one layer (524,288 vectors), cache evicted
         before each launch;
-      - 4-bit encode and decode latency of 4,096 vectors (cache-resident)."""
+      - 4-bit encode and decode latency of 4,096 vectors (cache-resident);
+      - latency of the paged write path (tq_encode_paged, 4 bits): the new K
+        rows of one decode step at batch 16 x 8 kv heads (128 vectors), and
+        the new K and V rows of all 32 layers (8,192 vectors), each scattered
+        into distinct random rows of the resident cache."""
     from kv_cache_vector_amd import _lib
     s = stream.cuda_stream
     res = {}
@@ -335,6 +339,19 @@ def codec_side_measurement(torch, dev, stream, x, packed, norms):
         med, mn = timed(fn, 20, False)
         res["%s_4096_vectors_us" % name] = round(med * 1e3, 1)
         res["%s_4096_vectors_min_us" % name] = round(mn * 1e3, 1)
+    gen = torch.Generator(device=dev).manual_seed(7)
+    rows = torch.randperm(N, device=dev, generator=gen)
+    for n in (128, 8192):
+        slots = rows[:n].contiguous()
+
+        def paged(n=n, slots=slots):
+            _lib.check(_lib.tq_encode_paged(x.data_ptr(), slots.data_ptr(), n, D, BITS, 0,
+                                            packed.data_ptr(), norms.data_ptr(), N, s),
+                       "tq_encode_paged")
+        med, mn = timed(paged, 20, False)
+        res["encode_paged_%d_us" % n] = round(med * 1e3, 1)
+        res["encode_paged_%d_min_us" % n] = round(mn * 1e3, 1)
+    del rows
     return res
 
 
