@@ -17,7 +17,7 @@
  *              query once, fold the inverse rotation into the output).
  *
  * Encode, per vector x of head_dim = d binary16 values (d = 64, 128 or 256;
- * the crucible page's sample and the attention entry points use 128):
+ * the crucible page's sample uses 128):
  *   n = ||x||_2 (stored as f32);  z = H * D * x / n  (D = diag(sigma), sigma
  *   the seeded +-1 sign flip, H the Sylvester Hadamard matrix, so
  *   z = sqrt(d) * R * (x/n) with R = H D / sqrt(d) orthogonal and z ~ N(0,1)
@@ -35,10 +35,9 @@
  *     surfaces at the caller's next synchronisation.
  *   - Argument errors are reported before anything is enqueued; no exception
  *     crosses the ABI.
- *   - bits must be 2, 3 or 4; head_dim 64, 128 or 256 for the codec entry
- *     points (tq_encode, tq_decode, tq_encode_paged, tq_packed_bytes,
- *     tq_signs) and 128 for the attention ones (TQ_ERR_UNSUPPORTED
- *     otherwise).
+ *   - bits must be 2, 3 or 4 and head_dim 64, 128 or 256, for every entry
+ *     point (TQ_ERR_UNSUPPORTED otherwise); at head_dim 256 the attention
+ *     entry points take at most 8 query heads per kv head.
  *   - binary16 and packed arrays must be 16-byte aligned, f32/int32 arrays
  *     4-byte aligned (TQ_ERR_MISALIGNED otherwise).  Inputs and outputs must
  *     not overlap (TQ_ERR_INVALID_ARG).
@@ -126,8 +125,9 @@ tq_status tq_encode_paged(const void *x_f16, const int64_t *slots, int64_t n, in
 
 /*
  * Workspace bytes tq_attn_decode needs for this problem shape: the partial
- * softmax state (running max, sum, 128 rotated-domain accumulators) of every
- * (sequence, query head, context split).  Deterministic in its arguments.
+ * softmax state (running max, sum, head_dim rotated-domain accumulators) of
+ * every (sequence, query head, context split).  Deterministic in its
+ * arguments.
  */
 size_t tq_attn_workspace_bytes(int batch, int num_q_heads, int num_kv_heads, int head_dim,
                                int block_size, int max_blocks_per_seq);
