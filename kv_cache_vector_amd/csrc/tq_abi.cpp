@@ -288,6 +288,7 @@ size_t tq_attn_workspace_bytes(int batch, int num_q_heads, int num_kv_heads, int
         num_q_heads % num_kv_heads || !attn_extents_ok(batch, num_q_heads, max_blocks_per_seq))
         return 0;
     tq::AttnShape s{batch, num_q_heads, num_kv_heads, head_dim, 4, 4, max_blocks_per_seq, 0};
+    if (!tq::attn_supported(s)) return 0;   // group size beyond what the kernels take
     return tq::attn_workspace_bytes(s);
 }
 

@@ -147,6 +147,11 @@ def test_attention_argument_errors(L):
     assert ws > 0 and ws % 16 == 0
     assert L.tq_attn_workspace_bytes(16, 32, 8, 96, 16, 2048) == 0
     assert L.tq_attn_workspace_bytes(16, 30, 8, 128, 16, 2048) == 0
+    # group sizes: at most 16 query heads per kv head, 8 at head_dim 256
+    assert L.tq_attn_workspace_bytes(16, 128, 8, 128, 16, 2048) > 0
+    assert L.tq_attn_workspace_bytes(16, 136, 8, 128, 16, 2048) == 0
+    assert L.tq_attn_workspace_bytes(16, 64, 8, 256, 16, 2048) > 0
+    assert L.tq_attn_workspace_bytes(16, 72, 8, 256, 16, 2048) == 0
     # one f32 entry of 2 + head_dim floats per (sequence, query head, split)
     for d in (64, 256):
         wd = L.tq_attn_workspace_bytes(16, 32, 8, d, 16, 2048)
