@@ -164,7 +164,8 @@ size_t tq_attn_workspace_bytes(int batch, int num_q_heads, int num_kv_heads, int
  * returns 0 for such shapes).  A context length outside
  * [0, max_blocks_per_seq * block_size] is clamped into that range.
  * Errors: TQ_ERR_INVALID_ARG (null pointers, negative sizes, a non-finite
- * scale, overlapping output), TQ_ERR_UNSUPPORTED (head_dim, bits, group size
+ * scale, an output or workspace overlapping any other array),
+ * TQ_ERR_UNSUPPORTED (head_dim, bits, group size
  * or block_size outside the supported set), TQ_ERR_MISALIGNED,
  * TQ_ERR_WORKSPACE (missing or short workspace), TQ_ERR_HIP (launch failure).
  */

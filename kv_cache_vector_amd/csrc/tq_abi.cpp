@@ -324,9 +324,23 @@ tq_status tq_attn_decode_kv(const void *q_f16, const uint8_t *k_packed, const fl
     if (!tq::attn_supported(s)) return TQ_ERR_UNSUPPORTED;
     const size_t need = tq::attn_workspace_bytes(s);
     if (need > 0 && (!workspace || workspace_bytes < need)) return TQ_ERR_WORKSPACE;
+    // the two written arrays (output, workspace) against each other and
+    // against every input
     const size_t nout = (size_t)batch * num_q_heads * head_dim * 2;
-    if (overlap(out_f16, nout, q_f16, nout) || overlap(out_f16, nout, workspace, need))
-        return TQ_ERR_INVALID_ARG;
+    const size_t rows = (size_t)num_blocks * tq::kAttnBlockSize * num_kv_heads;
+    const struct { const void *p; size_t n; } in[] = {
+        {q_f16, nout},
+        {k_packed, rows * tq_packed_bytes(head_dim, k_bits)},
+        {k_norms, rows * 4},
+        {v_packed, rows * tq_packed_bytes(head_dim, v_bits)},
+        {v_norms, rows * 4},
+        {block_tables, (size_t)batch * max_blocks_per_seq * 4},
+        {context_lens, (size_t)batch * 4},
+    };
+    if (overlap(out_f16, nout, workspace, need)) return TQ_ERR_INVALID_ARG;
+    for (const auto &a : in)
+        if (overlap(out_f16, nout, a.p, a.n) || overlap(workspace, need, a.p, a.n))
+            return TQ_ERR_INVALID_ARG;
     const CodecConsts kc = make_consts(head_dim, k_bits, seed);
     const CodecConsts vc = make_consts(head_dim, v_bits, seed);
     return from_hip(tq::launch_attn(s, kc, vc, q_f16, k_packed, k_norms, v_packed, v_norms,

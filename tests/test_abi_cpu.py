@@ -194,6 +194,11 @@ def test_attention_argument_errors(L):
     assert call(ws=None) == WS
     assert call(wsb=ws - 16) == WS
     assert call(out=A) == INVAL                     # output overlaps the query
+    assert call(out=B + 1024) == INVAL              # output overlaps the packed keys
+    assert call(out=A + (1 << 24)) == INVAL         # output overlaps the block tables
+    assert call(ws=C + (1 << 24)) == INVAL          # workspace overlaps the value norms
+    assert call(ws=A + (1 << 25)) == INVAL          # workspace overlaps the context lengths
+    assert call(ws=A + (1 << 26)) == INVAL          # workspace overlaps the output
 
     # keys and values at different widths
     kv = L.tq_attn_decode_kv
