@@ -135,8 +135,8 @@ def main() -> int:
                     help="only the batch-16 x 32K decode-attention measurement (for profiling)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU: the codec is data-parallel over vectors and "
-              "this build runs on a single MI355X (use --gpus 1)", file=sys.stderr)
+        print("bench.py measures one GPU: the codec is data-parallel over independent "
+              "vectors, and its figures are one MI355X's (use --gpus 1)", file=sys.stderr)
         return 2
     if args.attn_only:
         import torch

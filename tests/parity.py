@@ -1,6 +1,6 @@
 """Comparison helpers for the GPU-vs-oracle parity tests.
 
-Tolerances (fixed by the target this build is held to):
+Tolerances (the codec's accuracy contract):
   - packed codes bit-exact, except coordinates whose oracle z (double, in
     N(0,1) units) lies within 1e-6 of a decision threshold; there a code may
     differ by exactly 1.  The fraction of such coordinates is reported.
