@@ -74,9 +74,8 @@ constexpr int kMWaves = 8;                  // waves per workgroup
 constexpr int kMThreads = 64 * kMWaves;
 constexpr int kMPrefetch = 1;               // extra ring slots: pages of loads in flight ahead of use
 // split-kernel waves aimed for: one full round on MI355X, whose 256 CUs x 4
-// SIMDs hold 2 waves each of this kernel (its VGPRs and 72 KB of LDS per
-// workgroup allow no more); measured, 1.5 or 2-3 rounds are slower and half
-// a round much slower
+// SIMDs hold 2 waves each of this kernel (its 210-220 VGPRs allow no more);
+// measured, 1.5 or 2-3 rounds are slower and half a round much slower
 constexpr int kMTargetWaves = 2048;
 constexpr float kLevelScale = 16.0f;        // binary16 levels are 16 c
 constexpr float kWShift = 6.0f;             // value weights carry 2^6
