@@ -46,10 +46,9 @@ def test_ops_match_direct_calls(dev, d):
         assert torch.equal(p1, p2) and torch.equal(n1, n2) and torch.equal(y1, y2)
 
 
-def test_compiled_decode_step(dev):
-    """Encode the new token's K/V into its cache slots, then attend; the
-    compiled function must equal the eager one."""
-    print("[ops] torch.compile fullgraph decode step", flush=True)
+def _decode_step_inputs(dev):
+    """A small paged cache, a query and one new token's K/V per sequence,
+    with the slots of that token."""
     B, Hq, Hkv, T_ctx, bits, seed = 2, 8, 2, 40, 4, 7
     wl = W.attn_workload(batch=B, num_q_heads=Hq, num_kv_heads=Hkv, context=T_ctx, seed=11,
                          perm_seed=12, ragged=False)
@@ -75,6 +74,18 @@ def test_compiled_decode_step(dev):
         OPS.tq_encode_paged_(newv, slots, vp, vn, bits, seed)
         return OPS.tq_attn_decode(q, kp, kn, vp, vn, bt, cl, bits, seed, scale)
 
+    return dict(tq=tq, q=q, newk=newk, newv=newv, caches=(kp, kn, vp, vn), bt=bt, cl=cl,
+                slots=slots, scale=scale, Hq=Hq, bits=bits, seed=seed, step=step)
+
+
+def test_compiled_decode_step(dev):
+    """Encode the new token's K/V into its cache slots, then attend; the
+    compiled function must equal the eager one."""
+    print("[ops] torch.compile fullgraph decode step", flush=True)
+    inp = _decode_step_inputs(dev)
+    tq, q, newk, newv, step = inp["tq"], inp["q"], inp["newk"], inp["newv"], inp["step"]
+    kp, kn, vp, vn = inp["caches"]
+    bt, cl, slots, scale, Hq = inp["bt"], inp["cl"], inp["slots"], inp["scale"], inp["Hq"]
     caches = [c.clone() for c in (kp, kn, vp, vn)]
     eager = step(q, newk, newv, *caches)
     compiled = torch.compile(step, backend="aot_eager", fullgraph=True)
@@ -91,3 +102,45 @@ def test_compiled_decode_step(dev):
     # the class API gives the same attention
     attn = TQPagedAttention(tq, Hq, scale=scale)
     assert torch.equal(attn.forward(q, *caches2[:2], *caches2[2:], bt, cl), got)
+
+
+def test_graph_captured_decode_step(dev):
+    """The decode step (paged write of K and V, then attention) captured in a
+    HIP graph: libtq allocates nothing and issues no memset, and the operators
+    take their outputs and workspace from torch's allocator, so the captured
+    step replays.  Every replay, with eager work and synchronisations between
+    replays, must equal the eager step bit for bit."""
+    print("[ops] graph-captured decode step", flush=True)
+    inp = _decode_step_inputs(dev)
+    q, newk, newv, step = inp["q"], inp["newk"], inp["newv"], inp["step"]
+    init = [c.clone() for c in inp["caches"]]
+    eager_caches = [c.clone() for c in init]
+    eager = step(q, newk, newv, *eager_caches)
+    torch.cuda.synchronize()
+
+    caches = [c.clone() for c in init]          # the graph's static cache tensors
+    side = torch.cuda.Stream()                  # default priority
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for _ in range(2):                      # warm-up outside the capture
+            step(q, newk, newv, *caches)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        out = step(q, newk, newv, *caches)
+    torch.cuda.synchronize()
+
+    other_q = torch.randn_like(q)
+    for rep in range(4):
+        for c, c0 in zip(caches, init):         # eager work: reset the cache
+            c.copy_(c0)
+        # unrelated eager work on the same stream between replays
+        OPS.tq_attn_decode(other_q, *init, inp["bt"], inp["cl"], inp["bits"], inp["seed"],
+                           inp["scale"])
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), "replay %d" % rep
+        for a, b in zip(caches, eager_caches):
+            assert torch.equal(a, b), "replay %d" % rep
