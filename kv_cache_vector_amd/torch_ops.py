@@ -160,21 +160,18 @@ def _(x, slots, cache_packed, cache_norms, bits, seed):
 # ---------------------------------------------------------------------------
 # decode attention
 
-@torch.library.custom_op("kv_cache_vector::tq_attn_decode", mutates_args=())
-def tq_attn_decode(q: torch.Tensor, k_packed: torch.Tensor, k_norms: torch.Tensor,
-                   v_packed: torch.Tensor, v_norms: torch.Tensor, block_tables: torch.Tensor,
-                   context_lens: torch.Tensor, bits: int, seed: int,
-                   scale: float, v_bits: int = -1) -> torch.Tensor:
-    for t, name in ((q, "query"), (k_packed, "k_packed"), (k_norms, "k_norms"),
-                    (v_packed, "v_packed"), (v_norms, "v_norms"),
-                    (block_tables, "block_tables"), (context_lens, "context_lens")):
-        _gpu(t, name)
-    vb = bits if v_bits < 0 else v_bits
+def check_attn_args(q, k_packed, k_norms, v_packed, v_norms, block_tables, context_lens,
+                    bits: int, v_bits: int, out=None):
+    """Validate the arguments of a decode-attention call before anything is
+    launched: dtypes, shapes, one device for every tensor, and (when given) an
+    output tensor the kernel may write batch * num_q_heads * head_dim binary16
+    values into.  Works on tensors of any device (no GPU needed).  Returns
+    (B, Hq, D, num_blocks, block_size, Hkv, max_blocks)."""
     if q.dim() != 3 or q.dtype != torch.float16:
         raise ValueError("query must be float16 [batch, num_q_heads, head_dim]")
     B, Hq, D = q.shape
     P = _packed_dim(D, bits)
-    PV = _packed_dim(D, vb)
+    PV = _packed_dim(D, v_bits)
     if k_packed.dim() != 4:
         raise ValueError("k_packed must be [num_blocks, block_size, num_kv_heads, P]")
     nblk, bs, hkv, Pk = k_packed.shape
@@ -189,24 +186,62 @@ def tq_attn_decode(q: torch.Tensor, k_packed: torch.Tensor, k_norms: torch.Tenso
         raise ValueError("block_tables and context_lens must be int32")
     if block_tables.dim() != 2 or block_tables.shape[0] != B or tuple(context_lens.shape) != (B,):
         raise ValueError("block_tables [batch, max_blocks], context_lens [batch]")
+    for t, name in ((k_packed, "k_packed"), (k_norms, "k_norms"), (v_packed, "v_packed"),
+                    (v_norms, "v_norms"), (block_tables, "block_tables"),
+                    (context_lens, "context_lens")):
+        if t.device != q.device:
+            raise ValueError("%s is on %s, the query on %s" % (name, t.device, q.device))
+    if out is not None:
+        if out.dtype != torch.float16 or tuple(out.shape) != (B, Hq, D):
+            raise ValueError("out must be float16 [%d, %d, %d]" % (B, Hq, D))
+        if not out.is_contiguous():
+            raise ValueError("out must be contiguous")
+        if out.device != q.device:
+            raise ValueError("out is on %s, the query on %s" % (out.device, q.device))
+    return B, Hq, D, nblk, bs, hkv, block_tables.shape[1]
+
+
+def attn_decode_into(out, q, k_packed, k_norms, v_packed, v_norms, block_tables, context_lens,
+                     bits: int, v_bits: int, seed: int, scale: float) -> torch.Tensor:
+    """Run tq_attn_decode_kv on the current stream, writing `out`.  The
+    workspace comes from torch's caching allocator on every call, so calls on
+    different streams never share one (the allocator orders its reuse on the
+    stream that allocated it)."""
+    for t, name in ((q, "query"), (k_packed, "k_packed"), (k_norms, "k_norms"),
+                    (v_packed, "v_packed"), (v_norms, "v_norms"),
+                    (block_tables, "block_tables"), (context_lens, "context_lens"), (out, "out")):
+        _gpu(t, name)
+    B, Hq, D, nblk, bs, hkv, maxb = check_attn_args(q, k_packed, k_norms, v_packed, v_norms,
+                                                    block_tables, context_lens, bits, v_bits,
+                                                    out)
     q, k_packed, v_packed = q.contiguous(), k_packed.contiguous(), v_packed.contiguous()
     k_norms, v_norms = k_norms.contiguous(), v_norms.contiguous()
     block_tables, context_lens = block_tables.contiguous(), context_lens.contiguous()
-    maxb = block_tables.shape[1]
-    out = torch.empty_like(q)
     nbytes = _lib.tq_attn_workspace_bytes(B, Hq, hkv, D, bs, maxb)
     ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
     _lib.check(_lib.tq_attn_decode_kv(
         q.data_ptr(), k_packed.data_ptr(), k_norms.data_ptr(), v_packed.data_ptr(),
         v_norms.data_ptr(), block_tables.data_ptr(), context_lens.data_ptr(), B, Hq, hkv,
-        D, bits, vb, _seed_u64(seed), bs, maxb, nblk, float(scale), out.data_ptr(),
+        D, bits, v_bits, _seed_u64(seed), bs, maxb, nblk, float(scale), out.data_ptr(),
         ws.data_ptr(), ws.numel(), _stream(q.device)), "tq_attn_decode_kv")
     return out
+
+
+@torch.library.custom_op("kv_cache_vector::tq_attn_decode", mutates_args=())
+def tq_attn_decode(q: torch.Tensor, k_packed: torch.Tensor, k_norms: torch.Tensor,
+                   v_packed: torch.Tensor, v_norms: torch.Tensor, block_tables: torch.Tensor,
+                   context_lens: torch.Tensor, bits: int, seed: int,
+                   scale: float, v_bits: int = -1) -> torch.Tensor:
+    vb = bits if v_bits < 0 else v_bits
+    _gpu(q, "query")
+    out = torch.empty_like(q, memory_format=torch.contiguous_format)
+    return attn_decode_into(out, q, k_packed, k_norms, v_packed, v_norms, block_tables,
+                            context_lens, bits, vb, seed, scale)
 
 
 @tq_attn_decode.register_fake
 def _(q, k_packed, k_norms, v_packed, v_norms, block_tables, context_lens, bits, seed, scale,
       v_bits=-1):
-    _packed_dim(q.shape[-1], bits)
-    _packed_dim(q.shape[-1], bits if v_bits < 0 else v_bits)
-    return torch.empty_like(q)
+    check_attn_args(q, k_packed, k_norms, v_packed, v_norms, block_tables, context_lens, bits,
+                    bits if v_bits < 0 else v_bits)
+    return torch.empty_like(q, memory_format=torch.contiguous_format)

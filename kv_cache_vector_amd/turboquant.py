@@ -144,56 +144,29 @@ class TQPagedAttention:
             raise ValueError("keys and values must share head_dim and seed")
         self.num_query_heads = num_query_heads
         self.scale = (1.0 / math.sqrt(tq.head_dim)) if scale is None else float(scale)
-        self._ws = {}
-
-    def workspace(self, batch: int, num_kv_heads: int, max_blocks: int, block_size: int,
-                  device) -> torch.Tensor:
-        nbytes = _lib.tq_attn_workspace_bytes(batch, self.num_query_heads, num_kv_heads,
-                                              self.tq.head_dim, block_size, max_blocks)
-        key = (str(device), nbytes)
-        ws = self._ws.get(key)
-        if ws is None:
-            ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=device)
-            self._ws = {key: ws}
-        return ws
 
     def forward(self, query, k_packed, k_norms, v_packed, v_norms, block_tables, context_lens,
                 block_size: int = 16, out: torch.Tensor | None = None) -> torch.Tensor:
-        for t, name in ((query, "query"), (k_packed, "k_packed"), (k_norms, "k_norms"),
-                        (v_packed, "v_packed"), (v_norms, "v_norms"),
-                        (block_tables, "block_tables"), (context_lens, "context_lens")):
-            _require_gpu(t, name)
+        """softmax(scale * q K^T) V over each sequence's first context_lens[b]
+        cached tokens.  Every argument is validated before the launch
+        (torch_ops.check_attn_args); `out`, when given, must be a contiguous
+        float16 [batch, num_query_heads, head_dim] tensor on the query's
+        device.  The workspace is taken from torch's caching allocator per
+        call, on the current stream."""
         tq = self.tq
-        B, Hq, D = query.shape
-        if Hq != self.num_query_heads or D != tq.head_dim or query.dtype != torch.float16:
+        if query.dim() != 3 or query.shape[1] != self.num_query_heads or \
+                query.shape[2] != tq.head_dim:
             raise ValueError("query must be float16 [batch, %d, %d]" % (self.num_query_heads,
                                                                          tq.head_dim))
         if k_packed.dim() != 4 or k_packed.shape[1] != block_size:
             raise ValueError("k_packed must be [num_blocks, block_size, num_kv_heads, P]")
-        nblk, _, hkv, P = k_packed.shape
-        if P != tq.packed_dim or \
-                tuple(v_packed.shape) != (nblk, block_size, hkv, self.v_tq.packed_dim):
-            raise ValueError("k_packed / v_packed shape mismatch")
-        if tuple(k_norms.shape) != (nblk, block_size, hkv) or \
-                tuple(v_norms.shape) != (nblk, block_size, hkv):
-            raise ValueError("norms must be [num_blocks, block_size, num_kv_heads]")
-        if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
-            raise ValueError("block_tables and context_lens must be int32")
-        if block_tables.dim() != 2 or block_tables.shape[0] != B or context_lens.shape != (B,):
-            raise ValueError("block_tables [batch, max_blocks], context_lens [batch]")
-        query, k_packed, v_packed = query.contiguous(), k_packed.contiguous(), v_packed.contiguous()
-        k_norms, v_norms = k_norms.contiguous(), v_norms.contiguous()
-        block_tables, context_lens = block_tables.contiguous(), context_lens.contiguous()
-        maxb = block_tables.shape[1]
+        torch_ops.check_attn_args(query, k_packed, k_norms, v_packed, v_norms, block_tables,
+                                  context_lens, tq.bits, self.v_tq.bits, out)
         if out is None:
-            out = torch.empty_like(query)
-        ws = self.workspace(B, hkv, maxb, block_size, query.device)
-        _lib.check(_lib.tq_attn_decode_kv(
-            query.data_ptr(), k_packed.data_ptr(), k_norms.data_ptr(), v_packed.data_ptr(),
-            v_norms.data_ptr(), block_tables.data_ptr(), context_lens.data_ptr(), B, Hq, hkv,
-            tq.head_dim, tq.bits, self.v_tq.bits, tq.seed, block_size, maxb, nblk, self.scale,
-            out.data_ptr(), ws.data_ptr(), ws.numel(), _stream(query.device)),
-            "tq_attn_decode_kv")
-        return out
+            _require_gpu(query, "query")
+            out = torch.empty_like(query, memory_format=torch.contiguous_format)
+        return torch_ops.attn_decode_into(out, query, k_packed, k_norms, v_packed, v_norms,
+                                          block_tables, context_lens, tq.bits, self.v_tq.bits,
+                                          tq.seed, self.scale)
 
     __call__ = forward

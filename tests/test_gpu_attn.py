@@ -76,11 +76,21 @@ def run_attn(dev, what, bits=4, B=3, Hq=8, Hkv=2, T=37, ragged=True, seed=0, sca
         bt_o[bt_o >= kp.shape[0]] = 0
     _, ref = oracle.attn_decode(wl["q"], kp, kn, vp, vn, bt_o, cl, Hkv, bits, seed, sc,
                                 sel=sel, want_f64=True, v_bits=vb)
+    delta = None
+    if np.all(cl == 1):
+        # one token per sequence: its softmax weight is exactly 1 and the
+        # output is its value, so the kernel's f32 error is bounded tightly
+        # and the binary16 rounding is checked bit for bit outside that bound
+        cv, _ = oracle.codebook(vb)
+        heads = np.arange(Hq) // (Hq // Hkv)
+        rows = bt_o[:, 0][:, None]                               # [B, 1]
+        delta = P.single_token_delta(vp[rows, 0, heads[None, :]], vn[rows, 0, heads[None, :]],
+                                     cv, vb, d)                  # [B, Hq, 1]
     if sel is None:
-        P.compare_attn(g, ref, what)
+        P.compare_attn(g, ref, what, delta=delta)
     else:
         m = np.asarray(sel, bool)
-        P.compare_attn(g[m], ref[m], what)
+        P.compare_attn(g[m], ref[m], what, delta=None if delta is None else delta[m])
     return g
 
 
@@ -109,6 +119,17 @@ def test_widths_gqa_16(dev, bits):
 @pytest.mark.parametrize("T", [1, 2, 15, 16, 17, 255, 256, 257, 1000, 1500])
 def test_context_lengths(dev, T):
     run_attn(dev, "T=%d" % T, B=4, Hq=32, Hkv=8, T=T, ragged=(T > 3))
+
+
+@pytest.mark.parametrize("d", [64, 128, 256])
+@pytest.mark.parametrize("bits", [4, 3, 2])
+def test_single_token_rounding(dev, d, bits):
+    """Context 1 for every sequence: the output is the one cached value, and
+    its binary16 rounding (nearest-even) is compared bit for bit with the
+    oracle's, outside the kernel's f32 error bound."""
+    Hq = 32 if d < 256 else 16
+    run_attn(dev, "single token d=%d b%d" % (d, bits), bits=bits, B=32, Hq=Hq, Hkv=8, T=1,
+             ragged=False, d=d)
 
 
 # ---------------------------------------------------------------------------
@@ -230,3 +251,35 @@ def test_long_context_batch1_128k(dev):
     """One 131,072-token sequence, 64 query / 8 kv heads: 512 context splits
     merged by the combine kernel."""
     _c5(dev, False, [(0, 0), (0, 5)], B=1, Hq=64, Hkv=8, T=131072, heads_per_sample=2)
+
+
+def test_two_streams_one_instance(dev):
+    """One TQPagedAttention instance called on two default-priority streams
+    back to back, without synchronising in between: each call has its own
+    workspace, and both outputs match the oracle."""
+    B, Hq, Hkv, T = 4, 16, 4, 600
+    cases = []
+    for k in range(2):
+        wl = W.attn_workload(batch=B, num_q_heads=Hq, num_kv_heads=Hkv, context=T,
+                             seed=900 + k, perm_seed=910 + k, ragged=True)
+        kp, kn = oracle_encode_parallel(wl["k"], 4, 0)
+        vp, vn = oracle_encode_parallel(wl["v"], 4, 0)
+        cases.append((wl, kp, kn, vp, vn))
+    tq = TurboQuant(D, 4, 0, dev)
+    attn = TQPagedAttention(tq, Hq)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    dev_in = [tuple(t(a) for a in (wl["q"], kp, kn, vp, vn, wl["block_tables"],
+                                   wl["context_lens"])) for wl, kp, kn, vp, vn in cases]
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(dev), torch.cuda.Stream(dev)]
+    outs = []
+    P.log("[attn] two streams: B=%d Hq=%d Hkv=%d T=%d" % (B, Hq, Hkv, T))
+    for s, args in zip(streams, dev_in):
+        with torch.cuda.stream(s):
+            outs.append(attn.forward(*args))
+    torch.cuda.synchronize()
+    for (wl, kp, kn, vp, vn), o in zip(cases, outs):
+        _, ref = oracle.attn_decode(wl["q"], kp, kn, vp, vn, wl["block_tables"],
+                                    wl["context_lens"], Hkv, 4, 0, 1 / math.sqrt(D),
+                                    want_f64=True)
+        P.compare_attn(o.cpu().numpy(), ref, "stream")

@@ -68,3 +68,65 @@ def test_host_tensors_refused():
     x = torch.zeros(4, 128, dtype=torch.float16)
     with pytest.raises(ValueError, match="GPU"):
         OPS.tq_encode(x, 4, 0)
+
+
+def _attn_args(device="meta", P=64, **over):
+    a = dict(query=torch.empty(3, 8, 128, dtype=torch.float16, device=device),
+             k_packed=torch.empty(10, 16, 2, P, dtype=torch.uint8, device=device),
+             k_norms=torch.empty(10, 16, 2, dtype=torch.float32, device=device),
+             v_packed=torch.empty(10, 16, 2, P, dtype=torch.uint8, device=device),
+             v_norms=torch.empty(10, 16, 2, dtype=torch.float32, device=device),
+             block_tables=torch.empty(3, 4, dtype=torch.int32, device=device),
+             context_lens=torch.empty(3, dtype=torch.int32, device=device))
+    a.update(over)
+    return a
+
+
+def _paged_attention():
+    from kv_cache_vector_amd.turboquant import TQPagedAttention, TurboQuant
+    return TQPagedAttention(TurboQuant(128, 4, 0, "cuda"), 8)
+
+
+def test_paged_attention_valid_arguments_reach_the_launch():
+    """Valid (meta) arguments pass every check and stop only at the GPU
+    requirement, i.e. at the launch itself."""
+    attn = _paged_attention()
+    with pytest.raises(ValueError, match="GPU tensor"):
+        attn.forward(**_attn_args())
+    with pytest.raises(ValueError, match="GPU tensor"):
+        attn.forward(**_attn_args(), out=torch.empty(3, 8, 128, dtype=torch.float16,
+                                                     device="meta"))
+
+
+@pytest.mark.parametrize("bad", [
+    dict(out=torch.empty(3, 8, 64, dtype=torch.float16, device="meta")),        # short
+    dict(out=torch.empty(3, 8, 128, dtype=torch.float32, device="meta")),       # dtype
+    dict(out=torch.empty(3, 128, 8, dtype=torch.float16, device="meta").transpose(1, 2)),
+    dict(out=torch.empty(3, 8, 128, dtype=torch.float16, device="cpu")),        # device
+    dict(k_norms=torch.empty(10, 16, 2, dtype=torch.float16, device="meta")),
+    dict(v_norms=torch.empty(10, 16, 2, dtype=torch.float16, device="meta")),
+    dict(k_packed=torch.empty(10, 16, 2, 64, dtype=torch.int8, device="meta")),
+    dict(v_packed=torch.empty(10, 16, 2, 32, dtype=torch.uint8, device="meta")),
+    dict(block_tables=torch.empty(3, 4, dtype=torch.int64, device="meta")),
+    dict(context_lens=torch.empty(4, dtype=torch.int32, device="meta")),
+    dict(block_tables=torch.empty(3, 4, dtype=torch.int32, device="cpu")),      # device
+    dict(query=torch.empty(3, 8, 128, dtype=torch.float32, device="meta")),
+    dict(query=torch.empty(3, 4, 128, dtype=torch.float16, device="meta")),     # heads
+])
+def test_paged_attention_rejects_bad_arguments_before_launch(bad):
+    """Each bad argument raises a ValueError naming it, never the GPU
+    requirement (the check runs before anything reaches libtq)."""
+    attn = _paged_attention()
+    args = _attn_args()
+    out = bad.pop("out", None)
+    args.update(bad)
+    with pytest.raises(ValueError) as e:
+        attn.forward(**args, out=out)
+    assert "GPU tensor" not in str(e.value)
+
+
+def test_attention_op_fake_checks_arguments():
+    a = _attn_args()
+    a["k_norms"] = torch.empty(10, 16, 2, dtype=torch.float16, device="meta")
+    with pytest.raises(ValueError, match="float32"):
+        OPS.tq_attn_decode(*a.values(), 4, 0, 0.088)
