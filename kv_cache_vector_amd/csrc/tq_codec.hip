@@ -233,6 +233,39 @@ __device__ __forceinline__ void put_code2(uint32_t &acc, float y, float thr, uin
 #undef TQ_PUT_CODE
 #undef TQ_PUT_FIRST
 
+// LDS writes of a wave made visible to its other lanes: LDS instructions of
+// one wave execute in order, so only the compiler has to be kept from moving
+// the accesses across this point.
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Store QW consecutive dwords (a quarter of a packed row) at byte offset off.
+template <int QW>
+__device__ __forceinline__ void store_quarter(const uint32_t (&v)[QW], __amdgpu_buffer_rsrc_t rp,
+                                              uint32_t off) {
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
+    if constexpr (QW % 4 == 0) {
+#pragma unroll
+        for (int i = 0; i < QW; i += 4)
+            __builtin_amdgcn_raw_buffer_store_b128(u32x4{v[i], v[i + 1], v[i + 2], v[i + 3]}, rp,
+                                                   off + 4u * i, 0, 0);
+    } else if constexpr (QW == 3) {
+        __builtin_amdgcn_raw_buffer_store_b96(u32x3{v[0], v[1], v[2]}, rp, off, 0, 0);
+    } else if constexpr (QW == 6) {
+        __builtin_amdgcn_raw_buffer_store_b96(u32x3{v[0], v[1], v[2]}, rp, off, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b96(u32x3{v[3], v[4], v[5]}, rp, off + 12u, 0, 0);
+    } else if constexpr (QW == 2) {
+        __builtin_amdgcn_raw_buffer_store_b64(u32x2{v[0], v[1]}, rp, off, 0, 0);
+    } else {
+        static_assert(QW == 1, "quarter size");
+        __builtin_amdgcn_raw_buffer_store_b32(v[0], rp, off, 0, 0);
+    }
+}
+
 // 2-bit codes of f[R..]: code r = 8k + j of the lane's stream sits at bit
 // 16 (k & 1) + 2j of stream dword k / 2, i.e. in byte 2 (k & 1) + j / 4 at
 // position j % 4; a[p][m] collects position p of stream dword m.
@@ -282,6 +315,13 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(const u32x4 *__restric
     constexpr int NPK = (K * BITS + 3) / 4;     // dwords of the lane's field stream (4, 2 bits)
     __shared__ float2 qtab[2 * kCells + 1];
     __shared__ u32x4 smask[4 * K];
+    // one staging row per quad for the packed output: PW dwords, padded to a
+    // multiple of 4 dwords (16-byte reads) whose quarter is odd, so that the
+    // quads of a wave spread over the LDS banks
+    // (rows of a whole number of dwords per lane only: not 3 bits at head_dim 64)
+    constexpr bool kStage = !PAGED && PW % 4 == 0;
+    constexpr int kStageRow = ((PW / 4) % 2 == 0) ? PW + 4 : PW;
+    __shared__ __attribute__((aligned(16))) uint32_t stage[kStage ? kVecPerBlock * kStageRow : 1];
     for (int t = threadIdx.x; t < 2 * kCells + 1; t += blockDim.x) qtab[t] = tb.cell[t];
     if (threadIdx.x < 16 * K)
         store_sign_mask<K, true>(k, threadIdx.x, reinterpret_cast<uint32_t *>(smask));
@@ -421,12 +461,34 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(const u32x4 *__restric
             for (int i = 0; i < NS; ++i)
                 if (BITS != 3 || q < 3) dst[si[i]] = sv[i];
             if (q == 0) norms[row] = nrm;
-        } else {
+        } else if constexpr (!kStage) {
             const __amdgpu_buffer_rsrc_t rp = span_rsrc(packed + v0 * PW, nb * (PW * 4u));
 #pragma unroll
             for (int i = 0; i < NS; ++i)
                 if (BITS != 3 || q < 3)
                     __builtin_amdgcn_raw_buffer_store_b32(sv[i], rp, qv * (PW * 4u) + 4u * si[i], 0, 0);
+            if (q == 0)
+                __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, nrm),
+                                                      span_rsrc(norms + v0, nb * 4u), qv * 4u, 0, 0);
+        } else {
+            // Whole rows per store instruction: the quad's dwords go through
+            // its own LDS row (wave-local, so LDS order within the wave is
+            // the only synchronisation needed), then lane q stores the
+            // contiguous quarter q of the row.  A wave's store then covers
+            // its 16 consecutive rows without gaps.
+            uint32_t *srow = stage + (threadIdx.x >> 2) * kStageRow;
+#pragma unroll
+            for (int i = 0; i < NS; ++i)
+                if (BITS != 3 || q < 3) srow[si[i]] = sv[i];
+            wave_lds_sync();
+            constexpr int QW = PW / 4;                  // dwords per lane
+            uint32_t ov[QW];
+#pragma unroll
+            for (int i = 0; i < QW; ++i) ov[i] = srow[QW * q + i];
+            wave_lds_sync();
+            const __amdgpu_buffer_rsrc_t rp = span_rsrc(packed + v0 * PW, nb * (PW * 4u));
+            const uint32_t off = qv * (PW * 4u) + 4u * QW * q;
+            store_quarter<QW>(ov, rp, off);
             if (q == 0)
                 __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, nrm),
                                                       span_rsrc(norms + v0, nb * 4u), qv * 4u, 0, 0);
