@@ -29,7 +29,9 @@
  *   - Every data pointer is a DEVICE pointer (hipMalloc'd or a torch CUDA
  *     tensor's storage) owned by the caller; the library never allocates,
  *     frees or retains memory and keeps no state beyond an immutable codebook
- *     table computed once per process.
+ *     table computed once per process (and, for tq_attn_decode_kv_noalloc
+ *     only, one fixed workspace array per GPU that is part of the loaded
+ *     code object).
  *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = the default
  *     stream).  A status of TQ_OK means the work was enqueued; a kernel fault
  *     surfaces at the caller's next synchronisation.
@@ -192,6 +194,36 @@ tq_status tq_attn_decode_kv(const void *q_f16, const uint8_t *k_packed, const fl
                             int v_bits, uint64_t seed, int block_size, int max_blocks_per_seq,
                             int64_t num_blocks, float scale, void *out_f16, void *workspace,
                             size_t workspace_bytes, void *stream);
+
+/*
+ * tq_attn_decode_kv for callers that cannot allocate device memory (code
+ * under HIP graph capture, serving loops or harnesses that forbid hipMalloc):
+ * the same computation, arguments, output and errors, but no workspace
+ * argument.  The partial softmax state lives in a fixed array inside the
+ * library, TQ_ATTN_NOALLOC_WORKSPACE_BYTES bytes on each GPU it runs on
+ * (held from the first call on that device until the process ends); the
+ * first call on a device looks up that array's address there.  The call
+ * allocates nothing.
+ *   - A shape whose tq_attn_workspace_bytes(...) exceeds
+ *     TQ_ATTN_NOALLOC_WORKSPACE_BYTES returns TQ_ERR_WORKSPACE before
+ *     anything is enqueued (at head_dim 128: batch * num_q_heads * splits
+ *     up to 64,528 partial states, e.g. batch 16 x 32 heads at a 32K
+ *     context uses 4.3 MB).
+ *   - Every call on a GPU uses that GPU's one array: calls that may overlap
+ *     on one GPU (on different streams, or from different host threads)
+ *     race and must be serialised by the caller.  Nothing in the array needs
+ *     to start at zero; its contents after a call are unspecified.
+ *   - TQ_ERR_HIP also reports a failed address lookup.
+ */
+#define TQ_ATTN_NOALLOC_WORKSPACE_BYTES ((size_t)32 << 20)
+tq_status tq_attn_decode_kv_noalloc(const void *q_f16, const uint8_t *k_packed,
+                                    const float *k_norms, const uint8_t *v_packed,
+                                    const float *v_norms, const int32_t *block_tables,
+                                    const int32_t *context_lens, int batch, int num_q_heads,
+                                    int num_kv_heads, int head_dim, int k_bits, int v_bits,
+                                    uint64_t seed, int block_size, int max_blocks_per_seq,
+                                    int64_t num_blocks, float scale, void *out_f16,
+                                    void *stream);
 
 /*
  * Host-side test hooks (no device work).

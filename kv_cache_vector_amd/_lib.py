@@ -22,7 +22,11 @@ STATUS_NAMES = {0: "TQ_OK", 1: "TQ_ERR_INVALID_ARG", 2: "TQ_ERR_UNSUPPORTED",
 # every symbol include/tq.h declares
 SYMBOLS = ("tq_status_string", "tq_abi_version", "tq_packed_bytes", "tq_encode", "tq_decode",
            "tq_encode_paged", "tq_attn_workspace_bytes", "tq_attn_decode", "tq_attn_decode_kv",
-           "tq_codebook", "tq_signs")
+           "tq_attn_decode_kv_noalloc", "tq_codebook", "tq_signs")
+
+# bytes of the library-owned workspace of tq_attn_decode_kv_noalloc, per GPU
+# (TQ_ATTN_NOALLOC_WORKSPACE_BYTES in include/tq.h)
+TQ_ATTN_NOALLOC_WORKSPACE_BYTES = 32 << 20
 
 _P = ctypes.c_void_p
 _I64 = ctypes.c_int64
@@ -64,6 +68,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                                      _I, _I64, ctypes.c_float, _P, _P, ctypes.c_size_t, _P]
         L.tq_attn_decode_kv.argtypes = [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _U64,
                                         _I, _I, _I64, ctypes.c_float, _P, _P, ctypes.c_size_t, _P]
+        L.tq_attn_decode_kv_noalloc.argtypes = [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I,
+                                                _I, _U64, _I, _I, _I64, ctypes.c_float, _P, _P]
         L.tq_codebook.argtypes = [_I, _P, _P]
         L.tq_signs.argtypes = [_U64, _I, _P]
         _lib = L
@@ -120,6 +126,17 @@ def tq_attn_decode_kv(q_f16, k_packed, k_norms, v_packed, v_norms, block_tables,
                                     k_bits, v_bits, seed, block_size, max_blocks_per_seq,
                                     num_blocks, scale, out_f16, workspace, workspace_bytes,
                                     stream)
+
+
+def tq_attn_decode_kv_noalloc(q_f16, k_packed, k_norms, v_packed, v_norms, block_tables,
+                              context_lens, batch, num_q_heads, num_kv_heads, head_dim, k_bits,
+                              v_bits, seed, block_size, max_blocks_per_seq, num_blocks, scale,
+                              out_f16, stream) -> int:
+    return load().tq_attn_decode_kv_noalloc(q_f16, k_packed, k_norms, v_packed, v_norms,
+                                            block_tables, context_lens, batch, num_q_heads,
+                                            num_kv_heads, head_dim, k_bits, v_bits, seed,
+                                            block_size, max_blocks_per_seq, num_blocks, scale,
+                                            out_f16, stream)
 
 
 def tq_codebook(bits: int):

@@ -292,13 +292,20 @@ size_t tq_attn_workspace_bytes(int batch, int num_q_heads, int num_kv_heads, int
     return tq::attn_workspace_bytes(s);
 }
 
-tq_status tq_attn_decode_kv(const void *q_f16, const uint8_t *k_packed, const float *k_norms,
-                            const uint8_t *v_packed, const float *v_norms,
-                            const int32_t *block_tables, const int32_t *context_lens, int batch,
-                            int num_q_heads, int num_kv_heads, int head_dim, int k_bits,
-                            int v_bits, uint64_t seed, int block_size, int max_blocks_per_seq,
-                            int64_t num_blocks, float scale, void *out_f16, void *workspace,
-                            size_t workspace_bytes, void *stream) {
+}  // extern "C"
+
+namespace {
+
+// Shared by the attention entry points.  With `own_ws` the workspace is the
+// library's static per-device array (the caller passes none), checked
+// against its fixed size instead of a caller's buffer.
+tq_status attn_decode(const void *q_f16, const uint8_t *k_packed, const float *k_norms,
+                      const uint8_t *v_packed, const float *v_norms,
+                      const int32_t *block_tables, const int32_t *context_lens, int batch,
+                      int num_q_heads, int num_kv_heads, int head_dim, int k_bits, int v_bits,
+                      uint64_t seed, int block_size, int max_blocks_per_seq, int64_t num_blocks,
+                      float scale, void *out_f16, void *workspace, size_t workspace_bytes,
+                      bool own_ws, void *stream) {
     tq_status st = check_shape(head_dim, k_bits);
     if (st != TQ_OK) return st;
     st = check_shape(head_dim, v_bits);
@@ -317,15 +324,20 @@ tq_status tq_attn_decode_kv(const void *q_f16, const uint8_t *k_packed, const fl
         return TQ_ERR_INVALID_ARG;
     if (!aligned(q_f16, 16) || !aligned(out_f16, 16) || !aligned(k_packed, 16) ||
         !aligned(v_packed, 16) || !aligned(k_norms, 4) || !aligned(v_norms, 4) ||
-        !aligned(block_tables, 4) || !aligned(context_lens, 4) || !aligned(workspace, 16))
+        !aligned(block_tables, 4) || !aligned(context_lens, 4) ||
+        (!own_ws && !aligned(workspace, 16)))
         return TQ_ERR_MISALIGNED;
     tq::AttnShape s{batch, num_q_heads, num_kv_heads, head_dim, k_bits, v_bits,
                     max_blocks_per_seq, num_blocks};
     if (!tq::attn_supported(s)) return TQ_ERR_UNSUPPORTED;
     const size_t need = tq::attn_workspace_bytes(s);
-    if (need > 0 && (!workspace || workspace_bytes < need)) return TQ_ERR_WORKSPACE;
-    // the two written arrays (output, workspace) against each other and
-    // against every input
+    if (own_ws) {
+        if (need > tq::kAttnStaticWorkspaceBytes) return TQ_ERR_WORKSPACE;
+    } else if (need > 0 && (!workspace || workspace_bytes < need)) {
+        return TQ_ERR_WORKSPACE;
+    }
+    // the written arrays (output and a caller's workspace) against each other
+    // and against every input
     const size_t nout = (size_t)batch * num_q_heads * head_dim * 2;
     const size_t rows = (size_t)num_blocks * tq::kAttnBlockSize * num_kv_heads;
     const struct { const void *p; size_t n; } in[] = {
@@ -337,15 +349,52 @@ tq_status tq_attn_decode_kv(const void *q_f16, const uint8_t *k_packed, const fl
         {block_tables, (size_t)batch * max_blocks_per_seq * 4},
         {context_lens, (size_t)batch * 4},
     };
-    if (overlap(out_f16, nout, workspace, need)) return TQ_ERR_INVALID_ARG;
+    const size_t nws = own_ws ? 0 : need;
+    if (overlap(out_f16, nout, workspace, nws)) return TQ_ERR_INVALID_ARG;
     for (const auto &a : in)
-        if (overlap(out_f16, nout, a.p, a.n) || overlap(workspace, need, a.p, a.n))
+        if (overlap(out_f16, nout, a.p, a.n) || overlap(workspace, nws, a.p, a.n))
             return TQ_ERR_INVALID_ARG;
+    if (own_ws) {
+        // the library's array on the current device (looked up on the first
+        // call there); no allocation
+        if (tq::attn_static_workspace(&workspace) != hipSuccess) return TQ_ERR_HIP;
+    }
     const CodecConsts kc = make_consts(head_dim, k_bits, seed);
     const CodecConsts vc = make_consts(head_dim, v_bits, seed);
     return from_hip(tq::launch_attn(s, kc, vc, q_f16, k_packed, k_norms, v_packed, v_norms,
                                     block_tables, context_lens, scale, out_f16, workspace,
                                     (hipStream_t)stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+tq_status tq_attn_decode_kv(const void *q_f16, const uint8_t *k_packed, const float *k_norms,
+                            const uint8_t *v_packed, const float *v_norms,
+                            const int32_t *block_tables, const int32_t *context_lens, int batch,
+                            int num_q_heads, int num_kv_heads, int head_dim, int k_bits,
+                            int v_bits, uint64_t seed, int block_size, int max_blocks_per_seq,
+                            int64_t num_blocks, float scale, void *out_f16, void *workspace,
+                            size_t workspace_bytes, void *stream) {
+    return attn_decode(q_f16, k_packed, k_norms, v_packed, v_norms, block_tables, context_lens,
+                       batch, num_q_heads, num_kv_heads, head_dim, k_bits, v_bits, seed,
+                       block_size, max_blocks_per_seq, num_blocks, scale, out_f16, workspace,
+                       workspace_bytes, false, stream);
+}
+
+tq_status tq_attn_decode_kv_noalloc(const void *q_f16, const uint8_t *k_packed,
+                                    const float *k_norms, const uint8_t *v_packed,
+                                    const float *v_norms, const int32_t *block_tables,
+                                    const int32_t *context_lens, int batch, int num_q_heads,
+                                    int num_kv_heads, int head_dim, int k_bits, int v_bits,
+                                    uint64_t seed, int block_size, int max_blocks_per_seq,
+                                    int64_t num_blocks, float scale, void *out_f16,
+                                    void *stream) {
+    return attn_decode(q_f16, k_packed, k_norms, v_packed, v_norms, block_tables, context_lens,
+                       batch, num_q_heads, num_kv_heads, head_dim, k_bits, v_bits, seed,
+                       block_size, max_blocks_per_seq, num_blocks, scale, out_f16, nullptr, 0,
+                       true, stream);
 }
 
 tq_status tq_attn_decode(const void *q_f16, const uint8_t *k_packed, const float *k_norms,

@@ -59,6 +59,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "tq_attn_internal.h"
 
 namespace tq {
@@ -872,6 +874,35 @@ void launch_split(bool paired, dim3 grid, dim3 block, hipStream_t stream, const 
 }
 
 }  // namespace
+
+// Library-owned workspace for callers that cannot allocate: one fixed array
+// per GPU (each device holds its own copy at its own address, from the first
+// call on that device until the process ends).  The array's name is a host
+// stand-in; kernels get the device address that hipGetSymbolAddress returns.
+static __device__ __attribute__((aligned(256))) unsigned char scratch[kAttnStaticWorkspaceBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];
+}  // namespace
+
+hipError_t attn_static_workspace(void **ptr) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return hipSuccess;
+}
 
 bool attn_supported(const AttnShape &s) {
     if (s.num_kv_heads <= 0 || s.num_q_heads % s.num_kv_heads) return false;

@@ -2,6 +2,7 @@
 // attention kernels (tq_attn.hip).  Not installed; not part of the ABI.
 #pragma once
 
+#include "tq.h"
 #include "tq_internal.h"
 
 namespace tq {
@@ -26,6 +27,14 @@ bool attn_supported(const AttnShape &s);
 int attn_split_tokens(const AttnShape &s);
 int attn_num_splits(const AttnShape &s);
 size_t attn_workspace_bytes(const AttnShape &s);
+
+// Size of the library-owned attention workspace (per GPU) used by the
+// entry point that allocates nothing.
+constexpr size_t kAttnStaticWorkspaceBytes = TQ_ATTN_NOALLOC_WORKSPACE_BYTES;
+
+// Device address of that workspace on the current device, looked up once per
+// device (hipGetSymbolAddress) and cached.
+hipError_t attn_static_workspace(void **ptr);
 
 hipError_t launch_attn(const AttnShape &s, const CodecConsts &kc, const CodecConsts &vc,
                        const void *q, const uint8_t *k_packed, const float *k_norms,

@@ -221,3 +221,35 @@ def test_attention_argument_errors(L):
     assert call_kv(4, 2, batch=0) == OK
     assert call_kv(2, 4, q=None) == INVAL
     assert call_kv(3, 4, wsb=ws - 16) == WS
+
+
+def test_noalloc_attention_argument_errors(L):
+    """The allocation-free attention entry point checks its arguments like
+    tq_attn_decode_kv, and refuses shapes whose partial state does not fit its
+    fixed array, all before anything touches the GPU."""
+    f = L.tq_attn_decode_kv_noalloc
+
+    def call(kb=4, vb=4, **kw):
+        args = dict(q=A, kp=B, kn=B + (1 << 24), vp=C, vn=C + (1 << 24), bt=A + (1 << 24),
+                    cl=A + (1 << 25), batch=16, hq=32, hkv=8, d=128, seed=0, bs=16,
+                    maxb=2048, nblk=32768, scale=0.088, out=A + (1 << 26))
+        args.update(kw)
+        return f(args["q"], args["kp"], args["kn"], args["vp"], args["vn"], args["bt"],
+                 args["cl"], args["batch"], args["hq"], args["hkv"], args["d"], kb, vb,
+                 args["seed"], args["bs"], args["maxb"], args["nblk"], args["scale"],
+                 args["out"], None)
+
+    assert call(kb=5) == UNSUP
+    assert call(d=96) == UNSUP
+    assert call(batch=0) == OK
+    assert call(q=None) == INVAL
+    assert call(out=A + (1 << 26) + 2) == MISAL
+    assert call(out=A) == INVAL                     # output overlaps the query
+    assert call(bs=32) == UNSUP
+    # the fixed array: 32 MiB per GPU
+    assert _lib.TQ_ATTN_NOALLOC_WORKSPACE_BYTES == 32 << 20
+    need = L.tq_attn_workspace_bytes(512, 64, 8, 128, 16, 1024)
+    assert need > _lib.TQ_ATTN_NOALLOC_WORKSPACE_BYTES
+    assert call(batch=512, hq=64, maxb=1024, nblk=512 * 1024, out=0x70000000) == WS
+    header = open(HEADER).read()
+    assert "#define TQ_ATTN_NOALLOC_WORKSPACE_BYTES ((size_t)32 << 20)" in header
