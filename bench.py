@@ -16,8 +16,10 @@ Prints one JSON line.  `value` is fp16 key/value bytes passed through the
 codec per second (encode and decode both count their 256 B/vector of fp16).
 `roofline` rates the slower of the two kernels by its algorithmic bytes
 (256 B fp16 + 64 B codes + 4 B norm per vector) against the 8 TB/s HBM peak.
-`cpu_baseline` is the plain CPU oracle timed on this host's cores on a
-bounded sample of the same cache.
+`cpu_baseline` is the plain CPU oracle timed on this host: encode + decode of
+the same whole cache on up to 16 threads (and of layer 0 on one thread,
+reported in `extra`).  `extra` also rates the two kernels against
+no-arithmetic kernels that move the same byte mix (include/tq_ceiling.h).
 """
 from __future__ import annotations
 
@@ -71,15 +73,26 @@ def measured_traffic(kernel: str):
     return None if k is None else k.get("bytes_per_launch")
 
 
-def cpu_baseline(x_host, budget_s: float = 10.0, chunk: int = 2048):
-    """The oracle (encode + decode) on consecutive 2048-vector chunks of layers
-    0-1 of the cache, on up to 16 host threads, for ~budget_s seconds."""
-    import numpy as np
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def oracle_codec_rate(chunks, threads: int, budget_s: float, chunk: int = 4096):
+    """The unmodified oracle (encode + decode, 4 bits, codec seed 0) over the
+    host arrays in `chunks` (each [n, 128] fp16), split into `chunk`-vector
+    pieces taken in order by `threads` host threads, until done or until
+    budget_s has passed.  Returns (vectors done, wall seconds)."""
     import oracle
     oracle.build(force=False)
     o = oracle.default()
-    threads = max(1, min(16, os.cpu_count() or 1))
-    nchunks = x_host.shape[0] // chunk
+    pieces = [(ci, i) for ci, c in enumerate(chunks) for i in range(0, c.shape[0], chunk)]
     lock = threading.Lock()
     state = {"next": 0, "done": 0}
     deadline = [0.0]
@@ -87,15 +100,15 @@ def cpu_baseline(x_host, budget_s: float = 10.0, chunk: int = 2048):
     def worker():
         while True:
             with lock:
-                if time.perf_counter() > deadline[0] or state["next"] >= nchunks:
+                if time.perf_counter() > deadline[0] or state["next"] >= len(pieces):
                     return
-                i = state["next"]
+                ci, i = pieces[state["next"]]
                 state["next"] += 1
-            xs = x_host[i * chunk:(i + 1) * chunk]
+            xs = chunks[ci][i:i + chunk]
             p, n = o.encode(xs, BITS, 0)
             o.decode(p, n, D, BITS, 0)
             with lock:
-                state["done"] += 1
+                state["done"] += xs.shape[0]
 
     t0 = time.perf_counter()
     deadline[0] = t0 + budget_s
@@ -104,21 +117,28 @@ def cpu_baseline(x_host, budget_s: float = 10.0, chunk: int = 2048):
         t.start()
     for t in ts:
         t.join()
-    wall = time.perf_counter() - t0
-    nvec = state["done"] * chunk
+    return state["done"], time.perf_counter() - t0
+
+
+def cpu_baseline(layers, budget_s: float = 60.0, single_layer_budget_s: float = 30.0):
+    """The oracle timed on this host: encode + decode of the whole cache
+    (`layers`, a list of [n, 128] fp16 host arrays) on min(16, hardware
+    threads) threads, and of layer 0 on one thread.  A run that hits its
+    budget reports the vectors it finished.  Returns (record, 1-thread GB/s)."""
+    hw = os.cpu_count() or 1
+    threads = max(1, min(16, hw))
+    total = sum(x.shape[0] for x in layers)
+    nvec, wall = oracle_codec_rate(layers, threads, budget_s)
     value = 2 * nvec * 2 * D / wall / 1e9
-    cpu = "unknown"
-    try:
-        with open("/proc/cpuinfo") as f:
-            for line in f:
-                if line.startswith("model name"):
-                    cpu = line.split(":", 1)[1].strip()
-                    break
-    except OSError:
-        pass
-    return {"value": round(value, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": "encode+decode of the first %d vectors of layers 0-1 (4 bits), %d threads, "
-                      "%.1f s wall; %s" % (nvec, threads, wall, cpu)}
+    n1, w1 = oracle_codec_rate(layers[:1], 1, single_layer_budget_s)
+    one = 2 * n1 * 2 * D / w1 / 1e9
+    what = "the whole cache" if nvec == total else "the first %d of %d vectors" % (nvec, total)
+    rec = {"value": round(value, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+           "sample": "encode+decode (4 bits) of %s (%d vectors) on %d threads in %.1f s; "
+                     "1 thread: %.4f GB/s over %d vectors of layer 0 in %.1f s; %d hardware "
+                     "threads visible, at most 16 used (the host share of one GPU); %s"
+                     % (what, nvec, threads, wall, one, n1, w1, hw, _cpu_model())}
+    return rec, one
 
 
 def main() -> int:
@@ -163,11 +183,11 @@ def main() -> int:
 
     log("generating the 8B-shaped cache: %d vectors (%.2f GB fp16)" % (N, N * 2 * D / 1e9))
     x = torch.empty((N, D), dtype=torch.float16, device=dev)
-    host_sample = []
+    host_layers = []
     for layer in range(LAYERS):
         xl = W.llama8b_layer(layer)
-        if layer < 2:
-            host_sample.append(xl)
+        if not args.no_cpu_baseline:
+            host_layers.append(xl)
         x[layer * PER_LAYER:(layer + 1) * PER_LAYER].copy_(torch.from_numpy(xl))
         if layer % 8 == 7:
             log("  layer %d/%d uploaded" % (layer + 1, LAYERS))
@@ -228,16 +248,9 @@ def main() -> int:
         "decode_hbm_frac": round(N * ALGO_BYTES / (dec_avg * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
         "host_wall_s": round(wall, 3),
     }
-    # achievable-bandwidth reference: a device-to-device copy of the fp16 cache
-    cp = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    out.copy_(x)
-    cp[0].record(stream)
-    for _ in range(5):
-        out.copy_(x)
-    cp[1].record(stream)
-    torch.cuda.synchronize()
-    cms = cp[0].elapsed_time(cp[1]) / 5
-    extra["copy_GBps"] = round(2 * N * 2 * D / (cms * 1e-3) / 1e9, 1)
+    # achievable-bandwidth reference: the no-arithmetic kernels that move the
+    # codec's own byte mix with its work mapping (include/tq_ceiling.h)
+    extra.update(ceiling_measurement(torch, stream, x, packed, norms, out, enc_avg, dec_avg))
 
     if not args.no_extras:
         del out
@@ -259,17 +272,17 @@ def main() -> int:
         "extra": extra,
     }
     if not args.no_cpu_baseline:
-        log("timing the CPU oracle on a sample")
-        res["cpu_baseline"] = cpu_baseline(np.concatenate(host_sample))
+        log("timing the CPU oracle over the whole cache (16 threads) and layer 0 (1 thread)")
+        res["cpu_baseline"], one = cpu_baseline(host_layers)
+        extra["cpu_oracle_1thread_GBps"] = round(one, 4)
     print(json.dumps(res), flush=True)
     return 0
 
 
 def side_measurements(torch, dev, stream, x, packed, norms):
     """Decode attention at batch 16, 32/8 heads, 32768 tokens (4 bits, random
-    codes), and a 2-bit encode launch the size of one 70B-class 128K-context
-    layer (2,097,152 vectors; timed on the first vectors of the resident
-    cache, the launch shape of the layer-by-layer streaming encode)."""
+    codes), the 70B-class 128K-context cache encoded as a layer-by-layer
+    stream (2 bits), and other codec launch shapes."""
     res = attention_measurement(torch, dev, stream)
     res.update(stream_encode_measurement(torch, dev, stream, x, packed, norms))
     res.update(codec_side_measurement(torch, dev, stream, x, packed, norms))
@@ -413,28 +426,80 @@ def attention_measurement(torch, dev, stream, reps: int = 10, head_dim: int = 12
 
 
 def stream_encode_measurement(torch, dev, stream, x, packed, norms):
-    """2-bit encode of one 70B-class 128K layer, cache evicted before each."""
+    """The 70B-class 128K-context cache (80 layers x {K,V} x 8 KV heads x
+    131072 tokens, 2 bits) encoded as a stream, layer by layer: each layer's
+    2,097,152 vectors are generated on the device (N(0,1) times the layer's
+    per-(K/V, head) scales, drawn from its data seed 300 + layer), the
+    last-level cache is evicted, and the layer is encoded with codec seed =
+    layer into its own slice of a packed cache that stays resident (80 x 64 MiB
+    codes + 80 x 8 MiB norms).  Reported: the sum of the 80 per-layer encode
+    times (HIP events around each launch)."""
     from kv_cache_vector_amd import _lib
+    from kv_cache_vector_amd import workloads as W
     s = stream.cuda_stream
-    res = {}
+    layers, heads, tokens = 80, 8, 131072
+    n = 2 * heads * tokens
+    P = D * 2 // 8
+    xl = torch.empty((2, heads, tokens, D), dtype=torch.float16, device=dev)
+    pk = torch.empty((layers, n, P), dtype=torch.uint8, device=dev)
+    nm = torch.empty((layers, n), dtype=torch.float32, device=dev)
     flush = torch.ones(512 * 1024 * 1024 // 4, dtype=torch.float32, device=dev)
-    n = 2 * 8 * 131072
-    xl = x[:n]
-    pk2 = packed[: n // 2].view(-1)[: n * 32].view(n, 32)
+    gen = torch.Generator(device=dev)
     times = []
-    for layer in range(6):
+    for layer in range(layers):
+        gen.manual_seed(300 + layer)
+        sc = torch.from_numpy(W.llama70b_head_scales(layer, heads)).to(dev)
+        xl.normal_(generator=gen)
+        xl.mul_(sc[:, :, None, None].half())
         flush.sum()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
-        _lib.check(_lib.tq_encode(xl.data_ptr(), n, 128, 2, layer, pk2.data_ptr(),
-                                  norms.data_ptr(), s), "tq_encode")
+        _lib.check(_lib.tq_encode(xl.data_ptr(), n, D, 2, layer, pk[layer].data_ptr(),
+                                  nm[layer].data_ptr(), s), "tq_encode")
         e1.record(stream)
-        torch.cuda.synchronize()
-        times.append(e0.elapsed_time(e1))
-    t_us = statistics.median(times[1:]) * 1e3
-    res["stream_b2_layer_us"] = round(t_us, 1)
-    res["stream_b2_80_layers_ms"] = round(80 * t_us / 1e3, 3)
-    res["stream_b2_hbm_frac"] = round(n * (256 + 32 + 4) / (t_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)
+        times.append((e0, e1))
+    torch.cuda.synchronize()
+    ms = [a.elapsed_time(b) for a, b in times]
+    total = sum(ms)
+    res = {"stream_b2_80_layers_ms": round(total, 3),
+           "stream_b2_layer_median_us": round(statistics.median(ms) * 1e3, 1),
+           "stream_b2_hbm_frac": round(layers * n * (2 * D + P + 4) / (total * 1e-3) / 1e9
+                                       / HBM_PEAK_GBPS, 4)}
+    del pk, nm, xl
+    return res
+
+
+def ceiling_measurement(torch, stream, x, packed, norms, out, enc_ms, dec_ms):
+    """The codec's byte mix moved by the no-arithmetic kernels of
+    tq_ceiling.h over the whole 4 GiB cache (4 bits; median of 10 launches
+    each), and the encode and decode kernels' time against them."""
+    import ctypes
+    from kv_cache_vector_amd import _lib
+    L = _lib.load()
+    f = L.tq_ceiling_stream
+    f.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                  ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    s = stream.cuda_stream
+    calls = {"encode": lambda: f(0, CODE_BYTES, x.data_ptr(), None, N, packed.data_ptr(),
+                                 norms.data_ptr(), s),
+             "decode": lambda: f(1, CODE_BYTES, packed.data_ptr(), norms.data_ptr(), N,
+                                 out.data_ptr(), None, s)}
+    res = {}
+    for name, fn in calls.items():
+        assert fn() == 0, "tq_ceiling_stream"
+        ts = []
+        for _ in range(10):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        ms = statistics.median(ts)
+        res["ceiling_%s_mix_ms" % name] = round(ms, 4)
+        res["ceiling_%s_mix_GBps" % name] = round(N * ALGO_BYTES / (ms * 1e-3) / 1e9, 1)
+    res["encode_frac_of_ceiling"] = round(res["ceiling_encode_mix_ms"] / enc_ms, 4)
+    res["decode_frac_of_ceiling"] = round(res["ceiling_decode_mix_ms"] / dec_ms, 4)
     return res
 
 

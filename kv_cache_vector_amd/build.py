@@ -17,7 +17,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libtq.so")
-SOURCES = ["tq_abi.cpp", "tq_codec.hip", "tq_attn.hip"]
+SOURCES = ["tq_abi.cpp", "tq_codec.hip", "tq_attn.hip", "tq_ceiling.hip"]
 ARCH = os.environ.get("TQ_OFFLOAD_ARCH", "gfx950")
 
 

@@ -75,6 +75,13 @@ def llama8b_layer(layer: int, dist: str = "gauss_outliers", tokens: int = 8192,
 LLAMA70B_128K = dict(layers=80, kv=2, batch=1, heads=8, tokens=131072)
 
 
+def llama70b_head_scales(layer: int, heads: int = 8) -> np.ndarray:
+    """The per-(K/V, head) scale factors of one 70B-class layer, [2, heads]
+    (the first draw of the layer's data seed 300+layer)."""
+    rng = np.random.default_rng(300 + layer)
+    return rng.uniform(0.5, 2.0, size=(2, heads)).astype(np.float32)
+
+
 def llama70b_layer(layer: int, tokens: int = 131072, heads: int = 8) -> np.ndarray:
     """N(0,1) scaled per (K/V, head) by a factor drawn uniformly in [0.5, 2].
     Data seed 300+layer.  Returns [2*heads*tokens, 128]."""

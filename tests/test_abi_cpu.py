@@ -253,3 +253,27 @@ def test_noalloc_attention_argument_errors(L):
     assert call(batch=512, hq=64, maxb=1024, nblk=512 * 1024, out=0x70000000) == WS
     header = open(HEADER).read()
     assert "#define TQ_ATTN_NOALLOC_WORKSPACE_BYTES ((size_t)32 << 20)" in header
+
+
+def test_every_header_symbol_is_exported(L):
+    """libtq exports every function any include/*.h declares (the codec ABI
+    and the measurement hook of tq_ceiling.h)."""
+    import glob
+    for h in sorted(glob.glob(os.path.join(ROOT, "include", "*.h"))):
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names = sorted(set(re.findall(r"\b(tq_[a-z0-9_]+)\s*\(", text)))
+        assert names, h
+        for n in names:
+            assert hasattr(L, n), (h, n)
+
+
+def test_ceiling_hook_argument_errors(L):
+    f = L.tq_ceiling_stream
+    f.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                  ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    assert f(2, 64, A, None, 10, B, C, None) == 1          # no such mode
+    assert f(0, 40, A, None, 10, B, C, None) == 1          # packed bytes of no width
+    assert f(0, 64, A, None, -1, B, C, None) == 1
+    assert f(0, 64, A, None, 0, B, C, None) == 0           # nothing to do
+    assert f(0, 64, A, None, 10, B, None, None) == 1       # encode mix needs the norm output
+    assert f(1, 64, A, None, 10, B, None, None) == 1       # decode mix needs the norm input

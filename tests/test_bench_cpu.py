@@ -25,12 +25,21 @@ def test_refuses_more_than_one_gpu():
 
 
 def test_cpu_baseline_record():
-    x = np.random.default_rng(0).standard_normal((4096, bench.D)).astype(np.float16)
-    res = bench.cpu_baseline(x, budget_s=5.0)
+    rng = np.random.default_rng(0)
+    layers = [rng.standard_normal((4096, bench.D)).astype(np.float16) for _ in range(3)]
+    res, one = bench.cpu_baseline(layers, budget_s=20.0, single_layer_budget_s=10.0)
     assert set(res) == {"value", "unit", "cores", "kind", "sample"}
     assert res["kind"] == "oracle" and res["unit"] == "GB/s"
-    assert res["value"] > 0 and 1 <= res["cores"] <= 16
-    assert "4096 vectors" in res["sample"]      # the whole (bounded) sample ran
+    assert res["value"] > 0 and 1 <= res["cores"] <= 16 and one > 0
+    assert "the whole cache (12288 vectors)" in res["sample"]   # every layer ran
+    assert "over 4096 vectors of layer 0" in res["sample"]      # the 1-thread run
+    assert "hardware threads visible" in res["sample"]
+
+
+def test_cpu_baseline_budget_reports_the_subset():
+    layers = [np.zeros((8192, bench.D), np.float16)]
+    res, _ = bench.cpu_baseline(layers, budget_s=0.0, single_layer_budget_s=0.0)
+    assert "the first" in res["sample"] and "of 8192 vectors" in res["sample"]
 
 
 def test_traffic_record_matches_the_sources_or_is_withheld():
