@@ -42,16 +42,36 @@ def flags() -> list:
     ]
 
 
-def build(verbose: bool = False) -> str:
+SAN_LIB = os.path.join(PKG, "libtq_san.so")
+# Host code only (argument checks, codebook solver, tables, launches) with
+# AddressSanitizer and UndefinedBehaviorSanitizer; the GPU code is built as
+# usual.  Each sanitizer flag reaches the host compilation only.
+SAN_HOST_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                  "-Xarch_host", "-fno-sanitize-recover=all", "-Xarch_host",
+                  "-fno-omit-frame-pointer"]
+
+
+def asan_runtime() -> str:
+    """Path of the ROCm clang's AddressSanitizer runtime, which a process
+    loading libtq_san.so must preload."""
+    r = subprocess.run([os.path.join(os.path.dirname(os.path.realpath(hipcc())), "amdclang++"),
+                        "-print-file-name=libclang_rt.asan-x86_64.so"],
+                       capture_output=True, text=True, check=True)
+    return r.stdout.strip()
+
+
+def build(verbose: bool = False, sanitize: bool = False) -> str:
+    """Build libtq.so, or with ``sanitize`` libtq_san.so (host code under
+    AddressSanitizer and UndefinedBehaviorSanitizer, for the CPU tests)."""
     cc = hipcc()
     objs = []
-    tmpdir = os.path.join(PKG, "_build")
+    tmpdir = os.path.join(PKG, "_build_san" if sanitize else "_build")
     os.makedirs(tmpdir, exist_ok=True)
     for src in SOURCES:
         path = os.path.join(CSRC, src)
         obj = os.path.join(tmpdir, os.path.splitext(src)[0] + ".o")
         lang = ["-x", "hip"] if src.endswith(".hip") else []
-        cmd = [cc] + flags() + lang + ["-c", path, "-o", obj]
+        cmd = [cc] + flags() + (SAN_HOST_FLAGS if sanitize else []) + lang + ["-c", path, "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         r = subprocess.run(cmd, capture_output=True, text=True)
@@ -63,14 +83,16 @@ def build(verbose: bool = False) -> str:
         if verbose and msg:
             print(msg)
         objs.append(obj)
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [cc, "-shared", "-fPIC", "--offload-arch=" + ARCH, "-o", tmp] + objs
+    out = SAN_LIB if sanitize else LIB
+    tmp = out + ".tmp%d" % os.getpid()
+    cmd = [cc, "-shared", "-fPIC", "--offload-arch=" + ARCH] + \
+        (["-Xarch_host", "-shared-libsan"] if sanitize else []) + ["-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stdout + r.stderr)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    print(build(verbose="-v" in sys.argv, sanitize="--sanitize" in sys.argv))

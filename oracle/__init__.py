@@ -27,17 +27,34 @@ _lib = None
 _P = ctypes.c_void_p
 
 
-def build(force: bool = True) -> str:
-    """Compile the oracle into ``oracle/libtq_oracle.so`` (gcc -O2, no fast-math)."""
-    if not force and os.path.exists(_LIB_PATH) and \
-            os.path.getmtime(_LIB_PATH) >= os.path.getmtime(_SRC):
-        return _LIB_PATH
-    tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+SAN_LIB_PATH = os.path.join(_HERE, "libtq_oracle_san.so")
+# gcc's AddressSanitizer runtime: a process that loads the sanitized build
+# must have it preloaded (LD_PRELOAD), ahead of every other library
+SAN_FLAGS = ["-fsanitize=address,undefined", "-fno-sanitize-recover=all",
+             "-fno-omit-frame-pointer", "-g"]
+
+
+def build(force: bool = True, sanitize: bool = False) -> str:
+    """Compile the oracle into ``oracle/libtq_oracle.so`` (gcc -O2, no
+    fast-math), or with ``sanitize`` into ``oracle/libtq_oracle_san.so`` built
+    with AddressSanitizer and UndefinedBehaviorSanitizer (any report aborts)."""
+    path = SAN_LIB_PATH if sanitize else _LIB_PATH
+    if not force and os.path.exists(path) and \
+            os.path.getmtime(path) >= os.path.getmtime(_SRC):
+        return path
+    tmp = path + ".tmp%d" % os.getpid()
     cmd = ["gcc", "-O2", "-std=c11", "-D_GNU_SOURCE", "-Wall", "-Wextra", "-fPIC",
-           "-shared", "-o", tmp, _SRC, "-lm"]
+           "-shared"] + (SAN_FLAGS if sanitize else []) + ["-o", tmp, _SRC, "-lm"]
     subprocess.run(cmd, check=True)
-    os.replace(tmp, _LIB_PATH)
-    return _LIB_PATH
+    os.replace(tmp, path)
+    return path
+
+
+def asan_runtime() -> str:
+    """Path of gcc's AddressSanitizer runtime library."""
+    r = subprocess.run(["gcc", "-print-file-name=libasan.so"], capture_output=True, text=True,
+                       check=True)
+    return r.stdout.strip()
 
 
 def _bind(L: ctypes.CDLL) -> ctypes.CDLL:
