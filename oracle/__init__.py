@@ -89,7 +89,15 @@ def _bind(L: ctypes.CDLL) -> ctypes.CDLL:
                                      ctypes.c_int, ctypes.c_int, ctypes.c_int64,
                                      ctypes.c_double, _P, _P, _P]
     L.tqo_packed_bytes.argtypes = [ctypes.c_int, ctypes.c_int]
+    L.tqo_hybrid_packed_bytes.argtypes = [ctypes.c_int, ctypes.c_int]
+    L.tqo_hybrid_encode.argtypes = [_P, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+                                    ctypes.c_uint64, _P, _P, _P, _P]
+    L.tqo_hybrid_decode.argtypes = [_P, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+                                    ctypes.c_uint64, _P, _P, _P]
     return L
+
+
+HYBRID_MODES = {"tq35": 35, "tq25": 25}
 
 
 def _ptr(a):
@@ -237,6 +245,66 @@ class Oracle:
             raise ValueError("tqo_attn_decode_kv rejected its arguments (rc=%d)" % rc)
         out = out.view(np.float16)
         return (out, of) if want_f64 else out
+
+
+def _hybrid_mode(mode) -> int:
+    if mode not in HYBRID_MODES:
+        raise ValueError("mode must be one of %s" % sorted(HYBRID_MODES))
+    return HYBRID_MODES[mode]
+
+
+def _hybrid_methods():
+    def hybrid_packed_bytes(self, d: int, mode: str) -> int:
+        return self.L.tqo_hybrid_packed_bytes(d, _hybrid_mode(mode))
+
+    def hybrid_encode(self, x_f16, mode: str, seed: int, perm, want_z: bool = False,
+                      want_t: bool = False):
+        """Hybrid-mode encode of x [..., d] binary16 with channel permutation
+        perm [d].  Returns packed [..., row] u8 (and z, t [..., d] f64)."""
+        x = np.asarray(x_f16)
+        if x.dtype == np.float16:
+            x = x.view(np.uint16)
+        x = _c(x, np.uint16)
+        d = x.shape[-1]
+        lead = x.shape[:-1]
+        n = int(np.prod(lead)) if lead else 1
+        row = self.hybrid_packed_bytes(d, mode)
+        if row == 0:
+            raise ValueError("unsupported head_dim %d" % d)
+        packed = np.zeros(lead + (row,), dtype=np.uint8)
+        z = np.zeros(lead + (d,), dtype=np.float64) if want_z else None
+        t = np.zeros(lead + (d,), dtype=np.float64) if want_t else None
+        pm = _c(perm, np.int32)
+        rc = self.L.tqo_hybrid_encode(_ptr(x), n, d, _hybrid_mode(mode), ctypes.c_uint64(seed),
+                                      _ptr(pm), _ptr(packed), _ptr(z), _ptr(t))
+        if rc != 0:
+            raise ValueError("tqo_hybrid_encode rejected its arguments (rc=%d)" % rc)
+        res = (packed,)
+        if want_z:
+            res += (z,)
+        if want_t:
+            res += (t,)
+        return res if len(res) > 1 else packed
+
+    def hybrid_decode(self, packed, d: int, mode: str, seed: int, perm, want_f64: bool = False):
+        """Returns the binary16 decode [..., d] (and the unrounded doubles)."""
+        packed = _c(packed, np.uint8)
+        lead = packed.shape[:-1]
+        n = int(np.prod(lead)) if lead else 1
+        out = np.zeros(lead + (d,), dtype=np.uint16)
+        xh = np.zeros(lead + (d,), dtype=np.float64) if want_f64 else None
+        pm = _c(perm, np.int32)
+        rc = self.L.tqo_hybrid_decode(_ptr(packed), n, d, _hybrid_mode(mode),
+                                      ctypes.c_uint64(seed), _ptr(pm), _ptr(out), _ptr(xh))
+        if rc != 0:
+            raise ValueError("tqo_hybrid_decode rejected its arguments (rc=%d)" % rc)
+        out = out.view(np.float16)
+        return (out, xh) if want_f64 else out
+
+    return hybrid_packed_bytes, hybrid_encode, hybrid_decode
+
+
+(Oracle.hybrid_packed_bytes, Oracle.hybrid_encode, Oracle.hybrid_decode) = _hybrid_methods()
 
 
 def default() -> Oracle:

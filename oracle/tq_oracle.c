@@ -515,3 +515,230 @@ int tqo_packed_bytes(int d, int bits)
 {
     return valid_shape(d, bits) ? d * bits / 8 : 0;
 }
+
+/* ------------------------------------------------------------------------ */
+/* Hybrid modes tq35 / tq25 ([PyPI] "Hybrid modes (tq35/tq25)": split-group  */
+/* quantization with a QJL residual; "API Reference": HybridTurboQuant with  */
+/* calibrate, encode returning the packed bytes only (norms embedded),       */
+/* decode, packed_dim_for_mode)                                              */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * The pages give the mode names, the two-part description and the API; the
+ * construction below is this repository's reading of them (listed in the
+ * design notes):
+ *   - a mode's number is the bits per coordinate of its codes: tq35 = 3.5,
+ *     tq25 = 2.5, of which 1 bit is the QJL sign sketch, so the two channel
+ *     groups carry (3, 2) bits (tq35) or (2, 1) bits (tq25), 2.5 or 1.5 on
+ *     average;
+ *   - split groups: a permutation perm of the d channels (chosen by
+ *     calibration) puts channels perm[0..d/2) in group A (the more bits) and
+ *     perm[d/2..d) in group B; y = x[perm] is the vector in group order;
+ *   - each group is a TurboQuant vector of dimension h = d/2 on its own:
+ *     norm, sign flip, h-point Walsh-Hadamard transform, Lloyd-Max N(0,1)
+ *     code per coordinate, with sign vectors sigma_A = SplitMix64 outputs
+ *     [0, h) and sigma_B = outputs [h, d) of the seed;
+ *   - QJL residual: r = y - yhat_mse (yhat_mse decoded from the codes and
+ *     the stored f32 norms), t = H_d D_Q r with sigma_Q = SplitMix64 outputs
+ *     [d, 2d); the sketch keeps the sign bits of t (bit i set iff t_i < 0)
+ *     and rho = ||r||.  Decode adds sqrt(pi/2)/d * rho * D_Q H_d s, s_i = +-1
+ *     the stored signs: the QJL estimate with the structured random projection
+ *     S = H_d D_Q (QJL's projection is Gaussian; this one is the codec's own
+ *     kind of random rotation, scaled to the same expected norm);
+ *   - row layout (bytes): codes A (h*bA/8) | codes B (h*bB/8) | sign bits
+ *     (d/8) | f32 norm_A | f32 norm_B | f32 rho.
+ */
+
+static int hybrid_bits(int mode, int *ba, int *bb)
+{
+    if (mode == 35) { *ba = 3; *bb = 2; return 1; }
+    if (mode == 25) { *ba = 2; *bb = 1; return 1; }
+    return 0;
+}
+
+/* Bytes of one packed row, norms included; 0 for an unsupported shape. */
+int tqo_hybrid_packed_bytes(int d, int mode)
+{
+    int ba, bb;
+    if (!hybrid_bits(mode, &ba, &bb) || d < 16 || d > 1024 || (d & (d - 1))) return 0;
+    const int h = d / 2;
+    return h * ba / 8 + h * bb / 8 + d / 8 + 12;
+}
+
+typedef struct {
+    int d, h, ba, bb, PA, PB, PQ, row;
+    double ca[16], ta[15], cb[16], tb[15];
+    int8_t sa[512], sb[512], sq[1024];
+    int8_t *Hh, *Hd;
+} hybrid_t;
+
+static int hybrid_init(hybrid_t *k, int d, int mode, uint64_t seed)
+{
+    if (!tqo_hybrid_packed_bytes(d, mode)) return TQO_EINVAL;
+    hybrid_bits(mode, &k->ba, &k->bb);
+    k->d = d;
+    k->h = d / 2;
+    k->PA = k->h * k->ba / 8;
+    k->PB = k->h * k->bb / 8;
+    k->PQ = d / 8;
+    k->row = tqo_hybrid_packed_bytes(d, mode);
+    tqo_codebook(k->ba, k->ca, k->ta);
+    tqo_codebook(k->bb, k->cb, k->tb);
+    int8_t s[2048];
+    tqo_signs(seed, 2 * d, s);                 /* one stream: A, B, then Q */
+    memcpy(k->sa, s, (size_t)k->h);
+    memcpy(k->sb, s + k->h, (size_t)k->h);
+    memcpy(k->sq, s + d, (size_t)d);
+    k->Hh = malloc((size_t)k->h * k->h);
+    k->Hd = malloc((size_t)d * d);
+    if (!k->Hh || !k->Hd) { free(k->Hh); free(k->Hd); return TQO_EINVAL; }
+    tqo_hadamard(k->h, k->Hh);
+    tqo_hadamard(d, k->Hd);
+    return TQO_OK;
+}
+
+static void hybrid_free(hybrid_t *k) { free(k->Hh); free(k->Hd); }
+
+/* TurboQuant of one group of h coordinates (steps 1-5 of the codec at
+ * dimension h): returns the f32 norm, writes codes and (optional) z. */
+static float group_encode(const hybrid_t *k, const double *y, const int8_t *sg, const double *t,
+                          int bits, uint8_t *codes, double *z)
+{
+    const int h = k->h;
+    double ss = 0.0;
+    for (int i = 0; i < h; ++i) ss += y[i] * y[i];
+    const double n = sqrt(ss);
+    for (int i = 0; i < h; ++i) {
+        double acc = 0.0;
+        for (int j = 0; j < h; ++j)
+            acc += (double)k->Hh[(size_t)i * h + j] * sg[j] * ((n > 0.0) ? y[j] / n : 0.0);
+        z[i] = acc;
+        codes[i] = (uint8_t)tqo_quantize(acc, t, 1 << bits);
+    }
+    return (float)n;
+}
+
+/* yhat of one group: n * D * H_h * c[code] / h. */
+static void group_decode(const hybrid_t *k, const uint8_t *codes, const double *c,
+                         const int8_t *sg, float norm, double *yh)
+{
+    const int h = k->h;
+    for (int i = 0; i < h; ++i) {
+        double acc = 0.0;
+        for (int j = 0; j < h; ++j) acc += (double)k->Hh[(size_t)i * h + j] * c[codes[j]];
+        yh[i] = (double)norm * sg[i] * acc / h;
+    }
+}
+
+static void put_f32(uint8_t *p, float v) { memcpy(p, &v, 4); }
+
+/* perm must hold every channel 0..d-1 exactly once. */
+static int valid_perm(const int32_t *perm, int d)
+{
+    uint8_t seen[1024] = {0};
+    for (int i = 0; i < d; ++i) {
+        if (perm[i] < 0 || perm[i] >= d || seen[perm[i]]) return 0;
+        seen[perm[i]] = 1;
+    }
+    return 1;
+}
+static float get_f32(const uint8_t *p) { float v; memcpy(&v, p, 4); return v; }
+
+/* The MSE part of a row (both groups) in group order, double. */
+static void hybrid_mse(const hybrid_t *k, const uint8_t *pv, double *yh)
+{
+    uint8_t ca[512], cb[512];
+    tqo_unpack(pv, k->h, k->ba, ca);
+    tqo_unpack(pv + k->PA, k->h, k->bb, cb);
+    const uint8_t *nv = pv + k->PA + k->PB + k->PQ;
+    group_decode(k, ca, k->ca, k->sa, get_f32(nv), yh);
+    group_decode(k, cb, k->cb, k->sb, get_f32(nv + 4), yh + k->h);
+}
+
+/*
+ * Encode n vectors (x [n, d] binary16) with the channel permutation perm
+ * ([d], perm[k] = the channel at group-order position k) into packed rows
+ * [n, tqo_hybrid_packed_bytes(d, mode)].  Optional outputs, [n, d] doubles:
+ * z_out (the two groups' rotated coordinates, group A then B) and t_out (the
+ * QJL projection H_d D_Q r whose signs are stored).
+ */
+int tqo_hybrid_encode(const uint16_t *x, int64_t n, int d, int mode, uint64_t seed,
+                      const int32_t *perm, uint8_t *packed, double *z_out, double *t_out)
+{
+    if (n < 0 || !tqo_hybrid_packed_bytes(d, mode)) return TQO_EINVAL;
+    if (n == 0) return TQO_OK;
+    if (!x || !perm || !packed || !valid_perm(perm, d)) return TQO_EINVAL;
+    hybrid_t k;
+    if (hybrid_init(&k, d, mode, seed)) return TQO_EINVAL;
+    for (int64_t v = 0; v < n; ++v) {
+        const uint16_t *xv = x + v * d;
+        uint8_t *pv = packed + v * k.row;
+        double y[1024], z[1024], yh[1024], r[1024], t[1024];
+        uint8_t ca[512], cb[512], bits[1024];
+        for (int i = 0; i < d; ++i) y[i] = tqo_half_to_double(xv[perm[i]]);
+        memset(pv, 0, (size_t)k.row);
+        const float na = group_encode(&k, y, k.sa, k.ta, k.ba, ca, z);
+        const float nb = group_encode(&k, y + k.h, k.sb, k.tb, k.bb, cb, z + k.h);
+        tqo_pack(ca, k.h, k.ba, pv);
+        tqo_pack(cb, k.h, k.bb, pv + k.PA);
+        uint8_t *nv = pv + k.PA + k.PB + k.PQ;
+        put_f32(nv, na);
+        put_f32(nv + 4, nb);
+        /* residual of what decode reconstructs from the codes and f32 norms */
+        hybrid_mse(&k, pv, yh);
+        double rr = 0.0;
+        for (int i = 0; i < d; ++i) {
+            r[i] = y[i] - yh[i];
+            rr += r[i] * r[i];
+        }
+        put_f32(nv + 8, (float)sqrt(rr));
+        for (int i = 0; i < d; ++i) {
+            double acc = 0.0;
+            for (int j = 0; j < d; ++j) acc += (double)k.Hd[(size_t)i * d + j] * k.sq[j] * r[j];
+            t[i] = acc;
+            bits[i] = (acc < 0.0) ? 1 : 0;
+        }
+        tqo_pack(bits, d, 1, pv + k.PA + k.PB);
+        if (z_out) memcpy(z_out + v * d, z, sizeof(double) * d);
+        if (t_out) memcpy(t_out + v * d, t, sizeof(double) * d);
+    }
+    hybrid_free(&k);
+    return TQO_OK;
+}
+
+/*
+ * Decode packed rows: yhat = yhat_mse + sqrt(pi/2)/d * rho * D_Q H_d s
+ * (s_i = -1 where sign bit i is set, else +1), then x[perm[k]] = yhat[k].
+ * out (optional) binary16 nearest-even; xhat_out (optional) doubles; both
+ * [n, d] in channel order.
+ */
+int tqo_hybrid_decode(const uint8_t *packed, int64_t n, int d, int mode, uint64_t seed,
+                      const int32_t *perm, uint16_t *out, double *xhat_out)
+{
+    if (n < 0 || !tqo_hybrid_packed_bytes(d, mode)) return TQO_EINVAL;
+    if (n == 0) return TQO_OK;
+    if (!packed || !perm || (!out && !xhat_out) || !valid_perm(perm, d)) return TQO_EINVAL;
+    hybrid_t k;
+    if (hybrid_init(&k, d, mode, seed)) return TQO_EINVAL;
+    const double qscale = sqrt(M_PI / 2.0) / d;
+    for (int64_t v = 0; v < n; ++v) {
+        const uint8_t *pv = packed + v * k.row;
+        double yh[1024];
+        uint8_t bits[1024];
+        hybrid_mse(&k, pv, yh);
+        tqo_unpack(pv + k.PA + k.PB, d, 1, bits);
+        const double rho = (double)get_f32(pv + k.PA + k.PB + k.PQ + 8);
+        for (int i = 0; i < d; ++i) {
+            double acc = 0.0;
+            for (int j = 0; j < d; ++j) acc += (double)k.Hd[(size_t)i * d + j] * (bits[j] ? -1.0 : 1.0);
+            yh[i] += qscale * rho * k.sq[i] * acc;
+        }
+        for (int i = 0; i < d; ++i) {
+            const int c = perm[i];
+            if (out) out[v * d + c] = tqo_double_to_half(yh[i]);
+            if (xhat_out) xhat_out[v * d + c] = yh[i];
+        }
+    }
+    hybrid_free(&k);
+    return TQO_OK;
+}

@@ -674,6 +674,177 @@ def check_attn_head_dims(o):
         check_attn_special_cases(o, d=d)
 
 
+# ---------------------------------------------------------------------------
+# hybrid modes tq35 / tq25 (split groups + QJL residual)
+# ---------------------------------------------------------------------------
+
+SPLITMIX_GAMMA = 0x9E3779B97F4A7C15
+HYBRID_BITS = {"tq35": (3, 2), "tq25": (2, 1)}
+
+
+def _stream_seed(seed: int, skip: int) -> int:
+    """The seed whose SplitMix64 stream starts at output `skip` of seed's
+    stream (the state advances by the fixed increment per output)."""
+    return (seed + skip * SPLITMIX_GAMMA) % (1 << 64)
+
+
+def _hybrid_mse_only(o, packed, d, mode, seed, perm):
+    """Decode with rho set to 0: the two groups' TurboQuant part alone."""
+    p0 = np.array(packed, copy=True)
+    p0[..., -4:] = 0
+    return o.hybrid_decode(p0, d, mode, seed, perm, want_f64=True)[1]
+
+
+def check_hybrid_sizes(o):
+    """Row bytes: codes of the two halves at (3, 2) or (2, 1) bits, d sign bits
+    and three f32 norms (68 / 52 bytes at d = 128, 3.76x / 4.92x against 256
+    bytes of binary16); unsupported modes and sizes give 0."""
+    for d in (64, 128, 256):
+        for mode, (ba, bb) in HYBRID_BITS.items():
+            assert o.hybrid_packed_bytes(d, mode) == d // 2 * ba // 8 + d // 2 * bb // 8 + d // 8 + 12
+    assert o.hybrid_packed_bytes(128, "tq35") == 68 and o.hybrid_packed_bytes(128, "tq25") == 52
+    assert abs(256 / 68 - 3.7647) < 1e-4 and abs(256 / 52 - 4.9231) < 1e-4
+    assert o.L.tqo_hybrid_packed_bytes(128, 30) == 0 and o.L.tqo_hybrid_packed_bytes(96, 35) == 0
+
+
+def check_hybrid_groups_are_turboquant(o, seed=17):
+    """Each channel group is a TurboQuant vector of dimension d/2: group A's
+    codes and norm equal the (pinned) codec's encode of x[perm[:h]] with the
+    seed, group B's those of x[perm[h:]] with the seed whose stream starts at
+    output h; with rho zeroed, decode is the codec's decode of each group put
+    back through perm."""
+    rng = np.random.default_rng(seed)
+    for d in (64, 128, 256):
+        h = d // 2
+        x = (rng.standard_normal((300, d)) * rng.uniform(0.2, 5, (1, d))).astype(np.float16)
+        perm = rng.permutation(d).astype(np.int32)
+        for mode, (ba, bb) in HYBRID_BITS.items():
+            pk = o.hybrid_encode(x, mode, seed, perm)
+            PA, PB = h * ba // 8, h * bb // 8
+            nv = pk[:, PA + PB + d // 8:].copy().view(np.float32)
+            ra, na = o.encode(x[:, perm[:h]], ba, seed)
+            rb, nb = o.encode(x[:, perm[h:]], bb, _stream_seed(seed, h))
+            assert np.array_equal(pk[:, :PA], ra) and np.array_equal(nv[:, 0], na)
+            assert np.array_equal(pk[:, PA:PA + PB], rb) and np.array_equal(nv[:, 1], nb)
+            _, xa = o.decode(ra, na, h, ba, seed, want_f64=True)
+            _, xb = o.decode(rb, nb, h, bb, _stream_seed(seed, h), want_f64=True)
+            want = np.zeros((300, d))
+            want[:, perm[:h]] = xa
+            want[:, perm[h:]] = xb
+            got = _hybrid_mse_only(o, pk, d, mode, seed, perm)
+            assert np.allclose(got, want, rtol=1e-12, atol=1e-12)
+
+
+def check_hybrid_qjl_sketch(o, seed=19):
+    """The sign sketch: t = H_d D_Q r (scipy's Hadamard matrix, D_Q the signs
+    of the stream from output d, r = x[perm] minus the groups' decode) has the
+    stored signs (bit set iff t < 0) and ||r|| is the stored f32 rho; the
+    decoded correction has norm exactly sqrt(pi/2) rho (D_Q H_d s has norm d)
+    and inner product sqrt(pi/2)/d rho ||t||_1 with r."""
+    rng = np.random.default_rng(seed)
+    for d in (64, 128, 256):
+        H = sl.hadamard(d).astype(np.float64)
+        sq = o.signs(_stream_seed(seed, d), d).astype(np.float64)
+        x = rng.standard_normal((200, d)).astype(np.float16)
+        perm = rng.permutation(d).astype(np.int32)
+        for mode, (ba, bb) in HYBRID_BITS.items():
+            pk, t = o.hybrid_encode(x, mode, seed, perm, want_t=True)
+            off = d // 2 * ba // 8 + d // 2 * bb // 8
+            bits = np.unpackbits(pk[:, off:off + d // 8], axis=-1, bitorder="little")
+            rho = pk[:, off + d // 8 + 8:].copy().view(np.float32)[:, 0].astype(np.float64)
+            ym = _hybrid_mse_only(o, pk, d, mode, seed, perm)[:, perm]   # group order
+            r = x.astype(np.float64)[:, perm] - ym
+            tt = (r * sq) @ H.T
+            assert np.allclose(t, tt, rtol=1e-9, atol=1e-9 * np.abs(tt).max())
+            assert np.array_equal(bits, (t < 0).astype(np.uint8))
+            assert np.array_equal(rho.astype(np.float32),
+                                  np.sqrt((r ** 2).sum(1)).astype(np.float32))
+            _, xh = o.hybrid_decode(pk, d, mode, seed, perm, want_f64=True)
+            corr = xh[:, perm] - ym
+            cn = np.sqrt((corr ** 2).sum(1))
+            assert np.allclose(cn, math.sqrt(math.pi / 2) * rho, rtol=1e-10, atol=1e-12)
+            ip = (corr * r).sum(1)
+            assert np.allclose(ip, math.sqrt(math.pi / 2) / d * rho * np.abs(t).sum(1),
+                               rtol=1e-9, atol=1e-12)
+
+
+def check_hybrid_inner_products_unbiased(o, nseeds=3000):
+    """QJL's purpose: the correction is an unbiased estimate of the residual
+    in every direction, so over the seeds the hybrid decode's inner product
+    with x matches <x, r>-corrected truth: the pooled ratio
+    sum <x, correction> / sum <x, r> is 1 within 1.5% (the TurboQuant part
+    alone is biased low by the whole <x, r>, 7% of ||x||^2 at tq35 and 23% at
+    tq25), and <y, xhat> for independent y has no bias beyond 0.5% of
+    ||x|| ||y||."""
+    d = D
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((6, d)).astype(np.float16)
+    xd = x.astype(np.float64)
+    y = rng.standard_normal((6, d))
+    perm = np.arange(d, dtype=np.int32)
+    for mode in HYBRID_BITS:
+        qx = np.zeros((6, nseeds))
+        rx = np.zeros((6, nseeds))
+        ey = np.zeros((6, nseeds))
+        for s in range(nseeds):
+            pk = o.hybrid_encode(x, mode, s, perm)
+            _, xh = o.hybrid_decode(pk, d, mode, s, perm, want_f64=True)
+            xm = _hybrid_mse_only(o, pk, d, mode, s, perm)
+            qx[:, s] = (xd * (xh - xm)).sum(1)
+            rx[:, s] = (xd * (xd - xm)).sum(1)
+            ey[:, s] = (y * xh).sum(1)
+        ratio = qx.sum() / rx.sum()
+        assert abs(ratio - 1) < 0.015, (mode, ratio)
+        assert rx.mean() > 0.05 * (xd ** 2).sum(1).mean()      # the bias QJL removes is real
+        bias_y = np.abs(ey.mean(1) - (y * xd).sum(1)) / (np.linalg.norm(xd, axis=1) *
+                                                         np.linalg.norm(y, axis=1))
+        assert bias_y.max() < 5e-3, (mode, bias_y)
+
+
+def check_hybrid_mse(o, n=20000, seed=27):
+    """Round trip on N(0,1) vectors: ||x - xhat||^2 / ||x||^2 lies within 5% of
+    (pi/2 - 1) times the mean of the two groups' exact TurboQuant values at
+    dimension d/2 (the residual keeps (pi/2 - 1) of its energy when its
+    projection is Gaussian), and the sign sketch lowers it below the groups'
+    value alone."""
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((n, D)).astype(np.float16)
+    xd = x.astype(np.float64)
+    perm = np.arange(D, dtype=np.int32)
+    for mode, (ba, bb) in HYBRID_BITS.items():
+        pk = o.hybrid_encode(x, mode, 3, perm)
+        _, xh = o.hybrid_decode(pk, D, mode, 3, perm, want_f64=True)
+        mse = float(np.mean(((xd - xh) ** 2).sum(1) / (xd ** 2).sum(1)))
+        groups = 0.5 * sum(exact_mse_d(b, *o.codebook(b), d=D // 2) for b in (ba, bb))
+        assert abs(mse / ((math.pi / 2 - 1) * groups) - 1) < 0.05, (mode, mse, groups)
+        xm = _hybrid_mse_only(o, pk, D, mode, 3, perm)
+        assert mse < float(np.mean(((xd - xm) ** 2).sum(1) / (xd ** 2).sum(1)))
+
+
+def check_hybrid_special_cases(o):
+    """The zero vector stores zero norms and no sign bits and decodes to zeros;
+    encoding x with channel permutation perm equals encoding x[perm] with the
+    identity; decode puts group position k back on channel perm[k]."""
+    d = D
+    z = np.zeros((1, d), np.float16)
+    ident = np.arange(d, dtype=np.int32)
+    for mode in HYBRID_BITS:
+        pk = o.hybrid_encode(z, mode, 1, ident)
+        assert np.all(pk[:, -12:] == 0)
+        _, xh = o.hybrid_decode(pk, d, mode, 1, ident, want_f64=True)
+        assert np.all(xh == 0.0)
+    rng = np.random.default_rng(2)
+    x = rng.standard_normal((50, d)).astype(np.float16)
+    perm = rng.permutation(d).astype(np.int32)
+    for mode in HYBRID_BITS:
+        a = o.hybrid_encode(x, mode, 9, perm)
+        b = o.hybrid_encode(x[:, perm], mode, 9, ident)
+        assert np.array_equal(a, b)
+        _, xa = o.hybrid_decode(a, d, mode, 9, perm, want_f64=True)
+        _, xb = o.hybrid_decode(b, d, mode, 9, ident, want_f64=True)
+        assert np.array_equal(xa[:, perm], xb)
+
+
 ALL_CHECKS = [
     check_half_to_double, check_double_to_half, check_splitmix64, check_signs,
     check_hadamard, check_rotation_unit_vectors, check_rotation_norm,
@@ -685,4 +856,6 @@ ALL_CHECKS = [
     check_decode_definition, check_attn_rotated_domain_identity, check_attn_special_cases,
     check_attn_paging_invariance, check_attn_bruteforce_tiny, check_attn_gqa_grouping,
     check_attn_mixed_widths, check_head_dims, check_attn_head_dims,
+    check_hybrid_sizes, check_hybrid_groups_are_turboquant, check_hybrid_qjl_sketch,
+    check_hybrid_special_cases, check_hybrid_mse, check_hybrid_inner_products_unbiased,
 ]

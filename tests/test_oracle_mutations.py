@@ -47,6 +47,21 @@ MUTATIONS = [
      "int64_t row = ((int64_t)blk * block_size + (j + 1) % block_size) * Hkv + g;"),
     ("attn_off_by_one_len", "for (int j = 0; j < T; ++j) { s[j] = exp(s[j] - m); l += s[j]; }",
      "for (int j = 0; j < T; ++j) { s[j] = exp(s[j] - m); l += s[j]; }\n                if (T > 1) s[T - 1] = 0.0;"),
+    # hybrid modes (split groups + QJL residual)
+    ("hybrid_group_bits_swapped", "if (mode == 35) { *ba = 3; *bb = 2; return 1; }",
+     "if (mode == 35) { *ba = 2; *bb = 3; return 1; }"),
+    ("hybrid_qjl_scale", "const double qscale = sqrt(M_PI / 2.0) / d;",
+     "const double qscale = 1.05 * sqrt(M_PI / 2.0) / d;"),
+    ("hybrid_qjl_transposed_in_decode",
+     "acc += (double)k.Hd[(size_t)i * d + j] * (bits[j] ? -1.0 : 1.0);\n            yh[i] += qscale * rho * k.sq[i] * acc;",
+     "acc += (double)k.Hd[(size_t)i * d + j] * k.sq[j] * (bits[j] ? -1.0 : 1.0);\n            yh[i] += qscale * rho * acc;"),
+    ("hybrid_qjl_signs_overlap_group_b", "memcpy(k->sq, s + d, (size_t)d);",
+     "memcpy(k->sq, s + k->h, (size_t)d);"),
+    ("hybrid_sign_bit_polarity", "bits[i] = (acc < 0.0) ? 1 : 0;", "bits[i] = (acc > 0.0) ? 1 : 0;"),
+    ("hybrid_rho_squared", "put_f32(nv + 8, (float)sqrt(rr));", "put_f32(nv + 8, (float)rr);"),
+    ("hybrid_no_unpermute", "const int c = perm[i];", "const int c = i;"),
+    ("hybrid_residual_before_rounding_norms", "hybrid_mse(&k, pv, yh);\n        double rr = 0.0;",
+     "hybrid_mse(&k, pv, yh);\n        for (int i = 0; i < d; ++i) yh[i] *= 1.0 + 1e-3;\n        double rr = 0.0;"),
 ]
 
 # cheap checks first; the Monte-Carlo MSE and the other head dims last
