@@ -126,6 +126,38 @@ tq_status tq_encode_paged(const void *x_f16, const int64_t *slots, int64_t n, in
                           int64_t num_slots, void *stream);
 
 /*
+ * Hybrid modes tq35 and tq25 ([PyPI] "Hybrid modes (tq35/tq25)": split-group
+ * quantization with a QJL residual; "API Reference": HybridTurboQuant, whose
+ * encode returns the packed bytes only, norms embedded), head_dim 128.
+ *   mode  35 (tq35) or 25 (tq25): 3.5 or 2.5 bits per coordinate of codes
+ *   perm  HOST array of head_dim int32, a permutation of the channels from
+ *         calibration (NULL = identity): channels perm[0..63] form group A,
+ *         perm[64..127] group B
+ * Encode, for y = x[perm]: each half of y is a TurboQuant vector of dimension
+ * 64 (norm, sign flip, 64-point Walsh-Hadamard transform, Lloyd-Max code) at
+ * 3 and 2 bits (tq35) or 2 and 1 bits (tq25); the residual r = y - (decode
+ * of the halves) is kept as the sign bits of H_128 D_Q r and its norm rho
+ * (a QJL sign sketch with the structured projection H_128 D_Q).  The signs of
+ * the seed's SplitMix64 stream are those of group A (outputs 0-63), group B
+ * (64-127) and D_Q (128-255).  Row, one per vector: codes A | codes B |
+ * 16 bytes of sign bits | f32 norm A | f32 norm B | f32 rho, LSB-first
+ * bitstreams; 68 bytes (tq35) or 52 bytes (tq25), 4-byte aligned.
+ * Decode: yhat = (decode of the halves) + sqrt(pi/2)/128 * rho * D_Q H_128 s,
+ * s_i = -1 where sign bit i is set, else +1; out[perm[k]] = binary16
+ * (nearest-even) of yhat[k].
+ * tq_hybrid_packed_bytes returns the row bytes, 0 for an unsupported
+ * (head_dim, mode).  Errors: TQ_ERR_UNSUPPORTED (head_dim other than 128, an
+ * unknown mode), TQ_ERR_INVALID_ARG (null pointers, negative n, perm not a
+ * permutation, overlapping input and output), TQ_ERR_MISALIGNED (x or out not
+ * 16-byte aligned, packed not 4-byte aligned).  n == 0 is a no-op.
+ */
+size_t tq_hybrid_packed_bytes(int head_dim, int mode);
+tq_status tq_hybrid_encode(const void *x_f16, int64_t n, int head_dim, int mode, uint64_t seed,
+                           const int32_t *perm, uint8_t *packed, void *stream);
+tq_status tq_hybrid_decode(const uint8_t *packed, int64_t n, int head_dim, int mode,
+                           uint64_t seed, const int32_t *perm, void *out_f16, void *stream);
+
+/*
  * Workspace bytes tq_attn_decode needs for this problem shape: the partial
  * softmax state (running max, sum, head_dim rotated-domain accumulators) of
  * every (sequence, query head, context split).  Deterministic in its

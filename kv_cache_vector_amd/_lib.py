@@ -22,7 +22,8 @@ STATUS_NAMES = {0: "TQ_OK", 1: "TQ_ERR_INVALID_ARG", 2: "TQ_ERR_UNSUPPORTED",
 # every symbol include/tq.h declares
 SYMBOLS = ("tq_status_string", "tq_abi_version", "tq_packed_bytes", "tq_encode", "tq_decode",
            "tq_encode_paged", "tq_attn_workspace_bytes", "tq_attn_decode", "tq_attn_decode_kv",
-           "tq_attn_decode_kv_noalloc", "tq_codebook", "tq_signs")
+           "tq_attn_decode_kv_noalloc", "tq_hybrid_packed_bytes", "tq_hybrid_encode",
+           "tq_hybrid_decode", "tq_codebook", "tq_signs")
 
 # bytes of the library-owned workspace of tq_attn_decode_kv_noalloc, per GPU
 # (TQ_ATTN_NOALLOC_WORKSPACE_BYTES in include/tq.h)
@@ -70,6 +71,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                                         _I, _I, _I64, ctypes.c_float, _P, _P, ctypes.c_size_t, _P]
         L.tq_attn_decode_kv_noalloc.argtypes = [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I,
                                                 _I, _U64, _I, _I, _I64, ctypes.c_float, _P, _P]
+        L.tq_hybrid_packed_bytes.argtypes = [_I, _I]
+        L.tq_hybrid_packed_bytes.restype = ctypes.c_size_t
+        L.tq_hybrid_encode.argtypes = [_P, _I64, _I, _I, _U64, _P, _P, _P]
+        L.tq_hybrid_decode.argtypes = [_P, _I64, _I, _I, _U64, _P, _P, _P]
         L.tq_codebook.argtypes = [_I, _P, _P]
         L.tq_signs.argtypes = [_U64, _I, _P]
         _lib = L
@@ -137,6 +142,19 @@ def tq_attn_decode_kv_noalloc(q_f16, k_packed, k_norms, v_packed, v_norms, block
                                             num_kv_heads, head_dim, k_bits, v_bits, seed,
                                             block_size, max_blocks_per_seq, num_blocks, scale,
                                             out_f16, stream)
+
+
+def tq_hybrid_packed_bytes(head_dim, mode) -> int:
+    return load().tq_hybrid_packed_bytes(head_dim, mode)
+
+
+def tq_hybrid_encode(x_f16, n, head_dim, mode, seed, perm, packed, stream) -> int:
+    """perm: a HOST pointer (or None) to head_dim int32."""
+    return load().tq_hybrid_encode(x_f16, n, head_dim, mode, seed, perm, packed, stream)
+
+
+def tq_hybrid_decode(packed, n, head_dim, mode, seed, perm, out_f16, stream) -> int:
+    return load().tq_hybrid_decode(packed, n, head_dim, mode, seed, perm, out_f16, stream)
 
 
 def tq_codebook(bits: int):

@@ -83,7 +83,7 @@ const Codebook &codebook(int bits) {
     static Codebook cbs[5];
     static std::once_flag once;
     std::call_once(once, [] {
-        for (int b = 2; b <= 4; ++b) cbs[b] = solve_codebook(b);
+        for (int b = 1; b <= 4; ++b) cbs[b] = solve_codebook(b);   // 1 bit: hybrid tq25
     });
     return cbs[bits];
 }
@@ -151,6 +151,53 @@ const tq::EncTable &enc_table(int bits) {
         for (int b = 2; b <= 4; ++b) tabs[b] = make_enc_table(b);
     });
     return tabs[bits];
+}
+
+// Hybrid modes: the group widths of a mode (35: 3 and 2 bits; 25: 2 and 1).
+bool hybrid_widths(int mode, int *ba, int *bb) {
+    if (mode == 35) { *ba = 3; *bb = 2; return true; }
+    if (mode == 25) { *ba = 2; *bb = 1; return true; }
+    return false;
+}
+
+// Everything the hybrid kernels take by value.  The seed's SplitMix64 stream
+// gives the signs of group-order positions 0..127 (group A then B) and then
+// those of the sketch's projection; perm (host, head_dim entries, NULL for
+// the identity) becomes the per-lane channel table of the kernels' layout
+// (register r of lane q holds group-order position 32 (r / 8) + 8 q + r % 8).
+tq::HybridConsts make_hybrid_consts(int mode, uint64_t seed, const int32_t *perm) {
+    tq::HybridConsts k{};
+    int ba = 0, bb = 0;
+    hybrid_widths(mode, &ba, &bb);
+    uint32_t words[8];
+    sign_mask(seed, 256, words);
+    for (int w = 0; w < 4; ++w) {
+        k.sign[w] = words[w];
+        k.qsign[w] = words[4 + w];
+    }
+    const Codebook &ca = codebook(ba), &cb = codebook(bb);
+    for (int i = 0; i < (1 << ba); ++i) k.lev_a[i] = ca.level[i];
+    for (int i = 0; i + 1 < (1 << ba); ++i) k.thr_a[i] = 8.0f * ca.thr[i];
+    for (int i = 0; i < (1 << bb); ++i) k.lev_b[i] = cb.level[i];
+    for (int i = 0; i + 1 < (1 << bb); ++i) k.thr_b[i] = 8.0f * cb.thr[i];
+    uint8_t *g = reinterpret_cast<uint8_t *>(k.gidx);
+    for (int q = 0; q < 4; ++q)
+        for (int r = 0; r < 32; ++r) {
+            const int pos = 32 * (r / 8) + 8 * q + r % 8;
+            g[32 * q + r] = (uint8_t)(perm ? perm[pos] : pos);
+        }
+    return k;
+}
+
+// perm holds every channel 0..d-1 exactly once (NULL: the identity)
+bool valid_perm(const int32_t *perm, int d) {
+    if (!perm) return true;
+    bool seen[256] = {};
+    for (int i = 0; i < d; ++i) {
+        if (perm[i] < 0 || perm[i] >= d || seen[perm[i]]) return false;
+        seen[perm[i]] = true;
+    }
+    return true;
 }
 
 bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
@@ -279,6 +326,42 @@ tq_status tq_decode(const uint8_t *packed, const float *norms, int64_t n, int he
     const CodecConsts k = make_consts(head_dim, bits, seed);
     return from_hip(tq::launch_decode(head_dim, bits, packed, norms, n, k, out_f16,
                                       (hipStream_t)stream));
+}
+
+size_t tq_hybrid_packed_bytes(int head_dim, int mode) {
+    int ba, bb;
+    if (head_dim != tq::kHybridHeadDim || !hybrid_widths(mode, &ba, &bb)) return 0;
+    return (size_t)tq::hybrid_row_bytes(mode);
+}
+
+tq_status tq_hybrid_encode(const void *x_f16, int64_t n, int head_dim, int mode, uint64_t seed,
+                           const int32_t *perm, uint8_t *packed, void *stream) {
+    const size_t row = tq_hybrid_packed_bytes(head_dim, mode);
+    if (head_dim <= 0) return TQ_ERR_INVALID_ARG;
+    if (row == 0) return TQ_ERR_UNSUPPORTED;
+    if (n < 0 || !valid_perm(perm, head_dim)) return TQ_ERR_INVALID_ARG;
+    if (n == 0) return TQ_OK;
+    if (!x_f16 || !packed) return TQ_ERR_INVALID_ARG;
+    if (!aligned(x_f16, 16) || !aligned(packed, 4)) return TQ_ERR_MISALIGNED;
+    if (overlap(x_f16, (size_t)n * head_dim * 2, packed, (size_t)n * row))
+        return TQ_ERR_INVALID_ARG;
+    return from_hip(tq::launch_hybrid_encode(mode, x_f16, n, make_hybrid_consts(mode, seed, perm),
+                                             packed, (hipStream_t)stream));
+}
+
+tq_status tq_hybrid_decode(const uint8_t *packed, int64_t n, int head_dim, int mode,
+                           uint64_t seed, const int32_t *perm, void *out_f16, void *stream) {
+    const size_t row = tq_hybrid_packed_bytes(head_dim, mode);
+    if (head_dim <= 0) return TQ_ERR_INVALID_ARG;
+    if (row == 0) return TQ_ERR_UNSUPPORTED;
+    if (n < 0 || !valid_perm(perm, head_dim)) return TQ_ERR_INVALID_ARG;
+    if (n == 0) return TQ_OK;
+    if (!packed || !out_f16) return TQ_ERR_INVALID_ARG;
+    if (!aligned(out_f16, 16) || !aligned(packed, 4)) return TQ_ERR_MISALIGNED;
+    if (overlap(out_f16, (size_t)n * head_dim * 2, packed, (size_t)n * row))
+        return TQ_ERR_INVALID_ARG;
+    return from_hip(tq::launch_hybrid_decode(mode, packed, n, make_hybrid_consts(mode, seed, perm),
+                                             out_f16, (hipStream_t)stream));
 }
 
 size_t tq_attn_workspace_bytes(int batch, int num_q_heads, int num_kv_heads, int head_dim,

@@ -667,6 +667,439 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const uint32_t *__rest
     }
 }
 
+// ---------------------------------------------------------------------------
+// Hybrid modes tq35 / tq25 at head_dim 128 (aither-kvcache PyPI page, "Hybrid
+// modes (tq35/tq25)": split-group quantization with a QJL residual; "API
+// Reference": HybridTurboQuant, norms embedded in the packed bytes).
+//
+// A vector is taken in group order y = x[perm] (perm from calibration): the
+// halves y[0..64) and y[64..128) are two TurboQuant vectors of dimension 64
+// at (3, 2) bits (tq35) or (2, 1) bits (tq25); the residual r = y - yhat of
+// their decode is sketched by the signs of H_128 D_Q r and its norm rho, and
+// decode adds sqrt(pi/2)/128 * rho * D_Q H_128 s.  Row: codes A | codes B |
+// 128 sign bits | f32 norm A, norm B, rho (68 or 52 bytes).
+//
+// Work mapping: one quad per vector; lane q holds group-order positions
+// 32K + 8q + j in register 8K + j, i.e. the head_dim-128 layout, whose
+// registers 0-15 are the head_dim-64 layout of group A and 16-31 that of
+// group B.  So both 64-point transforms, the 128-point transform of the
+// sketch, the codes and the sign bits all stay in registers; only the
+// channel permutation goes through LDS (a gather on encode, a scatter on
+// decode, through a staged row per quad).
+// ---------------------------------------------------------------------------
+
+template <int MODE>
+struct HybridBits {
+    static constexpr int A = (MODE == 35) ? 3 : 2;
+    static constexpr int B = (MODE == 35) ? 2 : 1;
+    static constexpr int PA = 64 * A / 32;                 // dwords of group-A codes
+    static constexpr int PB = 64 * B / 32;                 // dwords of group-B codes
+    static constexpr int RW = PA + PB + 4 + 3;             // dwords per row
+};
+
+// code = number of the 2^B - 1 (scaled) thresholds strictly below y
+template <int B>
+__device__ __forceinline__ uint32_t count_below(float y, const float *thr) {
+    uint32_t c = 0;
+#pragma unroll
+    for (int k = 0; k < (1 << B) - 1; ++k) c += (thr[k] < y) ? 1u : 0u;
+    return c;
+}
+
+// v with its sign bit XORed by bit 31 of m (the binary16 sign-pair masks hold
+// the signs of registers 2i and 2i + 1 in bits 15 and 31 of word i)
+__device__ __forceinline__ float flip(float v, uint32_t m) {
+    return __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, v) ^ m);
+}
+
+// First butterfly stage (stride 1) on register pairs.
+template <int N>
+__device__ __forceinline__ void stage1(float (&f)[N]) {
+#pragma unroll
+    for (int i = 0; i < N; i += 2) {
+        const float a = f[i], b = f[i + 1];
+        f[i] = a + b;
+        f[i + 1] = a - b;
+    }
+}
+
+// Pack group codes of a half: N = 16 codes per lane (two runs of 8) at BITS
+// bits; returns the dwords this lane stores and their indices within the
+// group's section (count in *ns; lanes with nothing to store get 0).
+template <int BITS>
+__device__ __forceinline__ int pack_half(const uint32_t (&c)[16], int q, uint32_t (&sv)[2],
+                                         int (&si)[2]) {
+    if constexpr (BITS == 3) {
+        // run K: 24-bit field at bit 96K + 24q; lane q < 3 stores dword 3K + q
+        const uint32_t sh = 8 * q + 8;
+#pragma unroll
+        for (int K = 0; K < 2; ++K) {
+            uint32_t G = 0;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) G |= c[8 * K + j] << (3 * j);
+            const uint32_t nbv = quad_move<kQuadNext>(G);
+            sv[K] = __builtin_amdgcn_alignbit(nbv, G << 8, sh);
+            si[K] = 3 * K + q;
+        }
+        return q < 3 ? 2 : 0;
+    } else if constexpr (BITS == 2) {
+        // run K: 16-bit field at bit 64K + 16q, i.e. half (q & 1) of dword
+        // 2K + (q >> 1); lanes q and q ^ 1 splice their halves
+        uint32_t pk = 0;
+#pragma unroll
+        for (int K = 0; K < 2; ++K)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) pk |= c[8 * K + j] << (16 * K + 2 * j);
+        const uint32_t sel2 = (q & 1) ? 0x03020706u : 0x05040100u;
+        const uint32_t p = quad_move<kQuadXor1>(pk);
+        sv[0] = __builtin_amdgcn_perm(p, pk, sel2);
+        si[0] = 2 * (q & 1) + (q >> 1);
+        return 1;
+    } else {
+        // run K: byte 4K + q (code j at bit j); the quad ORs its bytes
+#pragma unroll
+        for (int K = 0; K < 2; ++K) {
+            uint32_t b = 0;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) b |= c[8 * K + j] << j;
+            uint32_t w = b << (8 * q);
+            w |= quad_move<kQuadXor1>(w);
+            w |= quad_move<kQuadXor2>(w);
+            sv[K] = w;
+            si[K] = K;
+        }
+        return q < 2 ? 1 : 0;   // lane q < 2 stores dword q (both lanes hold both)
+    }
+}
+
+// The codes of lane q's 16 positions of a half from that half's section
+// (row dwords `sec`), the inverse of pack_half.
+template <int BITS>
+__device__ __forceinline__ void unpack_half(const uint32_t *sec, int q, uint32_t (&c)[16]) {
+    if constexpr (BITS == 3) {
+        const int wa = (3 * q) >> 2;
+        const int wb = (wa + 1 < 3) ? wa + 1 : 2;
+        const uint32_t s3 = (24u * q) & 31u;
+#pragma unroll
+        for (int K = 0; K < 2; ++K) {
+            const uint32_t fld = __builtin_amdgcn_alignbit(sec[3 * K + wb], sec[3 * K + wa], s3);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) c[8 * K + j] = (fld >> (3 * j)) & 7u;
+        }
+    } else if constexpr (BITS == 2) {
+#pragma unroll
+        for (int K = 0; K < 2; ++K) {
+            const uint32_t w = sec[2 * K + (q >> 1)] >> (16 * (q & 1));
+#pragma unroll
+            for (int j = 0; j < 8; ++j) c[8 * K + j] = (w >> (2 * j)) & 3u;
+        }
+    } else {
+#pragma unroll
+        for (int K = 0; K < 2; ++K) {
+            const uint32_t b = sec[K] >> (8 * q);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) c[8 * K + j] = (b >> j) & 1u;
+        }
+    }
+}
+
+// TurboQuant decode of a half in registers: levels -> n D H_64 c / 64, with
+// the lane sign eps of the cross-lane stages folded into the scale.
+__device__ __forceinline__ void half_decode(float (&f)[16], float scale, const uint32_t (&xm)[8]) {
+    stage1(f);
+    fwht_quad<16>(f, (threadIdx.x & 1) ? -1.0f : 1.0f, (threadIdx.x & 2) ? -1.0f : 1.0f);
+    fwht_registers_scaled<2>(f, scale);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        f[2 * i] = flip(f[2 * i], (xm[i] << 16) & 0x80000000u);
+        f[2 * i + 1] = flip(f[2 * i + 1], xm[i] & 0x80000000u);
+    }
+}
+
+template <int MODE>
+__global__ __launch_bounds__(kThreads) void hybrid_encode_kernel(const u32x4 *__restrict__ x,
+                                                                 int64_t n,
+                                                                 uint32_t *__restrict__ packed,
+                                                                 HybridConsts k) {
+    using HB = HybridBits<MODE>;
+    constexpr int RW = HB::RW;
+    __shared__ __attribute__((aligned(16))) uint16_t xs[kVecPerBlock][128];
+    __shared__ __attribute__((aligned(16))) uint32_t rows[kVecPerBlock * RW];
+    __shared__ u32x4 gidx[8];
+    __shared__ u32x4 smask[16], qmask[16];
+    __shared__ float lev[12];
+    if (threadIdx.x < 8) gidx[threadIdx.x] = u32x4{k.gidx[4 * threadIdx.x], k.gidx[4 * threadIdx.x + 1],
+                                                   k.gidx[4 * threadIdx.x + 2], k.gidx[4 * threadIdx.x + 3]};
+    if (threadIdx.x < 12) lev[threadIdx.x] = threadIdx.x < 8 ? k.lev_a[threadIdx.x] : k.lev_b[threadIdx.x - 8];
+    if (threadIdx.x < 64) {
+        CodecConsts c{};
+        for (int w = 0; w < 4; ++w) c.sign[w] = k.sign[w];
+        store_sign_mask<4, true>(c, threadIdx.x, reinterpret_cast<uint32_t *>(smask));
+    } else if (threadIdx.x < 128) {
+        CodecConsts c{};
+        for (int w = 0; w < 4; ++w) c.sign[w] = k.qsign[w];
+        store_sign_mask<4, false>(c, threadIdx.x - 64, reinterpret_cast<uint32_t *>(qmask));
+    }
+    __syncthreads();
+
+    const int q = threadIdx.x & 3;
+    const uint32_t qi = threadIdx.x >> 2;
+    const int64_t v0 = (int64_t)blockIdx.x * kVecPerBlock;
+    const uint32_t nb = (uint32_t)((n - v0 < kVecPerBlock) ? n - v0 : kVecPerBlock);
+    // Quads past the end stay (their loads read zeros and their rows are not
+    // stored): every lane of a wave takes part in the wave's row stores.
+    if (16 * (threadIdx.x >> 6) >= nb) return;   // the whole wave is past the end
+    // the row, staged per quad for the channel gather
+    const __amdgpu_buffer_rsrc_t rx = span_rsrc(x + v0 * 16, nb * 256u);
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+        const u32x4 u = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, qi * 256u + 16u * q + 64u * g, 0, 0));
+        *reinterpret_cast<u32x4 *>(&xs[qi][8 * q + 32 * g]) = u;
+    }
+    wave_lds_sync();
+    uint32_t w[16];   // binary16 pairs of positions (2i, 2i + 1) in group order
+    {
+        const u32x4 ga = gidx[2 * q], gb = gidx[2 * q + 1];
+        const uint32_t gw[8] = {ga.x, ga.y, ga.z, ga.w, gb.x, gb.y, gb.z, gb.w};
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const uint32_t ch0 = (gw[i >> 1] >> (16 * (i & 1))) & 0xFFu;
+            const uint32_t ch1 = (gw[i >> 1] >> (16 * (i & 1) + 8)) & 0xFFu;
+            w[i] = (uint32_t)xs[qi][ch0] | ((uint32_t)xs[qi][ch1] << 16);
+        }
+    }
+    uint32_t sg[16], sq[16];
+    load_sign_masks<4>(smask, q, sg);
+    load_sign_masks<4>(qmask, q, sq);
+    const float ma = (q & 1) ? -1.0f : 1.0f;
+    const float mb = (q & 2) ? -1.0f : 1.0f;
+    const float eps = ma * mb;
+
+    // norms of the two halves
+    float ssa = 0.0f, ssb = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const half2_t ha = __builtin_bit_cast(half2_t, w[i]);
+        const half2_t hb = __builtin_bit_cast(half2_t, w[8 + i]);
+        ssa = __builtin_amdgcn_fdot2(ha, ha, ssa, false);
+        ssb = __builtin_amdgcn_fdot2(hb, hb, ssb, false);
+    }
+    ssa += quad_move<kQuadXor1>(ssa);
+    ssa += quad_move<kQuadXor2>(ssa);
+    ssb += quad_move<kQuadXor1>(ssb);
+    ssb += quad_move<kQuadXor2>(ssb);
+    const float na = __builtin_sqrtf(ssa), nbn = __builtin_sqrtf(ssb);
+
+    // forward transforms of the halves: sign flip and stride-1 stage in one
+    // dot2 per output, then the 64-point transform scaled to 8 z
+    float fa[16], fb[16];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        fa[2 * i] = dot2_sum(w[i], sg[i]);
+        fa[2 * i + 1] = dot2_diff(w[i], sg[i]);
+        fb[2 * i] = dot2_sum(w[8 + i], sg[8 + i]);
+        fb[2 * i + 1] = dot2_diff(w[8 + i], sg[8 + i]);
+    }
+    auto inv = [](float nv) {
+        float rc = __builtin_amdgcn_rcpf(nv);
+        rc = __builtin_fmaf(rc, __builtin_fmaf(-nv, rc, 1.0f), rc);
+        return (nv > 0.0f) ? rc : 0.0f;
+    };
+    fwht_quad<16>(fa, ma, mb);
+    fwht_registers_scaled<2>(fa, 8.0f * eps * inv(na));
+    fwht_quad<16>(fb, ma, mb);
+    fwht_registers_scaled<2>(fb, 8.0f * eps * inv(nbn));
+    uint32_t ca[16], cb[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        ca[r] = count_below<HB::A>(fa[r], k.thr_a);
+        cb[r] = count_below<HB::B>(fb[r], k.thr_b);
+    }
+    // decode of the halves and the residual, in group order
+    float ra[16], rb[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        ra[r] = lev[ca[r]];
+        rb[r] = lev[8 + cb[r]];
+    }
+    uint32_t xa[8], xb[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        xa[i] = sg[i];
+        xb[i] = sg[8 + i];
+    }
+    half_decode(ra, na * eps * (1.0f / 64), xa);
+    half_decode(rb, nbn * eps * (1.0f / 64), xb);
+    float t[32];
+    float rr = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const half2_t ha = __builtin_bit_cast(half2_t, w[i]);
+        const half2_t hb = __builtin_bit_cast(half2_t, w[8 + i]);
+        t[2 * i] = (float)ha.x - ra[2 * i];
+        t[2 * i + 1] = (float)ha.y - ra[2 * i + 1];
+        t[16 + 2 * i] = (float)hb.x - rb[2 * i];
+        t[16 + 2 * i + 1] = (float)hb.y - rb[2 * i + 1];
+    }
+#pragma unroll
+    for (int r = 0; r < 32; ++r) rr = __builtin_fmaf(t[r], t[r], rr);
+    rr += quad_move<kQuadXor1>(rr);
+    rr += quad_move<kQuadXor2>(rr);
+    const float rho = __builtin_sqrtf(rr);
+    // the sketch: signs of H_128 D_Q r (lane sign eps folded into the last stage)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        t[2 * i] = flip(t[2 * i], (sq[i] << 16) & 0x80000000u);
+        t[2 * i + 1] = flip(t[2 * i + 1], sq[i] & 0x80000000u);
+    }
+    stage1(t);
+    fwht_quad<32>(t, ma, mb);
+    fwht_registers_scaled<2>(t, eps);
+
+    // the row, assembled in LDS: codes A, codes B, sign bits, norms
+    uint32_t *row = rows + qi * RW;
+    {
+        uint32_t sv[2];
+        int si[2];
+        int c = pack_half<HB::A>(ca, q, sv, si);
+        for (int i = 0; i < c; ++i) row[si[i]] = sv[i];
+        c = pack_half<HB::B>(cb, q, sv, si);
+        if (HB::B == 1) {
+            if (c) row[HB::PA + q] = sv[q];
+        } else {
+            for (int i = 0; i < c; ++i) row[HB::PA + si[i]] = sv[i];
+        }
+        // sign bits: byte 4K + q holds the signs of positions 32K + 8q + j
+        uint32_t sb[4];
+#pragma unroll
+        for (int K = 0; K < 4; ++K) {
+            uint32_t b = 0;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) b |= (t[8 * K + j] < 0.0f ? 1u : 0u) << j;
+            uint32_t wv = b << (8 * q);
+            wv |= quad_move<kQuadXor1>(wv);
+            wv |= quad_move<kQuadXor2>(wv);
+            sb[K] = wv;
+        }
+        row[HB::PA + HB::PB + q] = sb[q];
+        if (q < 3)
+            row[HB::PA + HB::PB + 4 + q] = __builtin_bit_cast(uint32_t, q == 0 ? na : (q == 1 ? nbn : rho));
+    }
+    wave_lds_sync();
+    // the wave's rows go out as one contiguous span of dwords
+    const uint32_t wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const uint32_t wrow0 = 16 * wave;                         // first row of the wave in the block
+    const uint32_t wrows = (nb > wrow0) ? ((nb - wrow0 < 16) ? nb - wrow0 : 16) : 0;
+    const __amdgpu_buffer_rsrc_t rp = span_rsrc(packed + (v0 + wrow0) * RW, wrows * RW * 4u);
+#pragma unroll
+    for (uint32_t i = lane; i < 16 * RW; i += 64)
+        __builtin_amdgcn_raw_buffer_store_b32(rows[wrow0 * RW + i], rp, 4u * i, 0, 0);
+}
+
+template <int MODE>
+__global__ __launch_bounds__(kThreads) void hybrid_decode_kernel(const uint32_t *__restrict__ packed,
+                                                                 int64_t n,
+                                                                 u32x4 *__restrict__ out,
+                                                                 HybridConsts k) {
+    using HB = HybridBits<MODE>;
+    constexpr int RW = HB::RW;
+    __shared__ __attribute__((aligned(16))) uint16_t xs[kVecPerBlock][128];
+    __shared__ __attribute__((aligned(16))) uint32_t rows[kVecPerBlock * RW];
+    __shared__ u32x4 gidx[8];
+    __shared__ u32x4 smask[16], qmask[16];
+    __shared__ float lev[12];
+    if (threadIdx.x < 8) gidx[threadIdx.x] = u32x4{k.gidx[4 * threadIdx.x], k.gidx[4 * threadIdx.x + 1],
+                                                   k.gidx[4 * threadIdx.x + 2], k.gidx[4 * threadIdx.x + 3]};
+    if (threadIdx.x < 12) lev[threadIdx.x] = threadIdx.x < 8 ? k.lev_a[threadIdx.x] : k.lev_b[threadIdx.x - 8];
+    if (threadIdx.x < 64) {
+        CodecConsts c{};
+        for (int w = 0; w < 4; ++w) c.sign[w] = k.sign[w];
+        store_sign_mask<4, false>(c, threadIdx.x, reinterpret_cast<uint32_t *>(smask));
+    } else if (threadIdx.x < 128) {
+        CodecConsts c{};
+        for (int w = 0; w < 4; ++w) c.sign[w] = k.qsign[w];
+        store_sign_mask<4, false>(c, threadIdx.x - 64, reinterpret_cast<uint32_t *>(qmask));
+    }
+    __syncthreads();
+
+    const int q = threadIdx.x & 3;
+    const uint32_t qi = threadIdx.x >> 2;
+    const int64_t v0 = (int64_t)blockIdx.x * kVecPerBlock;
+    const uint32_t nb = (uint32_t)((n - v0 < kVecPerBlock) ? n - v0 : kVecPerBlock);
+    const uint32_t wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const uint32_t wrow0 = 16 * wave;
+    if (wrow0 >= nb) return;   // the whole wave is past the end; no barrier follows
+    const uint32_t wrows = (nb - wrow0 < 16) ? nb - wrow0 : 16;
+    // the wave's rows, one contiguous span of dwords, into LDS
+    {
+        const __amdgpu_buffer_rsrc_t rp = span_rsrc(packed + (v0 + wrow0) * RW, wrows * RW * 4u);
+#pragma unroll
+        for (uint32_t i = lane; i < 16 * RW; i += 64)
+            rows[wrow0 * RW + i] = __builtin_amdgcn_raw_buffer_load_b32(rp, 4u * i, 0, 0);
+    }
+    wave_lds_sync();
+    if (qi >= nb) return;      // uniform over the quad; only wave-local LDS follows
+    const uint32_t *row = rows + qi * RW;
+    uint32_t ca[16], cb[16];
+    unpack_half<HB::A>(row, q, ca);
+    unpack_half<HB::B>(row + HB::PA, q, cb);
+    const uint32_t *sbits = row + HB::PA + HB::PB;
+    const float na = __builtin_bit_cast(float, row[HB::PA + HB::PB + 4]);
+    const float nbn = __builtin_bit_cast(float, row[HB::PA + HB::PB + 5]);
+    const float rho = __builtin_bit_cast(float, row[HB::PA + HB::PB + 6]);
+    uint32_t sg[16], sq[16];
+    load_sign_masks<4>(smask, q, sg);
+    load_sign_masks<4>(qmask, q, sq);
+    const float eps = ((q & 1) ? -1.0f : 1.0f) * ((q & 2) ? -1.0f : 1.0f);
+
+    float ra[16], rb[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        ra[r] = lev[ca[r]];
+        rb[r] = lev[8 + cb[r]];
+    }
+    uint32_t xa[8], xb[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        xa[i] = sg[i];
+        xb[i] = sg[8 + i];
+    }
+    half_decode(ra, na * eps * (1.0f / 64), xa);
+    half_decode(rb, nbn * eps * (1.0f / 64), xb);
+    // the sketch's correction sqrt(pi/2)/128 rho D_Q H_128 s
+    float t[32];
+#pragma unroll
+    for (int K = 0; K < 4; ++K) {
+        const uint32_t b = sbits[K] >> (8 * q);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) t[8 * K + j] = ((b >> j) & 1u) ? -1.0f : 1.0f;
+    }
+    stage1(t);
+    fwht_quad<32>(t, (q & 1) ? -1.0f : 1.0f, (q & 2) ? -1.0f : 1.0f);
+    fwht_registers_scaled<2>(t, rho * eps * (1.2533141373155003f / 128));
+    uint16_t hv[32];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const float c0 = flip(t[2 * i], (sq[i] << 16) & 0x80000000u);
+        const float c1 = flip(t[2 * i + 1], sq[i] & 0x80000000u);
+        const float y0 = (i < 8 ? ra[2 * i] : rb[2 * i - 16]) + c0;
+        const float y1 = (i < 8 ? ra[2 * i + 1] : rb[2 * i - 15]) + c1;
+        hv[2 * i] = __builtin_bit_cast(uint16_t, (_Float16)y0);
+        hv[2 * i + 1] = __builtin_bit_cast(uint16_t, (_Float16)y1);
+    }
+    // back to channel order through the quad's staged row
+    {
+        const u32x4 ga = gidx[2 * q], gb = gidx[2 * q + 1];
+        const uint32_t gw[8] = {ga.x, ga.y, ga.z, ga.w, gb.x, gb.y, gb.z, gb.w};
+#pragma unroll
+        for (int r = 0; r < 32; ++r) xs[qi][(gw[r >> 2] >> (8 * (r & 3))) & 0xFFu] = hv[r];
+    }
+    wave_lds_sync();
+    u32x4 *dst = out + (v0 + qi) * 16 + q;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) dst[4 * g] = *reinterpret_cast<const u32x4 *>(&xs[qi][8 * q + 32 * g]);
+}
+
 // One block per 64 enc_vpq(d) (encode) or 64 dec_vpq(d, bits) (decode)
 // vectors: a full grid, so the hardware keeps every CU fed without a tail of
 // long-running blocks (a grid-stride loop measured 10-30% slower).
@@ -738,6 +1171,34 @@ hipError_t launch_decode(int head_dim, int bits, const uint8_t *packed, const fl
         default: return hipErrorInvalidValue;
     }
 #undef TQ_DEC
+    return hipGetLastError();
+}
+
+int hybrid_row_bytes(int mode) {
+    return mode == 35 ? 4 * HybridBits<35>::RW : (mode == 25 ? 4 * HybridBits<25>::RW : 0);
+}
+
+hipError_t launch_hybrid_encode(int mode, const void *x, int64_t n, const HybridConsts &k,
+                                uint8_t *packed, hipStream_t stream) {
+    if (n > (int64_t)kVecPerBlock * 0x7fffffff) return hipErrorInvalidValue;
+    const dim3 grid = grid_for(n, kVecPerBlock), block(kThreads);
+    const u32x4 *xs = static_cast<const u32x4 *>(x);
+    uint32_t *pk = reinterpret_cast<uint32_t *>(packed);
+    if (mode == 35) hipLaunchKernelGGL(hybrid_encode_kernel<35>, grid, block, 0, stream, xs, n, pk, k);
+    else if (mode == 25) hipLaunchKernelGGL(hybrid_encode_kernel<25>, grid, block, 0, stream, xs, n, pk, k);
+    else return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
+hipError_t launch_hybrid_decode(int mode, const uint8_t *packed, int64_t n,
+                                const HybridConsts &k, void *out, hipStream_t stream) {
+    if (n > (int64_t)kVecPerBlock * 0x7fffffff) return hipErrorInvalidValue;
+    const dim3 grid = grid_for(n, kVecPerBlock), block(kThreads);
+    const uint32_t *pk = reinterpret_cast<const uint32_t *>(packed);
+    u32x4 *o = static_cast<u32x4 *>(out);
+    if (mode == 35) hipLaunchKernelGGL(hybrid_decode_kernel<35>, grid, block, 0, stream, pk, n, o, k);
+    else if (mode == 25) hipLaunchKernelGGL(hybrid_decode_kernel<25>, grid, block, 0, stream, pk, n, o, k);
+    else return hipErrorInvalidValue;
     return hipGetLastError();
 }
 

@@ -41,6 +41,29 @@ hipError_t launch_encode(int head_dim, int bits, const void *x, int64_t n, const
 hipError_t launch_decode(int head_dim, int bits, const uint8_t *packed, const float *norms,
                          int64_t n, const CodecConsts &k, void *out, hipStream_t stream);
 
+// Hybrid modes (tq35 / tq25) at head_dim 128: two channel groups of 64 coded
+// as TurboQuant vectors at (3, 2) or (2, 1) bits, plus the sign sketch of the
+// residual.  Everything fixed by (mode, seed, channel permutation).
+struct HybridConsts {
+    uint32_t sign[4];   // sigma of group-order positions 0..127 (A: 0..63, B: 64..127)
+    uint32_t qsign[4];  // sigma_Q of the sketch
+    float thr_a[7];     // 8 x the group-A thresholds (2^bA - 1 used), ascending
+    float thr_b[3];     // 8 x the group-B thresholds
+    float lev_a[8];     // group-A levels
+    float lev_b[4];     // group-B levels
+    uint32_t gidx[32];  // byte 32 q + r: the channel held in register r of lane q
+};
+
+constexpr int kHybridHeadDim = 128;
+
+// Row bytes of a hybrid mode (35 or 25) at head_dim 128: 68 or 52.
+int hybrid_row_bytes(int mode);
+
+hipError_t launch_hybrid_encode(int mode, const void *x, int64_t n, const HybridConsts &k,
+                                uint8_t *packed, hipStream_t stream);
+hipError_t launch_hybrid_decode(int mode, const uint8_t *packed, int64_t n,
+                                const HybridConsts &k, void *out, hipStream_t stream);
+
 int device_cu_count();
 
 }  // namespace tq

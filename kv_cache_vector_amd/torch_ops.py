@@ -15,6 +15,9 @@ operators).
                                              context_lens, bits, seed, scale,
                                              v_bits=-1) -> out
       (v_bits: width of the value codes; -1 means the same as the keys')
+    torch.ops.kv_cache_vector.tq_hybrid_encode(x, mode, seed, perm) -> packed
+    torch.ops.kv_cache_vector.tq_hybrid_decode(packed, mode, seed, perm) -> x_hat
+      (hybrid modes: mode 35 or 25, head_dim 128, perm a host int32 tensor)
 
 Every operator takes head_dim 64, 128 or 256, read off the tensors' last
 dimension (the attention operator: at most 8 query heads per kv head at 256).
@@ -245,3 +248,69 @@ def _(q, k_packed, k_norms, v_packed, v_norms, block_tables, context_lens, bits,
     check_attn_args(q, k_packed, k_norms, v_packed, v_norms, block_tables, context_lens, bits,
                     bits if v_bits < 0 else v_bits)
     return torch.empty_like(q, memory_format=torch.contiguous_format)
+
+
+# ---------------------------------------------------------------------------
+# hybrid modes (tq35 / tq25), head_dim 128; perm is a host int32 tensor of
+# the 128 channels (group A = perm[:64])
+
+def _hybrid_row(mode) -> int:
+    # comparisons, not a dict lookup: under torch.compile mode may be a
+    # symbolic int, which cannot be hashed
+    if mode == 35:
+        return 68
+    if mode == 25:
+        return 52
+    raise ValueError("mode must be 35 (tq35) or 25 (tq25)")
+
+
+def _host_perm(perm: torch.Tensor) -> torch.Tensor:
+    if perm.device.type != "cpu" or perm.dtype != torch.int32 or tuple(perm.shape) != (128,):
+        raise ValueError("perm must be a host int32 tensor of 128 channels")
+    return perm.contiguous()
+
+
+@torch.library.custom_op("kv_cache_vector::tq_hybrid_encode", mutates_args=())
+def tq_hybrid_encode(x: torch.Tensor, mode: int, seed: int, perm: torch.Tensor) -> torch.Tensor:
+    _gpu(x, "x")
+    if x.dtype != torch.float16 or x.dim() < 1 or x.shape[-1] != 128:
+        raise ValueError("x must be float16 [..., 128]")
+    row = _hybrid_row(mode)
+    perm = _host_perm(perm)
+    x = x.contiguous()
+    packed = torch.empty(tuple(x.shape[:-1]) + (row,), dtype=torch.uint8, device=x.device)
+    _lib.check(_lib.tq_hybrid_encode(x.data_ptr(), x.numel() // 128, 128, mode, _seed_u64(seed),
+                                     perm.data_ptr(), packed.data_ptr(), _stream(x.device)),
+               "tq_hybrid_encode")
+    return packed
+
+
+@tq_hybrid_encode.register_fake
+def _(x, mode, seed, perm):
+    if x.shape[-1] != 128:
+        raise ValueError("x must be [..., 128]")
+    return x.new_empty(tuple(x.shape[:-1]) + (_hybrid_row(mode),), dtype=torch.uint8)
+
+
+@torch.library.custom_op("kv_cache_vector::tq_hybrid_decode", mutates_args=())
+def tq_hybrid_decode(packed: torch.Tensor, mode: int, seed: int,
+                     perm: torch.Tensor) -> torch.Tensor:
+    _gpu(packed, "packed")
+    row = _hybrid_row(mode)
+    if packed.dtype != torch.uint8 or packed.dim() < 1 or packed.shape[-1] != row:
+        raise ValueError("packed must be uint8 [..., %d]" % row)
+    perm = _host_perm(perm)
+    packed = packed.contiguous()
+    out = torch.empty(tuple(packed.shape[:-1]) + (128,), dtype=torch.float16,
+                      device=packed.device)
+    _lib.check(_lib.tq_hybrid_decode(packed.data_ptr(), packed.numel() // row, 128, mode,
+                                     _seed_u64(seed), perm.data_ptr(), out.data_ptr(),
+                                     _stream(packed.device)), "tq_hybrid_decode")
+    return out
+
+
+@tq_hybrid_decode.register_fake
+def _(packed, mode, seed, perm):
+    if packed.shape[-1] != _hybrid_row(mode):
+        raise ValueError("packed rows of %d bytes are not mode %d's" % (packed.shape[-1], mode))
+    return packed.new_empty(tuple(packed.shape[:-1]) + (128,), dtype=torch.float16)

@@ -1,7 +1,10 @@
 """torch-facing wrappers over libtq, shaped like the Python objects the pages
 describe (aither-kvcache PyPI page, "API Reference": TurboQuant(head_dim,
 bits, seed, device) with encode / decode / compression_ratio / validate /
-benchmark, and TQPagedAttention(tq, num_query_heads).forward(...)).
+benchmark, HybridTurboQuant(head_dim, mode, seed, device) with
+calibrate_uniform / calibrate / encode / decode / validate /
+compression_ratio / packed_dim_for_mode, and
+TQPagedAttention(tq, num_query_heads).forward(...)).
 
 torch provides device memory and the current stream; every step of the codec
 runs in libtq's HIP kernels.  CPU tensors are rejected: there is no host
@@ -11,6 +14,7 @@ from __future__ import annotations
 
 import math
 
+import numpy as np
 import torch
 
 from . import _lib
@@ -170,3 +174,104 @@ class TQPagedAttention:
                                           tq.seed, self.scale)
 
     __call__ = forward
+
+
+class HybridTurboQuant:
+    """Hybrid modes tq35 / tq25 (aither-kvcache PyPI page, "Hybrid modes
+    (tq35/tq25)" and "API Reference"): [..., 128] fp16 <-> [..., row] uint8
+    with the norms inside the row (68 bytes for tq35, 52 for tq25).
+
+    The channels are split into two groups of 64 by calibration (group A,
+    coded with the more bits, holds the channels with the largest mean square
+    in `calibrate`; `calibrate_uniform` keeps channels 0-63 / 64-127); each
+    group is a TurboQuant vector of dimension 64 at (3, 2) or (2, 1) bits, and
+    the residual is kept as a 128-bit sign sketch plus its norm (QJL), which
+    makes inner products with the decoded vectors unbiased."""
+
+    MODES = {"tq35": 35, "tq25": 25}
+
+    def __init__(self, head_dim: int = HEAD_DIM, mode: str = "tq35", seed: int = 42,
+                 device="cuda"):
+        if mode not in self.MODES:
+            raise ValueError("mode must be one of %s" % sorted(self.MODES))
+        if self.packed_dim_for_mode(head_dim, mode) == 0:
+            raise ValueError("hybrid modes take head_dim 128")
+        self.head_dim = head_dim
+        self.mode = mode
+        self.seed = int(seed) & (2 ** 64 - 1)
+        self.device = torch.device(device)
+        if self.device.type != "cuda":
+            raise ValueError("HybridTurboQuant runs on the GPU only")
+        self.num_kv_heads = 1
+        self._perm = np.arange(head_dim, dtype=np.int32)
+
+    @staticmethod
+    def packed_dim_for_mode(head_dim: int, mode: str) -> int:
+        """Bytes of one packed row (norms included); 0 when unsupported."""
+        if mode not in HybridTurboQuant.MODES:
+            return 0
+        return _lib.tq_hybrid_packed_bytes(head_dim, HybridTurboQuant.MODES[mode])
+
+    @property
+    def packed_dim(self) -> int:
+        return self.packed_dim_for_mode(self.head_dim, self.mode)
+
+    @property
+    def perm(self) -> np.ndarray:
+        """Channel permutation: perm[0..63] is group A, perm[64..127] group B."""
+        return self._perm.copy()
+
+    def compression_ratio(self) -> float:
+        return 2.0 * self.head_dim / self.packed_dim
+
+    def calibrate_uniform(self, num_kv_heads: int = 1) -> None:
+        """Data-free split: channels 0-63 in group A, 64-127 in group B (the
+        same for every one of the num_kv_heads heads)."""
+        if num_kv_heads < 1:
+            raise ValueError("num_kv_heads must be positive")
+        self.num_kv_heads = num_kv_heads
+        self._perm = np.arange(self.head_dim, dtype=np.int32)
+
+    def calibrate(self, sample_vectors: torch.Tensor) -> None:
+        """Group A = the 64 channels with the largest mean square over the
+        sample (ties to the lower channel), both groups in ascending channel
+        order."""
+        if sample_vectors.shape[-1] != self.head_dim:
+            raise ValueError("sample_vectors must be [..., %d]" % self.head_dim)
+        ms = sample_vectors.reshape(-1, self.head_dim).float().pow(2).mean(0).cpu().numpy()
+        order = np.lexsort((np.arange(self.head_dim), -ms))     # largest first, lower index on ties
+        h = self.head_dim // 2
+        self._perm = np.concatenate([np.sort(order[:h]), np.sort(order[h:])]).astype(np.int32)
+
+    def encode(self, x: torch.Tensor) -> torch.Tensor:
+        """x [..., 128] fp16 -> packed [..., packed_dim] uint8 (norms embedded)."""
+        _require_gpu(x, "x")
+        if x.dtype != torch.float16 or x.shape[-1] != self.head_dim:
+            raise ValueError("x must be float16 [..., %d]" % self.head_dim)
+        return torch.ops.kv_cache_vector.tq_hybrid_encode(
+            x, self.MODES[self.mode], torch_ops.seed_to_i64(self.seed),
+            torch.from_numpy(self._perm))
+
+    def decode(self, packed: torch.Tensor) -> torch.Tensor:
+        """packed [..., packed_dim] uint8 -> [..., 128] fp16."""
+        _require_gpu(packed, "packed")
+        if packed.dtype != torch.uint8 or packed.shape[-1] != self.packed_dim:
+            raise ValueError("packed must be uint8 [..., %d]" % self.packed_dim)
+        return torch.ops.kv_cache_vector.tq_hybrid_decode(
+            packed, self.MODES[self.mode], torch_ops.seed_to_i64(self.seed),
+            torch.from_numpy(self._perm))
+
+    def validate(self, num_vectors: int = 10000, seed: int = 0) -> dict:
+        """Round-trip MSE per coordinate of the unit vector on N(0,1) vectors,
+        and the relative bias of the inner products <x, xhat> against ||x||^2
+        (the direction in which the TurboQuant part alone shrinks; the QJL
+        sketch makes the estimate unbiased)."""
+        g = torch.Generator(device=self.device).manual_seed(seed)
+        x = torch.randn(num_vectors, self.head_dim, generator=g, device=self.device).half()
+        xh = self.decode(self.encode(x)).float()
+        xf = x.float()
+        mse = float((((xf - xh) ** 2).sum(1) / (xf ** 2).sum(1)).mean())
+        xx = (xf * xf).sum(1)
+        bias = float(((xf * xh).sum(1) - xx).mean() / xx.mean())
+        return {"mse": mse, "inner_product_bias": bias, "num_vectors": num_vectors,
+                "mode": self.mode}

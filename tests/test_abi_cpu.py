@@ -277,3 +277,31 @@ def test_ceiling_hook_argument_errors(L):
     assert f(0, 64, A, None, 0, B, C, None) == 0           # nothing to do
     assert f(0, 64, A, None, 10, B, None, None) == 1       # encode mix needs the norm output
     assert f(1, 64, A, None, 10, B, None, None) == 1       # decode mix needs the norm input
+
+
+def test_hybrid_argument_errors(L):
+    """The hybrid entry points check their arguments on the host, including
+    the channel permutation, before anything touches the GPU."""
+    assert L.tq_hybrid_packed_bytes(128, 35) == 68 and L.tq_hybrid_packed_bytes(128, 25) == 52
+    assert L.tq_hybrid_packed_bytes(64, 35) == 0 and L.tq_hybrid_packed_bytes(128, 40) == 0
+    ident = np.arange(128, dtype=np.int32)
+    dup = ident.copy()
+    dup[5] = 4
+    out_of_range = ident.copy()
+    out_of_range[0] = 128
+    e, dcd = L.tq_hybrid_encode, L.tq_hybrid_decode
+    p = ident.ctypes.data
+    assert e(A, 10, 128, 30, 0, p, B, None) == UNSUP
+    assert e(A, 10, 64, 35, 0, p, B, None) == UNSUP
+    assert e(A, -1, 128, 35, 0, p, B, None) == INVAL
+    assert e(A, 0, 128, 35, 0, p, B, None) == OK
+    assert e(A, 10, 128, 35, 0, dup.ctypes.data, B, None) == INVAL
+    assert e(A, 10, 128, 35, 0, out_of_range.ctypes.data, B, None) == INVAL
+    assert e(None, 10, 128, 35, 0, p, B, None) == INVAL
+    assert e(A + 8, 10, 128, 35, 0, p, B, None) == MISAL
+    assert e(A, 10, 128, 35, 0, p, B + 2, None) == MISAL
+    assert e(A, 10, 128, 35, 0, p, A + 1024, None) == INVAL      # rows overlap the input
+    assert dcd(B, 10, 128, 25, 0, p, A + 4, None) == MISAL
+    assert dcd(B, 10, 128, 25, 0, dup.ctypes.data, A, None) == INVAL
+    assert dcd(B, 10, 128, 25, 0, p, B + 64, None) == INVAL       # output overlaps the rows
+    assert dcd(B, 0, 128, 25, 0, None, A, None) == OK

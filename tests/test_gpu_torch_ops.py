@@ -144,3 +144,26 @@ def test_graph_captured_decode_step(dev):
         assert torch.equal(out, eager), "replay %d" % rep
         for a, b in zip(caches, eager_caches):
             assert torch.equal(a, b), "replay %d" % rep
+
+
+def test_hybrid_ops_compile_without_graph_breaks(dev):
+    """The hybrid modes' operators trace under torch.compile(fullgraph=True)
+    and give the same bytes as eager calls (the pages: every mode registers
+    custom ops for zero-graph-break decode)."""
+    from kv_cache_vector_amd.turboquant import HybridTurboQuant
+    x = torch.from_numpy(W.gaussian(1000, seed=12)).to(dev)
+    for mode in ("tq35", "tq25"):
+        h = HybridTurboQuant(128, mode, 4, dev)
+        h.calibrate(x)
+        perm = torch.from_numpy(h.perm)
+        m = HybridTurboQuant.MODES[mode]
+
+        def step(x, perm=perm, m=m):
+            p = OPS.tq_hybrid_encode(x, m, 4, perm)
+            return p, OPS.tq_hybrid_decode(p, m, 4, perm)
+
+        p1, y1 = step(x)
+        p2, y2 = torch.compile(step, fullgraph=True)(x)
+        torch.cuda.synchronize()
+        assert torch.equal(p1, p2) and torch.equal(y1, y2)
+        assert torch.equal(p1, h.encode(x)) and torch.equal(y1, h.decode(p1))

@@ -130,3 +130,33 @@ def test_attention_op_fake_checks_arguments():
     a["k_norms"] = torch.empty(10, 16, 2, dtype=torch.float16, device="meta")
     with pytest.raises(ValueError, match="float32"):
         OPS.tq_attn_decode(*a.values(), 4, 0, 0.088)
+
+
+def test_hybrid_ops_fake_shapes_and_checks():
+    from kv_cache_vector_amd.turboquant import HybridTurboQuant
+    x = torch.empty(3, 5, 128, dtype=torch.float16, device="meta")
+    perm = torch.arange(128, dtype=torch.int32)
+    for mode, row in ((35, 68), (25, 52)):
+        p = OPS.tq_hybrid_encode(x, mode, 0, perm)
+        assert p.shape == (3, 5, row) and p.dtype == torch.uint8
+        y = OPS.tq_hybrid_decode(p, mode, 0, perm)
+        assert y.shape == (3, 5, 128) and y.dtype == torch.float16
+    with pytest.raises(ValueError):
+        OPS.tq_hybrid_encode(x, 40, 0, perm)
+    with pytest.raises(ValueError):
+        OPS.tq_hybrid_decode(torch.empty(4, 60, dtype=torch.uint8, device="meta"), 35, 0, perm)
+    with pytest.raises(ValueError, match="GPU"):
+        OPS.tq_hybrid_encode(torch.zeros(2, 128, dtype=torch.float16), 35, 0, perm)
+    assert HybridTurboQuant.packed_dim_for_mode(128, "tq35") == 68
+    assert HybridTurboQuant.packed_dim_for_mode(128, "tq25") == 52
+    assert HybridTurboQuant.packed_dim_for_mode(64, "tq35") == 0
+    h = HybridTurboQuant(128, "tq25", 1, "cuda")
+    assert abs(h.compression_ratio() - 256 / 52) < 1e-12
+    # calibration (host statistics): the 64 channels of largest mean square form group A
+    scale = torch.ones(128)
+    scale[[3, 70, 127]] = 20.0
+    h.calibrate(torch.randn(2000, 128) * scale)
+    assert {3, 70, 127} <= set(h.perm[:64].tolist())
+    assert sorted(h.perm.tolist()) == list(range(128))
+    h.calibrate_uniform(8)
+    assert h.perm.tolist() == list(range(128)) and h.num_kv_heads == 8
