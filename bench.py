@@ -286,6 +286,43 @@ def side_measurements(torch, dev, stream, x, packed, norms):
     res = attention_measurement(torch, dev, stream)
     res.update(stream_encode_measurement(torch, dev, stream, x, packed, norms))
     res.update(codec_side_measurement(torch, dev, stream, x, packed, norms))
+    res.update(hybrid_measurement(torch, dev, stream, x))
+    return res
+
+
+def hybrid_measurement(torch, dev, stream, x):
+    """Hybrid modes tq35 / tq25 (split groups + QJL residual) over the whole
+    resident 8B-shaped cache: encode and decode, median of 5 launches each
+    (identity channel split; the split does not change the work)."""
+    from kv_cache_vector_amd import _lib
+    import numpy as np
+    s = stream.cuda_stream
+    res = {}
+    perm = np.arange(D, dtype=np.int32)
+    out = torch.empty_like(x)
+    for mode, name in ((35, "tq35"), (25, "tq25")):
+        row = _lib.tq_hybrid_packed_bytes(D, mode)
+        pk = torch.empty((N, row), dtype=torch.uint8, device=dev)
+        calls = {"encode": lambda: _lib.tq_hybrid_encode(x.data_ptr(), N, D, mode, 0,
+                                                         perm.ctypes.data, pk.data_ptr(), s),
+                 "decode": lambda: _lib.tq_hybrid_decode(pk.data_ptr(), N, D, mode, 0,
+                                                         perm.ctypes.data, out.data_ptr(), s)}
+        for what, fn in calls.items():
+            _lib.check(fn(), "tq_hybrid_" + what)
+            ts = []
+            for _ in range(5):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                _lib.check(fn(), "tq_hybrid_" + what)
+                e1.record(stream)
+                torch.cuda.synchronize()
+                ts.append(e0.elapsed_time(e1))
+            ms = statistics.median(ts)
+            res["hybrid_%s_%s_ms" % (name, what)] = round(ms, 4)
+            res["hybrid_%s_%s_hbm_frac" % (name, what)] = round(
+                N * (2 * D + row) / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)
+        del pk
+    del out
     return res
 
 
