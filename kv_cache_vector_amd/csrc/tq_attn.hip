@@ -246,14 +246,19 @@ __device__ __forceinline__ void score_chunks(const char *tab, const uint32_t (&k
 // Value operand builders: Bv[jj] holds value dim jj of the lane's slice for
 // tokens 4r .. 4r+3, as (c_hi, c_lo) pairs; vc[i] is the lane's packed value
 // bits for token 4r + i.
+// 4-bit values: the index bytes pair two tokens' codes of one dim, so one
+// lookup (the same byte -> two-code table as the keys') returns the (c_hi,
+// c_lo) pairs of both tokens, already in the order of the operand's K slots.
+// x[p] byte k: dim 2k of tokens 2p (low nibble) and 2p + 1 (high nibble);
+// y[p] byte k: dim 2k + 1.
 template <int K, int NJJ>
-__device__ __forceinline__ void value_bytes4(const char *tab, const uint32_t (&vc)[4],
-                                             uint32_t laneoff, u32x4 (&Bv)[NJJ]) {
-    u32x2 L[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) L[i] = lut8<K>(tab, vc[i], laneoff);
-    Bv[2 * K] = u32x4{L[0].x, L[1].x, L[2].x, L[3].x};
-    Bv[2 * K + 1] = u32x4{L[0].y, L[1].y, L[2].y, L[3].y};
+__device__ __forceinline__ void value_pairs4(const char *tab, const uint32_t (&x)[2],
+                                             const uint32_t (&y)[2], uint32_t laneoff,
+                                             u32x4 (&Bv)[NJJ]) {
+    const u32x2 e0 = lut8<K>(tab, x[0], laneoff), e1 = lut8<K>(tab, x[1], laneoff);
+    const u32x2 o0 = lut8<K>(tab, y[0], laneoff), o1 = lut8<K>(tab, y[1], laneoff);
+    Bv[2 * K] = u32x4{e0.x, e0.y, e1.x, e1.y};
+    Bv[2 * K + 1] = u32x4{o0.x, o0.y, o1.x, o1.y};
 }
 
 template <int K, int NJJ>
@@ -290,14 +295,18 @@ __device__ __forceinline__ void value_operands(const char *tab, const uint32_t (
                                                uint32_t laneoff, int q4, uint32_t vsh,
                                                u32x4 (&Bv)[NJJ]) {
     if constexpr (VB == 4) {
-        uint32_t w[4];
+        uint32_t x[2], y[2];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) w[i] = vc[i][0];
-        value_bytes4<0>(tab, w, laneoff, Bv);
-        value_bytes4<1>(tab, w, laneoff, Bv);
+        for (int p = 0; p < 2; ++p) {
+            const uint32_t a = vc[2 * p][0], b = vc[2 * p + 1][0];
+            x[p] = (a & 0x0F0F0F0Fu) | ((b << 4) & 0xF0F0F0F0u);
+            y[p] = ((a >> 4) & 0x0F0F0F0Fu) | (b & 0xF0F0F0F0u);
+        }
+        value_pairs4<0>(tab, x, y, laneoff, Bv);
+        value_pairs4<1>(tab, x, y, laneoff, Bv);
         if constexpr (NJJ == 8) {
-            value_bytes4<2>(tab, w, laneoff, Bv);
-            value_bytes4<3>(tab, w, laneoff, Bv);
+            value_pairs4<2>(tab, x, y, laneoff, Bv);
+            value_pairs4<3>(tab, x, y, laneoff, Bv);
         }
     } else if constexpr (VB == 2) {
         uint32_t w[4];
@@ -624,30 +633,36 @@ __global__ __launch_bounds__(kMThreads) void attn_split_kernel(AttnParams p) {
         // inside binary16.
         const int tbase = t0 + pg * kAttnBlockSize + 4 * r;
         const bool full = rok[d] && (t0 + pg * kAttnBlockSize + kAttnBlockSize <= t1);
-        float s2[4], vn[4];
+        // exponents against the current reference: t = s - Mc (one fma per token)
+        const float Mc0 = (M == -__builtin_inff()) ? 0.0f : M;
+        float t[4], vn[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            s2[i] = S[i] * (rkn[d][i] * qsl);
+            t[i] = __builtin_fmaf(S[i], rkn[d][i] * qsl, -Mc0);
             vn[i] = rvn[d][i];
         }
         if (!full) {                                    // wave-uniform
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const bool ok = rok[d] && (tbase + i < t1);
-                s2[i] = ok ? s2[i] : -__builtin_inff();
+                t[i] = ok ? t[i] : -__builtin_inff();
                 vn[i] = ok ? vn[i] : 0.0f;
             }
         }
-        float smax = __builtin_fmaxf(__builtin_fmaxf(s2[0], s2[1]), __builtin_fmaxf(s2[2], s2[3]));
+        float smax = __builtin_fmaxf(__builtin_fmaxf(t[0], t[1]), __builtin_fmaxf(t[2], t[3]));
         smax = hv ? smax : -__builtin_inff();
         const float vmax = __builtin_fmaxf(__builtin_fmaxf(vn[0], vn[1]), __builtin_fmaxf(vn[2], vn[3]));
-        if (__builtin_amdgcn_ballot_w64(smax > M + kLazy || vmax > vlim)) {
+        const float lim = (M == -__builtin_inff()) ? -__builtin_inff() : kLazy;
+        if (__builtin_amdgcn_ballot_w64(smax > lim || vmax > vlim)) {
             // new score reference of every head whose scores passed it by 2^8
             float mx = __builtin_fmaxf(smax, __shfl_xor(smax, 16));
             mx = __builtin_fmaxf(mx, __shfl_xor(mx, 32));
-            const float Mn = (mx > M + kLazy) ? mx : M;
+            const float Mn = (mx > lim) ? Mc0 + mx : M;
             const float f = (Mn == M) ? 1.0f : __builtin_amdgcn_exp2f(M - Mn);
             lsum *= f;
+            const float sh = (Mn == M) ? 0.0f : Mn - Mc0;   // the page against the new reference
+#pragma unroll
+            for (int i = 0; i < 4; ++i) t[i] -= sh;
             M = Mn;
             // new norm bound: the power of two above the wave's largest norm
             float vw = vmax;
@@ -669,12 +684,10 @@ __global__ __launch_bounds__(kMThreads) void attn_split_kernel(AttnParams p) {
                 for (int jj = 0; jj < NJJ; ++jj) acc[jj][i] *= fi;
             }
         }
-        // before any valid token M is -inf; masked tokens must still give 0
-        const float Mc = (M == -__builtin_inff()) ? 0.0f : M;
         uint32_t w1[4], w2[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const float pr = __builtin_amdgcn_exp2f(s2[i] - Mc);
+            const float pr = __builtin_amdgcn_exp2f(t[i]);
             lsum += pr;
             const float w = pr * (vn[i] * vscale);
             // w = hi + lo; hi is w truncated to binary16, lo the remainder
