@@ -81,7 +81,7 @@ constexpr int kMPrefetch = 1;               // extra ring slots: pages of loads 
 constexpr int kMTargetWaves = 2048;
 constexpr float kLevelScale = 16.0f;        // binary16 levels are 16 c
 constexpr float kWShift = 6.0f;             // value weights carry 2^6
-constexpr int kLutRow = 256;                // bytes per table row: keys' half, values' half
+constexpr int kLutRow = 256;                // bytes per table row (64 banks of 4 bytes)
 constexpr int kQuadPrev = 0x90;             // quad_perm [0,0,1,2]: lane q <- lane q-1 (0 <- 0)
 constexpr int kRowRor8 = 0x128;             // row_ror:8: lane m of a 16-lane row <- lane m ^ 8
 
@@ -152,34 +152,56 @@ __device__ __forceinline__ f4 mfma(const u32x4 &a, const u32x4 &b, f4 c) {
 // Code lookup tables.  One table entry turns a group of codes into their
 // (c_hi, c_lo) pairs: a byte of two 4-bit codes (8 bytes), a byte of four
 // 2-bit codes (16 bytes) or a 6-bit field of two 3-bit codes (8 bytes).
-// Entry e of a side lives in row e of the LDS table (256 bytes: keys in the
-// first half, values in the second), repeated once per lane of a group of
-// 128 / entry-bytes lanes, so that lanes of a group never share a bank.  For
-// a byte index one v_perm forms the address (byte << 8 | lane offset).
+// Entry e of a table fills row e (256 bytes), repeated once per lane of a
+// group of 256 / entry-bytes lanes.  gfx950's LDS serves a 64-bit read 32
+// lanes at a time (a 128-bit read 16 lanes) over its 64 four-byte banks, so
+// the lanes served together always cover every bank once: no bank conflicts,
+// whatever the codes.  Keys and values of one width share a codebook and so
+// one table; with different widths the value table follows the key table
+// (a byte-indexed table sits at a multiple of 64 KB, a 3-bit table at a
+// multiple of 16 KB, so the index bits and the table base never overlap).
+// For a byte index one v_perm forms the address (byte << 8 | lane offset,
+// table base from the lane offset's bits 16-23).
 template <int B>
 struct Side {
     static constexpr int EB = (B == 2) ? 16 : 8;           // bytes per table entry
     static constexpr int NE = (B == 3) ? 64 : 256;         // table entries
-    static constexpr int COPIES = 128 / EB;                // lane copies per half row
+    static constexpr int COPIES = kLutRow / EB;            // lane copies per row
+    static constexpr int BYTES = NE * kLutRow;
+};
+
+// LDS placement of the key and value tables for widths KB, VB.
+template <int KB, int VB>
+struct Tables {
+    static constexpr bool SHARED = KB == VB;
+    // a byte-indexed table first, at 0; the other one at 64 KB
+    static constexpr int KOFF = SHARED ? 0 : (KB == 3 ? 65536 : 0);
+    static constexpr int VOFF = SHARED ? 0 : (KB == 3 ? 0 : 65536);
+    static constexpr int BYTES = SHARED ? Side<KB>::BYTES
+                                        : 65536 + (KB == 3 ? Side<KB>::BYTES : Side<VB>::BYTES);
 };
 
 template <int B>
-__device__ __forceinline__ void fill_side(char *tab, const CodecConsts &k, int half) {
+__device__ __forceinline__ void fill_table(char *tab, const CodecConsts &k) {
     using S = Side<B>;
-    for (int t = threadIdx.x; t < S::NE * 32; t += kMThreads) {
-        const int e = t >> 5, w = t & 31;                  // entry, dword of the half row
-        const int dw = w % (S::EB / 4);                    // code group within the entry
-        int code;
-        if (B == 4) code = dw == 0 ? (e & 15) : (e >> 4);
-        else if (B == 3) code = dw == 0 ? (e & 7) : (e >> 3);
-        else code = (e >> (2 * dw)) & 3;
-        *reinterpret_cast<uint32_t *>(tab + e * kLutRow + half + 4 * w) = level_pair(k, code);
+    for (int t = threadIdx.x; t < S::NE * (kLutRow / 16); t += kMThreads) {
+        const int e = t / (kLutRow / 16), c = t % (kLutRow / 16);   // entry, 16-byte piece of its row
+        u32x4 v;
+        if constexpr (B == 2) {
+            v = u32x4{level_pair(k, e & 3), level_pair(k, (e >> 2) & 3), level_pair(k, (e >> 4) & 3),
+                      level_pair(k, e >> 6)};
+        } else {
+            constexpr int SH = B == 4 ? 4 : 3;
+            const uint32_t a = level_pair(k, e & ((1 << SH) - 1)), b = level_pair(k, e >> SH);
+            v = u32x4{a, b, a, b};
+        }
+        *reinterpret_cast<u32x4 *>(tab + e * kLutRow + 16 * c) = v;
     }
 }
 
 template <int K>
 __device__ __forceinline__ uint32_t byte_addr(uint32_t word, uint32_t laneoff) {
-    return __builtin_amdgcn_perm(word, laneoff, 0x0C0C0000u | ((4u + K) << 8));
+    return __builtin_amdgcn_perm(word, laneoff, 0x0C020000u | ((4u + K) << 8));
 }
 
 // Pairs of the codes in byte K of `word` (4-bit codes: 2 pairs).
@@ -411,7 +433,8 @@ __global__ __launch_bounds__(kMThreads) void attn_split_kernel(AttnParams p) {
     using SL = Slices<D, KB, VB>;
     constexpr int DG = SL::DG, NJ = SL::NJ, NJJ = SL::NJJ, WPH = SL::WPH;
     constexpr int partial = 2 + D;
-    __shared__ __attribute__((aligned(16))) char tab[256 * kLutRow];
+    using TB = Tables<KB, VB>;
+    __shared__ __attribute__((aligned(256))) char tab[TB::BYTES];
     __shared__ int32_t bt_all[kMWaves][kMaxSplitTokens / kAttnBlockSize];
 
     // The workgroup's waves form p.spw slots of kMWaves / (WPH p.spw) kv
@@ -427,8 +450,8 @@ __global__ __launch_bounds__(kMThreads) void attn_split_kernel(AttnParams p) {
     const int first = blockIdx.x * p.spw;
     if (first * p.split_tokens >= T) return;                 // the whole workgroup is past the context
 
-    fill_side<KB>(tab, p.k, 0);
-    fill_side<VB>(tab, p.v, kLutRow / 2);
+    fill_table<KB>(tab + TB::KOFF, p.k);
+    if constexpr (!TB::SHARED) fill_table<VB>(tab + TB::VOFF, p.v);
     for (int sl = 0; sl < p.spw; ++sl) {                      // block-table entries of every slot
         const int u0 = (first + sl) * p.split_tokens;
         if (u0 >= T) break;
@@ -455,8 +478,8 @@ __global__ __launch_bounds__(kMThreads) void attn_split_kernel(AttnParams p) {
     const int hcol = PAIRED ? (m & 7) : m;                    // head of this lane's column
     const bool lo_col = PAIRED && m >= 8;                     // a column of low halves
     const bool hv = hcol < grp;                               // a real query head column
-    const uint32_t lok = (uint32_t)(lane & (SK::COPIES - 1)) * SK::EB;
-    const uint32_t lov = kLutRow / 2 + (uint32_t)(lane & (SV::COPIES - 1)) * SV::EB;
+    const uint32_t lok = TB::KOFF + (uint32_t)(lane & (SK::COPIES - 1)) * SK::EB;
+    const uint32_t lov = TB::VOFF + (uint32_t)(lane & (SV::COPIES - 1)) * SV::EB;
 
     // ---- rotated query, one head per lane column, dims DG r .. DG r + DG - 1 ----
     u32x4 bq1[NJ], bq2[PAIRED ? 1 : NJ];
@@ -465,9 +488,14 @@ __global__ __launch_bounds__(kMThreads) void attn_split_kernel(AttnParams p) {
         float qv[DG];
         const int mq = hv ? hcol : 0;                         // padding columns read head 0, then drop it
         const uint16_t *qp = p.q + ((size_t)b * p.hq + (size_t)g * grp + mq) * D + DG * r;
+        // all loads first (the address is valid for padding columns too),
+        // then the padding zeroed: one memory latency instead of one per load
+        uint16_t qh[DG];
+#pragma unroll
+        for (int e = 0; e < DG; ++e) qh[e] = qp[e];
 #pragma unroll
         for (int e = 0; e < DG; ++e) {
-            const float v = hv ? half_bits_to_float(qp[e]) : 0.0f;
+            const float v = hv ? half_bits_to_float(qh[e]) : 0.0f;
             qv[e] = sign_of(p.k, DG * r + e) ? -v : v;
         }
 #pragma unroll
