@@ -17,8 +17,9 @@ codec per second (encode and decode both count their 256 B/vector of fp16).
 `roofline` rates the slower of the two kernels by its algorithmic bytes
 (256 B fp16 + 64 B codes + 4 B norm per vector) against the 8 TB/s HBM peak.
 `cpu_baseline` is the plain CPU oracle timed on this host: encode + decode of
-the same whole cache on up to 16 threads (and of layer 0 on one thread,
-reported in `extra`).  `extra` also rates the two kernels against
+the same whole cache on up to 16 threads (and, reported in `extra`: layer 0
+on one thread, layers 0/40/79 of the 70B-class 128K cache at 2 bits, and the
+batch-16 x 32K decode-attention step).  `extra` also rates the two kernels against
 no-arithmetic kernels that move the same byte mix (include/tq_ceiling.h).
 """
 from __future__ import annotations
@@ -84,34 +85,28 @@ def _cpu_model() -> str:
     return "unknown"
 
 
-def oracle_codec_rate(chunks, threads: int, budget_s: float, chunk: int = 4096):
-    """The unmodified oracle (encode + decode, 4 bits, codec seed 0) over the
-    host arrays in `chunks` (each [n, 128] fp16), split into `chunk`-vector
-    pieces taken in order by `threads` host threads, until done or until
-    budget_s has passed.  Returns (vectors done, wall seconds)."""
-    import oracle
-    oracle.build(force=False)
-    o = oracle.default()
-    pieces = [(ci, i) for ci, c in enumerate(chunks) for i in range(0, c.shape[0], chunk)]
+def run_pieces(pieces, work, threads: int, budget_s: float):
+    """work(piece) -> units done, for the pieces in order on `threads` host
+    threads (the oracle's C calls release the interpreter lock), until all
+    are done or budget_s has passed (the first piece runs regardless).
+    Returns (units done, wall seconds)."""
     lock = threading.Lock()
     state = {"next": 0, "done": 0}
-    deadline = [0.0]
+    t0 = time.perf_counter()
+    deadline = t0 + budget_s
 
     def worker():
         while True:
             with lock:
-                if time.perf_counter() > deadline[0] or state["next"] >= len(pieces):
+                # the first piece always runs, so every leg has a measured basis
+                if state["next"] >= len(pieces) or (state["next"] and time.perf_counter() > deadline):
                     return
-                ci, i = pieces[state["next"]]
+                piece = pieces[state["next"]]
                 state["next"] += 1
-            xs = chunks[ci][i:i + chunk]
-            p, n = o.encode(xs, BITS, 0)
-            o.decode(p, n, D, BITS, 0)
+            n = work(piece)
             with lock:
-                state["done"] += xs.shape[0]
+                state["done"] += n
 
-    t0 = time.perf_counter()
-    deadline[0] = t0 + budget_s
     ts = [threading.Thread(target=worker) for _ in range(threads)]
     for t in ts:
         t.start()
@@ -120,11 +115,71 @@ def oracle_codec_rate(chunks, threads: int, budget_s: float, chunk: int = 4096):
     return state["done"], time.perf_counter() - t0
 
 
-def cpu_baseline(layers, budget_s: float = 60.0, single_layer_budget_s: float = 30.0):
-    """The oracle timed on this host: encode + decode of the whole cache
-    (`layers`, a list of [n, 128] fp16 host arrays) on min(16, hardware
-    threads) threads, and of layer 0 on one thread.  A run that hits its
-    budget reports the vectors it finished.  Returns (record, 1-thread GB/s)."""
+def oracle_codec_rate(chunks, threads: int, budget_s: float, chunk: int = 4096,
+                      bits: int = BITS, seeds=None):
+    """The unmodified oracle (encode + decode at `bits`, codec seed seeds[c],
+    default 0) over the host arrays in `chunks` (each [n, 128] fp16), split
+    into `chunk`-vector pieces taken in order by `threads` host threads, until
+    done or until budget_s has passed.  Returns (vectors done, wall seconds)."""
+    import oracle
+    oracle.build(force=False)
+    o = oracle.default()
+    seeds = [0] * len(chunks) if seeds is None else seeds
+    pieces = [(ci, i) for ci, c in enumerate(chunks) for i in range(0, c.shape[0], chunk)]
+
+    def work(piece):
+        ci, i = piece
+        xs = chunks[ci][i:i + chunk]
+        p, n = o.encode(xs, bits, seeds[ci])
+        o.decode(p, n, D, bits, seeds[ci])
+        return xs.shape[0]
+
+    return run_pieces(pieces, work, threads, budget_s)
+
+
+def oracle_attention_time(threads: int, budget_s: float, batch: int = 16, tokens: int = 32768):
+    """The unmodified oracle's paged decode attention at batch `batch` x
+    `tokens` cached tokens, 32 / 8 heads, head_dim 128, 4 bits, random codes,
+    norms in [8, 14) and a random block permutation (the GPU side
+    measurement's inputs), one sequence per piece on `threads` host threads.
+    Returns (sequences done, wall seconds)."""
+    import numpy as np
+    import oracle
+    oracle.build(force=False)
+    o = oracle.default()
+    hq, hkv, bs = 32, 8, 16
+    rng = np.random.default_rng(5)
+    nblk = batch * tokens // bs
+    kp = rng.integers(0, 256, (nblk, bs, hkv, CODE_BYTES), dtype=np.uint8)
+    vp = rng.integers(0, 256, (nblk, bs, hkv, CODE_BYTES), dtype=np.uint8)
+    kn = (rng.random((nblk, bs, hkv), dtype=np.float32) * 6 + 8).astype(np.float32)
+    vn = (rng.random((nblk, bs, hkv), dtype=np.float32) * 6 + 8).astype(np.float32)
+    q = rng.standard_normal((batch, hq, D)).astype(np.float16)
+    bt = rng.permutation(nblk).astype(np.int32).reshape(batch, tokens // bs)
+    cl = np.full(batch, tokens, np.int32)
+
+    def work(b):
+        sel = np.zeros((batch, hq), np.uint8)
+        sel[b] = 1
+        o.attn_decode(q, kp, kn, vp, vn, bt, cl, hkv, BITS, 0, 1.0 / D ** 0.5, sel=sel)
+        return 1
+
+    return run_pieces(list(range(batch)), work, threads, budget_s)
+
+
+def cpu_baseline(layers, budget_s: float = 60.0, single_layer_budget_s: float = 30.0,
+                 c4_layers=(0, 40, 79), c4_budget_s: float = 40.0, c5_budget_s: float = 60.0,
+                 c4_tokens: int = 131072, c5_tokens: int = 32768):
+    """The oracle timed on this host:
+      - encode + decode of the whole cache (`layers`, a list of [n, 128] fp16
+        host arrays) on min(16, hardware threads) threads: the record's value;
+      - the same over layer 0 on one thread;
+      - the 70B-class 128K cache's layers `c4_layers` (2 bits, codec seed =
+        layer) on the same threads;
+      - the batch-16 x 32K decode-attention step, one sequence per thread.
+    A leg that hits its budget reports what it finished (scaled up for the
+    attention step).  Returns (record, extra figures)."""
+    from kv_cache_vector_amd import workloads as W
     hw = os.cpu_count() or 1
     threads = max(1, min(16, hw))
     total = sum(x.shape[0] for x in layers)
@@ -132,13 +187,31 @@ def cpu_baseline(layers, budget_s: float = 60.0, single_layer_budget_s: float = 
     value = 2 * nvec * 2 * D / wall / 1e9
     n1, w1 = oracle_codec_rate(layers[:1], 1, single_layer_budget_s)
     one = 2 * n1 * 2 * D / w1 / 1e9
+    c4 = [W.llama70b_layer(layer, tokens=c4_tokens) for layer in c4_layers]
+    c4_total = sum(x.shape[0] for x in c4)
+    n4, w4 = oracle_codec_rate(c4, threads, c4_budget_s, bits=2, seeds=list(c4_layers))
+    del c4
+    c4_rate = 2 * n4 * 2 * D / w4 / 1e9
+    batch = 16
+    n5, w5 = oracle_attention_time(threads, c5_budget_s, batch=batch, tokens=c5_tokens)
+    c5_ms = w5 / max(n5, 1) * batch * 1e3 if n5 < batch else w5 * 1e3
     what = "the whole cache" if nvec == total else "the first %d of %d vectors" % (nvec, total)
+    what4 = "all %d vectors" % c4_total if n4 == c4_total else "the first %d of %d vectors" % (n4, c4_total)
+    what5 = "all %d sequences" % batch if n5 == batch else "%d of %d sequences, scaled to %d" % (n5, batch, batch)
     rec = {"value": round(value, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
            "sample": "encode+decode (4 bits) of %s (%d vectors) on %d threads in %.1f s; "
-                     "1 thread: %.4f GB/s over %d vectors of layer 0 in %.1f s; %d hardware "
-                     "threads visible, at most 16 used (the host share of one GPU); %s"
-                     % (what, nvec, threads, wall, one, n1, w1, hw, _cpu_model())}
-    return rec, one
+                     "1 thread: %.4f GB/s over %d vectors of layer 0 in %.1f s; "
+                     "70B-class 128K cache, layers %s at 2 bits: %.4f GB/s over %s in %.1f s; "
+                     "decode attention batch %d x %d tokens, 32/8 heads, 4 bits: %.0f ms per step "
+                     "(%s in %.1f s); %d hardware threads visible, at most 16 used (the host "
+                     "share of one GPU); %s"
+                     % (what, nvec, threads, wall, one, n1, w1,
+                        "/".join(str(x) for x in c4_layers), c4_rate, what4, w4,
+                        batch, c5_tokens, c5_ms, what5, w5, hw, _cpu_model())}
+    extra = {"cpu_oracle_1thread_GBps": round(one, 4),
+             "cpu_oracle_70b_layers_b2_GBps": round(c4_rate, 4),
+             "cpu_oracle_attn_batch16_32k_ms": round(c5_ms, 1)}
+    return rec, extra
 
 
 def main() -> int:
@@ -275,9 +348,10 @@ def main() -> int:
         "extra": extra,
     }
     if not args.no_cpu_baseline:
-        log("timing the CPU oracle over the whole cache (16 threads) and layer 0 (1 thread)")
-        res["cpu_baseline"], one = cpu_baseline(host_layers)
-        extra["cpu_oracle_1thread_GBps"] = round(one, 4)
+        log("timing the CPU oracle: the whole cache (16 threads), layer 0 (1 thread), "
+            "70B-class layers 0/40/79, the batch-16 x 32K attention step")
+        res["cpu_baseline"], cpu_extra = cpu_baseline(host_layers)
+        extra.update(cpu_extra)
     print(json.dumps(res), flush=True)
     return 0
 

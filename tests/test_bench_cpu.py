@@ -24,22 +24,57 @@ def test_refuses_more_than_one_gpu():
     assert r.stdout == ""            # no JSON line for a run that did not happen
 
 
+SMALL = dict(c4_tokens=256, c5_tokens=256)     # the 70B layers and the attention step, shrunk
+
+
 def test_cpu_baseline_record():
     rng = np.random.default_rng(0)
     layers = [rng.standard_normal((4096, bench.D)).astype(np.float16) for _ in range(3)]
-    res, one = bench.cpu_baseline(layers, budget_s=20.0, single_layer_budget_s=10.0)
+    res, extra = bench.cpu_baseline(layers, budget_s=20.0, single_layer_budget_s=10.0, **SMALL)
     assert set(res) == {"value", "unit", "cores", "kind", "sample"}
     assert res["kind"] == "oracle" and res["unit"] == "GB/s"
-    assert res["value"] > 0 and 1 <= res["cores"] <= 16 and one > 0
+    assert res["value"] > 0 and 1 <= res["cores"] <= 16
     assert "the whole cache (12288 vectors)" in res["sample"]   # every layer ran
     assert "over 4096 vectors of layer 0" in res["sample"]      # the 1-thread run
+    # 70B-class layers 0/40/79: 2 x 8 heads x 256 tokens each, all of them
+    assert "layers 0/40/79 at 2 bits" in res["sample"] and "all 12288 vectors" in res["sample"]
+    assert "all 16 sequences" in res["sample"]                  # the whole attention step
     assert "hardware threads visible" in res["sample"]
+    assert set(extra) == {"cpu_oracle_1thread_GBps", "cpu_oracle_70b_layers_b2_GBps",
+                          "cpu_oracle_attn_batch16_32k_ms"}
+    assert all(v > 0 for v in extra.values())
 
 
 def test_cpu_baseline_budget_reports_the_subset():
     layers = [np.zeros((8192, bench.D), np.float16)]
-    res, _ = bench.cpu_baseline(layers, budget_s=0.0, single_layer_budget_s=0.0)
+    res, extra = bench.cpu_baseline(layers, budget_s=0.0, single_layer_budget_s=0.0,
+                                    c4_budget_s=0.0, c5_budget_s=0.0, **SMALL)
     assert "the first" in res["sample"] and "of 8192 vectors" in res["sample"]
+    # every leg finishes at least its first piece; the attention leg scales it to the step
+    assert "of 16 sequences, scaled to 16" in res["sample"]
+
+
+def test_oracle_attention_pieces_match_one_call():
+    """The per-sequence pieces of the attention leg compute what one call
+    over the whole batch computes (the leg times real work)."""
+    import oracle
+    o = oracle.default()
+    rng = np.random.default_rng(1)
+    B, hq, hkv, bs, T = 2, 4, 1, 16, 64
+    nblk = B * T // bs
+    kp = rng.integers(0, 256, (nblk, bs, hkv, 64), dtype=np.uint8)
+    vp = rng.integers(0, 256, (nblk, bs, hkv, 64), dtype=np.uint8)
+    kn = rng.random((nblk, bs, hkv), dtype=np.float32) + 1
+    vn = rng.random((nblk, bs, hkv), dtype=np.float32) + 1
+    q = rng.standard_normal((B, hq, bench.D)).astype(np.float16)
+    bt = rng.permutation(nblk).astype(np.int32).reshape(B, T // bs)
+    cl = np.full(B, T, np.int32)
+    whole = o.attn_decode(q, kp, kn, vp, vn, bt, cl, hkv, 4, 0, 0.1)
+    for b in range(B):
+        sel = np.zeros((B, hq), np.uint8)
+        sel[b] = 1
+        part = o.attn_decode(q, kp, kn, vp, vn, bt, cl, hkv, 4, 0, 0.1, sel=sel)
+        assert np.array_equal(part[b].view(np.uint16), whole[b].view(np.uint16))
 
 
 def test_traffic_record_matches_the_sources_or_is_withheld():
