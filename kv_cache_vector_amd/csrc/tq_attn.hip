@@ -426,8 +426,18 @@ __device__ __forceinline__ void load_key(__amdgpu_buffer_rsrc_t rs, uint32_t off
 // Each wave accumulates VH = min(D, 128) value dims; at D = 256 a kv head
 // takes two waves, which both form the full scores and accumulate one half
 // of the value dims each.
-template <int D, int KB, int VB, bool PAIRED>
+//
+// KVW kv heads per wave (KVW = 2: at most 4 query heads per kv head, head_dim
+// up to 128).  The 8 head slots of the paired tile then hold the query heads
+// of two kv heads, g (slots 0-3) and g + 1 (slots 4-7), so no column is
+// padding: each kv head's keys form their own score chain against the
+// shared query operand and a lane keeps the chain of its column's kv head;
+// the value products run once per kv head, with the other kv head's weight
+// rows zero.  Per kv head the matrix products are those of KVW = 1, the
+// softmax arithmetic is halved, and each wave reads whole 128-byte lines.
+template <int D, int KB, int VB, bool PAIRED, int KVW>
 __global__ __launch_bounds__(kMThreads) void attn_split_kernel(AttnParams p) {
+    static_assert(KVW == 1 || (KVW == 2 && PAIRED && D <= 128), "two kv heads per wave: paired, d <= 128");
     using SK = Side<KB>;
     using SV = Side<VB>;
     using SL = Slices<D, KB, VB>;
@@ -437,16 +447,16 @@ __global__ __launch_bounds__(kMThreads) void attn_split_kernel(AttnParams p) {
     __shared__ __attribute__((aligned(256))) char tab[TB::BYTES];
     __shared__ int32_t bt_all[kMWaves][kMaxSplitTokens / kAttnBlockSize];
 
-    // The workgroup's waves form p.spw slots of kMWaves / (WPH p.spw) kv
-    // heads; slot s works on split blockIdx.x * p.spw + s (several splits per
-    // workgroup when the cache has fewer kv heads than waves).
+    // The workgroup's waves form p.spw slots of kMWaves / (WPH p.spw) units of
+    // KVW kv heads; slot s works on split blockIdx.x * p.spw + s (several
+    // splits per workgroup when the cache has fewer kv-head units than waves).
     const int b = blockIdx.y;
     int T = p.context_lens[b];
     T = T < 0 ? 0 : T;
     const int tmax = p.max_blocks * kAttnBlockSize;
     T = T > tmax ? tmax : T;
     if (p.num_blocks <= 0) T = 0;
-    const int hps = kMWaves / WPH / p.spw;                    // kv heads per slot
+    const int hps = kMWaves / WPH / p.spw;                    // kv-head units per slot
     const int first = blockIdx.x * p.spw;
     if (first * p.split_tokens >= T) return;                 // the whole workgroup is past the context
 
@@ -465,7 +475,7 @@ __global__ __launch_bounds__(kMThreads) void attn_split_kernel(AttnParams p) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int unit = wave / WPH, half = wave % WPH;           // kv-head unit, value half
     const int slot = unit / hps;
-    const int g = blockIdx.z * hps + unit % hps;              // kv head
+    const int g = (blockIdx.z * hps + unit % hps) * KVW;      // (first) kv head
     const int split = first + slot;
     const int t0 = split * p.split_tokens;
     if (g >= p.hkv || t0 >= T) return;                        // no barrier follows
@@ -475,9 +485,11 @@ __global__ __launch_bounds__(kMThreads) void attn_split_kernel(AttnParams p) {
     const int lane = threadIdx.x & 63;
     const int m = lane & 15, r = lane >> 4;
     const int grp = p.hq / p.hkv;
-    const int hcol = PAIRED ? (m & 7) : m;                    // head of this lane's column
+    const int hcol = PAIRED ? (m & 7) : m;                    // head slot of this lane's column
     const bool lo_col = PAIRED && m >= 8;                     // a column of low halves
-    const bool hv = hcol < grp;                               // a real query head column
+    const int kvs = KVW == 2 ? (hcol >> 2) : 0;               // the column's kv head: g + kvs
+    const int hh = KVW == 2 ? (hcol & 3) : hcol;              // its query head within the kv head's group
+    const bool hv = hh < grp;                                 // a real query head column
     const uint32_t lok = TB::KOFF + (uint32_t)(lane & (SK::COPIES - 1)) * SK::EB;
     const uint32_t lov = TB::VOFF + (uint32_t)(lane & (SV::COPIES - 1)) * SV::EB;
 
@@ -486,8 +498,8 @@ __global__ __launch_bounds__(kMThreads) void attn_split_kernel(AttnParams p) {
     float qsl;
     {
         float qv[DG];
-        const int mq = hv ? hcol : 0;                         // padding columns read head 0, then drop it
-        const uint16_t *qp = p.q + ((size_t)b * p.hq + (size_t)g * grp + mq) * D + DG * r;
+        const int mq = hv ? hh : 0;                           // padding columns read head 0, then drop it
+        const uint16_t *qp = p.q + ((size_t)b * p.hq + (size_t)(g + kvs) * grp + mq) * D + DG * r;
         // all loads first (the address is valid for padding columns too),
         // then the padding zeroed: one memory latency instead of one per load
         uint16_t qh[DG];
@@ -569,7 +581,7 @@ __global__ __launch_bounds__(kMThreads) void attn_split_kernel(AttnParams p) {
         else if (VB == 2) offv[i] = row + (uint32_t)(NJJ / 4) * m;
         else if (NJJ == 8) offv[i] = row + 4u * (3u * (uint32_t)(m >> 2) + (uint32_t)(q4 < 2 ? q4 : 2));
         else offv[i] = row + 4u * ((12u * (uint32_t)m) >> 5);
-        offn[i] = ((uint32_t)(4 * r + i) * p.hkv + g) * 4u;
+        offn[i] = ((uint32_t)(4 * r + i) * p.hkv + g + kvs) * 4u;   // the column's kv head
     }
     const uint32_t pagek = kAttnBlockSize * rowk;
     const uint32_t pagev = kAttnBlockSize * rowv;
@@ -582,8 +594,8 @@ __global__ __launch_bounds__(kMThreads) void attn_split_kernel(AttnParams p) {
     // is still faster than a one-slot ring.)
     constexpr int R = kMPrefetch + 1;
     constexpr int KW = SL::KW, VW = SL::VW;
-    uint32_t rk[R][KW];
-    uint32_t rv[R][4][VW];
+    uint32_t rk[R][KVW][KW];
+    uint32_t rv[R][KVW][4][VW];
     float rkn[R][4], rvn[R][4];
     bool rok[R];
     // The loads are unconditional (a page past the split re-reads the split's
@@ -598,19 +610,23 @@ __global__ __launch_bounds__(kMThreads) void attn_split_kernel(AttnParams p) {
         const __amdgpu_buffer_rsrc_t rsv = page_rsrc(p.vp + (size_t)blk * pagev, pagev);
         const __amdgpu_buffer_rsrc_t rkn_ = page_rsrc(p.kn + (size_t)blk * kAttnBlockSize * p.hkv, pagen);
         const __amdgpu_buffer_rsrc_t rvn_ = page_rsrc(p.vn + (size_t)blk * kAttnBlockSize * p.hkv, pagen);
-        load_key<SL::KBY, KW>(rsk, offk, rk[slot]);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            if constexpr (VW == 2) {
-                const u32x2 t = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rsv, offv[i], 0, 0));
-                rv[slot][i][0] = t.x;
-                rv[slot][i][VW - 1] = t.y;
-            } else if constexpr (VB == 2 && NJJ == 4) {
-                rv[slot][i][0] = __builtin_amdgcn_raw_buffer_load_b8(rsv, offv[i], 0, 0);
-            } else if constexpr ((VB == 2 && NJJ == 8) || (VB == 4 && NJJ == 4)) {
-                rv[slot][i][0] = __builtin_amdgcn_raw_buffer_load_b16(rsv, offv[i], 0, 0);
-            } else {
-                rv[slot][i][0] = __builtin_amdgcn_raw_buffer_load_b32(rsv, offv[i], 0, 0);
+        for (int kv = 0; kv < KVW; ++kv) {   // kv head g + kv: SL::PK / SL::PV bytes further in the row
+            load_key<SL::KBY, KW>(rsk, offk + kv * SL::PK, rk[slot][kv]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const uint32_t ov = offv[i] + kv * SL::PV;
+                if constexpr (VW == 2) {
+                    const u32x2 t = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rsv, ov, 0, 0));
+                    rv[slot][kv][i][0] = t.x;
+                    rv[slot][kv][i][VW - 1] = t.y;
+                } else if constexpr (VB == 2 && NJJ == 4) {
+                    rv[slot][kv][i][0] = __builtin_amdgcn_raw_buffer_load_b8(rsv, ov, 0, 0);
+                } else if constexpr ((VB == 2 && NJJ == 8) || (VB == 4 && NJJ == 4)) {
+                    rv[slot][kv][i][0] = __builtin_amdgcn_raw_buffer_load_b16(rsv, ov, 0, 0);
+                } else {
+                    rv[slot][kv][i][0] = __builtin_amdgcn_raw_buffer_load_b32(rsv, ov, 0, 0);
+                }
             }
         }
 #pragma unroll
@@ -627,20 +643,32 @@ __global__ __launch_bounds__(kMThreads) void attn_split_kernel(AttnParams p) {
 
     // one page: score tiles, value operands, softmax, value tiles, refill
     auto step = [&](const int pg, const int d) {
-        // the lane's key slice, from bit 0 (3 bits at D = 64: shifted into place)
-        uint32_t kc[KW];
-        if constexpr (SL::KBY % 4) {
-            kc[0] = __builtin_amdgcn_alignbit(rk[d][1], rk[d][0], ksh);
-            kc[KW - 1] = rk[d][1] >> ksh;
-        } else {
+        // the lane's key slice of kv head g + kv, from bit 0 (3 bits at D = 64:
+        // shifted into place)
+        auto key_slice = [&](int kv, uint32_t (&kc)[KW]) {
+            if constexpr (SL::KBY % 4) {
+                kc[0] = __builtin_amdgcn_alignbit(rk[d][kv][1], rk[d][kv][0], ksh);
+                kc[KW - 1] = rk[d][kv][1] >> ksh;
+            } else {
 #pragma unroll
-            for (int w = 0; w < KW; ++w) kc[w] = rk[d][w];
-        }
+                for (int w = 0; w < KW; ++w) kc[w] = rk[d][kv][w];
+            }
+        };
+        uint32_t kc[KW];
+        key_slice(0, kc);
         // scores of tokens 4r .. 4r+3 for head hcol
         f4 S;
         if constexpr (PAIRED) {
             f4 S0 = f4{0.0f, 0.0f, 0.0f, 0.0f};
             score_chunks_paired<0, NJ, KB>(tab, kc, lok, bq1, S0);
+            if constexpr (KVW == 2) {   // kv head g + 1's chain; each column keeps its own kv head's
+                uint32_t kc1[KW];
+                key_slice(1, kc1);
+                f4 S1 = f4{0.0f, 0.0f, 0.0f, 0.0f};
+                score_chunks_paired<0, NJ, KB>(tab, kc1, lok, bq1, S1);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) S0[i] = kvs ? S1[i] : S0[i];
+            }
             // column m + (q_lo column m ^ 8): row_ror:8 pairs lanes m and m ^ 8
             // of each 16-lane row, so both columns end with the full score
 #pragma unroll
@@ -650,9 +678,9 @@ __global__ __launch_bounds__(kMThreads) void attn_split_kernel(AttnParams p) {
             score_chunks<0, NJ, KB>(tab, kc, lok, bq1, bq2, S0, S1);
             S = S0 + S1;
         }
-        // value codes of the page
+        // value codes of the page (KVW = 2: kv head g's; g + 1's follow below)
         u32x4 Bv[NJJ];
-        value_operands<NJJ, VB, VW>(tab, rv[d], lov, q4, vsh, Bv);
+        value_operands<NJJ, VB, VW>(tab, rv[d][0], lov, q4, vsh, Bv);
 
         // online softmax in base 2.  Two lazily raised references: M per head
         // (rescale when a score passes M + 8) and a power of two vlim per wave
@@ -725,7 +753,18 @@ __global__ __launch_bounds__(kMThreads) void attn_split_kernel(AttnParams p) {
             w2[i] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(w - hf));
         }
         // values: dims NJJ m + jj of the wave's half, tokens 4r .. 4r+3
-        if constexpr (PAIRED) {
+        if constexpr (PAIRED && KVW == 2) {
+            // rows 0-7: (w_hi, w_hi) of head slots 0-7; rows 8-15: (w_lo, 0);
+            // the rows of the other kv head are zero in each product
+            const u32x4 A = lo_col ? u32x4{w2[0], w2[1], w2[2], w2[3]} : u32x4{w1[0], w1[1], w1[2], w1[3]};
+            const u32x4 z = u32x4{0u, 0u, 0u, 0u};
+            const u32x4 A0 = kvs ? z : A, A1 = kvs ? A : z;
+#pragma unroll
+            for (int jj = 0; jj < NJJ; ++jj) acc[jj] = mfma(A0, Bv[jj], acc[jj]);
+            value_operands<NJJ, VB, VW>(tab, rv[d][1], lov, q4, vsh, Bv);
+#pragma unroll
+            for (int jj = 0; jj < NJJ; ++jj) acc[jj] = mfma(A1, Bv[jj], acc[jj]);
+        } else if constexpr (PAIRED) {
             // rows 0-7: (w_hi, w_hi) of heads 0-7; rows 8-15: (w_lo, 0)
             const u32x4 A = lo_col ? u32x4{w2[0], w2[1], w2[2], w2[3]} : u32x4{w1[0], w1[1], w1[2], w1[3]};
 #pragma unroll
@@ -764,21 +803,27 @@ __global__ __launch_bounds__(kMThreads) void attn_split_kernel(AttnParams p) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) acc[jj][i] += __shfl_xor(acc[jj][i], 32);
     }
-    // partial state of head g*grp + h: m and l from lane h, accumulators from
-    // lanes (column c, row h / 4) at register h % 4 -> dims NJJ c .. NJJ c + NJJ - 1
-    // of the wave's value half
+    // partial state of head g*grp + h: m and l from the lane of h's column,
+    // accumulators from lanes (column c, row s / 4) at register s % 4 (s: the
+    // head slot of h) -> dims NJJ c .. NJJ c + NJJ - 1 of the wave's value
+    // half.  KVW = 2: slot s holds head (s / 4) grp + s % 4.
     const float unscale = vlim / (kLevelScale * 64.0f);     // undo 16 c and 2^6 / vlim
     float *base = p.ws + (((size_t)b * p.hq + (size_t)g * grp) * p.num_splits + split) * partial;
     const size_t hstride = (size_t)p.num_splits * partial;
     if (r == 0 && hv && !lo_col && half == 0) {
-        float *dst = base + (size_t)m * hstride;
+        float *dst = base + (size_t)(KVW == 2 ? kvs * grp + hh : m) * hstride;
         dst[0] = M;
         dst[1] = lsum;
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const int h = 4 * r + i;
-        if (h >= grp || (PAIRED && r >= 2)) break;
+        int h = 4 * r + i;
+        if constexpr (KVW == 2) {
+            if (r >= 2 || i >= grp) break;
+            h = r * grp + i;
+        } else {
+            if (h >= grp || (PAIRED && r >= 2)) break;
+        }
         float2 *dst = reinterpret_cast<float2 *>(base + (size_t)h * hstride + 2 + SL::VH * half + NJJ * m);   // 8-byte aligned
 #pragma unroll
         for (int jj = 0; jj < NJJ; jj += 2) dst[jj >> 1] = float2(acc[jj][i] * unscale, acc[jj + 1][i] * unscale);
@@ -905,12 +950,13 @@ bool bits_ok(int b) { return b == 2 || b == 3 || b == 4; }
 // The split kernel for (D, KB, VB); head_dim 256 has the paired form only
 // (attn_supported keeps its group size at 8 or below).
 template <int D, int KB, int VB>
-void launch_split(bool paired, dim3 grid, dim3 block, hipStream_t stream, const AttnParams &p) {
+void launch_split(bool paired, int kvw, dim3 grid, dim3 block, hipStream_t stream, const AttnParams &p) {
     if constexpr (D <= 128) {
-        if (paired) hipLaunchKernelGGL((attn_split_kernel<D, KB, VB, true>), grid, block, 0, stream, p);
-        else hipLaunchKernelGGL((attn_split_kernel<D, KB, VB, false>), grid, block, 0, stream, p);
+        if (kvw == 2) hipLaunchKernelGGL((attn_split_kernel<D, KB, VB, true, 2>), grid, block, 0, stream, p);
+        else if (paired) hipLaunchKernelGGL((attn_split_kernel<D, KB, VB, true, 1>), grid, block, 0, stream, p);
+        else hipLaunchKernelGGL((attn_split_kernel<D, KB, VB, false, 1>), grid, block, 0, stream, p);
     } else {
-        hipLaunchKernelGGL((attn_split_kernel<D, KB, VB, true>), grid, block, 0, stream, p);
+        hipLaunchKernelGGL((attn_split_kernel<D, KB, VB, true, 1>), grid, block, 0, stream, p);
     }
 }
 
@@ -954,11 +1000,18 @@ bool attn_supported(const AttnShape &s) {
     return grp >= 1 && grp <= gmax && bits_ok(s.k_bits) && bits_ok(s.v_bits);
 }
 
+// kv heads per wave of the split kernel: two where at most 4 query heads
+// share a kv head (head_dim up to 128, an even number of kv heads), else one
+int attn_kv_per_wave(const AttnShape &s) {
+    const int grp = s.num_q_heads / s.num_kv_heads;
+    return (s.head_dim <= 128 && grp <= 4 && s.num_kv_heads % 2 == 0) ? 2 : 1;
+}
+
 int attn_split_tokens(const AttnShape &s) {
-    // waves_per_head waves per (sequence, kv head) and split; about
-    // kMTargetWaves waves
+    // waves_per_head waves per (sequence, unit of attn_kv_per_wave kv heads)
+    // and split; about kMTargetWaves waves
     const int ctx = s.max_blocks * kAttnBlockSize;
-    const int units = s.batch * s.num_kv_heads * waves_per_head(s.head_dim);
+    const int units = s.batch * s.num_kv_heads / attn_kv_per_wave(s) * waves_per_head(s.head_dim);
     const int per_seq = units > 0 ? (kMTargetWaves + units - 1) / units : 1;
     int st = (ctx + per_seq - 1) / per_seq;
     st = (st + kAttnBlockSize - 1) / kAttnBlockSize * kAttnBlockSize;
@@ -1004,24 +1057,27 @@ hipError_t launch_attn(const AttnShape &s, const CodecConsts &kc, const CodecCon
     p.qscale = scale * 1.4426950408889634f / s.head_dim;
     p.k = kc;
     p.v = vc;
-    // fewer kv heads than kv-head units: the spare waves take further splits
-    const int hpw = kMWaves / waves_per_head(s.head_dim);     // kv heads per workgroup
-    p.spw = (s.num_kv_heads < hpw && hpw % s.num_kv_heads == 0) ? hpw / s.num_kv_heads : 1;
-    const int hps = hpw / p.spw;
-    const dim3 grid((p.num_splits + p.spw - 1) / p.spw, s.batch, (s.num_kv_heads + hps - 1) / hps);
+    // units of kvw kv heads; fewer units per split than a workgroup's: the
+    // spare waves take further splits
+    const int kvw = attn_kv_per_wave(s);
+    const int units = s.num_kv_heads / kvw;                   // per split
+    const int upw = kMWaves / waves_per_head(s.head_dim);     // units per workgroup
+    p.spw = (units < upw && upw % units == 0) ? upw / units : 1;
+    const int ups = upw / p.spw;
+    const dim3 grid((p.num_splits + p.spw - 1) / p.spw, s.batch, (units + ups - 1) / ups);
     const dim3 block(kMThreads);
     const bool paired = s.num_q_heads / s.num_kv_heads <= 8;
 #define TQ_WIDTHS(D)                                                                                 \
     switch (s.k_bits * 10 + s.v_bits) {                                                              \
-        case 44: launch_split<D, 4, 4>(paired, grid, block, stream, p); break;                       \
-        case 43: launch_split<D, 4, 3>(paired, grid, block, stream, p); break;                       \
-        case 42: launch_split<D, 4, 2>(paired, grid, block, stream, p); break;                       \
-        case 34: launch_split<D, 3, 4>(paired, grid, block, stream, p); break;                       \
-        case 33: launch_split<D, 3, 3>(paired, grid, block, stream, p); break;                       \
-        case 32: launch_split<D, 3, 2>(paired, grid, block, stream, p); break;                       \
-        case 24: launch_split<D, 2, 4>(paired, grid, block, stream, p); break;                       \
-        case 23: launch_split<D, 2, 3>(paired, grid, block, stream, p); break;                       \
-        case 22: launch_split<D, 2, 2>(paired, grid, block, stream, p); break;                       \
+        case 44: launch_split<D, 4, 4>(paired, kvw, grid, block, stream, p); break;                       \
+        case 43: launch_split<D, 4, 3>(paired, kvw, grid, block, stream, p); break;                       \
+        case 42: launch_split<D, 4, 2>(paired, kvw, grid, block, stream, p); break;                       \
+        case 34: launch_split<D, 3, 4>(paired, kvw, grid, block, stream, p); break;                       \
+        case 33: launch_split<D, 3, 3>(paired, kvw, grid, block, stream, p); break;                       \
+        case 32: launch_split<D, 3, 2>(paired, kvw, grid, block, stream, p); break;                       \
+        case 24: launch_split<D, 2, 4>(paired, kvw, grid, block, stream, p); break;                       \
+        case 23: launch_split<D, 2, 3>(paired, kvw, grid, block, stream, p); break;                       \
+        case 22: launch_split<D, 2, 2>(paired, kvw, grid, block, stream, p); break;                       \
         default: return hipErrorInvalidValue;                                                        \
     }
     switch (s.head_dim) {
