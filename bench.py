@@ -331,6 +331,7 @@ def main() -> int:
     if not args.no_extras:
         del out
         extra.update(side_measurements(torch, dev, stream, x, packed, norms))
+        extra.update(ceiling_fractions(extra))
 
     res = {
         "metric": "fp16-KV GB/s encoded/decoded (+% of HBM peak), 4-bit d=128, 1 MI355X",
@@ -358,9 +359,12 @@ def main() -> int:
 
 def side_measurements(torch, dev, stream, x, packed, norms):
     """Decode attention at batch 16, 32/8 heads, 32768 tokens (4 bits, random
-    codes), the 70B-class 128K-context cache encoded as a layer-by-layer
-    stream (2 bits), and other codec launch shapes."""
+    codes; head_dim 128, 64 and 256), the 70B-class 128K-context cache
+    encoded as a layer-by-layer stream (2 bits), and other codec launch
+    shapes."""
     res = attention_measurement(torch, dev, stream)
+    for hd in (64, 256):
+        res.update(attention_measurement(torch, dev, stream, head_dim=hd))
     res.update(stream_encode_measurement(torch, dev, stream, x, packed, norms))
     res.update(codec_side_measurement(torch, dev, stream, x, packed, norms))
     res.update(hybrid_measurement(torch, dev, stream, x))
@@ -585,8 +589,9 @@ def stream_encode_measurement(torch, dev, stream, x, packed, norms):
 
 def ceiling_measurement(torch, stream, x, packed, norms, out, enc_ms, dec_ms):
     """The codec's byte mix moved by the no-arithmetic kernels of
-    tq_ceiling.h over the whole 4 GiB cache (4 bits; median of 10 launches
-    each), and the encode and decode kernels' time against them."""
+    tq_ceiling.h over the whole 4 GiB cache (4, 3 and 2 bits; median of 10
+    launches each), and the 4-bit encode and decode kernels' time against
+    them (the 3- and 2-bit kernels are rated in ceiling_fractions)."""
     import ctypes
     from kv_cache_vector_amd import _lib
     L = _lib.load()
@@ -594,10 +599,14 @@ def ceiling_measurement(torch, stream, x, packed, norms, out, enc_ms, dec_ms):
     f.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
                   ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
     s = stream.cuda_stream
-    calls = {"encode": lambda: f(0, CODE_BYTES, x.data_ptr(), None, N, packed.data_ptr(),
-                                 norms.data_ptr(), s),
-             "decode": lambda: f(1, CODE_BYTES, packed.data_ptr(), norms.data_ptr(), N,
-                                 out.data_ptr(), None, s)}
+    calls = {}
+    for bits in (4, 3, 2):
+        pb = D * bits // 8
+        sfx = "" if bits == BITS else "_b%d" % bits
+        calls["encode" + sfx] = lambda pb=pb: f(0, pb, x.data_ptr(), None, N, packed.data_ptr(),
+                                                norms.data_ptr(), s)
+        calls["decode" + sfx] = lambda pb=pb: f(1, pb, packed.data_ptr(), norms.data_ptr(), N,
+                                                out.data_ptr(), None, s)
     res = {}
     for name, fn in calls.items():
         assert fn() == 0, "tq_ceiling_stream"
@@ -610,10 +619,23 @@ def ceiling_measurement(torch, stream, x, packed, norms, out, enc_ms, dec_ms):
             torch.cuda.synchronize()
             ts.append(e0.elapsed_time(e1))
         ms = statistics.median(ts)
+        bits = int(name[-1]) if "_b" in name else BITS
         res["ceiling_%s_mix_ms" % name] = round(ms, 4)
-        res["ceiling_%s_mix_GBps" % name] = round(N * ALGO_BYTES / (ms * 1e-3) / 1e9, 1)
+        res["ceiling_%s_mix_GBps" % name] = round(N * (2 * D + D * bits // 8 + 4) / (ms * 1e-3) / 1e9, 1)
     res["encode_frac_of_ceiling"] = round(res["ceiling_encode_mix_ms"] / enc_ms, 4)
     res["decode_frac_of_ceiling"] = round(res["ceiling_decode_mix_ms"] / dec_ms, 4)
+    return res
+
+
+def ceiling_fractions(extra):
+    """The 3- and 2-bit codec kernels' times (side measurements) against
+    their byte mixes' no-arithmetic times."""
+    res = {}
+    for bits in (3, 2):
+        for name in ("encode", "decode"):
+            c, k = extra.get("ceiling_%s_b%d_mix_ms" % (name, bits)), extra.get("%s_b%d_ms" % (name, bits))
+            if c and k:
+                res["%s_b%d_frac_of_ceiling" % (name, bits)] = round(c / k, 4)
     return res
 
 
