@@ -861,8 +861,10 @@ __global__ __launch_bounds__(64) void attn_combine_kernel(AttnParams p) {
         const float other = __shfl_xor(mx, o);
         mx = other > mx ? other : mx;
     }
-    // split weights, then this lane's coordinates; the partials of 8 splits
-    // are loaded before any of them is accumulated
+    // split weights, then this lane's coordinates; the partials of G splits
+    // are loaded before any of them is accumulated (G = 32 at head_dim up to
+    // 128: a 32-split merge takes one round of loads)
+    constexpr int G = E <= 2 ? 32 : 16;
     float lsum = 0.0f;
     float a[E];
 #pragma unroll
@@ -876,10 +878,10 @@ __global__ __launch_bounds__(64) void attn_combine_kernel(AttnParams p) {
             lsum += w * ls;
         }
         const int cnt = (ns - s0 < 64) ? ns - s0 : 64;
-        for (int j0 = 0; j0 < cnt; j0 += 8) {
-            float ev[8][E];
+        for (int j0 = 0; j0 < cnt; j0 += G) {
+            float ev[G][E];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
+            for (int u = 0; u < G; ++u) {
                 const int j = (j0 + u < cnt) ? j0 + u : j0;          // in range; weight 0 below
                 const float *q = src + (size_t)(s0 + j) * partial + 2 + E * lane;
                 if constexpr (E == 1) {
@@ -895,7 +897,7 @@ __global__ __launch_bounds__(64) void attn_combine_kernel(AttnParams p) {
                 }
             }
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
+            for (int u = 0; u < G; ++u) {
                 float wj = __builtin_bit_cast(
                     float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), (j0 + u) & 63));
                 wj = (j0 + u < cnt) ? wj : 0.0f;
