@@ -169,13 +169,18 @@ def oracle_attention_time(threads: int, budget_s: float, batch: int = 16, tokens
 
 def cpu_baseline(layers, budget_s: float = 60.0, single_layer_budget_s: float = 30.0,
                  c4_layers=(0, 40, 79), c4_budget_s: float = 40.0, c5_budget_s: float = 60.0,
-                 c4_tokens: int = 131072, c5_tokens: int = 32768):
+                 c4_tokens: int = 131072, c5_tokens: int = 32768, c3_tokens: int = 8192,
+                 c3_budget_s: float = 20.0, c4_sample: float = 0.01):
     """The oracle timed on this host:
       - encode + decode of the whole cache (`layers`, a list of [n, 128] fp16
         host arrays) on min(16, hardware threads) threads: the record's value;
       - the same over layer 0 on one thread;
-      - the 70B-class 128K cache's layers `c4_layers` (2 bits, codec seed =
-        layer) on the same threads;
+      - the 4,096-vector outlier workload (1 thread);
+      - the heavy-tailed (Student-t) layer 0 of the same cache at 3 and at 2
+        bits (the layer-0 subset of that workload);
+      - the 70B-class 128K cache's layers `c4_layers` in full and a seeded
+        `c4_sample` of every other layer's tokens (2 bits, codec seed =
+        layer);
       - the batch-16 x 32K decode-attention step, one sequence per thread.
     A leg that hits its budget reports what it finished (scaled up for the
     attention step).  Returns (record, extra figures)."""
@@ -187,31 +192,69 @@ def cpu_baseline(layers, budget_s: float = 60.0, single_layer_budget_s: float = 
     value = 2 * nvec * 2 * D / wall / 1e9
     n1, w1 = oracle_codec_rate(layers[:1], 1, single_layer_budget_s)
     one = 2 * n1 * 2 * D / w1 / 1e9
+    c1 = W.outlier_channels_fixed()
+    n1c, w1c = oracle_codec_rate([c1], 1, 60.0)
+    c3 = W.llama8b_layer(0, dist="student_t", tokens=c3_tokens)
+    c3_rates = {}
+    for bits in (3, 2):
+        n3, w3 = oracle_codec_rate([c3], threads, c3_budget_s, bits=bits)
+        c3_rates[bits] = (2 * n3 * 2 * D / w3 / 1e9, n3)
+    del c3
     c4 = [W.llama70b_layer(layer, tokens=c4_tokens) for layer in c4_layers]
+    c4_seeds = list(c4_layers)
+    c4_full = sum(x.shape[0] for x in c4)
+    others = [layer for layer in range(80) if layer not in c4_layers] if c4_sample > 0 else []
+    c4 += [W.llama70b_layer_sample(layer, c4_sample, tokens=c4_tokens) for layer in others]
+    c4_seeds += others
     c4_total = sum(x.shape[0] for x in c4)
-    n4, w4 = oracle_codec_rate(c4, threads, c4_budget_s, bits=2, seeds=list(c4_layers))
+    n4, w4 = oracle_codec_rate(c4, threads, c4_budget_s, bits=2, seeds=c4_seeds)
     del c4
     c4_rate = 2 * n4 * 2 * D / w4 / 1e9
     batch = 16
     n5, w5 = oracle_attention_time(threads, c5_budget_s, batch=batch, tokens=c5_tokens)
     c5_ms = w5 / max(n5, 1) * batch * 1e3 if n5 < batch else w5 * 1e3
     what = "the whole cache" if nvec == total else "the first %d of %d vectors" % (nvec, total)
-    what4 = "all %d vectors" % c4_total if n4 == c4_total else "the first %d of %d vectors" % (n4, c4_total)
+    what4 = ("all %d vectors (%d in the full layers, %d in the %d samples)" % (c4_total, c4_full, c4_total - c4_full, len(others))
+             if n4 == c4_total else "the first %d of %d vectors" % (n4, c4_total))
     what5 = "all %d sequences" % batch if n5 == batch else "%d of %d sequences, scaled to %d" % (n5, batch, batch)
     rec = {"value": round(value, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
            "sample": "encode+decode (4 bits) of %s (%d vectors) on %d threads in %.1f s; "
                      "1 thread: %.4f GB/s over %d vectors of layer 0 in %.1f s; "
-                     "70B-class 128K cache, layers %s at 2 bits: %.4f GB/s over %s in %.1f s; "
+                     "the 4,096-vector outlier workload on 1 thread in %.1f ms; "
+                     "Student-t layer 0 (%d vectors) at 3 / 2 bits: %.4f / %.4f GB/s; "
+                     "70B-class 128K cache, layers %s in full plus a %g sample of the others, "
+                     "at 2 bits: %.4f GB/s over %s in %.1f s; "
                      "decode attention batch %d x %d tokens, 32/8 heads, 4 bits: %.0f ms per step "
                      "(%s in %.1f s); %d hardware threads visible, at most 16 used (the host "
                      "share of one GPU); %s"
-                     % (what, nvec, threads, wall, one, n1, w1,
-                        "/".join(str(x) for x in c4_layers), c4_rate, what4, w4,
+                     % (what, nvec, threads, wall, one, n1, w1, w1c * 1e3,
+                        c3_rates[3][1], c3_rates[3][0], c3_rates[2][0],
+                        "/".join(str(x) for x in c4_layers), c4_sample, c4_rate, what4, w4,
                         batch, c5_tokens, c5_ms, what5, w5, hw, _cpu_model())}
     extra = {"cpu_oracle_1thread_GBps": round(one, 4),
+             "cpu_oracle_outlier_4096_ms": round(w1c * 1e3, 1),
+             "cpu_oracle_student_t_b3_GBps": round(c3_rates[3][0], 4),
+             "cpu_oracle_student_t_b2_GBps": round(c3_rates[2][0], 4),
              "cpu_oracle_70b_layers_b2_GBps": round(c4_rate, 4),
              "cpu_oracle_attn_batch16_32k_ms": round(c5_ms, 1)}
     return rec, extra
+
+
+def gpu_clocks():
+    """The current sclk / mclk levels as rocm-smi reports them (None when it
+    is not available)."""
+    import re
+    import subprocess
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True, timeout=20)
+    except (OSError, subprocess.SubprocessError):
+        return None
+    found = {}
+    for line in r.stdout.splitlines():
+        m = re.search(r"\b(sclk|mclk|fclk)\b.*\((\d+)\s*Mhz\)", line, re.I)
+        if m and m.group(1).lower() not in found:
+            found[m.group(1).lower()] = int(m.group(2))
+    return found or None
 
 
 def main() -> int:
@@ -303,6 +346,7 @@ def main() -> int:
     ms_step = total_ms / K
     value = 2 * N * 2 * D / (ms_step * 1e-3) / 1e9
 
+    clocks = gpu_clocks()
     enc_avg, dec_avg = statistics.mean(enc_ms), statistics.mean(dec_ms)
     kern, t_ms = ("encode_kernel<4>", enc_avg) if enc_avg >= dec_avg else ("decode_kernel<4>", dec_avg)
     achieved = N * ALGO_BYTES / (t_ms * 1e-3) / 1e9
@@ -321,6 +365,8 @@ def main() -> int:
         "decode_hbm_frac": round(N * ALGO_BYTES / (dec_avg * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
         "host_wall_s": round(wall, 3),
     }
+    if clocks:
+        extra["clocks_MHz_after_timed_steps"] = clocks
     # achievable-bandwidth reference: the no-arithmetic kernels that move the
     # codec's own byte mix with its work mapping (include/tq_ceiling.h)
     extra.update(ceiling_measurement(torch, stream, x, packed, norms, out, enc_avg, dec_avg))
@@ -486,8 +532,8 @@ def codec_side_measurement(torch, dev, stream, x, packed, norms):
     return res
 
 
-def attention_measurement(torch, dev, stream, reps: int = 10, head_dim: int = 128):
-    """Median time of tq_attn_decode (split + combine kernels) at batch 16,
+def attention_measurement(torch, dev, stream, reps: int = 20, head_dim: int = 128):
+    """Median (and minimum) time of tq_attn_decode (split + combine kernels) at batch 16,
     32/8 heads, 32768 tokens, 4 bits, random codes and a random block
     permutation, with the last-level cache evicted before each call.  The
     keys are named attn_batch16_32k_* at head_dim 128 and carry a _d<D>
@@ -534,6 +580,7 @@ def attention_measurement(torch, dev, stream, reps: int = 10, head_dim: int = 12
         torch.cuda.synchronize()
         times.append(e0.elapsed_time(e1))
     t_us = statistics.median(times) * 1e3
+    res["attn_batch16_32k_min_us" + ("" if head_dim == 128 else "_d%d" % head_dim)] = round(min(times) * 1e3, 1)
     packed_bytes = B * Hkv * T * 2 * (P + 4)
     sfx = "" if d == 128 else "_d%d" % d
     res["attn_batch16_32k_us" + sfx] = round(t_us, 1)

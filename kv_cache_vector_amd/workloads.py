@@ -91,6 +91,19 @@ def llama70b_layer(layer: int, tokens: int = 131072, heads: int = 8) -> np.ndarr
     return _f16(x.reshape(-1, HEAD_DIM))
 
 
+def llama70b_layer_sample(layer: int, frac: float = 0.01, tokens: int = 131072,
+                          heads: int = 8) -> np.ndarray:
+    """A seeded sample of one 70B-class layer: round(frac * tokens) tokens
+    per (K/V, head), N(0,1) times the layer's per-(K/V, head) scales, drawn
+    from the stream (300 + layer, 1) -- the layer's distribution, not its
+    exact rows.  Returns [2*heads*round(frac*tokens), 128]."""
+    n = int(round(frac * tokens))
+    scale = llama70b_head_scales(layer, heads)[:, :, None, None]
+    rng = np.random.default_rng([300 + layer, 1])
+    x = rng.standard_normal((2, heads, n, HEAD_DIM), dtype=np.float32) * scale
+    return _f16(x.reshape(-1, HEAD_DIM))
+
+
 # ---------------------------------------------------------------------------
 # decode-attention workload: batch 16, 32 query heads / 8 KV heads,
 # 32768 cached tokens per sequence in 16-token pages

@@ -24,7 +24,7 @@ def test_refuses_more_than_one_gpu():
     assert r.stdout == ""            # no JSON line for a run that did not happen
 
 
-SMALL = dict(c4_tokens=256, c5_tokens=256)     # the 70B layers and the attention step, shrunk
+SMALL = dict(c4_tokens=256, c5_tokens=256, c3_tokens=64)   # the 70B layers, attention step, Student-t layer, shrunk
 
 
 def test_cpu_baseline_record():
@@ -36,22 +36,43 @@ def test_cpu_baseline_record():
     assert res["value"] > 0 and 1 <= res["cores"] <= 16
     assert "the whole cache (12288 vectors)" in res["sample"]   # every layer ran
     assert "over 4096 vectors of layer 0" in res["sample"]      # the 1-thread run
-    # 70B-class layers 0/40/79: 2 x 8 heads x 256 tokens each, all of them
-    assert "layers 0/40/79 at 2 bits" in res["sample"] and "all 12288 vectors" in res["sample"]
+    # 70B-class layers 0/40/79 (2 x 8 heads x 256 tokens each) in full, and
+    # 1% of the others' tokens (3 per K/V and head: 48 vectors each)
+    assert "layers 0/40/79 in full plus a 0.01 sample of the others" in res["sample"]
+    assert "all 15984 vectors (12288 in the full layers, 3696 in the 77 samples)" in res["sample"]
+    assert "Student-t layer 0 (4096 vectors) at 3 / 2 bits" in res["sample"]
+    assert "the 4,096-vector outlier workload on 1 thread" in res["sample"]
     assert "all 16 sequences" in res["sample"]                  # the whole attention step
     assert "hardware threads visible" in res["sample"]
     assert set(extra) == {"cpu_oracle_1thread_GBps", "cpu_oracle_70b_layers_b2_GBps",
-                          "cpu_oracle_attn_batch16_32k_ms"}
+                          "cpu_oracle_attn_batch16_32k_ms", "cpu_oracle_outlier_4096_ms",
+                          "cpu_oracle_student_t_b3_GBps", "cpu_oracle_student_t_b2_GBps"}
     assert all(v > 0 for v in extra.values())
 
 
 def test_cpu_baseline_budget_reports_the_subset():
     layers = [np.zeros((8192, bench.D), np.float16)]
     res, extra = bench.cpu_baseline(layers, budget_s=0.0, single_layer_budget_s=0.0,
-                                    c4_budget_s=0.0, c5_budget_s=0.0, **SMALL)
+                                    c4_budget_s=0.0, c5_budget_s=0.0, c3_budget_s=0.0, **SMALL)
     assert "the first" in res["sample"] and "of 8192 vectors" in res["sample"]
     # every leg finishes at least its first piece; the attention leg scales it to the step
     assert "of 16 sequences, scaled to 16" in res["sample"]
+
+
+def test_70b_layer_sample_has_the_layer_scales():
+    """The 1% sample of a 70B-class layer: 2 x 8 heads x round(0.01 T) rows,
+    each (K/V, head) block scaled by that layer's factor."""
+    from kv_cache_vector_amd import workloads as W
+    x = W.llama70b_layer_sample(7, 0.01, tokens=131072).astype(np.float64)
+    n = round(0.01 * 131072)
+    assert x.shape == (2 * 8 * n, bench.D)
+    sd = x.reshape(2, 8, n * bench.D).std(axis=2)
+    np.testing.assert_allclose(sd, W.llama70b_head_scales(7), rtol=0.02)
+
+
+def test_gpu_clocks_never_raises():
+    r = bench.gpu_clocks()
+    assert r is None or all(isinstance(v, int) for v in r.values())
 
 
 def test_oracle_attention_pieces_match_one_call():
