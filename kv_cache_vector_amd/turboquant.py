@@ -32,6 +32,22 @@ def _require_gpu(t: torch.Tensor, name: str) -> None:
         raise ValueError("%s must be a GPU tensor (libtq has no host implementation)" % name)
 
 
+def verify_slots(slots: torch.Tensor, num_slots: int) -> None:
+    """Raise ValueError unless the non-negative entries of `slots` are
+    distinct and below num_slots (negative entries mark skipped vectors):
+    the paged write's contract, which its kernel does not check (an
+    out-of-range slot is skipped, duplicates race)."""
+    s = slots.reshape(-1)
+    s = s[s >= 0]
+    if s.numel() == 0:
+        return
+    top = int(s.max())
+    if top >= num_slots:
+        raise ValueError("slot %d is past the cache's %d rows" % (top, num_slots))
+    if torch.unique(s).numel() != s.numel():
+        raise ValueError("slots must be distinct (duplicate rows would race)")
+
+
 class TurboQuant:
     """TurboQuant codec: [..., head_dim] fp16 <-> ([..., head_dim*bits/8] uint8, [...] f32),
     head_dim 64, 128 or 256."""
@@ -75,10 +91,13 @@ class TurboQuant:
                                                    torch_ops.seed_to_i64(self.seed))
 
     def encode_into(self, x: torch.Tensor, slots: torch.Tensor, cache_packed: torch.Tensor,
-                    cache_norms: torch.Tensor) -> None:
+                    cache_norms: torch.Tensor, check_slots: bool = False) -> None:
         """Encode x [n, head_dim] into rows `slots` [n] (int64) of a paged cache
         ([num_blocks, block_size, Hkv, P] uint8 and [num_blocks, block_size, Hkv]
-        f32, rows counted as (block*block_size + offset)*Hkv + kv_head)."""
+        f32, rows counted as (block*block_size + offset)*Hkv + kv_head).  A
+        negative slot skips its vector.  The kernel takes the other slots as
+        distinct and in range; check_slots=True verifies that first (reading
+        the slots back: a device synchronisation)."""
         for t, name in ((x, "x"), (slots, "slots"), (cache_packed, "cache_packed"),
                         (cache_norms, "cache_norms")):
             _require_gpu(t, name)
@@ -93,6 +112,8 @@ class TurboQuant:
         num_slots = cache_norms.numel()
         if cache_packed.numel() != num_slots * self.packed_dim:
             raise ValueError("cache_packed and cache_norms disagree on the number of rows")
+        if check_slots:
+            verify_slots(slots, num_slots)
         x = x.contiguous()
         slots = slots.contiguous()
         _lib.check(_lib.tq_encode_paged(x.data_ptr(), slots.data_ptr(), slots.numel(),

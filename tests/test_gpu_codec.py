@@ -199,6 +199,26 @@ def test_encode_paged(dev, bits):
     _encode_paged(dev, bits, D)
 
 
+def test_encode_paged_slot_check(dev):
+    """encode_into(check_slots=True) refuses a slot past the cache and a
+    duplicate before anything is written, and writes valid slots as usual."""
+    tq = TurboQuant(D, 4, 42, dev)
+    cache_p = torch.full((4, 16, 8, tq.packed_dim), 0x5A, dtype=torch.uint8, device=dev)
+    cache_n = torch.full((4, 16, 8), -1.0, dtype=torch.float32, device=dev)
+    x = torch.from_numpy(W.gaussian(3, seed=5)).to(dev)
+    for bad in ([0, 1, 512], [4, 9, 4]):
+        with pytest.raises(ValueError):
+            tq.encode_into(x, torch.tensor(bad, dtype=torch.int64, device=dev), cache_p, cache_n,
+                           check_slots=True)
+    torch.cuda.synchronize()
+    assert bool((cache_n == -1.0).all())                 # nothing written
+    tq.encode_into(x, torch.tensor([7, -1, 100], dtype=torch.int64, device=dev), cache_p, cache_n,
+                   check_slots=True)
+    p, n = tq.encode(x)
+    flat_p, flat_n = cache_p.view(-1, tq.packed_dim), cache_n.view(-1)
+    assert torch.equal(flat_p[[7, 100]], p[[0, 2]]) and torch.equal(flat_n[[7, 100]], n[[0, 2]])
+
+
 # ---------------------------------------------------------------------------
 # head_dim 64 and 256
 # ---------------------------------------------------------------------------

@@ -160,3 +160,17 @@ def test_hybrid_ops_fake_shapes_and_checks():
     assert sorted(h.perm.tolist()) == list(range(128))
     h.calibrate_uniform(8)
     assert h.perm.tolist() == list(range(128)) and h.num_kv_heads == 8
+
+
+def test_verify_slots_rejects_what_the_paged_write_assumes_away():
+    """The paged write's slot contract: non-negative slots distinct and in
+    range, negative ones skipped (checked on the host, opt-in)."""
+    import torch
+    from kv_cache_vector_amd.turboquant import verify_slots
+    verify_slots(torch.tensor([3, 0, 7, -1, -1], dtype=torch.int64), 8)
+    verify_slots(torch.tensor([-1, -5], dtype=torch.int64), 8)
+    verify_slots(torch.tensor([], dtype=torch.int64), 8)
+    with pytest.raises(ValueError, match="past the cache"):
+        verify_slots(torch.tensor([1, 8], dtype=torch.int64), 8)
+    with pytest.raises(ValueError, match="distinct"):
+        verify_slots(torch.tensor([2, 5, 2], dtype=torch.int64), 8)
