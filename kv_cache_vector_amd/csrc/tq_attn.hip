@@ -74,10 +74,11 @@ constexpr float kLazy = 8.0f;               // rescale when a score passes m + 8
 constexpr int kMaxSplitTokens = 4096;       // block-table entries of a split staged in LDS
 constexpr int kMWaves = 8;                  // waves per workgroup
 constexpr int kMThreads = 64 * kMWaves;
-constexpr int kMPrefetch = 1;               // extra ring slots: pages of loads in flight ahead of use
 // split-kernel waves aimed for: one full round on MI355X, whose 256 CUs x 4
-// SIMDs hold 2 waves each of this kernel (its 210-220 VGPRs allow no more);
-// measured, 1.5 or 2-3 rounds are slower and half a round much slower
+// SIMDs hold 2 waves each of this kernel with its 8-wave workgroups (170-210
+// VGPRs at head_dim 128); measured, 1.5 or 2-3 rounds are slower, half a
+// round much slower, and 12-wave workgroups at 168 VGPRs (3 waves per SIMD,
+// 3072 waves) slower too
 constexpr int kMTargetWaves = 2048;
 constexpr float kLevelScale = 16.0f;        // binary16 levels are 16 c
 constexpr float kWShift = 6.0f;             // value weights carry 2^6
@@ -587,32 +588,37 @@ __global__ __launch_bounds__(kMThreads) void attn_split_kernel(AttnParams p) {
     const uint32_t pagev = kAttnBlockSize * rowv;
     const uint32_t pagen = kAttnBlockSize * p.hkv * 4u;
 
-    // Loads of page pg sit in ring slot pg % R.  The refill for page pg + R
-    // is issued at the end of step pg, once the slot has been consumed; its
-    // block number was read from LDS one step earlier.  (At D = 256 with
-    // 4-bit keys the two slots cost a few spilled registers; measured, that
-    // is still faster than a one-slot ring.)
-    constexpr int R = kMPrefetch + 1;
-    constexpr int KW = SL::KW, VW = SL::VW;
-    uint32_t rk[R][KVW][KW];
-    uint32_t rv[R][KVW][4][VW];
-    float rkn[R][4], rvn[R][4];
-    bool rok[R];
+    // Ring of two page slots: even pages in slot 0, odd pages in slot 1.  The
+    // pages are taken two at a time: the scores of both, one softmax update
+    // for both, then the value products of each.  A slot's key words are
+    // refilled (with the page two further on) as soon as its scores are
+    // formed, its value words and norms once its value products are issued,
+    // so each load has about one pair of pages of work in which to arrive.
     // The loads are unconditional (a page past the split re-reads the split's
     // last page, an L2 hit): straight-line loads let every wait for a page
-    // leave the later pages' loads in flight.
-    auto fetch = [&](int pg, int32_t blk, int slot) {
-        blk = __builtin_amdgcn_readfirstlane(blk);
-        const bool bok = pg < npages && blk >= 0 && blk < p.num_blocks;
-        rok[slot] = bok;
+    // leave the later pages' loads in flight.  (At D = 256 with 4-bit keys
+    // the two slots cost a few spilled registers; measured, that is still
+    // faster than a one-slot ring.)
+    constexpr int KW = SL::KW, VW = SL::VW;
+    uint32_t rk[2][KVW][KW];
+    uint32_t rv[2][KVW][4][VW];
+    float rkn[2][4], rvn[2][4];
+    bool rok[2];
+    auto fetch_keys = [&](int32_t blk, int slot) {     // blk wave-uniform
         blk = (blk >= 0 && blk < p.num_blocks) ? blk : 0;
         const __amdgpu_buffer_rsrc_t rsk = page_rsrc(p.kp + (size_t)blk * pagek, pagek);
+#pragma unroll
+        for (int kv = 0; kv < KVW; ++kv)     // kv head g + kv: SL::PK bytes further in the row
+            load_key<SL::KBY, KW>(rsk, offk + kv * SL::PK, rk[slot][kv]);
+    };
+    auto fetch_values = [&](int pg, int32_t blk, int slot) {   // blk wave-uniform
+        rok[slot] = pg < npages && blk >= 0 && blk < p.num_blocks;
+        blk = (blk >= 0 && blk < p.num_blocks) ? blk : 0;
         const __amdgpu_buffer_rsrc_t rsv = page_rsrc(p.vp + (size_t)blk * pagev, pagev);
         const __amdgpu_buffer_rsrc_t rkn_ = page_rsrc(p.kn + (size_t)blk * kAttnBlockSize * p.hkv, pagen);
         const __amdgpu_buffer_rsrc_t rvn_ = page_rsrc(p.vn + (size_t)blk * kAttnBlockSize * p.hkv, pagen);
 #pragma unroll
-        for (int kv = 0; kv < KVW; ++kv) {   // kv head g + kv: SL::PK / SL::PV bytes further in the row
-            load_key<SL::KBY, KW>(rsk, offk + kv * SL::PK, rk[slot][kv]);
+        for (int kv = 0; kv < KVW; ++kv) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const uint32_t ov = offv[i] + kv * SL::PV;
@@ -636,13 +642,12 @@ __global__ __launch_bounds__(kMThreads) void attn_split_kernel(AttnParams p) {
         for (int i = 0; i < 4; ++i)
             rvn[slot][i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rvn_, offn[i], 0, 0));
     };
-    auto bt_at = [&](int pg) -> int32_t { return bt_lds[pg < npages ? pg : npages - 1]; };
-#pragma unroll
-    for (int d = 0; d < R; ++d) fetch(d, bt_at(d), d);
-    int32_t blk_next = bt_at(R);
+    auto bt_at = [&](int pg) -> int32_t {
+        return __builtin_amdgcn_readfirstlane(bt_lds[pg < npages ? pg : npages - 1]);
+    };
 
-    // one page: score tiles, value operands, softmax, value tiles, refill
-    auto step = [&](const int pg, const int d) {
+    // scores of the page in slot d: tokens 4r .. 4r+3 for head column hcol
+    auto scores = [&](int d) -> f4 {
         // the lane's key slice of kv head g + kv, from bit 0 (3 bits at D = 64:
         // shifted into place)
         auto key_slice = [&](int kv, uint32_t (&kc)[KW]) {
@@ -656,7 +661,6 @@ __global__ __launch_bounds__(kMThreads) void attn_split_kernel(AttnParams p) {
         };
         uint32_t kc[KW];
         key_slice(0, kc);
-        // scores of tokens 4r .. 4r+3 for head hcol
         f4 S;
         if constexpr (PAIRED) {
             f4 S0 = f4{0.0f, 0.0f, 0.0f, 0.0f};
@@ -678,36 +682,47 @@ __global__ __launch_bounds__(kMThreads) void attn_split_kernel(AttnParams p) {
             score_chunks<0, NJ, KB>(tab, kc, lok, bq1, bq2, S0, S1);
             S = S0 + S1;
         }
-        // value codes of the page (KVW = 2: kv head g's; g + 1's follow below)
-        u32x4 Bv[NJJ];
-        value_operands<NJJ, VB, VW>(tab, rv[d][0], lov, q4, vsh, Bv);
+        return S;
+    };
 
-        // online softmax in base 2.  Two lazily raised references: M per head
-        // (rescale when a score passes M + 8) and a power of two vlim per wave
-        // bounding the value norms (rescale when a norm passes it); the
-        // weights w = 2^(s - M) * n_v * 2^6 / vlim then stay below 2^14,
-        // inside binary16.
-        const int tbase = t0 + pg * kAttnBlockSize + 4 * r;
-        const bool full = rok[d] && (t0 + pg * kAttnBlockSize + kAttnBlockSize <= t1);
+    // Online softmax in base 2 over the NP pages of slots ds[] (pages pgs[]).
+    // Two lazily raised references: M per head (rescale when a score passes
+    // M + 8) and a power of two vlim per wave bounding the value norms
+    // (rescale when a norm passes it); the weights w = 2^(s - M) * n_v * 2^6 /
+    // vlim then stay below 2^14, inside binary16.  Leaves t = s - M and the
+    // value norms of the pages' tokens.
+    auto softmax = [&](auto np, const f4 *S, const int *pgs, const int *ds, float *t, float *vn) {
+        constexpr int NP = decltype(np)::value;
         // exponents against the current reference: t = s - Mc (one fma per token)
         const float Mc0 = (M == -__builtin_inff()) ? 0.0f : M;
-        float t[4], vn[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            t[i] = __builtin_fmaf(S[i], rkn[d][i] * qsl, -Mc0);
-            vn[i] = rvn[d][i];
-        }
-        if (!full) {                                    // wave-uniform
+        for (int q = 0; q < NP; ++q)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const bool ok = rok[d] && (tbase + i < t1);
-                t[i] = ok ? t[i] : -__builtin_inff();
-                vn[i] = ok ? vn[i] : 0.0f;
+                t[4 * q + i] = __builtin_fmaf(S[q][i], rkn[ds[q]][i] * qsl, -Mc0);
+                vn[4 * q + i] = rvn[ds[q]][i];
             }
+        bool full = true;                                             // wave-uniform
+#pragma unroll
+        for (int q = 0; q < NP; ++q)
+            full = full & rok[ds[q]] & (t0 + (pgs[q] + 1) * kAttnBlockSize <= t1);
+        if (!full) {                                                  // one join for all pages
+#pragma unroll
+            for (int q = 0; q < NP; ++q)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const bool ok = rok[ds[q]] & (t0 + pgs[q] * kAttnBlockSize + 4 * r + i < t1);
+                    t[4 * q + i] = ok ? t[4 * q + i] : -__builtin_inff();
+                    vn[4 * q + i] = ok ? vn[4 * q + i] : 0.0f;
+                }
         }
-        float smax = __builtin_fmaxf(__builtin_fmaxf(t[0], t[1]), __builtin_fmaxf(t[2], t[3]));
+        float smax = t[0], vmax = vn[0];
+#pragma unroll
+        for (int e = 1; e < 4 * NP; ++e) {
+            smax = __builtin_fmaxf(smax, t[e]);
+            vmax = __builtin_fmaxf(vmax, vn[e]);
+        }
         smax = hv ? smax : -__builtin_inff();
-        const float vmax = __builtin_fmaxf(__builtin_fmaxf(vn[0], vn[1]), __builtin_fmaxf(vn[2], vn[3]));
         const float lim = (M == -__builtin_inff()) ? -__builtin_inff() : kLazy;
         if (__builtin_amdgcn_ballot_w64(smax > lim || vmax > vlim)) {
             // new score reference of every head whose scores passed it by 2^8
@@ -716,9 +731,9 @@ __global__ __launch_bounds__(kMThreads) void attn_split_kernel(AttnParams p) {
             const float Mn = (mx > lim) ? Mc0 + mx : M;
             const float f = (Mn == M) ? 1.0f : __builtin_amdgcn_exp2f(M - Mn);
             lsum *= f;
-            const float sh = (Mn == M) ? 0.0f : Mn - Mc0;   // the page against the new reference
+            const float sh = (Mn == M) ? 0.0f : Mn - Mc0;   // the pages against the new reference
 #pragma unroll
-            for (int i = 0; i < 4; ++i) t[i] -= sh;
+            for (int e = 0; e < 4 * NP; ++e) t[e] -= sh;
             M = Mn;
             // new norm bound: the power of two above the wave's largest norm
             float vw = vmax;
@@ -726,11 +741,11 @@ __global__ __launch_bounds__(kMThreads) void attn_split_kernel(AttnParams p) {
             for (int o = 1; o < 64; o <<= 1) vw = __builtin_fmaxf(vw, __shfl_xor(vw, o));
             float fv = 1.0f;
             if (vw > vlim) {                              // wave-uniform
-                const int e = __builtin_amdgcn_frexp_expf(vw);   // vw in [2^(e-1), 2^e)
-                const float vn_lim = __builtin_bit_cast(float, (uint32_t)(127 + (e > 127 ? 127 : e)) << 23);
-                fv = vlim / vn_lim;                         // exact: both powers of two (or 0)
-                vlim = vn_lim;
-                vscale = (float)(1 << (int)kWShift) / vlim;
+                int e = __builtin_amdgcn_frexp_expf(vw);         // vw in [2^(e-1), 2^e)
+                e = e > 126 ? 126 : (e < -120 ? -120 : e);         // keeps 2^e, 2^-e, 2^(6-e) normal
+                fv = vlim * __builtin_bit_cast(float, (uint32_t)(127 - e) << 23);   // exact: powers of two (or 0)
+                vlim = __builtin_bit_cast(float, (uint32_t)(127 + e) << 23);
+                vscale = __builtin_bit_cast(float, (uint32_t)(127 + (int)kWShift - e) << 23);   // 2^6 / vlim
             }
             // accumulator rows are heads 4r + i (PAIRED: row h holds head h % 8)
 #pragma unroll
@@ -740,6 +755,11 @@ __global__ __launch_bounds__(kMThreads) void attn_split_kernel(AttnParams p) {
                 for (int jj = 0; jj < NJJ; ++jj) acc[jj][i] *= fi;
             }
         }
+    };
+
+    // Value products of the page in slot d with exponents t and norms vn of
+    // its 4 tokens per lane; Bv holds the value operands of kv head g.
+    auto values = [&](int d, const float *t, const float *vn, u32x4 (&Bv)[NJJ]) {
         uint32_t w1[4], w2[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -778,20 +798,44 @@ __global__ __launch_bounds__(kMThreads) void attn_split_kernel(AttnParams p) {
                 acc[jj] = mfma(A2, Bv[jj], acc[jj]);
             }
         }
-
-        fetch(pg + R, blk_next, d);
-        blk_next = bt_at(pg + R + 1);
     };
-    // Whole rounds of R pages, then the remainder after the loop, so that the
-    // loop head sees the R slots refilled in the same order on every path.
-    int pg0 = 0;
-    for (; pg0 + R <= npages; pg0 += R) {      // wave-uniform
-#pragma unroll
-        for (int d = 0; d < R; ++d) step(pg0 + d, d);
+
+    {
+        const int32_t b0 = bt_at(0), b1 = bt_at(1);
+        fetch_keys(b0, 0);
+        fetch_values(0, b0, 0);
+        fetch_keys(b1, 1);
+        fetch_values(1, b1, 1);
     }
-#pragma unroll
-    for (int d = 0; d < R - 1; ++d)
-        if (pg0 + d < npages) step(pg0 + d, d);
+    int pg0 = 0;
+    for (; pg0 + 2 <= npages; pg0 += 2) {     // wave-uniform
+        const int32_t bA = bt_at(pg0 + 2), bB = bt_at(pg0 + 3);
+        f4 S[2];
+        S[0] = scores(0);
+        fetch_keys(bA, 0);
+        S[1] = scores(1);
+        fetch_keys(bB, 1);
+        u32x4 Bv[NJJ];   // value codes of kv head g (KVW = 2: g + 1's follow in values())
+        value_operands<NJJ, VB, VW>(tab, rv[0][0], lov, q4, vsh, Bv);
+        const int pgs[2] = {pg0, pg0 + 1}, ds[2] = {0, 1};
+        float t[8], vn[8];
+        softmax(std::integral_constant<int, 2>{}, S, pgs, ds, t, vn);
+        values(0, t, vn, Bv);
+        fetch_values(pg0 + 2, bA, 0);
+        value_operands<NJJ, VB, VW>(tab, rv[1][0], lov, q4, vsh, Bv);
+        values(1, t + 4, vn + 4, Bv);
+        fetch_values(pg0 + 3, bB, 1);
+    }
+    if (pg0 < npages) {                       // the last page of an odd count, in slot 0
+        f4 S[1];
+        S[0] = scores(0);
+        u32x4 Bv[NJJ];
+        value_operands<NJJ, VB, VW>(tab, rv[0][0], lov, q4, vsh, Bv);
+        const int pgs[1] = {pg0}, ds[1] = {0};
+        float t[4], vn[4];
+        softmax(std::integral_constant<int, 1>{}, S, pgs, ds, t, vn);
+        values(0, t, vn, Bv);
+    }
 
     lsum += __shfl_xor(lsum, 16);
     lsum += __shfl_xor(lsum, 32);
