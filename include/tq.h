@@ -239,8 +239,8 @@ tq_status tq_attn_decode_kv(const void *q_f16, const uint8_t *k_packed, const fl
  *   - A shape whose tq_attn_workspace_bytes(...) exceeds
  *     TQ_ATTN_NOALLOC_WORKSPACE_BYTES returns TQ_ERR_WORKSPACE before
  *     anything is enqueued (at head_dim 128: batch * num_q_heads * splits
- *     up to 64,528 partial states, e.g. batch 16 x 32 heads at a 32K
- *     context uses 4.3 MB).
+ *     up to 64,527 partial states of 520 bytes, e.g. batch 16 x 32 heads at
+ *     a 32K context uses 8.5 MB).
  *   - Every call on a GPU uses that GPU's one array: calls that may overlap
  *     on one GPU (on different streams, or from different host threads)
  *     race and must be serialised by the caller.  Nothing in the array needs
