@@ -11,6 +11,7 @@ tq_decode of it (one launch).  Inputs are resident in HBM before timing.
     python bench.py --attn-only [--steps K] [--head-dim D]
                                                 (attention side measurement only;
                                                  D = 64, 128 (default) or 256)
+    python bench.py --hybrid-only               (hybrid-mode side measurement only)
 
 Prints one JSON line.  `value` is fp16 key/value bytes passed through the
 codec per second (encode and decode both count their 256 B/vector of fp16).
@@ -269,6 +270,8 @@ def main() -> int:
                     help="head_dim of the --attn-only measurement")
     ap.add_argument("--attn-only", action="store_true",
                     help="only the batch-16 x 32K decode-attention measurement (for profiling)")
+    ap.add_argument("--hybrid-only", action="store_true",
+                    help="only the hybrid-mode (tq35 / tq25) whole-cache measurement (for profiling)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: the codec is data-parallel over independent "
@@ -289,7 +292,6 @@ def main() -> int:
     import torch
 
     from kv_cache_vector_amd import _lib
-    from kv_cache_vector_amd import workloads as W
 
     _lib.load()
     dev = torch.device("cuda:0")
@@ -297,16 +299,10 @@ def main() -> int:
     stream = torch.cuda.current_stream(dev)
     s = stream.cuda_stream
 
-    log("generating the 8B-shaped cache: %d vectors (%.2f GB fp16)" % (N, N * 2 * D / 1e9))
-    x = torch.empty((N, D), dtype=torch.float16, device=dev)
-    host_layers = []
-    for layer in range(LAYERS):
-        xl = W.llama8b_layer(layer)
-        if not args.no_cpu_baseline:
-            host_layers.append(xl)
-        x[layer * PER_LAYER:(layer + 1) * PER_LAYER].copy_(torch.from_numpy(xl))
-        if layer % 8 == 7:
-            log("  layer %d/%d uploaded" % (layer + 1, LAYERS))
+    x, host_layers = upload_cache(torch, dev, keep_host=not (args.no_cpu_baseline or args.hybrid_only))
+    if args.hybrid_only:
+        print(json.dumps(hybrid_measurement(torch, dev, stream, x)), flush=True)
+        return 0
     packed = torch.empty((N, CODE_BYTES), dtype=torch.uint8, device=dev)
     norms = torch.empty((N,), dtype=torch.float32, device=dev)
     out = torch.empty((N, D), dtype=torch.float16, device=dev)
@@ -415,6 +411,23 @@ def side_measurements(torch, dev, stream, x, packed, norms):
     res.update(codec_side_measurement(torch, dev, stream, x, packed, norms))
     res.update(hybrid_measurement(torch, dev, stream, x))
     return res
+
+
+def upload_cache(torch, dev, keep_host):
+    """The 8B-shaped cache, generated layer by layer on the host and uploaded
+    to one resident [N, D] fp16 tensor; the host layers too if keep_host."""
+    from kv_cache_vector_amd import workloads as W
+    log("generating the 8B-shaped cache: %d vectors (%.2f GB fp16)" % (N, N * 2 * D / 1e9))
+    x = torch.empty((N, D), dtype=torch.float16, device=dev)
+    host_layers = []
+    for layer in range(LAYERS):
+        xl = W.llama8b_layer(layer)
+        if keep_host:
+            host_layers.append(xl)
+        x[layer * PER_LAYER:(layer + 1) * PER_LAYER].copy_(torch.from_numpy(xl))
+        if layer % 8 == 7:
+            log("  layer %d/%d uploaded" % (layer + 1, LAYERS))
+    return x, host_layers
 
 
 def hybrid_measurement(torch, dev, stream, x):
