@@ -243,9 +243,14 @@ def cpu_baseline(layers, budget_s: float = 60.0, single_layer_budget_s: float = 
 
 def gpu_clocks():
     """The current sclk / mclk levels as rocm-smi reports them (None when it
-    is not available)."""
+    is not available).  Under a profiler (rocprofv3 preloads its library into
+    every child, which would start the GPU runtime inside the rocm-smi
+    process before that script's interpreter runs) it is not run."""
+    import os
     import re
     import subprocess
+    if "rocprof" in os.environ.get("LD_PRELOAD", "") or any(k.startswith("ROCPROF") for k in os.environ):
+        return None
     try:
         r = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True, timeout=20)
     except (OSError, subprocess.SubprocessError):

@@ -688,6 +688,13 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const uint32_t *__rest
 // decode, through a staged row per quad).
 // ---------------------------------------------------------------------------
 
+// Staged binary16 rows of the hybrid kernels: 128 channels padded to 136
+// (272 bytes), so that the 16 rows a wave touches start 16 bytes apart in
+// the 64 LDS banks: the channel gather / scatter, where every quad reads or
+// writes the same channel of its own row, then hits 16 different banks
+// instead of one, and the 16-byte row accesses stay aligned.
+constexpr int kHybridRowPad = 136;
+
 template <int MODE>
 struct HybridBits {
     static constexpr int A = (MODE == 35) ? 3 : 2;
@@ -823,7 +830,7 @@ __global__ __launch_bounds__(kThreads) void hybrid_encode_kernel(const u32x4 *__
                                                                  HybridConsts k) {
     using HB = HybridBits<MODE>;
     constexpr int RW = HB::RW;
-    __shared__ __attribute__((aligned(16))) uint16_t xs[kVecPerBlock][128];
+    __shared__ __attribute__((aligned(16))) uint16_t xs[kVecPerBlock][kHybridRowPad];
     __shared__ __attribute__((aligned(16))) uint32_t rows[kVecPerBlock * RW];
     __shared__ u32x4 gidx[8];
     __shared__ u32x4 smask[16], qmask[16];
@@ -1003,7 +1010,7 @@ __global__ __launch_bounds__(kThreads) void hybrid_decode_kernel(const uint32_t 
                                                                  HybridConsts k) {
     using HB = HybridBits<MODE>;
     constexpr int RW = HB::RW;
-    __shared__ __attribute__((aligned(16))) uint16_t xs[kVecPerBlock][128];
+    __shared__ __attribute__((aligned(16))) uint16_t xs[kVecPerBlock][kHybridRowPad];
     __shared__ __attribute__((aligned(16))) uint32_t rows[kVecPerBlock * RW];
     __shared__ u32x4 gidx[8];
     __shared__ u32x4 smask[16], qmask[16];
