@@ -823,7 +823,10 @@ __device__ __forceinline__ void half_decode(float (&f)[16], float scale, const u
     }
 }
 
-template <int MODE>
+// IDENT: the channel permutation is the identity (the data-free split), so
+// the group-order registers are the channel-order loads themselves and the
+// LDS staging and gather (scatter on decode) are skipped.
+template <int MODE, bool IDENT>
 __global__ __launch_bounds__(kThreads) void hybrid_encode_kernel(const u32x4 *__restrict__ x,
                                                                  int64_t n,
                                                                  uint32_t *__restrict__ packed,
@@ -856,16 +859,27 @@ __global__ __launch_bounds__(kThreads) void hybrid_encode_kernel(const u32x4 *__
     // Quads past the end stay (their loads read zeros and their rows are not
     // stored): every lane of a wave takes part in the wave's row stores.
     if (16 * (threadIdx.x >> 6) >= nb) return;   // the whole wave is past the end
-    // the row, staged per quad for the channel gather
     const __amdgpu_buffer_rsrc_t rx = span_rsrc(x + v0 * 16, nb * 256u);
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-        const u32x4 u = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, qi * 256u + 16u * q + 64u * g, 0, 0));
-        *reinterpret_cast<u32x4 *>(&xs[qi][8 * q + 32 * g]) = u;
-    }
-    wave_lds_sync();
     uint32_t w[16];   // binary16 pairs of positions (2i, 2i + 1) in group order
-    {
+    if constexpr (IDENT) {
+        // position 32 K + 8 q + j is channel 32 K + 8 q + j: w[4 K .. 4 K + 3]
+        // are the 16 bytes at 64 K + 16 q of the lane's row
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const u32x4 u = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, qi * 256u + 16u * q + 64u * g, 0, 0));
+            w[4 * g] = u.x;
+            w[4 * g + 1] = u.y;
+            w[4 * g + 2] = u.z;
+            w[4 * g + 3] = u.w;
+        }
+    } else {
+        // the row, staged per quad for the channel gather
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const u32x4 u = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, qi * 256u + 16u * q + 64u * g, 0, 0));
+            *reinterpret_cast<u32x4 *>(&xs[qi][8 * q + 32 * g]) = u;
+        }
+        wave_lds_sync();
         const u32x4 ga = gidx[2 * q], gb = gidx[2 * q + 1];
         const uint32_t gw[8] = {ga.x, ga.y, ga.z, ga.w, gb.x, gb.y, gb.z, gb.w};
 #pragma unroll
@@ -1003,7 +1017,7 @@ __global__ __launch_bounds__(kThreads) void hybrid_encode_kernel(const u32x4 *__
         __builtin_amdgcn_raw_buffer_store_b32(rows[wrow0 * RW + i], rp, 4u * i, 0, 0);
 }
 
-template <int MODE>
+template <int MODE, bool IDENT>
 __global__ __launch_bounds__(kThreads) void hybrid_decode_kernel(const uint32_t *__restrict__ packed,
                                                                  int64_t n,
                                                                  u32x4 *__restrict__ out,
@@ -1094,17 +1108,28 @@ __global__ __launch_bounds__(kThreads) void hybrid_decode_kernel(const uint32_t 
         hv[2 * i] = __builtin_bit_cast(uint16_t, (_Float16)y0);
         hv[2 * i + 1] = __builtin_bit_cast(uint16_t, (_Float16)y1);
     }
-    // back to channel order through the quad's staged row
-    {
-        const u32x4 ga = gidx[2 * q], gb = gidx[2 * q + 1];
-        const uint32_t gw[8] = {ga.x, ga.y, ga.z, ga.w, gb.x, gb.y, gb.z, gb.w};
-#pragma unroll
-        for (int r = 0; r < 32; ++r) xs[qi][(gw[r >> 2] >> (8 * (r & 3))) & 0xFFu] = hv[r];
-    }
-    wave_lds_sync();
     u32x4 *dst = out + (v0 + qi) * 16 + q;
+    if constexpr (IDENT) {
+        // register 8 K + j is channel 32 K + 8 q + j: 16 bytes at 64 K + 16 q
 #pragma unroll
-    for (int g = 0; g < 4; ++g) dst[4 * g] = *reinterpret_cast<const u32x4 *>(&xs[qi][8 * q + 32 * g]);
+        for (int g = 0; g < 4; ++g) {
+            uint32_t d[4];
+#pragma unroll
+            for (int m = 0; m < 4; ++m) d[m] = (uint32_t)hv[8 * g + 2 * m] | ((uint32_t)hv[8 * g + 2 * m + 1] << 16);
+            dst[4 * g] = u32x4{d[0], d[1], d[2], d[3]};
+        }
+    } else {
+        // back to channel order through the quad's staged row
+        {
+            const u32x4 ga = gidx[2 * q], gb = gidx[2 * q + 1];
+            const uint32_t gw[8] = {ga.x, ga.y, ga.z, ga.w, gb.x, gb.y, gb.z, gb.w};
+#pragma unroll
+            for (int r = 0; r < 32; ++r) xs[qi][(gw[r >> 2] >> (8 * (r & 3))) & 0xFFu] = hv[r];
+        }
+        wave_lds_sync();
+#pragma unroll
+        for (int g = 0; g < 4; ++g) dst[4 * g] = *reinterpret_cast<const u32x4 *>(&xs[qi][8 * q + 32 * g]);
+    }
 }
 
 // One block per 64 enc_vpq(d) (encode) or 64 dec_vpq(d, bits) (decode)
@@ -1185,14 +1210,27 @@ int hybrid_row_bytes(int mode) {
     return mode == 35 ? 4 * HybridBits<35>::RW : (mode == 25 ? 4 * HybridBits<25>::RW : 0);
 }
 
+// Whether the channel table is the identity (register r of lane q holds
+// channel 32 (r / 8) + 8 q + r % 8).
+bool hybrid_identity(const HybridConsts &k) {
+    const uint8_t *g = reinterpret_cast<const uint8_t *>(k.gidx);
+    for (int q = 0; q < 4; ++q)
+        for (int r = 0; r < 32; ++r)
+            if (g[32 * q + r] != 32 * (r / 8) + 8 * q + r % 8) return false;
+    return true;
+}
+
 hipError_t launch_hybrid_encode(int mode, const void *x, int64_t n, const HybridConsts &k,
                                 uint8_t *packed, hipStream_t stream) {
     if (n > (int64_t)kVecPerBlock * 0x7fffffff) return hipErrorInvalidValue;
     const dim3 grid = grid_for(n, kVecPerBlock), block(kThreads);
     const u32x4 *xs = static_cast<const u32x4 *>(x);
     uint32_t *pk = reinterpret_cast<uint32_t *>(packed);
-    if (mode == 35) hipLaunchKernelGGL(hybrid_encode_kernel<35>, grid, block, 0, stream, xs, n, pk, k);
-    else if (mode == 25) hipLaunchKernelGGL(hybrid_encode_kernel<25>, grid, block, 0, stream, xs, n, pk, k);
+    const bool id = hybrid_identity(k);
+    if (mode == 35 && id) hipLaunchKernelGGL((hybrid_encode_kernel<35, true>), grid, block, 0, stream, xs, n, pk, k);
+    else if (mode == 35) hipLaunchKernelGGL((hybrid_encode_kernel<35, false>), grid, block, 0, stream, xs, n, pk, k);
+    else if (mode == 25 && id) hipLaunchKernelGGL((hybrid_encode_kernel<25, true>), grid, block, 0, stream, xs, n, pk, k);
+    else if (mode == 25) hipLaunchKernelGGL((hybrid_encode_kernel<25, false>), grid, block, 0, stream, xs, n, pk, k);
     else return hipErrorInvalidValue;
     return hipGetLastError();
 }
@@ -1203,8 +1241,11 @@ hipError_t launch_hybrid_decode(int mode, const uint8_t *packed, int64_t n,
     const dim3 grid = grid_for(n, kVecPerBlock), block(kThreads);
     const uint32_t *pk = reinterpret_cast<const uint32_t *>(packed);
     u32x4 *o = static_cast<u32x4 *>(out);
-    if (mode == 35) hipLaunchKernelGGL(hybrid_decode_kernel<35>, grid, block, 0, stream, pk, n, o, k);
-    else if (mode == 25) hipLaunchKernelGGL(hybrid_decode_kernel<25>, grid, block, 0, stream, pk, n, o, k);
+    const bool id = hybrid_identity(k);
+    if (mode == 35 && id) hipLaunchKernelGGL((hybrid_decode_kernel<35, true>), grid, block, 0, stream, pk, n, o, k);
+    else if (mode == 35) hipLaunchKernelGGL((hybrid_decode_kernel<35, false>), grid, block, 0, stream, pk, n, o, k);
+    else if (mode == 25 && id) hipLaunchKernelGGL((hybrid_decode_kernel<25, true>), grid, block, 0, stream, pk, n, o, k);
+    else if (mode == 25) hipLaunchKernelGGL((hybrid_decode_kernel<25, false>), grid, block, 0, stream, pk, n, o, k);
     else return hipErrorInvalidValue;
     return hipGetLastError();
 }

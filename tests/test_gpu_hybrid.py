@@ -157,15 +157,16 @@ def test_calibrated_split(dev, mode):
 
 @pytest.mark.parametrize("mode", ["tq35", "tq25"])
 def test_random_split_and_ragged_counts(dev, mode):
-    """Random channel permutations; counts that leave partial quads, waves
-    and blocks; nothing past the n rows is written."""
+    """Random channel permutations and the identity (which takes the kernels'
+    direct-load path); counts that leave partial quads, waves and blocks;
+    nothing past the n rows is written."""
     rng = np.random.default_rng(11)
     row = HybridTurboQuant.packed_dim_for_mode(D, mode)
     s = torch.cuda.current_stream().cuda_stream
-    for n in (1, 3, 17, 63, 64, 65, 1000):
-        perm = rng.permutation(D).astype(np.int32)
+    for n, perm in [(n, p) for n in (1, 3, 17, 63, 64, 65, 1000)
+                    for p in (rng.permutation(D).astype(np.int32), np.arange(D, dtype=np.int32))]:
         x_np = W.gaussian(n, seed=n)
-        run_hybrid(dev, x_np, mode, 5, perm, "n=%d %s" % (n, mode))
+        run_hybrid(dev, x_np, mode, 5, perm, "n=%d %s %s" % (n, mode, "identity" if np.array_equal(perm, np.arange(D)) else "random"))
         x = torch.from_numpy(x_np).to(dev)
         buf = torch.full((n * row + 256,), 0xA5, dtype=torch.uint8, device=dev)
         assert _lib.tq_hybrid_encode(x.data_ptr(), n, D, HybridTurboQuant.MODES[mode], 5,
