@@ -158,6 +158,20 @@ __device__ __forceinline__ void store_sign_mask(const CodecConsts &k, int t, uin
     smask[t] = ONES ? (m | 0x3C003C00u) : m;   // 0x3C00: binary16 1.0
 }
 
+// The mask word store_sign_mask writes for thread t, from K sign words that
+// are selected as scalars: a private copy of the words indexed per lane would
+// live in scratch memory.
+template <int K, bool ONES>
+__device__ __forceinline__ uint32_t sign_mask_word(const uint32_t *sign, int t) {
+    const int q = t / (4 * K), i = t % (4 * K);
+    uint32_t sw = __builtin_amdgcn_readfirstlane(sign[0]);
+#pragma unroll
+    for (int j = 1; j < K; ++j) sw = (i >> 2) == j ? __builtin_amdgcn_readfirstlane(sign[j]) : sw;
+    const uint32_t w = sw >> (8 * q + 2 * (i & 3));
+    const uint32_t m = ((w & 1u) << 15) | (((w >> 1) & 1u) << 31);
+    return ONES ? (m | 0x3C003C00u) : m;   // 0x3C00: binary16 1.0
+}
+
 // sigma_a a + sigma_b b and sigma_a a - sigma_b b for binary16 pairs
 // x = (a, b), s = (sigma_a, sigma_b): v_dot2_f32_f16 with a zero addend (the
 // three-operand form, which needs no zeroed destination), the second with
@@ -841,15 +855,10 @@ __global__ __launch_bounds__(kThreads) void hybrid_encode_kernel(const u32x4 *__
     if (threadIdx.x < 8) gidx[threadIdx.x] = u32x4{k.gidx[4 * threadIdx.x], k.gidx[4 * threadIdx.x + 1],
                                                    k.gidx[4 * threadIdx.x + 2], k.gidx[4 * threadIdx.x + 3]};
     if (threadIdx.x < 12) lev[threadIdx.x] = threadIdx.x < 8 ? k.lev_a[threadIdx.x] : k.lev_b[threadIdx.x - 8];
-    if (threadIdx.x < 64) {
-        CodecConsts c{};
-        for (int w = 0; w < 4; ++w) c.sign[w] = k.sign[w];
-        store_sign_mask<4, true>(c, threadIdx.x, reinterpret_cast<uint32_t *>(smask));
-    } else if (threadIdx.x < 128) {
-        CodecConsts c{};
-        for (int w = 0; w < 4; ++w) c.sign[w] = k.qsign[w];
-        store_sign_mask<4, false>(c, threadIdx.x - 64, reinterpret_cast<uint32_t *>(qmask));
-    }
+    if (threadIdx.x < 64)
+        reinterpret_cast<uint32_t *>(smask)[threadIdx.x] = sign_mask_word<4, true>(k.sign, threadIdx.x);
+    else if (threadIdx.x < 128)
+        reinterpret_cast<uint32_t *>(qmask)[threadIdx.x - 64] = sign_mask_word<4, false>(k.qsign, threadIdx.x - 64);
     __syncthreads();
 
     const int q = threadIdx.x & 3;
@@ -1008,7 +1017,8 @@ __global__ __launch_bounds__(kThreads) void hybrid_encode_kernel(const u32x4 *__
     }
     wave_lds_sync();
     // the wave's rows go out as one contiguous span of dwords
-    const uint32_t wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    // wave-uniform (readfirstlane): the buffer resources built from it stay scalar
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const uint32_t wrow0 = 16 * wave;                         // first row of the wave in the block
     const uint32_t wrows = (nb > wrow0) ? ((nb - wrow0 < 16) ? nb - wrow0 : 16) : 0;
     const __amdgpu_buffer_rsrc_t rp = span_rsrc(packed + (v0 + wrow0) * RW, wrows * RW * 4u);
@@ -1025,38 +1035,49 @@ __global__ __launch_bounds__(kThreads) void hybrid_decode_kernel(const uint32_t 
     using HB = HybridBits<MODE>;
     constexpr int RW = HB::RW;
     __shared__ __attribute__((aligned(16))) uint16_t xs[kVecPerBlock][kHybridRowPad];
-    __shared__ __attribute__((aligned(16))) uint32_t rows[kVecPerBlock * RW];
+    __shared__ __attribute__((aligned(16))) uint32_t rows[kVecPerBlock * RW + 64];   // + a spare slot per lane
     __shared__ u32x4 gidx[8];
     __shared__ u32x4 smask[16], qmask[16];
     __shared__ float lev[12];
-    if (threadIdx.x < 8) gidx[threadIdx.x] = u32x4{k.gidx[4 * threadIdx.x], k.gidx[4 * threadIdx.x + 1],
-                                                   k.gidx[4 * threadIdx.x + 2], k.gidx[4 * threadIdx.x + 3]};
-    if (threadIdx.x < 12) lev[threadIdx.x] = threadIdx.x < 8 ? k.lev_a[threadIdx.x] : k.lev_b[threadIdx.x - 8];
-    if (threadIdx.x < 64) {
-        CodecConsts c{};
-        for (int w = 0; w < 4; ++w) c.sign[w] = k.sign[w];
-        store_sign_mask<4, false>(c, threadIdx.x, reinterpret_cast<uint32_t *>(smask));
-    } else if (threadIdx.x < 128) {
-        CodecConsts c{};
-        for (int w = 0; w < 4; ++w) c.sign[w] = k.qsign[w];
-        store_sign_mask<4, false>(c, threadIdx.x - 64, reinterpret_cast<uint32_t *>(qmask));
-    }
-    __syncthreads();
+    // the kernel-argument words this thread puts into LDS, read first (their
+    // wait then leaves the row loads in flight)
+    u32x4 gv{};
+    if (threadIdx.x < 8) gv = u32x4{k.gidx[4 * threadIdx.x], k.gidx[4 * threadIdx.x + 1],
+                                    k.gidx[4 * threadIdx.x + 2], k.gidx[4 * threadIdx.x + 3]};
+    const float lv = threadIdx.x < 8 ? k.lev_a[threadIdx.x] : (threadIdx.x < 12 ? k.lev_b[threadIdx.x - 8] : 0.0f);
 
     const int q = threadIdx.x & 3;
     const uint32_t qi = threadIdx.x >> 2;
     const int64_t v0 = (int64_t)blockIdx.x * kVecPerBlock;
     const uint32_t nb = (uint32_t)((n - v0 < kVecPerBlock) ? n - v0 : kVecPerBlock);
-    const uint32_t wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    // wave-uniform (readfirstlane): the buffer resources built from it stay scalar
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const uint32_t wrow0 = 16 * wave;
-    if (wrow0 >= nb) return;   // the whole wave is past the end; no barrier follows
-    const uint32_t wrows = (nb - wrow0 < 16) ? nb - wrow0 : 16;
-    // the wave's rows, one contiguous span of dwords, into LDS
+    const uint32_t wrows = (wrow0 >= nb) ? 0 : ((nb - wrow0 < 16) ? nb - wrow0 : 16);
+    // the wave's rows, one contiguous span of dwords: every load is issued
+    // before the tables are built and the barrier taken
+    constexpr int NL = (16 * RW + 63) / 64;              // loads per lane
+    uint32_t rv[NL];
     {
         const __amdgpu_buffer_rsrc_t rp = span_rsrc(packed + (v0 + wrow0) * RW, wrows * RW * 4u);
 #pragma unroll
-        for (uint32_t i = lane; i < 16 * RW; i += 64)
-            rows[wrow0 * RW + i] = __builtin_amdgcn_raw_buffer_load_b32(rp, 4u * i, 0, 0);
+        for (int j = 0; j < NL; ++j)
+            rv[j] = __builtin_amdgcn_raw_buffer_load_b32(rp, 4u * (lane + 64u * j), 0, 0);
+    }
+    if (threadIdx.x < 8) gidx[threadIdx.x] = gv;
+    if (threadIdx.x < 12) lev[threadIdx.x] = lv;
+    if (threadIdx.x < 64)
+        reinterpret_cast<uint32_t *>(smask)[threadIdx.x] = sign_mask_word<4, false>(k.sign, threadIdx.x);
+    else if (threadIdx.x < 128)
+        reinterpret_cast<uint32_t *>(qmask)[threadIdx.x - 64] = sign_mask_word<4, false>(k.qsign, threadIdx.x - 64);
+    __syncthreads();
+    if (wrows == 0) return;    // the whole wave is past the end; no barrier follows
+    // into LDS; lanes past the wave's 16 rows write their (zero) word to a
+    // spare slot: an unconditional write keeps the last load with the others
+#pragma unroll
+    for (int j = 0; j < NL; ++j) {
+        const uint32_t i = lane + 64u * j;
+        rows[i < 16u * RW ? wrow0 * RW + i : kVecPerBlock * RW + lane] = rv[j];
     }
     wave_lds_sync();
     if (qi >= nb) return;      // uniform over the quad; only wave-local LDS follows
