@@ -75,6 +75,21 @@ def test_gpu_clocks_never_raises():
     assert r is None or all(isinstance(v, int) for v in r.values())
 
 
+def test_gpu_clocks_not_run_under_a_profiler(monkeypatch):
+    """Under rocprofv3 (its library preloaded, ROCPROF_* set) no rocm-smi
+    child is started: the profiler's library would start the GPU runtime in
+    that child before its interpreter runs."""
+    import subprocess
+    def no_child(*a, **k):
+        raise AssertionError("rocm-smi started under a profiler")
+    monkeypatch.setattr(subprocess, "run", no_child)
+    monkeypatch.setenv("LD_PRELOAD", "/opt/rocm/lib/rocprofiler-sdk/librocprofiler-sdk-tool.so")
+    assert bench.gpu_clocks() is None
+    monkeypatch.delenv("LD_PRELOAD")
+    monkeypatch.setenv("ROCPROF_OUTPUT_PATH", "/tmp")
+    assert bench.gpu_clocks() is None
+
+
 def test_oracle_attention_pieces_match_one_call():
     """The per-sequence pieces of the attention leg compute what one call
     over the whole batch computes (the leg times real work)."""
