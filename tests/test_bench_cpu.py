@@ -79,7 +79,6 @@ def test_gpu_clocks_not_run_under_a_profiler(monkeypatch):
     """Under rocprofv3 (its library preloaded, ROCPROF_* set) no rocm-smi
     child is started: the profiler's library would start the GPU runtime in
     that child before its interpreter runs."""
-    import subprocess
     def no_child(*a, **k):
         raise AssertionError("rocm-smi started under a profiler")
     monkeypatch.setattr(subprocess, "run", no_child)
