@@ -718,6 +718,21 @@ struct HybridBits {
     static constexpr int RW = PA + PB + 4 + 3;             // dwords per row
 };
 
+// The same count from the positive half of a codebook symmetric about 0
+// (thresholds thr[2^(B-1) + k] = -thr[2^(B-1) - 2 - k], thr[2^(B-1) - 1] = 0):
+// 2^(B-1) + #(t < |y|) for y > 0, 2^(B-1) - 1 - #(t < |y|) otherwise, over
+// the 2^(B-1) - 1 positive thresholds t.  It differs from count_below only
+// where |y| equals a threshold exactly.
+template <int B>
+__device__ __forceinline__ uint32_t count_below_sym(float y, const float *thr) {
+    constexpr int H = 1 << (B - 1);
+    const float a = __builtin_fabsf(y);
+    uint32_t c = 0;
+#pragma unroll
+    for (int k = 0; k < H - 1; ++k) c += (thr[H + k] < a) ? 1u : 0u;
+    return y > 0.0f ? H + c : H - 1 - c;
+}
+
 // code = number of the 2^B - 1 (scaled) thresholds strictly below y
 template <int B>
 __device__ __forceinline__ uint32_t count_below(float y, const float *thr) {
@@ -942,8 +957,8 @@ __global__ __launch_bounds__(kThreads) void hybrid_encode_kernel(const u32x4 *__
     uint32_t ca[16], cb[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-        ca[r] = count_below<HB::A>(fa[r], k.thr_a);
-        cb[r] = count_below<HB::B>(fb[r], k.thr_b);
+        ca[r] = count_below_sym<HB::A>(fa[r], k.thr_a);
+        cb[r] = count_below_sym<HB::B>(fb[r], k.thr_b);
     }
     // decode of the halves and the residual, in group order
     float ra[16], rb[16];
