@@ -289,7 +289,8 @@ def main() -> int:
         dev = torch.device("cuda:0")
         torch.cuda.set_device(dev)
         res = attention_measurement(torch, dev, torch.cuda.current_stream(dev),
-                                    reps=max(1, args.steps), head_dim=args.head_dim)
+                                    reps=max(1, args.steps), head_dim=args.head_dim,
+                                    warmup=max(1, args.warmup))
         print(json.dumps(res), flush=True)
         return 0
 
@@ -550,10 +551,12 @@ def codec_side_measurement(torch, dev, stream, x, packed, norms):
     return res
 
 
-def attention_measurement(torch, dev, stream, reps: int = 20, head_dim: int = 128):
+def attention_measurement(torch, dev, stream, reps: int = 20, head_dim: int = 128,
+                          warmup: int = 5):
     """Median (and minimum) time of tq_attn_decode (split + combine kernels) at batch 16,
     32/8 heads, 32768 tokens, 4 bits, random codes and a random block
-    permutation, with the last-level cache evicted before each call.  The
+    permutation, with the last-level cache evicted before each call, after
+    `warmup` untimed calls (the first calls run while the clocks rise).  The
     keys are named attn_batch16_32k_* at head_dim 128 and carry a _d<D>
     suffix otherwise."""
     from kv_cache_vector_amd import _lib
@@ -587,7 +590,10 @@ def attention_measurement(torch, dev, stream, reps: int = 20, head_dim: int = 12
                                        1 / math.sqrt(d), out.data_ptr(), ws.data_ptr(), wsb,
                                        s), "tq_attn_decode")
 
-    attn()
+    for _ in range(max(1, warmup)):
+        flush.sum()
+        attn()
+    torch.cuda.synchronize()
     times = []
     for _ in range(reps):
         flush.sum()        # evict the 256 MB last-level cache between repetitions

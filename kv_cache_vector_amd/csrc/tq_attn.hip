@@ -17,10 +17,8 @@
 //
 // Two kernels, flash-decoding style:
 //   split   8 waves per workgroup, one per (kv head, context split) of a
-//           sequence (two per kv head at head_dim 256, each accumulating
-//           half of the value dims): a workgroup takes the kv heads of one
-//           split, or, for caches with fewer kv heads, all of them for
-//           several splits.  Per 16-token page the scores and the value
+//           sequence: a workgroup takes the kv heads of one split, or, for
+//           caches with fewer kv heads, all of them for several splits.  Per 16-token page the scores and the value
 //           accumulation run as 16x16x32 f16 MFMA tiles:
 //             scores  S^T[16 tokens][16 heads] = C_k[16 tokens][K] Q[K][16 heads]
 //             values  O[16 heads][16 dims]    += W[16 heads][K] C_v[K][16 dims]
@@ -53,9 +51,9 @@
 // r.  The query operand of lane (head m, r) covers the same dims.  The score
 // tile leaves lane (head m, r) with tokens 4r .. 4r+3 -- exactly the K slots
 // the value product wants in its A operand, so the weights never move
-// between lanes.  Values (N = min(d, 128) / 16 dims per lane column): lane
-// (column m, r) reads dims N m .. N m + N - 1 of tokens 4r .. 4r+3 (of the
-// wave's half at d = 256); chunk jj accumulates dim N m + jj.
+// between lanes.  Values (N = d / 16 dims per lane column): lane (column m,
+// r) reads dims N m .. N m + N - 1 of tokens 4r .. 4r+3; chunk jj
+// accumulates dim N m + jj.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -68,8 +66,6 @@ namespace {
 
 // workspace entry per (sequence, query head, split): m, l, acc[head_dim]
 constexpr int partial_floats(int head_dim) { return 2 + head_dim; }
-// waves per kv head of the split kernel (two at head_dim 256)
-constexpr int waves_per_head(int head_dim) { return head_dim > 128 ? 2 : 1; }
 constexpr float kLazy = 8.0f;               // rescale when a score passes m + 8 (base 2)
 constexpr int kMaxSplitTokens = 4096;       // block-table entries of a split staged in LDS
 constexpr int kMWaves = 8;                  // waves per workgroup
@@ -284,14 +280,14 @@ __device__ __forceinline__ void value_pairs4(const char *tab, const uint32_t (&x
     Bv[2 * K + 1] = u32x4{o0.x, o0.y, o1.x, o1.y};
 }
 
-template <int K, int NJJ>
+template <int K, int K0, int NJJ>
 __device__ __forceinline__ void value_bytes2(const char *tab, const uint32_t (&vc)[4],
                                              uint32_t laneoff, u32x4 (&Bv)[NJJ]) {
     u32x4 L[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) L[i] = lut16<K>(tab, vc[i], laneoff);
 #pragma unroll
-    for (int t = 0; t < 4; ++t) Bv[4 * K + t] = u32x4{L[0][t], L[1][t], L[2][t], L[3][t]};
+    for (int t = 0; t < 4; ++t) Bv[4 * (K - K0) + t] = u32x4{L[0][t], L[1][t], L[2][t], L[3][t]};
 }
 
 // 3-bit values: v[i] holds the lane's fields (NJJ / 2 fields of two codes)
@@ -309,35 +305,37 @@ __device__ __forceinline__ void value_fields3(const char *tab, const uint32_t (&
     }
 }
 
-// The value operands of the page for a slice of NJJ dims per lane column:
-// 4-bit NJJ / 2 bytes, 2-bit NJJ / 4 bytes, 3-bit 3 NJJ / 8 bytes.  vc holds
+// The value operands of the page for a slice of NT dims per lane column
+// (4-bit NT / 2 bytes, 2-bit NT / 4 bytes, 3-bit 3 NT / 8 bytes), built NB =
+// min(NT, 8) dims at a time: Bv[jj] is dim 8 H + jj of the slice.  vc holds
 // VW words per token as loaded (see the value loads in the split kernel);
 // vsh is the 3-bit field's bit offset within them.
-template <int NJJ, int VB, int VW>
+template <int NT, int VB, int VW, int H = 0>
 __device__ __forceinline__ void value_operands(const char *tab, const uint32_t (&vc)[4][VW],
                                                uint32_t laneoff, int q4, uint32_t vsh,
-                                               u32x4 (&Bv)[NJJ]) {
-    if constexpr (VB == 4) {
+                                               u32x4 (&Bv)[NT > 8 ? 8 : NT]) {
+    constexpr int NB = NT > 8 ? 8 : NT;
+    if constexpr (VB == 4) {             // word H: dims 8H .. 8H+7
         uint32_t x[2], y[2];
 #pragma unroll
         for (int p = 0; p < 2; ++p) {
-            const uint32_t a = vc[2 * p][0], b = vc[2 * p + 1][0];
+            const uint32_t a = vc[2 * p][H], b = vc[2 * p + 1][H];
             x[p] = (a & 0x0F0F0F0Fu) | ((b << 4) & 0xF0F0F0F0u);
             y[p] = ((a >> 4) & 0x0F0F0F0Fu) | (b & 0xF0F0F0F0u);
         }
         value_pairs4<0>(tab, x, y, laneoff, Bv);
         value_pairs4<1>(tab, x, y, laneoff, Bv);
-        if constexpr (NJJ == 8) {
+        if constexpr (NB == 8) {
             value_pairs4<2>(tab, x, y, laneoff, Bv);
             value_pairs4<3>(tab, x, y, laneoff, Bv);
         }
-    } else if constexpr (VB == 2) {
+    } else if constexpr (VB == 2) {      // bytes 2H, 2H+1
         uint32_t w[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) w[i] = vc[i][0];
-        value_bytes2<0>(tab, w, laneoff, Bv);
-        if constexpr (NJJ == 8) value_bytes2<1>(tab, w, laneoff, Bv);
-    } else if constexpr (NJJ == 8) {
+        value_bytes2<2 * H, 2 * H>(tab, w, laneoff, Bv);
+        if constexpr (NB == 8) value_bytes2<2 * H + 1, 2 * H>(tab, w, laneoff, Bv);
+    } else if constexpr (NT == 8) {
         // 24 bits at bit 24m of the slice.  Lanes m = 4a .. 4a+3 of a quad
         // loaded dwords 3a, 3a+1, 3a+2, 3a+2; lane q's field starts in the
         // dword of lane q-1 (lane 0: its own) at bit 24q mod 32.
@@ -349,14 +347,19 @@ __device__ __forceinline__ void value_operands(const char *tab, const uint32_t (
             const uint32_t lo = q4 == 0 ? vc[i][0] : prev;
             v24[i] = __builtin_amdgcn_alignbit(vc[i][0], lo, sh);
         }
-        value_fields3<NJJ>(tab, v24, laneoff, Bv);
+        value_fields3<NB>(tab, v24, laneoff, Bv);
     } else {
-        // 12 bits at bit 12m of the slice, inside the two dwords the lane
-        // loaded from the dword that holds its first bit
-        uint32_t v12[4];
+        // 3 NT bits at bit 3 NT m of the slice (12 at NT = 4, 48 at NT = 16),
+        // inside the two dwords the lane loaded from the dword that holds its
+        // first bit; half H takes bits 24H .. 24H+23
+        uint32_t v[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) v12[i] = __builtin_amdgcn_alignbit(vc[i][VW - 1], vc[i][0], vsh);
-        value_fields3<NJJ>(tab, v12, laneoff, Bv);
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t lo = __builtin_amdgcn_alignbit(vc[i][VW - 1], vc[i][0], vsh);
+            if constexpr (H == 0) v[i] = lo;
+            else v[i] = __builtin_amdgcn_alignbit(vc[i][VW - 1] >> vsh, lo, 24);
+        }
+        value_fields3<NB>(tab, v, laneoff, Bv);
     }
 }
 
@@ -374,12 +377,12 @@ struct Slices {
     // key words per lane: the slice, or at D = 64 and 3 bits (6 bytes at a
     // 2-byte offset) the two dwords around it
     static constexpr int KW = (KBY % 4) ? 2 : KBY / 4;
-    static constexpr int VH = D < 128 ? D : 128;      // value dims per wave
-    static constexpr int WPH = D / VH;                // waves per kv head
-    static constexpr int NJJ = VH / 16;               // value dims per lane column
-    // value words per lane and token: one, or at D = 64 and 3 bits (12 bits
-    // at bit 12m) the two dwords around the field
-    static constexpr int VW = (VB == 3 && NJJ == 4) ? 2 : 1;
+    static constexpr int NJJ = D / 16;                // value dims per lane column
+    // value words per lane and token: one; two for 4 bits at D = 256 (8
+    // bytes), and for 3 bits at D = 64 and 256 (12 or 48 bits at bit 3 NJJ m,
+    // not dword-aligned: the two dwords from the one holding the first bit)
+    static constexpr int VW = ((VB == 3 && NJJ != 8) || (VB == 4 && NJJ == 16)) ? 2 : 1;
+    static constexpr int NB = NJJ > 8 ? 8 : NJJ;      // value operands built at a time
     static constexpr int PK = D * KB / 8;             // packed bytes per key row
     static constexpr int PV = D * VB / 8;
 };
@@ -423,10 +426,9 @@ __device__ __forceinline__ void load_key(__amdgpu_buffer_rsrc_t rs, uint32_t off
 // matrix products instead of twice that.  Otherwise (9-16 heads) the low
 // halves take a second product per tile.
 //
-// Head dimension D: lane row group r holds score dims D/4 r .. D/4 r + D/4 - 1.
-// Each wave accumulates VH = min(D, 128) value dims; at D = 256 a kv head
-// takes two waves, which both form the full scores and accumulate one half
-// of the value dims each.
+// Head dimension D: lane row group r holds score dims D/4 r .. D/4 r + D/4 - 1,
+// and lane column m accumulates value dims D/16 m .. D/16 m + D/16 - 1.  At
+// D = 256 the value operands are built and multiplied 8 dims at a time.
 //
 // KVW kv heads per wave (KVW = 2: at most 4 query heads per kv head, head_dim
 // up to 128).  The 8 head slots of the paired tile then hold the query heads
@@ -442,13 +444,13 @@ __global__ __launch_bounds__(kMThreads) void attn_split_kernel(AttnParams p) {
     using SK = Side<KB>;
     using SV = Side<VB>;
     using SL = Slices<D, KB, VB>;
-    constexpr int DG = SL::DG, NJ = SL::NJ, NJJ = SL::NJJ, WPH = SL::WPH;
+    constexpr int DG = SL::DG, NJ = SL::NJ, NJJ = SL::NJJ, NB = SL::NB;
     constexpr int partial = 2 + D;
     using TB = Tables<KB, VB>;
     __shared__ __attribute__((aligned(256))) char tab[TB::BYTES];
     __shared__ int32_t bt_all[kMWaves][kMaxSplitTokens / kAttnBlockSize];
 
-    // The workgroup's waves form p.spw slots of kMWaves / (WPH p.spw) units of
+    // The workgroup's waves form p.spw slots of kMWaves / p.spw units of
     // KVW kv heads; slot s works on split blockIdx.x * p.spw + s (several
     // splits per workgroup when the cache has fewer kv-head units than waves).
     const int b = blockIdx.y;
@@ -457,7 +459,7 @@ __global__ __launch_bounds__(kMThreads) void attn_split_kernel(AttnParams p) {
     const int tmax = p.max_blocks * kAttnBlockSize;
     T = T > tmax ? tmax : T;
     if (p.num_blocks <= 0) T = 0;
-    const int hps = kMWaves / WPH / p.spw;                    // kv-head units per slot
+    const int hps = kMWaves / p.spw;                          // kv-head units per slot
     const int first = blockIdx.x * p.spw;
     if (first * p.split_tokens >= T) return;                 // the whole workgroup is past the context
 
@@ -474,7 +476,7 @@ __global__ __launch_bounds__(kMThreads) void attn_split_kernel(AttnParams p) {
     __syncthreads();
 
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int unit = wave / WPH, half = wave % WPH;           // kv-head unit, value half
+    const int unit = wave;                                    // kv-head unit
     const int slot = unit / hps;
     const int g = (blockIdx.z * hps + unit % hps) * KVW;      // (first) kv head
     const int split = first + slot;
@@ -572,16 +574,15 @@ __global__ __launch_bounds__(kMThreads) void attn_split_kernel(AttnParams p) {
     const uint32_t offk = (uint32_t)m * rowk + (uint32_t)g * SL::PK + (kslice & ~3u);
     const uint32_t ksh = (kslice & 3u) * 8u;                  // 3 bits at D = 64: 0 or 16
     const int q4 = m & 3;
-    const uint32_t vhalf = (uint32_t)half * (SL::VH * VB / 8);
-    const uint32_t vsh = (12u * (uint32_t)m) & 31u;           // 3 bits at D = 64
+    const uint32_t vsh = (3u * NJJ * (uint32_t)m) & 31u;      // 3 bits at D = 64, 256
     uint32_t offv[4], offn[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const uint32_t row = (uint32_t)(4 * r + i) * rowv + (uint32_t)g * SL::PV + vhalf;
+        const uint32_t row = (uint32_t)(4 * r + i) * rowv + (uint32_t)g * SL::PV;
         if (VB == 4) offv[i] = row + (uint32_t)(NJJ / 2) * m;
         else if (VB == 2) offv[i] = row + (uint32_t)(NJJ / 4) * m;
         else if (NJJ == 8) offv[i] = row + 4u * (3u * (uint32_t)(m >> 2) + (uint32_t)(q4 < 2 ? q4 : 2));
-        else offv[i] = row + 4u * ((12u * (uint32_t)m) >> 5);
+        else offv[i] = row + 4u * ((3u * NJJ * (uint32_t)m) >> 5);
         offn[i] = ((uint32_t)(4 * r + i) * p.hkv + g + kvs) * 4u;   // the column's kv head
     }
     const uint32_t pagek = kAttnBlockSize * rowk;
@@ -596,9 +597,9 @@ __global__ __launch_bounds__(kMThreads) void attn_split_kernel(AttnParams p) {
     // so each load has about one pair of pages of work in which to arrive.
     // The loads are unconditional (a page past the split re-reads the split's
     // last page, an L2 hit): straight-line loads let every wait for a page
-    // leave the later pages' loads in flight.  (At D = 256 with 4-bit keys
-    // the two slots cost a few spilled registers; measured, that is still
-    // faster than a one-slot ring.)
+    // leave the later pages' loads in flight.  (At D = 256 the kernel fills
+    // the 256 VGPRs that keep 2 waves per SIMD; with 4-bit keys and 3-bit
+    // values two values are spilled.)
     constexpr int KW = SL::KW, VW = SL::VW;
     uint32_t rk[2][KVW][KW];
     uint32_t rv[2][KVW][4][VW];
@@ -759,7 +760,7 @@ __global__ __launch_bounds__(kMThreads) void attn_split_kernel(AttnParams p) {
 
     // Value products of the page in slot d with exponents t and norms vn of
     // its 4 tokens per lane; Bv holds the value operands of kv head g.
-    auto values = [&](int d, const float *t, const float *vn, u32x4 (&Bv)[NJJ]) {
+    auto values = [&](int d, const float *t, const float *vn, u32x4 (&Bv)[NB]) {
         uint32_t w1[4], w2[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -772,7 +773,7 @@ __global__ __launch_bounds__(kMThreads) void attn_split_kernel(AttnParams p) {
             w1[i] = hh;
             w2[i] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(w - hf));
         }
-        // values: dims NJJ m + jj of the wave's half, tokens 4r .. 4r+3
+        // values: dims NJJ m + jj, tokens 4r .. 4r+3
         if constexpr (PAIRED && KVW == 2) {
             // rows 0-7: (w_hi, w_hi) of head slots 0-7; rows 8-15: (w_lo, 0);
             // the rows of the other kv head are zero in each product
@@ -788,7 +789,12 @@ __global__ __launch_bounds__(kMThreads) void attn_split_kernel(AttnParams p) {
             // rows 0-7: (w_hi, w_hi) of heads 0-7; rows 8-15: (w_lo, 0)
             const u32x4 A = lo_col ? u32x4{w2[0], w2[1], w2[2], w2[3]} : u32x4{w1[0], w1[1], w1[2], w1[3]};
 #pragma unroll
-            for (int jj = 0; jj < NJJ; ++jj) acc[jj] = mfma(A, Bv[jj], acc[jj]);
+            for (int jj = 0; jj < NB; ++jj) acc[jj] = mfma(A, Bv[jj], acc[jj]);
+            if constexpr (NJJ > NB) {        // the second 8 value dims of each lane column
+                value_operands<NJJ, VB, VW, 1>(tab, rv[d][0], lov, q4, vsh, Bv);
+#pragma unroll
+                for (int jj = 0; jj < NB; ++jj) acc[NB + jj] = mfma(A, Bv[jj], acc[NB + jj]);
+            }
         } else {
             const u32x4 A1 = u32x4{w1[0], w1[1], w1[2], w1[3]};
             const u32x4 A2 = u32x4{w2[0], w2[1], w2[2], w2[3]};
@@ -815,7 +821,7 @@ __global__ __launch_bounds__(kMThreads) void attn_split_kernel(AttnParams p) {
         fetch_keys(bA, 0);
         S[1] = scores(1);
         fetch_keys(bB, 1);
-        u32x4 Bv[NJJ];   // value codes of kv head g (KVW = 2: g + 1's follow in values())
+        u32x4 Bv[NB];    // value codes of kv head g (KVW = 2: g + 1's follow in values())
         value_operands<NJJ, VB, VW>(tab, rv[0][0], lov, q4, vsh, Bv);
         const int pgs[2] = {pg0, pg0 + 1}, ds[2] = {0, 1};
         float t[8], vn[8];
@@ -829,7 +835,7 @@ __global__ __launch_bounds__(kMThreads) void attn_split_kernel(AttnParams p) {
     if (pg0 < npages) {                       // the last page of an odd count, in slot 0
         f4 S[1];
         S[0] = scores(0);
-        u32x4 Bv[NJJ];
+        u32x4 Bv[NB];
         value_operands<NJJ, VB, VW>(tab, rv[0][0], lov, q4, vsh, Bv);
         const int pgs[1] = {pg0}, ds[1] = {0};
         float t[4], vn[4];
@@ -849,12 +855,12 @@ __global__ __launch_bounds__(kMThreads) void attn_split_kernel(AttnParams p) {
     }
     // partial state of head g*grp + h: m and l from the lane of h's column,
     // accumulators from lanes (column c, row s / 4) at register s % 4 (s: the
-    // head slot of h) -> dims NJJ c .. NJJ c + NJJ - 1 of the wave's value
-    // half.  KVW = 2: slot s holds head (s / 4) grp + s % 4.
+    // head slot of h) -> dims NJJ c .. NJJ c + NJJ - 1.  KVW = 2: slot s
+    // holds head (s / 4) grp + s % 4.
     const float unscale = vlim / (kLevelScale * 64.0f);     // undo 16 c and 2^6 / vlim
     float *base = p.ws + (((size_t)b * p.hq + (size_t)g * grp) * p.num_splits + split) * partial;
     const size_t hstride = (size_t)p.num_splits * partial;
-    if (r == 0 && hv && !lo_col && half == 0) {
+    if (r == 0 && hv && !lo_col) {
         float *dst = base + (size_t)(KVW == 2 ? kvs * grp + hh : m) * hstride;
         dst[0] = M;
         dst[1] = lsum;
@@ -868,7 +874,7 @@ __global__ __launch_bounds__(kMThreads) void attn_split_kernel(AttnParams p) {
         } else {
             if (h >= grp || (PAIRED && r >= 2)) break;
         }
-        float2 *dst = reinterpret_cast<float2 *>(base + (size_t)h * hstride + 2 + SL::VH * half + NJJ * m);   // 8-byte aligned
+        float2 *dst = reinterpret_cast<float2 *>(base + (size_t)h * hstride + 2 + NJJ * m);   // 8-byte aligned
 #pragma unroll
         for (int jj = 0; jj < NJJ; jj += 2) dst[jj >> 1] = float2(acc[jj][i] * unscale, acc[jj + 1][i] * unscale);
     }
@@ -1054,10 +1060,10 @@ int attn_kv_per_wave(const AttnShape &s) {
 }
 
 int attn_split_tokens(const AttnShape &s) {
-    // waves_per_head waves per (sequence, unit of attn_kv_per_wave kv heads)
-    // and split; about kMTargetWaves waves
+    // one wave per (sequence, unit of attn_kv_per_wave kv heads) and split;
+    // about kMTargetWaves waves
     const int ctx = s.max_blocks * kAttnBlockSize;
-    const int units = s.batch * s.num_kv_heads / attn_kv_per_wave(s) * waves_per_head(s.head_dim);
+    const int units = s.batch * s.num_kv_heads / attn_kv_per_wave(s);
     const int per_seq = units > 0 ? (kMTargetWaves + units - 1) / units : 1;
     int st = (ctx + per_seq - 1) / per_seq;
     st = (st + kAttnBlockSize - 1) / kAttnBlockSize * kAttnBlockSize;
@@ -1107,7 +1113,7 @@ hipError_t launch_attn(const AttnShape &s, const CodecConsts &kc, const CodecCon
     // spare waves take further splits
     const int kvw = attn_kv_per_wave(s);
     const int units = s.num_kv_heads / kvw;                   // per split
-    const int upw = kMWaves / waves_per_head(s.head_dim);     // units per workgroup
+    const int upw = kMWaves;                                  // units per workgroup
     p.spw = (units < upw && upw % units == 0) ? upw / units : 1;
     const int ups = upw / p.spw;
     const dim3 grid((p.num_splits + p.spw - 1) / p.spw, s.batch, (units + ups - 1) / ups);

@@ -149,6 +149,15 @@ def test_head_dim_mixed_widths(dev, d, kb, vb):
              Hq=16, Hkv=4, T=300, d=d)
 
 
+@pytest.mark.parametrize("kb,vb", [(4, 3), (3, 2), (2, 4)])
+def test_head_dim_256_remaining_widths(dev, kb, vb):
+    """The width pairs at head_dim 256 not covered above (4-bit keys with 3-bit
+    values is the instance whose registers overflow by two values), over
+    several splits with a ragged last page."""
+    run_attn(dev, "d=256 keys %d bits, values %d bits" % (kb, vb), bits=kb, v_bits=vb, B=2,
+             Hq=8, Hkv=2, T=2500, ragged=True, d=256)
+
+
 @pytest.mark.parametrize("d,Hq,Hkv", [(64, 32, 2), (64, 8, 8), (64, 24, 8), (256, 16, 2),
                                       (256, 8, 8), (256, 4, 1), (256, 24, 8)])
 def test_head_dim_gqa(dev, d, Hq, Hkv):
