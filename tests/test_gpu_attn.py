@@ -201,9 +201,9 @@ def test_scale_and_peaked_softmax(dev):
     run_attn(dev, "scale 0.02", B=2, Hq=8, Hkv=2, T=300, scale=0.02)
 
 
-def _c5(dev, ragged, samples, vb=4, B=16, Hq=32, Hkv=8, T=32768, heads_per_sample=None):
+def _c5(dev, ragged, samples, vb=4, B=16, Hq=32, Hkv=8, T=32768, heads_per_sample=None, d=D):
     """Batch 16, 32/8 heads, 32768 tokens, 4-bit keys (values: vb bits), in the
-    launch configuration the benchmark times (or another shape).  The sampled
+    launch configuration the benchmark times (or another shape or head_dim).  The sampled
     (sequence, kv head) streams hold oracle-encoded N(0,1)+outlier data; the
     rest of the cache is random codes.  The first heads_per_sample query heads
     of each sampled kv head are compared (default: all of the group)."""
@@ -213,16 +213,16 @@ def _c5(dev, ragged, samples, vb=4, B=16, Hq=32, Hkv=8, T=32768, heads_per_sampl
     maxb = T // bs
     nblk = B * maxb
     rng = np.random.default_rng(502)
-    kp = rng.integers(0, 256, (nblk, bs, Hkv, 64), dtype=np.uint8)
-    vp = rng.integers(0, 256, (nblk, bs, Hkv, 16 * vb), dtype=np.uint8)
+    kp = rng.integers(0, 256, (nblk, bs, Hkv, d // 2), dtype=np.uint8)
+    vp = rng.integers(0, 256, (nblk, bs, Hkv, d * vb // 8), dtype=np.uint8)
     kn = rng.uniform(8, 14, (nblk, bs, Hkv)).astype(np.float32)
     vn = rng.uniform(8, 14, (nblk, bs, Hkv)).astype(np.float32)
-    q = W.attn_query(B, Hq)
+    q = W.attn_query(B, Hq, head_dim=d)
     bt = W.attn_block_tables(B, maxb, nblk)
     cl = W.attn_context_lens(B, T, ragged)
     sel = np.zeros((B, Hq), bool)
     for b, g in samples:
-        kv = W.attn_kv_rows(b, g, T)
+        kv = W.attn_kv_rows(b, g, T, head_dim=d)
         p_k, n_k = oracle_encode_parallel(kv[0], 4, 0)
         p_v, n_v = oracle_encode_parallel(kv[1], vb, 0)
         W.scatter_pages(kp, p_k, bt[b], g)
@@ -230,18 +230,18 @@ def _c5(dev, ragged, samples, vb=4, B=16, Hq=32, Hkv=8, T=32768, heads_per_sampl
         W.scatter_pages(vp, p_v, bt[b], g)
         W.scatter_pages(vn, n_v, bt[b], g)
         sel[b, g * grp:g * grp + hps] = True
-    P.log("[attn] full size B=%d Hq=%d Hkv=%d T=%d ragged=%s values %d bits samples=%s"
-          % (B, Hq, Hkv, T, ragged, vb, samples))
-    tq = TurboQuant(D, 4, 0, dev)
-    attn = TQPagedAttention(tq, Hq, v_tq=TurboQuant(D, vb, 0, dev))
+    P.log("[attn] full size B=%d Hq=%d Hkv=%d T=%d d=%d ragged=%s values %d bits samples=%s"
+          % (B, Hq, Hkv, T, d, ragged, vb, samples))
+    tq = TurboQuant(d, 4, 0, dev)
+    attn = TQPagedAttention(tq, Hq, v_tq=TurboQuant(d, vb, 0, dev))
     t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
     out = attn.forward(t(q), t(kp), t(kn), t(vp), t(vn), t(bt), t(cl))
     torch.cuda.synchronize()
     g = out.cpu().numpy()
     assert np.all(np.isfinite(g.astype(np.float64)))
-    _, ref = oracle.attn_decode(q, kp, kn, vp, vn, bt, cl, Hkv, 4, 0, 1 / math.sqrt(D),
+    _, ref = oracle.attn_decode(q, kp, kn, vp, vn, bt, cl, Hkv, 4, 0, 1 / math.sqrt(d),
                                 sel=sel, want_f64=True, v_bits=vb)
-    P.compare_attn(g[sel], ref[sel], "full size ragged=%s values %d bits" % (ragged, vb))
+    P.compare_attn(g[sel], ref[sel], "full size d=%d ragged=%s values %d bits" % (d, ragged, vb))
 
 
 def test_full_size_batch16_32k(dev):
@@ -254,6 +254,12 @@ def test_full_size_batch16_ragged(dev):
 
 def test_full_size_batch16_k4_v2(dev):
     _c5(dev, True, [(5, 2), (14, 6)], vb=2)
+
+
+def test_full_size_batch16_32k_d256(dev):
+    """head_dim 256 at batch 16 x 32K (the benchmark's launch: 16 splits of
+    2,048 tokens, one wave per kv head), ragged lengths."""
+    _c5(dev, True, [(3, 1), (12, 6)], d=256)
 
 
 def test_long_context_batch1_128k(dev):
