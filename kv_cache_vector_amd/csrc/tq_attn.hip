@@ -76,6 +76,9 @@ constexpr int kMThreads = 64 * kMWaves;
 // round much slower, and 12-wave workgroups at 168 VGPRs (3 waves per SIMD,
 // 3072 waves) slower too
 constexpr int kMTargetWaves = 2048;
+// Share of a split (in 64ths) that each even split takes from the odd split
+// after it when the two share a SIMD (see split_bounds).
+constexpr int kSkew64 = 8;
 constexpr float kLevelScale = 16.0f;        // binary16 levels are 16 c
 constexpr float kWShift = 6.0f;             // value weights carry 2^6
 constexpr int kLutRow = 256;                // bytes per table row (64 banks of 4 bytes)
@@ -100,11 +103,24 @@ struct AttnParams {
     uint16_t *out;
     int batch, hq, hkv, max_blocks, split_tokens, num_splits;
     int spw;             // splits per workgroup of the split kernel
+    int skew;            // tokens moved from each odd split to the even split before it
     int64_t num_blocks;
     float qscale;        // scale * log2(e) / head_dim
     CodecConsts k;       // key codebook and the sign mask (shared by keys and values)
     CodecConsts v;       // value codebook
 };
+
+// Token range [t0, t1) of a context split (t1 clipped to the context T).
+// Splits are split_tokens long, except that each even split takes `skew`
+// more tokens and the odd split after it `skew` fewer: the two run as
+// waves w and w + 4 of one workgroup, which share a SIMD, and the SIMD's
+// issue arbiter favours the older wave.
+__device__ __forceinline__ void split_bounds(const AttnParams &p, int split, int T, int &t0, int &t1) {
+    const int odd = split & 1;
+    t0 = split * p.split_tokens + (odd ? p.skew : 0);
+    const int e = (split + 1) * p.split_tokens + (odd ? 0 : p.skew);
+    t1 = e < T ? e : T;
+}
 
 __device__ __forceinline__ float half_bits_to_float(uint32_t h) {
     return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
@@ -466,9 +482,9 @@ __global__ __launch_bounds__(kMThreads) void attn_split_kernel(AttnParams p) {
     fill_table<KB>(tab + TB::KOFF, p.k);
     if constexpr (!TB::SHARED) fill_table<VB>(tab + TB::VOFF, p.v);
     for (int sl = 0; sl < p.spw; ++sl) {                      // block-table entries of every slot
-        const int u0 = (first + sl) * p.split_tokens;
+        int u0, u1;
+        split_bounds(p, first + sl, T, u0, u1);
         if (u0 >= T) break;
-        const int u1 = (u0 + p.split_tokens < T) ? u0 + p.split_tokens : T;
         const int np = (u1 - u0 + kAttnBlockSize - 1) / kAttnBlockSize;
         const int32_t *bt = p.block_tables + (size_t)b * p.max_blocks + u0 / kAttnBlockSize;
         for (int i = threadIdx.x; i < np; i += kMThreads) bt_all[sl][i] = bt[i];
@@ -480,9 +496,9 @@ __global__ __launch_bounds__(kMThreads) void attn_split_kernel(AttnParams p) {
     const int slot = unit / hps;
     const int g = (blockIdx.z * hps + unit % hps) * KVW;      // (first) kv head
     const int split = first + slot;
-    const int t0 = split * p.split_tokens;
+    int t0, t1;
+    split_bounds(p, split, T, t0, t1);
     if (g >= p.hkv || t0 >= T) return;                        // no barrier follows
-    const int t1 = (t0 + p.split_tokens < T) ? t0 + p.split_tokens : T;
     const int npages = (t1 - t0 + kAttnBlockSize - 1) / kAttnBlockSize;
     const int32_t *bt_lds = bt_all[slot];
     const int lane = threadIdx.x & 63;
@@ -894,7 +910,10 @@ __global__ __launch_bounds__(64) void attn_combine_kernel(AttnParams p) {
     const int tmax = p.max_blocks * kAttnBlockSize;
     T = T > tmax ? tmax : T;
     if (p.num_blocks <= 0) T = 0;
-    const int ns = (T + p.split_tokens - 1) / p.split_tokens;
+    int ns = (T + p.split_tokens - 1) / p.split_tokens;
+    // the last of these splits is empty when it is odd and the even split
+    // before it (skew tokens longer) reaches T; it wrote no partial
+    if (ns > 0 && ((ns - 1) & 1) && (ns - 1) * p.split_tokens + p.skew >= T) --ns;
     const float *src = p.ws + (size_t)bh * p.num_splits * partial;
 
     // the largest running maximum over the splits (lane s reads split s)
@@ -1115,6 +1134,12 @@ hipError_t launch_attn(const AttnShape &s, const CodecConsts &kc, const CodecCon
     const int units = s.num_kv_heads / kvw;                   // per split
     const int upw = kMWaves;                                  // units per workgroup
     p.spw = (units < upw && upw % units == 0) ? upw / units : 1;
+    p.skew = 0;
+    if (p.spw == 2) {            // slots 0 and 1: even and odd splits, waves w and w + 4
+        int sk = p.split_tokens * kSkew64 / 64 / kAttnBlockSize * kAttnBlockSize;
+        if (p.split_tokens + sk > kMaxSplitTokens) sk = kMaxSplitTokens - p.split_tokens;
+        p.skew = sk;
+    }
     const int ups = upw / p.spw;
     const dim3 grid((p.num_splits + p.spw - 1) / p.spw, s.batch, (units + ups - 1) / ups);
     const dim3 block(kMThreads);

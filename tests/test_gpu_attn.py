@@ -121,6 +121,15 @@ def test_context_lengths(dev, T):
     run_attn(dev, "T=%d" % T, B=4, Hq=32, Hkv=8, T=T, ragged=(T > 3))
 
 
+@pytest.mark.parametrize("T", [270, 288, 289, 788, 800, 801])
+def test_split_pair_boundaries(dev, T):
+    """Contexts ending inside or at the edge of an odd split that its even
+    partner has grown into (at 4 x 8 kv heads the splits are 256 tokens, each
+    even split taking 32 of the next one's): the odd split is empty for 257-288
+    and 769-800 tokens, and one token long at 289 and 801."""
+    run_attn(dev, "split pairs T=%d" % T, B=4, Hq=32, Hkv=8, T=T, ragged=False)
+
+
 @pytest.mark.parametrize("d", [64, 128, 256])
 @pytest.mark.parametrize("bits", [4, 3, 2])
 def test_single_token_rounding(dev, d, bits):
