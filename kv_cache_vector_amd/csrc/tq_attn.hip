@@ -122,6 +122,40 @@ __device__ __forceinline__ void split_bounds(const AttnParams &p, int split, int
     t1 = e < T ? e : T;
 }
 
+// The value of lane l ^ S (S = 16 or 32) of a wave, from gfx950's
+// v_permlane16_swap / v_permlane32_swap with both operands v: a VALU
+// exchange, where a shuffle through ds_bpermute would take an LDS round
+// trip.  permlane16_swap(a, b) trades the odd 16-lane rows of a with the
+// even rows of b, so the first result holds row r ^ 1 in the odd rows and
+// the second in the even rows; permlane32_swap trades rows 2-3 of a with
+// rows 0-1 of b in the same way.
+// Within a 16-lane row the exchange is a DPP move: quad permutations for 1
+// and 2, the row shifted by 4 lanes one way or the other for 4 (row_shl
+// reads lane l + 4, row_shr lane l - 4), the row rotated by 8 for 8.
+template <int S>
+__device__ __forceinline__ float lane_xor(float v) {
+    static_assert(S == 1 || S == 2 || S == 4 || S == 8 || S == 16 || S == 32, "power of two below 64");
+    const uint32_t u = __builtin_bit_cast(uint32_t, v);
+    const bool hi = (threadIdx.x & S) != 0;
+    if constexpr (S == 1) {
+        return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0u, u, 0xB1, 0xF, 0xF, false));   // quad_perm [1,0,3,2]
+    } else if constexpr (S == 2) {
+        return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0u, u, 0x4E, 0xF, 0xF, false));   // quad_perm [2,3,0,1]
+    } else if constexpr (S == 4) {
+        const uint32_t up = __builtin_amdgcn_update_dpp(0u, u, 0x104, 0xF, 0xF, false);   // row_shl:4
+        const uint32_t dn = __builtin_amdgcn_update_dpp(0u, u, 0x114, 0xF, 0xF, false);   // row_shr:4
+        return __builtin_bit_cast(float, hi ? dn : up);
+    } else if constexpr (S == 8) {
+        return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0u, u, 0x128, 0xF, 0xF, false));  // row_ror:8
+    } else if constexpr (S == 16) {
+        const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+        return __builtin_bit_cast(float, hi ? r[0] : r[1]);
+    } else {
+        const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+        return __builtin_bit_cast(float, hi ? r[0] : r[1]);
+    }
+}
+
 __device__ __forceinline__ float half_bits_to_float(uint32_t h) {
     return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
 }
@@ -194,19 +228,39 @@ struct Tables {
                                         : 65536 + (KB == 3 ? Side<KB>::BYTES : Side<VB>::BYTES);
 };
 
+// Thread t = 64 w + l writes 16-byte piece l % 16 of entries e = 32 i + 4 w + r
+// (r = l / 16, i < NE / 32).  Every code index is then either wave-uniform,
+// read as a scalar, or a uniform base plus r, one of four scalars: the table
+// needs no per-lane load, so it is built without waiting on the vector loads
+// the kernel has in flight.
 template <int B>
 __device__ __forceinline__ void fill_table(char *tab, const CodecConsts &k) {
     using S = Side<B>;
-    for (int t = threadIdx.x; t < S::NE * (kLutRow / 16); t += kMThreads) {
-        const int e = t / (kLutRow / 16), c = t % (kLutRow / 16);   // entry, 16-byte piece of its row
+    constexpr int IT = S::NE * (kLutRow / 16) / kMThreads;
+    static_assert(IT * kMThreads == S::NE * (kLutRow / 16), "whole rounds of the workgroup");
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int r = (threadIdx.x >> 4) & 3, c = threadIdx.x & 15;
+    auto lvl = [&](int code) -> uint32_t {        // code wave-uniform
+        return level_pair(k, __builtin_amdgcn_readfirstlane(code));
+    };
+    auto lane_lvl = [&](int base) -> uint32_t {   // code base + r
+        const uint32_t a0 = lvl(base), a1 = lvl(base + 1), a2 = lvl(base + 2), a3 = lvl(base + 3);
+        return r == 0 ? a0 : (r == 1 ? a1 : (r == 2 ? a2 : a3));
+    };
+    // 4 bits: codes e % 16 = 4 (w % 4) + r and e / 16 = 2 i + w / 4; 3 bits:
+    // e % 8 = 4 (w % 2) + r and e / 8 = 4 i + w / 2; 2 bits: e % 4 = r,
+    // (e / 4) % 4 = w % 4, (e / 16) % 4 = (2 i + w / 4) % 4, e / 64 = i / 2
+    const uint32_t a = (B == 4) ? lane_lvl(4 * (w & 3)) : (B == 3 ? lane_lvl(4 * (w & 1)) : lane_lvl(0));
+    const uint32_t b2 = (B == 2) ? lvl(w & 3) : 0u;
+#pragma unroll
+    for (int i = 0; i < IT; ++i) {
+        const int e = 32 * i + 4 * w + r;
         u32x4 v;
         if constexpr (B == 2) {
-            v = u32x4{level_pair(k, e & 3), level_pair(k, (e >> 2) & 3), level_pair(k, (e >> 4) & 3),
-                      level_pair(k, e >> 6)};
+            v = u32x4{a, b2, lvl((2 * i + (w >> 2)) & 3), lvl(i >> 1)};
         } else {
-            constexpr int SH = B == 4 ? 4 : 3;
-            const uint32_t a = level_pair(k, e & ((1 << SH) - 1)), b = level_pair(k, e >> SH);
-            v = u32x4{a, b, a, b};
+            const uint32_t hi = (B == 4) ? lvl(2 * i + (w >> 2)) : lvl(4 * i + (w >> 1));
+            v = u32x4{a, hi, a, hi};
         }
         *reinterpret_cast<u32x4 *>(tab + e * kLutRow + 16 * c) = v;
     }
@@ -479,18 +533,6 @@ __global__ __launch_bounds__(kMThreads) void attn_split_kernel(AttnParams p) {
     const int first = blockIdx.x * p.spw;
     if (first * p.split_tokens >= T) return;                 // the whole workgroup is past the context
 
-    fill_table<KB>(tab + TB::KOFF, p.k);
-    if constexpr (!TB::SHARED) fill_table<VB>(tab + TB::VOFF, p.v);
-    for (int sl = 0; sl < p.spw; ++sl) {                      // block-table entries of every slot
-        int u0, u1;
-        split_bounds(p, first + sl, T, u0, u1);
-        if (u0 >= T) break;
-        const int np = (u1 - u0 + kAttnBlockSize - 1) / kAttnBlockSize;
-        const int32_t *bt = p.block_tables + (size_t)b * p.max_blocks + u0 / kAttnBlockSize;
-        for (int i = threadIdx.x; i < np; i += kMThreads) bt_all[sl][i] = bt[i];
-    }
-    __syncthreads();
-
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int unit = wave;                                    // kv-head unit
     const int slot = unit / hps;
@@ -498,8 +540,8 @@ __global__ __launch_bounds__(kMThreads) void attn_split_kernel(AttnParams p) {
     const int split = first + slot;
     int t0, t1;
     split_bounds(p, split, T, t0, t1);
-    if (g >= p.hkv || t0 >= T) return;                        // no barrier follows
-    const int npages = (t1 - t0 + kAttnBlockSize - 1) / kAttnBlockSize;
+    const bool live = g < p.hkv && t0 < T;                    // wave-uniform
+    const int npages = live ? (t1 - t0 + kAttnBlockSize - 1) / kAttnBlockSize : 0;
     const int32_t *bt_lds = bt_all[slot];
     const int lane = threadIdx.x & 63;
     const int m = lane & 15, r = lane >> 4;
@@ -511,77 +553,6 @@ __global__ __launch_bounds__(kMThreads) void attn_split_kernel(AttnParams p) {
     const bool hv = hh < grp;                                 // a real query head column
     const uint32_t lok = TB::KOFF + (uint32_t)(lane & (SK::COPIES - 1)) * SK::EB;
     const uint32_t lov = TB::VOFF + (uint32_t)(lane & (SV::COPIES - 1)) * SV::EB;
-
-    // ---- rotated query, one head per lane column, dims DG r .. DG r + DG - 1 ----
-    u32x4 bq1[NJ], bq2[PAIRED ? 1 : NJ];
-    float qsl;
-    {
-        float qv[DG];
-        const int mq = hv ? hh : 0;                           // padding columns read head 0, then drop it
-        const uint16_t *qp = p.q + ((size_t)b * p.hq + (size_t)(g + kvs) * grp + mq) * D + DG * r;
-        // all loads first (the address is valid for padding columns too),
-        // then the padding zeroed: one memory latency instead of one per load
-        uint16_t qh[DG];
-#pragma unroll
-        for (int e = 0; e < DG; ++e) qh[e] = qp[e];
-#pragma unroll
-        for (int e = 0; e < DG; ++e) {
-            const float v = hv ? half_bits_to_float(qh[e]) : 0.0f;
-            qv[e] = sign_of(p.k, DG * r + e) ? -v : v;
-        }
-#pragma unroll
-        for (int s = 1; s < DG; s <<= 1)
-#pragma unroll
-            for (int e = 0; e < DG; ++e) {
-                if (e & s) continue;
-                const float a = qv[e], c = qv[e + s];
-                qv[e] = a + c;
-                qv[e + s] = a - c;
-            }
-#pragma unroll
-        for (int s = 16; s < 64; s <<= 1)
-#pragma unroll
-            for (int e = 0; e < DG; ++e) {
-                const float o = __shfl_xor(qv[e], s);
-                qv[e] = (lane & s) ? (o - qv[e]) : (qv[e] + o);
-            }
-        // per-head power of two bringing max |q~| to [2^13, 2^14)
-        float amax = 0.0f;
-#pragma unroll
-        for (int e = 0; e < DG; ++e) amax = __builtin_fmaxf(amax, __builtin_fabsf(qv[e]));
-        amax = __builtin_fmaxf(amax, __shfl_xor(amax, 16));
-        amax = __builtin_fmaxf(amax, __shfl_xor(amax, 32));
-        int ex = amax > 0.0f ? __builtin_amdgcn_frexp_expf(amax) : 14;   // amax in [2^(ex-1), 2^ex)
-        ex = ex < -100 ? -100 : ex;
-        const float sc = __builtin_bit_cast(float, (uint32_t)(127 + 14 - ex) << 23);   // 2^(14 - ex)
-        qsl = p.qscale / (sc * kLevelScale);
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) {
-            uint32_t w1[4], w2[4];
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                const float v = qv[4 * j + t] * sc;
-                const _Float16 hi = (_Float16)v;
-                const _Float16 lo = (_Float16)(v - (float)hi);
-                w1[t] = pack_half2(hi, hi);
-                w2[t] = pack_half2(lo, (_Float16)0.0f);
-            }
-            if constexpr (PAIRED) {
-                bq1[j] = lo_col ? u32x4{w2[0], w2[1], w2[2], w2[3]} : u32x4{w1[0], w1[1], w1[2], w1[3]};
-            } else {
-                bq1[j] = u32x4{w1[0], w1[1], w1[2], w1[3]};
-                bq2[j] = u32x4{w2[0], w2[1], w2[2], w2[3]};
-            }
-        }
-    }
-
-    f4 acc[NJJ];
-#pragma unroll
-    for (int jj = 0; jj < NJJ; ++jj) acc[jj] = f4{0.0f, 0.0f, 0.0f, 0.0f};
-    float M = -__builtin_inff();          // base-2 reference of head m (uniform over r)
-    float lsum = 0.0f;                    // sum of exp2(s - M) over this lane's tokens
-    float vlim = 0.0f;                    // power of two above every value norm seen (wave-uniform)
-    float vscale = 0.0f;                  // 2^6 / vlim
 
     // per-lane byte offsets inside one page of this kv head
     const uint32_t rowk = (uint32_t)p.hkv * SL::PK;           // one token of all kv heads
@@ -662,6 +633,143 @@ __global__ __launch_bounds__(kMThreads) void attn_split_kernel(AttnParams p) {
     auto bt_at = [&](int pg) -> int32_t {
         return __builtin_amdgcn_readfirstlane(bt_lds[pg < npages ? pg : npages - 1]);
     };
+
+    // Vector loads count down in issue order, so a load the prologue uses must
+    // be issued before the first pages' loads, or using it would wait for
+    // them too: first the lane's query slice and the block-table entries of
+    // the wave's slot (copied to LDS by the slot's waves), then the first two
+    // pages, whose block ids are read straight from the block table, so that
+    // they arrive while the tables are built and the query is rotated.
+    // Every one of these loads is issued unconditionally, at a valid address
+    // (a wave without work reads the first query, the start of the block
+    // table and block 0), so that no path merge makes the compiler wait for
+    // all loads at once.
+    constexpr int QV = DG / 8;                                // 16-byte pieces of the query slice
+    u32x4 qraw[QV];
+    {
+        // padding columns read head 0, then drop it
+        const uint16_t *qp = live ? p.q + ((size_t)b * p.hq + (size_t)(g + kvs) * grp + (hv ? hh : 0)) * D + DG * r
+                                  : p.q;
+#pragma unroll
+        for (int j = 0; j < QV; ++j) qraw[j] = reinterpret_cast<const u32x4 *>(qp)[j];
+    }
+    int s0, s1;
+    split_bounds(p, first + slot, T, s0, s1);
+    const int np_slot = s0 < T ? (s1 - s0 + kAttnBlockSize - 1) / kAttnBlockSize : 0;
+    const int32_t *bts = p.block_tables + (size_t)b * p.max_blocks + (np_slot > 0 ? s0 / kAttnBlockSize : 0);
+    constexpr int kCopy = kMaxSplitTokens / kAttnBlockSize / 64;   // entries per lane at one wave per slot
+    const int cbase = (unit % hps) * 64 + lane, cstride = hps * 64;
+    int32_t bv[kCopy];
+#pragma unroll
+    for (int k = 0; k < kCopy; ++k) {
+        const int i = cbase + k * cstride;
+        bv[k] = bts[i < np_slot ? i : 0];
+    }
+    {
+        const int32_t *btg = p.block_tables + (size_t)b * p.max_blocks + (live ? t0 / kAttnBlockSize : 0);
+        const int32_t b0 = __builtin_amdgcn_readfirstlane(btg[0]);
+        const int32_t b1 = __builtin_amdgcn_readfirstlane(btg[npages > 1 ? 1 : 0]);
+        fetch_keys(b0, 0);
+        fetch_values(0, b0, 0);
+        fetch_keys(b1, 1);
+        fetch_values(1, b1, 1);
+    }
+
+    fill_table<KB>(tab + TB::KOFF, p.k);
+    if constexpr (!TB::SHARED) fill_table<VB>(tab + TB::VOFF, p.v);
+#pragma unroll
+    for (int k = 0; k < kCopy; ++k) {
+        const int i = cbase + k * cstride;
+        if (i < np_slot) bt_all[slot][i] = bv[k];
+    }
+    // the barrier orders the LDS writes only: the page loads stay in flight
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+
+    if (!live) {                                              // no barrier follows
+        __builtin_amdgcn_s_waitcnt(0);                        // its loads end before the wave
+        return;
+    }
+
+    // ---- rotated query, one head per lane column, dims DG r .. DG r + DG - 1 ----
+    u32x4 bq1[NJ], bq2[PAIRED ? 1 : NJ];
+    float qsl;
+    {
+        float qv[DG];
+        // the sign words of dims DG r .. DG r + DG - 1, selected from scalar reads
+        constexpr int NW = DG >= 32 ? DG / 32 : 1;
+        uint32_t sw[NW];
+#pragma unroll
+        for (int j = 0; j < NW; ++j) {
+            const int widx = (DG * r) / 32 + j;
+            // (readfirstlane keeps each word a scalar value: a select of the
+            // words themselves would become one per-lane load)
+            uint32_t v = __builtin_amdgcn_readfirstlane(p.k.sign[0]);
+#pragma unroll
+            for (int q = 1; q < D / 32; ++q) v = (widx == q) ? __builtin_amdgcn_readfirstlane(p.k.sign[q]) : v;
+            sw[j] = v;
+        }
+#pragma unroll
+        for (int e = 0; e < DG; ++e) {
+            const uint32_t wq = qraw[e >> 3][(e >> 1) & 3];
+            const float v = hv ? half_bits_to_float((e & 1) ? (wq >> 16) : (wq & 0xFFFFu)) : 0.0f;
+            const int i = DG * r + e;
+            qv[e] = ((sw[DG >= 32 ? (e >> 5) : 0] >> (i & 31)) & 1u) ? -v : v;
+        }
+#pragma unroll
+        for (int s = 1; s < DG; s <<= 1)
+#pragma unroll
+            for (int e = 0; e < DG; ++e) {
+                if (e & s) continue;
+                const float a = qv[e], c = qv[e + s];
+                qv[e] = a + c;
+                qv[e + s] = a - c;
+            }
+#pragma unroll
+        for (int s = 16; s < 64; s <<= 1)
+#pragma unroll
+            for (int e = 0; e < DG; ++e) {
+                const float o = __shfl_xor(qv[e], s);
+                qv[e] = (lane & s) ? (o - qv[e]) : (qv[e] + o);
+            }
+        // per-head power of two bringing max |q~| to [2^13, 2^14)
+        float amax = 0.0f;
+#pragma unroll
+        for (int e = 0; e < DG; ++e) amax = __builtin_fmaxf(amax, __builtin_fabsf(qv[e]));
+        amax = __builtin_fmaxf(amax, __shfl_xor(amax, 16));
+        amax = __builtin_fmaxf(amax, __shfl_xor(amax, 32));
+        int ex = amax > 0.0f ? __builtin_amdgcn_frexp_expf(amax) : 14;   // amax in [2^(ex-1), 2^ex)
+        ex = ex < -100 ? -100 : ex;
+        const float sc = __builtin_bit_cast(float, (uint32_t)(127 + 14 - ex) << 23);   // 2^(14 - ex)
+        qsl = p.qscale / (sc * kLevelScale);
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+            uint32_t w1[4], w2[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const float v = qv[4 * j + t] * sc;
+                const _Float16 hi = (_Float16)v;
+                const _Float16 lo = (_Float16)(v - (float)hi);
+                w1[t] = pack_half2(hi, hi);
+                w2[t] = pack_half2(lo, (_Float16)0.0f);
+            }
+            if constexpr (PAIRED) {
+                bq1[j] = lo_col ? u32x4{w2[0], w2[1], w2[2], w2[3]} : u32x4{w1[0], w1[1], w1[2], w1[3]};
+            } else {
+                bq1[j] = u32x4{w1[0], w1[1], w1[2], w1[3]};
+                bq2[j] = u32x4{w2[0], w2[1], w2[2], w2[3]};
+            }
+        }
+    }
+
+    f4 acc[NJJ];
+#pragma unroll
+    for (int jj = 0; jj < NJJ; ++jj) acc[jj] = f4{0.0f, 0.0f, 0.0f, 0.0f};
+    float M = -__builtin_inff();          // base-2 reference of head m (uniform over r)
+    float lsum = 0.0f;                    // sum of exp2(s - M) over this lane's tokens
+    float vlim = 0.0f;                    // power of two above every value norm seen (wave-uniform)
+    float vscale = 0.0f;                  // 2^6 / vlim
 
     // scores of the page in slot d: tokens 4r .. 4r+3 for head column hcol
     auto scores = [&](int d) -> f4 {
@@ -822,13 +930,6 @@ __global__ __launch_bounds__(kMThreads) void attn_split_kernel(AttnParams p) {
         }
     };
 
-    {
-        const int32_t b0 = bt_at(0), b1 = bt_at(1);
-        fetch_keys(b0, 0);
-        fetch_values(0, b0, 0);
-        fetch_keys(b1, 1);
-        fetch_values(1, b1, 1);
-    }
     int pg0 = 0;
     for (; pg0 + 2 <= npages; pg0 += 2) {     // wave-uniform
         const int32_t bA = bt_at(pg0 + 2), bB = bt_at(pg0 + 3);
@@ -925,11 +1026,12 @@ __global__ __launch_bounds__(64) void attn_combine_kernel(AttnParams p) {
             mx = ms > mx ? ms : mx;
         }
     }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-        const float other = __shfl_xor(mx, o);
-        mx = other > mx ? other : mx;
-    }
+    mx = __builtin_fmaxf(mx, lane_xor<32>(mx));
+    mx = __builtin_fmaxf(mx, lane_xor<16>(mx));
+    mx = __builtin_fmaxf(mx, lane_xor<8>(mx));
+    mx = __builtin_fmaxf(mx, lane_xor<4>(mx));
+    mx = __builtin_fmaxf(mx, lane_xor<2>(mx));
+    mx = __builtin_fmaxf(mx, lane_xor<1>(mx));
     // split weights, then this lane's coordinates; the partials of G splits
     // are loaded before any of them is accumulated (G = 32 at head_dim up to
     // 128: a 32-split merge takes one round of loads)
@@ -975,8 +1077,12 @@ __global__ __launch_bounds__(64) void attn_combine_kernel(AttnParams p) {
             }
         }
     }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) lsum += __shfl_xor(lsum, o);
+    lsum += lane_xor<32>(lsum);
+    lsum += lane_xor<16>(lsum);
+    lsum += lane_xor<8>(lsum);
+    lsum += lane_xor<4>(lsum);
+    lsum += lane_xor<2>(lsum);
+    lsum += lane_xor<1>(lsum);
     const float inv = (lsum > 0.0f) ? 1.0f / lsum : 0.0f;
     // inverse transform: x = D H acc / D -- the low log2(E) coordinate bits
     // in registers, the next 6 across lanes
@@ -992,13 +1098,20 @@ __global__ __launch_bounds__(64) void attn_combine_kernel(AttnParams p) {
             x[e] = u + v;
             x[e + st] = u - v;
         }
-#pragma unroll
-    for (int s = 1; s < 64; s <<= 1)
+    auto cross = [&](auto sc) {          // the stage across lanes l and l ^ S
+        constexpr int S = decltype(sc)::value;
 #pragma unroll
         for (int e = 0; e < E; ++e) {
-            const float o = __shfl_xor(x[e], s);
-            x[e] = (lane & s) ? (o - x[e]) : (x[e] + o);
+            const float o = lane_xor<S>(x[e]);
+            x[e] = (lane & S) ? (o - x[e]) : (x[e] + o);
         }
+    };
+    cross(std::integral_constant<int, 1>{});
+    cross(std::integral_constant<int, 2>{});
+    cross(std::integral_constant<int, 4>{});
+    cross(std::integral_constant<int, 8>{});
+    cross(std::integral_constant<int, 16>{});
+    cross(std::integral_constant<int, 32>{});
     uint16_t hv[E];
 #pragma unroll
     for (int e = 0; e < E; ++e) {
