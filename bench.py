@@ -571,7 +571,7 @@ def codec_side_measurement(torch, dev, stream, x, packed, norms):
 
 
 def attention_measurement(torch, dev, stream, reps: int = 20, head_dim: int = 128,
-                          warmup: int = 5):
+                          warmup: int = 10):
     """Median (and minimum) time of tq_attn_decode (split + combine kernels) at batch 16,
     32/8 heads, 32768 tokens, 4 bits, random codes and a random block
     permutation, with the last-level cache evicted before each call, after
