@@ -1017,9 +1017,53 @@ __global__ __launch_bounds__(64) void attn_combine_kernel(AttnParams p) {
     if (ns > 0 && ((ns - 1) & 1) && (ns - 1) * p.split_tokens + p.skew >= T) --ns;
     const float *src = p.ws + (size_t)bh * p.num_splits * partial;
 
-    // the largest running maximum over the splits (lane s reads split s)
-    float mx = -__builtin_inff();
-    for (int s0 = 0; s0 < ns; s0 += 64) {
+    // The partials of the first G splits and the (m, l) pairs of the first 64
+    // (lane s: split s) are loaded together, before the maximum is formed:
+    // one round of loads for up to G splits instead of three in a row.
+    constexpr int G = E <= 2 ? 32 : 16;
+    auto load_batch = [&](float (&ev)[G][E], int s0, int j0, int cnt) {
+#pragma unroll
+        for (int u = 0; u < G; ++u) {
+            const int j = (j0 + u < cnt) ? j0 + u : j0;          // in range; weight 0 below
+            const float *q = src + (size_t)(s0 + j) * partial + 2 + E * lane;
+            if constexpr (E == 1) {
+                ev[u][0] = *q;
+            } else {
+                // entries are 4 (2 + D) bytes, so only 8-byte alignment holds
+#pragma unroll
+                for (int e = 0; e < E; e += 2) {
+                    const float2 v = *reinterpret_cast<const float2 *>(q + e);
+                    ev[u][e] = v.x;
+                    ev[u][e + 1] = v.y;
+                }
+            }
+        }
+    };
+    float a[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) a[e] = 0.0f;
+    auto accumulate = [&](const float (&ev)[G][E], int j0, int cnt, float w) {
+#pragma unroll
+        for (int u = 0; u < G; ++u) {
+            float wj = __builtin_bit_cast(
+                float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), (j0 + u) & 63));
+            wj = (j0 + u < cnt) ? wj : 0.0f;
+#pragma unroll
+            for (int e = 0; e < E; ++e) a[e] = __builtin_fmaf(wj, ev[u][e], a[e]);
+        }
+    };
+    const int cnt0 = ns < 64 ? ns : 64;
+    float m0 = -__builtin_inff(), l0 = 0.0f;
+    if (lane < cnt0) {
+        m0 = src[(size_t)lane * partial];
+        l0 = src[(size_t)lane * partial + 1];
+    }
+    float ev0[G][E];
+    load_batch(ev0, 0, 0, cnt0);          // in range even for no split (never accumulated then)
+
+    // the largest running maximum over the splits (lane s holds split s)
+    float mx = m0;
+    for (int s0 = 64; s0 < ns; s0 += 64) {
         const int s = s0 + lane;
         if (s < ns) {
             const float ms = src[(size_t)s * partial];
@@ -1032,49 +1076,31 @@ __global__ __launch_bounds__(64) void attn_combine_kernel(AttnParams p) {
     mx = __builtin_fmaxf(mx, lane_xor<4>(mx));
     mx = __builtin_fmaxf(mx, lane_xor<2>(mx));
     mx = __builtin_fmaxf(mx, lane_xor<1>(mx));
-    // split weights, then this lane's coordinates; the partials of G splits
-    // are loaded before any of them is accumulated (G = 32 at head_dim up to
-    // 128: a 32-split merge takes one round of loads)
-    constexpr int G = E <= 2 ? 32 : 16;
+    // split weights, then this lane's coordinates, G splits per round of loads
     float lsum = 0.0f;
-    float a[E];
-#pragma unroll
-    for (int e = 0; e < E; ++e) a[e] = 0.0f;
     for (int s0 = 0; s0 < ns; s0 += 64) {
         const int s = s0 + lane;
         float w = 0.0f;
-        if (s < ns) {
+        if (s0 == 0) {
+            if (lane < cnt0) {
+                w = (l0 > 0.0f) ? __builtin_amdgcn_exp2f(m0 - mx) : 0.0f;
+                lsum += w * l0;
+            }
+        } else if (s < ns) {
             const float ls = src[(size_t)s * partial + 1];
             w = (ls > 0.0f) ? __builtin_amdgcn_exp2f(src[(size_t)s * partial] - mx) : 0.0f;
             lsum += w * ls;
         }
         const int cnt = (ns - s0 < 64) ? ns - s0 : 64;
-        for (int j0 = 0; j0 < cnt; j0 += G) {
+        int j0 = 0;
+        if (s0 == 0) {
+            accumulate(ev0, 0, cnt, w);
+            j0 = G;
+        }
+        for (; j0 < cnt; j0 += G) {
             float ev[G][E];
-#pragma unroll
-            for (int u = 0; u < G; ++u) {
-                const int j = (j0 + u < cnt) ? j0 + u : j0;          // in range; weight 0 below
-                const float *q = src + (size_t)(s0 + j) * partial + 2 + E * lane;
-                if constexpr (E == 1) {
-                    ev[u][0] = *q;
-                } else {
-                    // entries are 4 (2 + D) bytes, so only 8-byte alignment holds
-#pragma unroll
-                    for (int e = 0; e < E; e += 2) {
-                        const float2 v = *reinterpret_cast<const float2 *>(q + e);
-                        ev[u][e] = v.x;
-                        ev[u][e + 1] = v.y;
-                    }
-                }
-            }
-#pragma unroll
-            for (int u = 0; u < G; ++u) {
-                float wj = __builtin_bit_cast(
-                    float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), (j0 + u) & 63));
-                wj = (j0 + u < cnt) ? wj : 0.0f;
-#pragma unroll
-                for (int e = 0; e < E; ++e) a[e] = __builtin_fmaf(wj, ev[u][e], a[e]);
-            }
+            load_batch(ev, s0, j0, cnt);
+            accumulate(ev, j0, cnt, w);
         }
     }
     lsum += lane_xor<32>(lsum);
