@@ -121,6 +121,14 @@ def test_context_lengths(dev, T):
     run_attn(dev, "T=%d" % T, B=4, Hq=32, Hkv=8, T=T, ragged=(T > 3))
 
 
+@pytest.mark.parametrize("Hq,Hkv", [(12, 6), (10, 5), (6, 3), (30, 6)])
+def test_idle_waves(dev, Hq, Hkv):
+    """kv-head counts whose units do not fill a workgroup's 8 waves (3 units
+    of two kv heads; 5 or 3 single kv heads): the idle waves issue their
+    prologue loads at clamped addresses and return before the main loop."""
+    run_attn(dev, "idle waves %d/%d" % (Hq, Hkv), B=3, Hq=Hq, Hkv=Hkv, T=700)
+
+
 @pytest.mark.parametrize("T", [270, 288, 289, 788, 800, 801])
 def test_split_pair_boundaries(dev, T):
     """Contexts ending inside or at the edge of an odd split that its even
