@@ -410,6 +410,11 @@ def side_measurements(torch, dev, stream, x, packed, norms):
     codes; head_dim 128, 64 and 256), the 70B-class 128K-context cache
     encoded as a layer-by-layer stream (2 bits), and other codec launch
     shapes."""
+    # one second idle first, so that the attention figures start from the
+    # same settled clocks as `--attn-only` rather than right after the
+    # codec's sustained load
+    torch.cuda.synchronize()
+    time.sleep(1.0)
     res = attention_measurement(torch, dev, stream)
     for hd in (64, 256):
         res.update(attention_measurement(torch, dev, stream, head_dim=hd))
