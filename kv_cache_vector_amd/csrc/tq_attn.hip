@@ -960,15 +960,15 @@ __global__ __launch_bounds__(kMThreads) void attn_split_kernel(AttnParams p) {
         values(0, t, vn, Bv);
     }
 
-    lsum += __shfl_xor(lsum, 16);
-    lsum += __shfl_xor(lsum, 32);
+    lsum += lane_xor<16>(lsum);
+    lsum += lane_xor<32>(lsum);
     if constexpr (PAIRED) {
         // rows 4r + i and 4r + i + 8 (lanes l and l ^ 32) are one head's
         // high and low parts
 #pragma unroll
         for (int jj = 0; jj < NJJ; ++jj)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) acc[jj][i] += __shfl_xor(acc[jj][i], 32);
+            for (int i = 0; i < 4; ++i) acc[jj][i] += lane_xor<32>(acc[jj][i]);
     }
     // partial state of head g*grp + h: m and l from the lane of h's column,
     // accumulators from lanes (column c, row s / 4) at register s % 4 (s: the
