@@ -369,6 +369,12 @@ def main() -> int:
     }
     if clocks:
         extra["clocks_MHz_after_timed_steps"] = clocks
+    props = torch.cuda.get_device_properties(dev)
+    extra["device"] = {k: getattr(props, a) for k, a in (
+        ("arch", "gcnArchName"), ("compute_units", "multi_processor_count"),
+        ("lds_bytes_per_workgroup", "shared_memory_per_block"),
+        ("threads_per_cu", "max_threads_per_multi_processor"), ("l2_bytes", "L2_cache_size"),
+        ("hbm_bytes", "total_memory")) if hasattr(props, a)}
     # achievable-bandwidth reference: the no-arithmetic kernels that move the
     # codec's own byte mix with its work mapping (include/tq_ceiling.h)
     extra.update(ceiling_measurement(torch, stream, x, packed, norms, out, enc_avg, dec_avg))
