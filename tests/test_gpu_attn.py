@@ -279,6 +279,12 @@ def test_full_size_batch16_32k_d256(dev):
     _c5(dev, True, [(3, 1), (12, 6)], d=256)
 
 
+def test_full_size_batch16_32k_d64(dev):
+    """head_dim 64 at batch 16 x 32K (the benchmark's launch: 32 splits, two
+    kv heads per wave, skewed split pairs), fixed lengths."""
+    _c5(dev, False, [(4, 0), (13, 7)], d=64)
+
+
 def test_long_context_batch1_128k(dev):
     """One 131,072-token sequence, 64 query / 8 kv heads: 512 context splits
     merged by the combine kernel."""
