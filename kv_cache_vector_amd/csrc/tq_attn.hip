@@ -122,8 +122,9 @@ __device__ __forceinline__ void split_bounds(const AttnParams &p, int split, int
     t1 = e < T ? e : T;
 }
 
-// The value of lane l ^ S (S = 16 or 32) of a wave, from gfx950's
-// v_permlane16_swap / v_permlane32_swap with both operands v: a VALU
+// The value of lane l ^ S of a wave (S a power of two below 64).  For S = 16
+// and 32 it comes from gfx950's v_permlane16_swap / v_permlane32_swap with
+// both operands v: a VALU
 // exchange, where a shuffle through ds_bpermute would take an LDS round
 // trip.  permlane16_swap(a, b) trades the odd 16-lane rows of a with the
 // even rows of b, so the first result holds row r ^ 1 in the odd rows and
