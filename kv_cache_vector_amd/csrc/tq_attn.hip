@@ -124,12 +124,11 @@ __device__ __forceinline__ void split_bounds(const AttnParams &p, int split, int
 
 // The value of lane l ^ S of a wave (S a power of two below 64).  For S = 16
 // and 32 it comes from gfx950's v_permlane16_swap / v_permlane32_swap with
-// both operands v: a VALU
-// exchange, where a shuffle through ds_bpermute would take an LDS round
-// trip.  permlane16_swap(a, b) trades the odd 16-lane rows of a with the
-// even rows of b, so the first result holds row r ^ 1 in the odd rows and
-// the second in the even rows; permlane32_swap trades rows 2-3 of a with
-// rows 0-1 of b in the same way.
+// both operands v: a VALU exchange, where a shuffle through ds_bpermute
+// would take an LDS round trip.  permlane16_swap(a, b) trades the odd 16-lane
+// rows of a with the even rows of b, so the first result holds row r ^ 1 in
+// the odd rows and the second in the even rows; permlane32_swap trades rows
+// 2-3 of a with rows 0-1 of b in the same way.
 // Within a 16-lane row the exchange is a DPP move: quad permutations for 1
 // and 2, the row shifted by 4 lanes one way or the other for 4 (row_shl
 // reads lane l + 4, row_shr lane l - 4), the row rotated by 8 for 8.
