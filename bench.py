@@ -275,6 +275,8 @@ def main() -> int:
                     help="head_dim of the --attn-only measurement")
     ap.add_argument("--attn-only", action="store_true",
                     help="only the batch-16 x 32K decode-attention measurement (for profiling)")
+    ap.add_argument("--attn-warmup", type=int, default=100,
+                    help="untimed attention calls before the timed ones (--attn-only)")
     ap.add_argument("--hybrid-only", action="store_true",
                     help="only the hybrid-mode (tq35 / tq25) whole-cache measurement (for profiling)")
     args = ap.parse_args()
@@ -290,7 +292,7 @@ def main() -> int:
         torch.cuda.set_device(dev)
         res = attention_measurement(torch, dev, torch.cuda.current_stream(dev),
                                     reps=max(1, args.steps), head_dim=args.head_dim,
-                                    warmup=max(1, args.warmup))
+                                    warmup=max(1, args.attn_warmup))
         print(json.dumps(res), flush=True)
         return 0
 
@@ -416,14 +418,14 @@ def side_measurements(torch, dev, stream, x, packed, norms):
     codes; head_dim 128, 64 and 256), the 70B-class 128K-context cache
     encoded as a layer-by-layer stream (2 bits), and other codec launch
     shapes."""
-    # one second idle first, so that the attention figures start from the
-    # same settled clocks as `--attn-only` rather than right after the
-    # codec's sustained load
-    torch.cuda.synchronize()
-    time.sleep(1.0)
+    # 100 untimed calls (about 20 ms) before each attention measurement let
+    # the clocks settle under the attention's own load (the first follows the
+    # codec's sustained load)
     res = attention_measurement(torch, dev, stream)
     for hd in (64, 256):
         res.update(attention_measurement(torch, dev, stream, head_dim=hd))
+    for kb, vb in ((4, 2), (3, 3), (2, 2)):        # other widths at head_dim 128
+        res.update(attention_measurement(torch, dev, stream, k_bits=kb, v_bits=vb))
     res.update(stream_encode_measurement(torch, dev, stream, x, packed, norms))
     res.update(codec_side_measurement(torch, dev, stream, x, packed, norms))
     res.update(hybrid_measurement(torch, dev, stream, x))
@@ -582,13 +584,14 @@ def codec_side_measurement(torch, dev, stream, x, packed, norms):
 
 
 def attention_measurement(torch, dev, stream, reps: int = 20, head_dim: int = 128,
-                          warmup: int = 10):
-    """Median (and minimum) time of tq_attn_decode (split + combine kernels) at batch 16,
-    32/8 heads, 32768 tokens, 4 bits, random codes and a random block
-    permutation, with the last-level cache evicted before each call, after
-    `warmup` untimed calls (the first calls run while the clocks rise).  The
-    keys are named attn_batch16_32k_* at head_dim 128 and carry a _d<D>
-    suffix otherwise."""
+                          warmup: int = 100, k_bits: int = 4, v_bits: int = 4):
+    """Median (and minimum) time of tq_attn_decode_kv (split + combine kernels) at
+    batch 16, 32/8 heads, 32768 tokens, 4-bit keys and values unless stated,
+    random codes and a random block permutation, with the last-level cache
+    evicted before each call, after `warmup` untimed calls (the first calls
+    run while the clocks rise).  The keys are named attn_batch16_32k_* at
+    head_dim 128 and 4/4 bits, with a _d<D> suffix at another head_dim and a
+    _k<kb>v<vb> suffix at other widths."""
     from kv_cache_vector_amd import _lib
     import math
     s = stream.cuda_stream
@@ -598,9 +601,9 @@ def attention_measurement(torch, dev, stream, reps: int = 20, head_dim: int = 12
     nblk = B * maxb
     g = torch.Generator(device=dev).manual_seed(5)
     d = head_dim
-    P = d * 4 // 8                       # packed bytes per row at 4 bits
-    kp = torch.randint(0, 256, (nblk, bs, Hkv, P), dtype=torch.uint8, device=dev, generator=g)
-    vp = torch.randint(0, 256, (nblk, bs, Hkv, P), dtype=torch.uint8, device=dev, generator=g)
+    PK, PV = d * k_bits // 8, d * v_bits // 8     # packed bytes per key / value row
+    kp = torch.randint(0, 256, (nblk, bs, Hkv, PK), dtype=torch.uint8, device=dev, generator=g)
+    vp = torch.randint(0, 256, (nblk, bs, Hkv, PV), dtype=torch.uint8, device=dev, generator=g)
     kn = torch.rand((nblk, bs, Hkv), device=dev, generator=g) * 6 + 8
     vn = torch.rand((nblk, bs, Hkv), device=dev, generator=g) * 6 + 8
     q = torch.randn((B, Hq, d), device=dev, generator=g).half()
@@ -614,11 +617,11 @@ def attention_measurement(torch, dev, stream, reps: int = 20, head_dim: int = 12
     flush = torch.ones(512 * 1024 * 1024 // 4, dtype=torch.float32, device=dev)
 
     def attn():
-        _lib.check(_lib.tq_attn_decode(q.data_ptr(), kp.data_ptr(), kn.data_ptr(),
-                                       vp.data_ptr(), vn.data_ptr(), bt.data_ptr(),
-                                       cl.data_ptr(), B, Hq, Hkv, d, 4, 0, bs, maxb, nblk,
-                                       1 / math.sqrt(d), out.data_ptr(), ws.data_ptr(), wsb,
-                                       s), "tq_attn_decode")
+        _lib.check(_lib.tq_attn_decode_kv(q.data_ptr(), kp.data_ptr(), kn.data_ptr(),
+                                          vp.data_ptr(), vn.data_ptr(), bt.data_ptr(),
+                                          cl.data_ptr(), B, Hq, Hkv, d, k_bits, v_bits, 0, bs,
+                                          maxb, nblk, 1 / math.sqrt(d), out.data_ptr(),
+                                          ws.data_ptr(), wsb, s), "tq_attn_decode_kv")
 
     for _ in range(max(1, warmup)):
         flush.sum()
@@ -634,9 +637,9 @@ def attention_measurement(torch, dev, stream, reps: int = 20, head_dim: int = 12
         torch.cuda.synchronize()
         times.append(e0.elapsed_time(e1))
     t_us = statistics.median(times) * 1e3
-    res["attn_batch16_32k_min_us" + ("" if head_dim == 128 else "_d%d" % head_dim)] = round(min(times) * 1e3, 1)
-    packed_bytes = B * Hkv * T * 2 * (P + 4)
-    sfx = "" if d == 128 else "_d%d" % d
+    sfx = ("" if d == 128 else "_d%d" % d) + ("" if (k_bits, v_bits) == (4, 4) else "_k%dv%d" % (k_bits, v_bits))
+    res["attn_batch16_32k_min_us" + sfx] = round(min(times) * 1e3, 1)
+    packed_bytes = B * Hkv * T * (PK + 4 + PV + 4)
     res["attn_batch16_32k_us" + sfx] = round(t_us, 1)
     res["attn_packed_GBps" + sfx] = round(packed_bytes / (t_us * 1e-6) / 1e9, 1)
     res["attn_fp16_equiv_GBps" + sfx] = round(B * Hkv * T * 2 * 2 * d / (t_us * 1e-6) / 1e9, 1)
